@@ -1,0 +1,188 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache codec for AMD Instinct MI355X
+ * (gfx950).  One shared library, libtq.so; plain pointers and sizes only.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [Engine]  "TurboQuantEngine — Specification": 2.1 Accuracy contract,
+ *             2.2 Memory contract (fp32 norm + ceil(d*bits/8) packed bytes per
+ *             head row), 3 Codec, 6 P1 follow-ups (append-only encode of the
+ *             new row; compressed-domain attention).
+ *   [Foundry] "TurboQuant KV Cache Compression — Spec": Overview, As-Built
+ *             Notes (signs before the Hadamard; L2-norm normalisation),
+ *             Algorithm Detail steps 1-3, API (init / cache / quantize /
+ *             dequantize / attention), Integration Points (circular
+ *             addressing pos % max_seq), Hadamard Transform Detail,
+ *             Optimization: Fused dequant-dot.
+ *   [KVC]     "Implementation specification: TurboAngle and TurboQuant-style
+ *             KV compression": Core implementation contract (rows [B, d],
+ *             power-of-two d, K and V may use different codecs).
+ *
+ * Conventions shared by every call
+ *   - Return value: TQ_OK (0) or a negative tq_status.  The message of the
+ *     last failure on the calling thread is returned by tq_last_error().
+ *     Nothing is printed; no C++ exception crosses this boundary.
+ *   - Device pointers are HIP device allocations owned by the caller; the
+ *     library allocates no device memory and keeps no device state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls are asynchronous on that stream and never synchronise;
+ *     faults during execution surface at the caller's next synchronisation.
+ *   - Row layout: a row is one head vector of d coordinates.  Packed row r of
+ *     a buffer starts at byte r * tq_packed_row_bytes(d, bits); index i of a
+ *     row occupies bits [i*bits, (i+1)*bits) of the row's little-endian
+ *     bitstream (3-bit rows are dense: 8 indices per 3 bytes).
+ *   - Alignment: fp32/bf16 row buffers and norm buffers 4-byte aligned;
+ *     packed buffers 16-byte aligned.  Misaligned pointers -> TQ_EINVAL.
+ *   - Device kernels accept d in {64, 128, 256} and bits in {2, 3, 4};
+ *     other valid values return TQ_EUNSUPPORTED.
+ *   - n_rows == 0 (or an empty context) succeeds and launches nothing.
+ *   - Non-finite inputs are not screened: outputs for such rows are
+ *     unspecified, but every access stays inside the buffers described here.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_EINVAL = -1,        /* invalid argument (null, size, alignment, shape) */
+    TQ_EUNSUPPORTED = -2,  /* valid, but no device kernel for this case */
+    TQ_EHIP = -3           /* the HIP runtime reported an error at launch */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+/* Coordinate density a codebook is optimised for.
+ *   TQ_BETA_HALF_D    Beta(d/2, d/2) mapped to [-1, 1]: [Foundry] Step 2.
+ *   TQ_GAUSS_1_OVER_D N(0, 1/d): [Atlas citations page] "Prior art" item 4.
+ * Every call below other than tq_codebook_init_density uses TQ_BETA_HALF_D. */
+typedef enum { TQ_BETA_HALF_D = 0, TQ_GAUSS_1_OVER_D = 1 } tq_density;
+
+/* Lloyd-Max scalar quantiser for one (d, bits, density), in units of a
+ * unit-norm coordinate ([Foundry] Step 2's fa_tq_codebook, plus d, density
+ * and the expected per-coordinate squared error under the density).
+ * centroids[0..levels-1] increase; boundaries[0..levels-2] are midpoints of
+ * neighbouring centroids; the table is symmetric and the middle boundary is
+ * exactly 0. Unused trailing entries are 0. */
+typedef struct {
+    int32_t d;
+    int32_t bits;
+    int32_t levels;
+    int32_t density;
+    float centroids[16];
+    float boundaries[15];
+    double distortion_per_coord;
+} tq_codebook;
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char *tq_last_error(void);
+
+/* Library version string. */
+const char *tq_version(void);
+
+/* Host only, synchronous, thread-safe, memoised.  d: power of two in
+ * [2, 2^20]; bits: 1..4.  [Foundry] "Codebook Generation": Lloyd iteration
+ * (boundaries = midpoints, centroids = conditional means) run to
+ * convergence.  TQ_EINVAL on bad d/bits/density or a NULL out. */
+int tq_codebook_init(int d, int bits, tq_codebook *out);
+int tq_codebook_init_density(int d, int bits, int density, tq_codebook *out);
+
+/* Host only.  The rotation's sign diagonal D ([Foundry] Step 1: generated once
+ * from a seed and reused for every row, head and layer): out_pm1[i] = -1 when
+ * the top bit of the i-th SplitMix64 output for `seed` is set, else +1.
+ * d in [1, 2^20]. */
+int tq_signs(int d, uint64_t seed, int8_t *out_pm1);
+
+/* Bytes of one packed row: d * bits / 8 rounded up ([Engine] 2.2).  0 when
+ * d <= 0 or bits outside 1..8. */
+size_t tq_packed_row_bytes(int d, int bits);
+
+/* Rotation only, for checking the transform on the device.
+ * Forward (inverse == 0): out = H (D x) / sqrt(d)   ([Foundry] As-Built 1).
+ * Inverse (inverse != 0): out = D (H x) / sqrt(d)    ([Foundry] Hadamard
+ * Transform Detail: H/sqrt(d) and D are each their own inverse).
+ * in: [n_rows][d] of `dtype` (device); out: [n_rows][d] fp32 (device). */
+int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint64_t seed,
+              int inverse, float *out, void *stream);
+
+/* Encode K and/or V rows ([Foundry] Steps 1-3 with As-Built 2; [KVC] K and V
+ * may use different bit widths).  Per row x: n = ||x||_2 (fp32, stored),
+ * u = H (D x) / (sqrt(d) n) (u = 0 when n = 0), idx_i = #{j : b_j < u_i}
+ * against the (d, bits) boundaries, indices bit-packed.
+ * k_rows / v_rows: [n_rows][d] of `dtype` (device); either side may be NULL
+ * (its outputs are then ignored) but not both.
+ * k_packed: [n_rows][d*bits_k/8], k_norms: [n_rows] (device, written).
+ * Same for v_*.  One kernel launch covers both sides. */
+int tq_encode(const void *k_rows, const void *v_rows, int dtype, int64_t n_rows,
+              int d, int bits_k, int bits_v, uint64_t seed, uint8_t *k_packed,
+              float *k_norms, uint8_t *v_packed, float *v_norms, void *stream);
+
+/* Decode ([Foundry] Step 2 lookup, then the inverse rotation):
+ * out = D H (n * c[idx]) / sqrt(d), fp32 [n_rows][d] (device).
+ * packed: [n_rows][d*bits/8], norms: [n_rows] (device, read). */
+int tq_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
+              int bits, uint64_t seed, float *out, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Ring-buffer KV cache ([Foundry] API "Cache" and Integration Points:
+ * per-head [n_kv_heads, max_seq, head_dim] layout, slot = pos % window).
+ * The descriptor is a host struct; every buffer it points to is a caller-
+ * owned device allocation.  Layer l holds, for K and for V,
+ *   packed [batch][n_kv_heads][window][head_dim[l] * bits / 8] bytes
+ *   norms  [batch][n_kv_heads][window] floats.                               */
+#define TQ_MAX_LAYERS 256
+
+typedef struct {
+    int32_t n_layers;         /* 1..TQ_MAX_LAYERS */
+    int32_t batch;            /* sequences */
+    int32_t n_kv_heads;
+    int32_t window;           /* ring slots per (sequence, head) */
+    int32_t bits_k, bits_v;
+    uint64_t seed;            /* sign seed shared by K, V and q */
+    const int32_t *head_dim;  /* host array [n_layers] */
+    uint8_t *const *k_packed; /* host array [n_layers] of device pointers */
+    float *const *k_norms;
+    uint8_t *const *v_packed;
+    float *const *v_norms;
+} tq_cache_desc;
+
+/* Append-only encode of the new K and V rows ([Engine] 6, W3: encode only the
+ * new row) into slot pos % window ([Foundry] Integration Points).
+ * layer = -1 appends to every layer (one launch per distinct head_dim);
+ * otherwise only that layer.  k_new / v_new are host arrays of device
+ * pointers with n_layers entries (layer = -1) or 1 entry; entry i points to
+ * [batch][n_kv_heads][head_dim] rows of `dtype`.  pos >= 0. */
+int tq_append_row(const tq_cache_desc *cache, int layer, const void *const *k_new,
+                  const void *const *v_new, int dtype, int64_t pos, void *stream);
+
+/* Workspace bytes tq_attn_decode needs for this (cache, layer, n_q_heads,
+ * ctx_len); 0 on invalid arguments. */
+size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
+                               int n_q_heads, int64_t ctx_len);
+
+/* Decode-step attention over the compressed cache of one layer, in the
+ * rotated domain ([Foundry] Optimization: Fused dequant-dot; [Engine] 6
+ * "Compressed-domain attention"): q' = H (D q) / sqrt(d) once per head;
+ * score_t = scale * n_t <q', c_K[idx_t]>; softmax over t; o' = sum_t p_t
+ * n^V_t c_V[idx^V_t]; out = D H o' / sqrt(d).  Equal, up to rounding, to
+ * softmax attention over the decoded rows.
+ * q_bf16: [batch][n_q_heads][d] bf16 (device).  Query head h reads KV head
+ * h / (n_q_heads / n_kv_heads); n_q_heads must be a multiple of n_kv_heads
+ * with a ratio of 1, 2, 4 or 8.  Context = slots [0, min(ctx_len, window)).
+ * scale <= 0 selects 1/sqrt(d).  out: [batch][n_q_heads][d] fp32 (device).
+ * workspace: device buffer of at least tq_attn_workspace_bytes(...) bytes,
+ * 16-byte aligned; its contents need no initialisation.  ctx_len >= 1. */
+int tq_attn_decode(const tq_cache_desc *cache, int layer, const uint16_t *q_bf16,
+                   int n_q_heads, int64_t ctx_len, float scale, float *out,
+                   void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,223 @@
+"""TurboQuant KV-cache codec on AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libtq.so`` (declared in include/tq.h).
+The functions here only marshal arguments -- torch tensors supply device
+memory and the current HIP stream -- and every step of the codec runs in the
+library's HIP kernels.  There is no CPU fallback: if the library or a GPU is
+missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import (TQ_BETA_HALF_D, TQ_BF16, TQ_EHIP, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_F32,
+                   TQ_GAUSS_1_OVER_D, TQ_MAX_LAYERS, TQ_OK, TqCodebook, TqError, lib,
+                   library_path)
+
+__all__ = [
+    "TqError", "TQCache", "lib", "library_path", "tq_codebook_init", "tq_signs",
+    "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
+    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
+    "TQ_F32", "TQ_BF16", "TQ_BETA_HALF_D", "TQ_GAUSS_1_OVER_D", "TQ_OK", "TQ_EINVAL",
+    "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS",
+]
+
+_DTYPES = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
+
+
+def _check(rc: int, fn: str):
+    if rc != TQ_OK:
+        raise TqError(rc, f"{fn}: {lib().tq_last_error().decode()}")
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def tq_last_error() -> str:
+    return lib().tq_last_error().decode()
+
+
+def tq_version() -> str:
+    return lib().tq_version().decode()
+
+
+def tq_codebook_init(d: int, bits: int, density: int = TQ_BETA_HALF_D) -> dict:
+    cb = TqCodebook()
+    _check(lib().tq_codebook_init_density(d, bits, density, ctypes.byref(cb)),
+           "tq_codebook_init")
+    L = cb.levels
+    return {
+        "d": cb.d, "bits": cb.bits, "levels": L, "density": cb.density,
+        "centroids": np.array(cb.centroids[:L], np.float32),
+        "boundaries": np.array(cb.boundaries[: L - 1], np.float32),
+        "distortion_per_coord": cb.distortion_per_coord,
+    }
+
+
+def tq_signs(d: int, seed: int) -> np.ndarray:
+    out = np.zeros(d, np.int8)
+    _check(lib().tq_signs(d, ctypes.c_uint64(seed), out.ctypes.data_as(ctypes.c_void_p)),
+           "tq_signs")
+    return out
+
+
+def tq_packed_row_bytes(d: int, bits: int) -> int:
+    return int(lib().tq_packed_row_bytes(d, bits))
+
+
+def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, stream=None):
+    """Rotation only: out = H(D x)/sqrt(d) (or D H x / sqrt(d) when inverse)."""
+    d = x.shape[-1]
+    n = x.numel() // d if d else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check(lib().tq_rotate(_dev(x, "x"), _DTYPES[x.dtype], n, d, ctypes.c_uint64(seed),
+                           1 if inverse else 0, _dev(out, "out", torch.float32), _stream(stream)),
+           "tq_rotate")
+    return out
+
+
+def tq_encode(k: torch.Tensor | None, v: torch.Tensor | None, bits_k: int, bits_v: int,
+              seed: int, k_packed=None, k_norms=None, v_packed=None, v_norms=None,
+              stream=None):
+    """Encode K and/or V rows ([..., d], fp32 or bf16) in one launch.
+    Returns (k_packed, k_norms, v_packed, v_norms) with None for a missing side."""
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("tq_encode: k and v are both None")
+    d = ref.shape[-1]
+    n = ref.numel() // d
+    lead = ref.shape[:-1]
+    if k is not None and v is not None and (k.shape != v.shape or k.dtype != v.dtype):
+        raise ValueError("tq_encode: k and v must have the same shape and dtype")
+    dt = _DTYPES[ref.dtype]
+    args = []
+    outs = []
+    for x, bits, pk, nm in ((k, bits_k, k_packed, k_norms), (v, bits_v, v_packed, v_norms)):
+        if x is None:
+            args += [None, None, None]
+            outs += [None, None]
+            continue
+        rb = tq_packed_row_bytes(d, bits)
+        if pk is None:
+            pk = torch.empty(*lead, rb, dtype=torch.uint8, device=x.device)
+        if nm is None:
+            nm = torch.empty(*lead, dtype=torch.float32, device=x.device)
+        if pk.numel() != n * rb or nm.numel() != n:
+            raise ValueError("tq_encode: output buffers have the wrong size")
+        args += [_dev(x, "rows"), _dev(pk, "packed", torch.uint8), _dev(nm, "norms", torch.float32)]
+        outs += [pk, nm]
+    _check(lib().tq_encode(args[0], args[3], dt, n, d, bits_k, bits_v, ctypes.c_uint64(seed),
+                           args[1], args[2], args[4], args[5], _stream(stream)), "tq_encode")
+    return tuple(outs)
+
+
+def tq_decode(packed: torch.Tensor, norms: torch.Tensor, d: int, bits: int, seed: int,
+              out=None, stream=None):
+    n = norms.numel()
+    rb = tq_packed_row_bytes(d, bits)
+    if packed.numel() != n * rb:
+        raise ValueError("tq_decode: packed size does not match norms")
+    if out is None:
+        out = torch.empty(*norms.shape, d, dtype=torch.float32, device=packed.device)
+    if out.numel() != n * d:
+        raise ValueError("tq_decode: out has the wrong size")
+    _check(lib().tq_decode(_dev(packed, "packed", torch.uint8), _dev(norms, "norms", torch.float32),
+                           n, d, bits, ctypes.c_uint64(seed), _dev(out, "out", torch.float32),
+                           _stream(stream)), "tq_decode")
+    return out
+
+
+class TQCache:
+    """Ring-buffer compressed KV cache; buffers are torch device tensors.
+
+    Per layer l: k_packed[l] uint8 [batch, n_kv, window, d_l*bits_k/8],
+    k_norms[l] float32 [batch, n_kv, window] (likewise for V).  The C
+    descriptor holds host arrays of their device pointers."""
+
+    def __init__(self, n_layers, batch, n_kv_heads, window, head_dim, bits_k, bits_v,
+                 seed=42, device="cuda"):
+        hd = [head_dim] * n_layers if isinstance(head_dim, int) else list(head_dim)
+        if len(hd) != n_layers:
+            raise ValueError("head_dim list must have n_layers entries")
+        self.n_layers, self.batch, self.n_kv_heads, self.window = n_layers, batch, n_kv_heads, window
+        self.head_dim, self.bits_k, self.bits_v, self.seed = hd, bits_k, bits_v, seed
+        self.k_packed, self.k_norms, self.v_packed, self.v_norms = [], [], [], []
+        for d in hd:
+            self.k_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bits_k),
+                                             dtype=torch.uint8, device=device))
+            self.v_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bits_v),
+                                             dtype=torch.uint8, device=device))
+            self.k_norms.append(torch.zeros(batch, n_kv_heads, window, dtype=torch.float32, device=device))
+            self.v_norms.append(torch.zeros(batch, n_kv_heads, window, dtype=torch.float32, device=device))
+        self._refresh()
+
+    def _refresh(self):
+        n = self.n_layers
+        self._hd = (ctypes.c_int32 * n)(*self.head_dim)
+        self._kp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.k_packed])
+        self._kn = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.k_norms])
+        self._vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.v_packed])
+        self._vn = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.v_norms])
+        self.desc = _abi.TqCacheDesc(
+            n, self.batch, self.n_kv_heads, self.window, self.bits_k, self.bits_v, self.seed,
+            ctypes.cast(self._hd, ctypes.c_void_p), ctypes.cast(self._kp, ctypes.c_void_p),
+            ctypes.cast(self._kn, ctypes.c_void_p), ctypes.cast(self._vp, ctypes.c_void_p),
+            ctypes.cast(self._vn, ctypes.c_void_p))
+
+
+def tq_append_row(cache: TQCache, layer: int, k_new, v_new, pos: int, stream=None):
+    """k_new / v_new: a list of per-layer tensors [batch, n_kv, d_l] (layer = -1)
+    or one tensor (a single layer)."""
+    ks = list(k_new) if layer < 0 else [k_new]
+    vs = list(v_new) if layer < 0 else [v_new]
+    if not ks or len(ks) != len(vs):
+        raise ValueError("tq_append_row: k_new / v_new lengths differ")
+    dt = _DTYPES[ks[0].dtype]
+    for t in ks + vs:
+        if t.dtype != ks[0].dtype:
+            raise ValueError("tq_append_row: mixed dtypes")
+    kp = (ctypes.c_void_p * len(ks))(*[_dev(t, "k_new").value for t in ks])
+    vp = (ctypes.c_void_p * len(vs))(*[_dev(t, "v_new").value for t in vs])
+    _check(lib().tq_append_row(ctypes.byref(cache.desc), layer, kp, vp, dt, pos, _stream(stream)),
+           "tq_append_row")
+
+
+def tq_attn_workspace_bytes(cache: TQCache, layer: int, n_q_heads: int, ctx_len: int) -> int:
+    return int(lib().tq_attn_workspace_bytes(ctypes.byref(cache.desc), layer, n_q_heads, ctx_len))
+
+
+def tq_attn_decode(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int, scale: float = 0.0,
+                   out=None, workspace=None, stream=None):
+    """q: bf16 [batch, n_q_heads, d]; returns fp32 [batch, n_q_heads, d]."""
+    n_q = q.shape[-2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = tq_attn_workspace_bytes(cache, layer, n_q, ctx_len)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().tq_attn_decode(ctypes.byref(cache.desc), layer, _dev(q, "q", torch.bfloat16), n_q,
+                                ctx_len, ctypes.c_float(scale), _dev(out, "out", torch.float32),
+                                _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "tq_attn_decode")
+    return out

@@ -1,0 +1,520 @@
+// Decode-step attention over the compressed cache, in the rotated domain.
+//
+// Pages (cited by title and section):
+//   "TurboQuant KV Cache Compression — Spec", Optimization: Fused
+//     dequant-dot -- since the rotation R is orthogonal, <q, R^T k'> =
+//     <R q, k'>: rotate q once, score against centroid values directly,
+//     accumulate the V sum in the rotated domain, rotate the output back once.
+//   "TurboQuantEngine — Specification", 6 P1 follow-ups, "Compressed-domain
+//     attention".
+//
+// With k_t = D H (n_t c_K[idx_t]) / sqrt(d) (decode), the score is
+//   scale <q, k_t> = scale n_t <H (D q) / sqrt(d), c_K[idx_t]>,
+// and sum_t p_t v_t = D H (sum_t p_t n^V_t c_V[idx^V_t]) / sqrt(d).
+//
+// Split over the context: workgroup (chunk, kv head, sequence) handles the G
+// query heads of one KV head over one chunk of rows, in tiles of 256 rows with
+// an online softmax (scores in log2 units), and writes (o', max, sum) for its
+// chunk.  A second kernel merges the chunks of each (sequence, query head) in
+// chunk order (log-sum-exp) and applies the single inverse rotation.  No
+// atomics; the order of every sum is fixed.
+//
+// Centroid lookup: pairs of neighbouring indices (2*bits bits) address a
+// table of centroid pairs in LDS, one 8-byte read per two coordinates.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <string>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+using namespace tqd;
+
+namespace {
+
+constexpr int kTile = 256;           // rows per online-softmax tile (= threads)
+constexpr int kTargetBlocks = 1024;  // split the context until about this many workgroups
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnParams {
+    const uint16_t *q;        // [B][Hq][D] bf16
+    const uint8_t *kp;        // layer K packed rows [B][Hkv][window][D*BK/8]
+    const float *kn;          // [B][Hkv][window]
+    const uint8_t *vp;
+    const float *vn;
+    float *part;              // [B][Hq][n_chunks][D + 4]: o'[D], max, sum
+    float *out;               // [B][Hq][D]
+    int Hq, Hkv, window, T, n_chunks, chunk_len;
+    float qscale;             // scale * log2(e) / sqrt(D)
+    float centK[16];
+    float centV[16];
+    uint32_t signs[8];
+};
+
+template <int M>
+__device__ __forceinline__ float lane_xor_any(float v)
+{
+    if constexpr (M >= 32)
+        return __shfl_xor(v, M);
+    else
+        return lane_xor<M>(v);
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, lane_xor<1>(x));
+    x = fmaxf(x, lane_xor<2>(x));
+    x = fmaxf(x, lane_xor<4>(x));
+    x = fmaxf(x, lane_xor<8>(x));
+    x = fmaxf(x, lane_xor<16>(x));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += lane_xor<1>(x);
+    x += lane_xor<2>(x);
+    x += lane_xor<4>(x);
+    x += lane_xor<8>(x);
+    x += lane_xor<16>(x);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Bits of one lane's slice of a packed row: CPL indices of BITS bits starting
+// at byte `off` of the row (the slice never crosses the row end).  Reads the
+// 4-byte words that cover it and shifts the slice down to bit 0.
+template <int BITS, int CPL>
+__device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *row, int off)
+{
+    constexpr int NB = CPL * BITS / 8;  // bytes in the slice
+    if constexpr (NB == 8) {
+        return *reinterpret_cast<const uint64_t *>(row + off);  // off % 8 == 0
+    } else if constexpr (NB == 4) {
+        return *reinterpret_cast<const uint32_t *>(row + off);  // off % 4 == 0
+    } else if constexpr (NB == 2) {
+        return *reinterpret_cast<const uint16_t *>(row + off);  // off % 2 == 0
+    } else {
+        const int a = off & ~3, sh = off & 3;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(row + a);
+        uint64_t v = w[0];
+        if (sh + NB > 4)
+            v |= (uint64_t)w[1] << 32;
+        return (v >> (8 * sh)) & ((1ull << (8 * NB)) - 1ull);
+    }
+}
+
+template <int D, int BK, int BV, int G>
+__global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
+{
+    constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
+    constexpr int P = D / CPL;            // lanes per row
+    constexpr int RPW = 64 / P;
+    constexpr int RPB = RPW * (kBlock / 64);
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int NPK = 1 << (2 * BK), NPV = 1 << (2 * BV);
+    constexpr int RS = D + 4;
+    static_assert(kTile == kBlock, "one tile row per thread in the softmax step");
+    static_assert(kTile % RPB == 0, "tile covered by whole passes");
+
+    __shared__ float2 tabK[NPK];
+    __shared__ float2 tabV[NPV];
+    __shared__ float qs[G][D];
+    __shared__ float sc[kTile][G];
+    __shared__ float red[kBlock / 64][G];
+    __shared__ float accs[kBlock / 64][G][D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+
+    for (int i = tid; i < NPK; i += kBlock)
+        tabK[i] = make_float2(p.centK[i & ((1 << BK) - 1)], p.centK[i >> BK]);
+    for (int i = tid; i < NPV; i += kBlock)
+        tabV[i] = make_float2(p.centV[i & ((1 << BV) - 1)], p.centV[i >> BV]);
+
+    // q' = H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV head
+    if (wave == 0) {
+        constexpr int P2 = D / kCPL;
+        const int sub2 = lane % P2, r2 = lane / P2;
+        float v[kCPL];
+        const int h = g * G + (r2 < G ? r2 : 0);
+        load_slice(p.q + ((int64_t)b * p.Hq + h) * D + sub2 * kCPL, v);
+        apply_signs(v, p.signs[sub2]);
+        fwht_row<P2>(v, sub2);
+        if (r2 < G) {
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                qs[r2][sub2 * kCPL + k] = v[k] * p.qscale;
+        }
+    }
+    __syncthreads();
+
+    const int sub = lane % P, rig = lane / P;
+    float qr[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            qr[h][k] = qs[h][sub * CPL + k];
+
+    float acc[G][CPL];
+    float m_run[G], l_part[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        m_run[h] = -__builtin_huge_valf();
+        l_part[h] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            acc[h][k] = 0.0f;
+    }
+
+    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.T, t_begin + p.chunk_len);
+
+    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+        // ---- scores of the tile
+#pragma unroll 1
+        for (int it = 0; it < kTile / RPB; it++) {
+            const int tl = it * RPB + wave * RPW + rig;
+            const int t = t0 + tl;
+            const bool valid = t < t_end;
+            const int64_t row = rowbase + (valid ? t : t_begin);
+            const uint64_t bits = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
+            const float n = p.kn[row];
+            float s[G];
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                s[h] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CPL / 2; m++) {
+                const float2 c = tabK[(bits >> (2 * BK * m)) & (NPK - 1)];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    s[h] = fmaf(qr[h][2 * m], c.x, s[h]);
+                    s[h] = fmaf(qr[h][2 * m + 1], c.y, s[h]);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                s[h] = sum_across<P>(s[h]);
+            if (sub == 0) {
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    sc[tl][h] = valid ? s[h] * n : -__builtin_huge_valf();
+            }
+        }
+        __syncthreads();
+        // ---- running max, weights of the tile
+        float mx[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            mx[h] = wave_max(sc[tid][h]);
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                red[wave][h] = mx[h];
+        }
+        __syncthreads();
+        float fac[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float mt = red[0][h];
+#pragma unroll
+            for (int w = 1; w < kBlock / 64; w++)
+                mt = fmaxf(mt, red[w][h]);
+            const float mnew = fmaxf(m_run[h], mt);
+            fac[h] = exp2f(m_run[h] - mnew);
+            m_run[h] = mnew;
+            const float pr = exp2f(sc[tid][h] - mnew);
+            l_part[h] = l_part[h] * fac[h] + pr;
+            sc[tid][h] = pr;
+        }
+        __syncthreads();
+        // ---- V sum of the tile (rotated domain)
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                acc[h][k] *= fac[h];
+#pragma unroll 1
+        for (int it = 0; it < kTile / RPB; it++) {
+            const int tl = it * RPB + wave * RPW + rig;
+            const int t = t0 + tl;
+            const bool valid = t < t_end;
+            const int64_t row = rowbase + (valid ? t : t_begin);
+            const uint64_t bits = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+            const float nv = valid ? p.vn[row] : 0.0f;
+            float w[G];
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                w[h] = sc[tl][h] * nv;
+#pragma unroll
+            for (int m = 0; m < CPL / 2; m++) {
+                const float2 c = tabV[(bits >> (2 * BV * m)) & (NPV - 1)];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    acc[h][2 * m] = fmaf(w[h], c.x, acc[h][2 * m]);
+                    acc[h][2 * m + 1] = fmaf(w[h], c.y, acc[h][2 * m + 1]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- reduce over the rows of the wave (lanes with equal `sub`)
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int k = 0; k < CPL; k++) {
+            float a = acc[h][k];
+            if constexpr (P <= 1) a += lane_xor_any<1>(a);
+            if constexpr (P <= 2) a += lane_xor_any<2>(a);
+            if constexpr (P <= 4) a += lane_xor_any<4>(a);
+            if constexpr (P <= 8) a += lane_xor_any<8>(a);
+            if constexpr (P <= 16) a += lane_xor_any<16>(a);
+            if constexpr (P <= 32) a += lane_xor_any<32>(a);
+            acc[h][k] = a;
+        }
+    if (rig == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                accs[wave][h][sub * CPL + k] = acc[h][k];
+    }
+    // sum of weights over the block
+#pragma unroll
+    for (int h = 0; h < G; h++)
+        l_part[h] = wave_sum(l_part[h]);
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            red[wave][h] = l_part[h];
+    }
+    __syncthreads();
+    float *rec0 = p.part + (((int64_t)b * p.Hq + g * G) * p.n_chunks + chunk) * RS;
+    const int64_t hstride = (int64_t)p.n_chunks * RS;
+    for (int i = tid; i < G * D; i += kBlock) {
+        const int h = i / D, j = i % D;
+        float o = accs[0][h][j];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            o += accs[w][h][j];
+        rec0[h * hstride + j] = o;
+    }
+    if (tid < G) {
+        float l = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            l += red[w][tid];
+        rec0[tid * hstride + D] = m_run[tid];
+        rec0[tid * hstride + D + 1] = l;
+    }
+}
+
+// Merge the chunks of one (sequence, query head) and rotate back.  One wave
+// per (sequence, query head); the first D/32 lanes hold the row.
+template <int D>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p)
+{
+    constexpr int P = D / kCPL, RS = D + 4;
+    const int lane = threadIdx.x, sub = lane % P;
+    const int64_t bh = blockIdx.x;
+    const float *rec = p.part + bh * p.n_chunks * RS;
+    float M = -__builtin_huge_valf();
+    for (int c = 0; c < p.n_chunks; c++)
+        M = fmaxf(M, rec[c * RS + D]);
+    float o[kCPL];
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        o[k] = 0.0f;
+    float L = 0.0f;
+    for (int c = 0; c < p.n_chunks; c++) {
+        const float w = exp2f(rec[c * RS + D] - M);
+        L = fmaf(w, rec[c * RS + D + 1], L);
+        const float4 *src = reinterpret_cast<const float4 *>(rec + c * RS + sub * kCPL);
+#pragma unroll
+        for (int j = 0; j < kCPL / 4; j++) {
+            const float4 t = src[j];
+            o[4 * j] = fmaf(w, t.x, o[4 * j]);
+            o[4 * j + 1] = fmaf(w, t.y, o[4 * j + 1]);
+            o[4 * j + 2] = fmaf(w, t.z, o[4 * j + 2]);
+            o[4 * j + 3] = fmaf(w, t.w, o[4 * j + 3]);
+        }
+    }
+    fwht_row<P>(o, sub);
+    const float sc = 1.0f / (L * sqrtf((float)D));
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        o[k] *= sc;
+    apply_signs(o, p.signs[sub]);
+    if (lane < P)
+        store_slice(p.out + bh * D + sub * kCPL, o);
+}
+
+int check_cache(const tq_cache_desc *c, int layer, const char *fn)
+{
+    if (!c)
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": cache is NULL");
+    if (c->n_layers < 1 || c->n_layers > TQ_MAX_LAYERS || c->batch < 0 || c->n_kv_heads < 1 ||
+        c->window < 1 || !c->head_dim || !c->k_packed || !c->k_norms || !c->v_packed ||
+        !c->v_norms)
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": invalid cache descriptor");
+    if (layer < 0 || layer >= c->n_layers)
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": layer out of range");
+    return TQ_OK;
+}
+
+struct Split {
+    int T, n_chunks, chunk_len;
+};
+
+// Context split: enough chunks for about kTargetBlocks workgroups, chunks a
+// whole number of tiles.  Depends only on the arguments, so results are the
+// same on every device.
+Split split_for(int batch, int n_kv, int64_t ctx_len, int window)
+{
+    Split s;
+    s.T = (int)(ctx_len < window ? ctx_len : window);
+    const int units = batch * n_kv > 0 ? batch * n_kv : 1;
+    const int tiles = (s.T + kTile - 1) / kTile;
+    int want = (kTargetBlocks + units - 1) / units;
+    if (want > tiles)
+        want = tiles;
+    if (want < 1)
+        want = 1;
+    const int tiles_per_chunk = (tiles + want - 1) / want;
+    s.chunk_len = tiles_per_chunk * kTile;
+    s.n_chunks = (s.T + s.chunk_len - 1) / s.chunk_len;
+    return s;
+}
+
+template <int D, int BK, int BV>
+void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+{
+    dim3 block(kBlock);
+    switch (G) {
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 8>), grid, block, 0, st, p); break;
+    }
+}
+
+template <int D, int BK>
+void launch_attn_bv(int BV, int G, dim3 grid, const AttnParams &p, hipStream_t st)
+{
+    switch (BV) {
+    case 2: launch_attn_g<D, BK, 2>(G, grid, p, st); break;
+    case 3: launch_attn_g<D, BK, 3>(G, grid, p, st); break;
+    default: launch_attn_g<D, BK, 4>(G, grid, p, st); break;
+    }
+}
+
+template <int D>
+void launch_attn_d(int BK, int BV, int G, dim3 grid, const AttnParams &p, hipStream_t st)
+{
+    switch (BK) {
+    case 2: launch_attn_bv<D, 2>(BV, G, grid, p, st); break;
+    case 3: launch_attn_bv<D, 3>(BV, G, grid, p, st); break;
+    default: launch_attn_bv<D, 4>(BV, G, grid, p, st); break;
+    }
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(grid.z * p.Hq)), dim3(64), 0, st, p);
+}
+
+}  // namespace
+
+extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int n_q_heads,
+                                          int64_t ctx_len)
+{
+    if (!c || layer < 0 || layer >= c->n_layers || !c->head_dim || n_q_heads < 1 ||
+        ctx_len < 1 || c->window < 1 || c->batch < 0 || c->n_kv_heads < 1)
+        return 0;
+    const int d = c->head_dim[layer];
+    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
+    return (size_t)c->batch * n_q_heads * s.n_chunks * (size_t)(d + 4) * sizeof(float);
+}
+
+extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
+                              int n_q_heads, int64_t ctx_len, float scale, float *out,
+                              void *workspace, size_t ws_bytes, void *stream)
+{
+    static const char *fn = "tq_attn_decode";
+    tq::clear_error();
+    int rc = check_cache(c, layer, fn);
+    if (rc != TQ_OK)
+        return rc;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: n_q_heads must be a positive multiple of n_kv_heads");
+    const int G = n_q_heads / c->n_kv_heads;
+    if (ctx_len < 1)
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: ctx_len must be >= 1");
+    const int d = c->head_dim[layer];
+    if (!(d == 64 || d == 128 || d == 256))
+        return tq::fail(tq::is_pow2(d) ? TQ_EUNSUPPORTED : TQ_EINVAL,
+                        "tq_attn_decode: device kernels take head_dim in {64, 128, 256}");
+    for (int bits : {c->bits_k, c->bits_v}) {
+        if (bits < 1 || bits > 4)
+            return tq::fail(TQ_EINVAL, "tq_attn_decode: bits must be in 1..4");
+        if (bits == 1)
+            return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: device kernels take bits in {2, 3, 4}");
+    }
+    if (!(G == 1 || G == 2 || G == 4 || G == 8))
+        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: query/KV head ratio must be 1, 2, 4 or 8");
+    if (c->batch == 0)
+        return TQ_OK;
+    if (!q_bf16 || !out || !workspace || !c->k_packed[layer] || !c->k_norms[layer] ||
+        !c->v_packed[layer] || !c->v_norms[layer])
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: NULL buffer");
+    if (((uintptr_t)q_bf16 | (uintptr_t)out | (uintptr_t)workspace |
+         (uintptr_t)c->k_packed[layer] | (uintptr_t)c->v_packed[layer]) % 16 != 0 ||
+        ((uintptr_t)c->k_norms[layer] | (uintptr_t)c->v_norms[layer]) % 4 != 0)
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: misaligned buffer");
+    const size_t need = tq_attn_workspace_bytes(c, layer, n_q_heads, ctx_len);
+    if (ws_bytes < need)
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: workspace too small (need " +
+                                       std::to_string(need) + " bytes)");
+    if (tq::take_injected_launch_failure())
+        return tq::fail(TQ_EHIP, "tq_attn_decode: injected launch failure (TQ_TEST_FAIL_LAUNCH)");
+    tq_codebook ck, cv;
+    if ((rc = tq::get_codebook(d, c->bits_k, TQ_BETA_HALF_D, &ck)) != TQ_OK ||
+        (rc = tq::get_codebook(d, c->bits_v, TQ_BETA_HALF_D, &cv)) != TQ_OK)
+        return rc;
+    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
+    AttnParams p;
+    p.q = q_bf16;
+    p.kp = c->k_packed[layer];
+    p.kn = c->k_norms[layer];
+    p.vp = c->v_packed[layer];
+    p.vn = c->v_norms[layer];
+    p.part = static_cast<float *>(workspace);
+    p.out = out;
+    p.Hq = n_q_heads;
+    p.Hkv = c->n_kv_heads;
+    p.window = c->window;
+    p.T = s.T;
+    p.n_chunks = s.n_chunks;
+    p.chunk_len = s.chunk_len;
+    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)d);
+    p.qscale = sc * kLog2e / sqrtf((float)d);
+    for (int j = 0; j < 16; j++) {
+        p.centK[j] = j < ck.levels ? ck.centroids[j] : 0.0f;
+        p.centV[j] = j < cv.levels ? cv.centroids[j] : 0.0f;
+    }
+    tq::sign_words(d, c->seed, p.signs);
+    dim3 grid((unsigned)s.n_chunks, (unsigned)c->n_kv_heads, (unsigned)c->batch);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (d) {
+    case 64: launch_attn_d<64>(c->bits_k, c->bits_v, G, grid, p, st); break;
+    case 128: launch_attn_d<128>(c->bits_k, c->bits_v, G, grid, p, st); break;
+    default: launch_attn_d<256>(c->bits_k, c->bits_v, G, grid, p, st); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return tq::fail(TQ_EHIP, std::string("tq_attn_decode: ") + hipGetErrorString(e));
+    return TQ_OK;
+}

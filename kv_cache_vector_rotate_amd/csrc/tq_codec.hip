@@ -1,0 +1,628 @@
+// Codec kernels of libtq.so: rotate, encode (K and V in one launch), decode
+// and the append-only ring-cache encode.
+//
+// Pages (cited by title and section):
+//   "TurboQuant KV Cache Compression — Spec" -- As-Built Notes 1 (signs
+//     before the Hadamard) and 2 (L2-norm normalisation); Algorithm Detail
+//     steps 1-3; Hadamard Transform Detail; Integration Points (pos % max_seq).
+//   "TurboQuantEngine — Specification" -- 2.2 Memory contract (fp32 norm and
+//     packed indices per head row); 6 P1 follow-ups, W3 (encode only the new
+//     row each step).
+//
+// Work decomposition: each row is owned by P = d/32 lanes (32 coordinates per
+// lane, see tq_device.h); workgroups of 256 threads walk the rows with a grid
+// stride.  Nothing is shared between rows, so there are no atomics and the
+// result does not depend on the launch shape.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <mutex>
+#include <string>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+using namespace tqd;
+
+namespace {
+
+// ----------------------------------------------------------------- encode
+
+struct CodeTable {
+    float bnd[15];
+    int bits;
+};
+
+// One row: norm, sign, rotate, normalise, bucketize, pack.  `valid` false
+// lanes compute on zeros and store nothing.  The caller has built the
+// bucketize table `lut` for BITS.
+template <int D, int BITS, typename T>
+__device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int sub,
+                                           uint32_t smask, const float2 *lut,
+                                           uint8_t *dst_row, float *dst_norm)
+{
+    constexpr int P = Shape<D>::P;
+    float v[kCPL];
+    if (valid) {
+        load_slice(src_slice, v);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            v[k] = 0.0f;
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        ss = fmaf(v[k], v[k], ss);
+    ss = sum_across<P>(ss);
+    // Rows whose sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or
+    // non-finite) are rescaled by an exact power of two first; indices are
+    // invariant under such scaling and the norm is scaled back.
+    float nscale = 1.0f;
+    if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
+        float m = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            m = fmaxf(m, fabsf(v[k]));
+        m = max_across<P>(m);
+        if (m > 0.0f && m <= FLT_MAX) {
+            int e;
+            (void)frexpf(m, &e);
+            const float sc = ldexpf(1.0f, -e);
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                v[k] *= sc;
+            nscale = ldexpf(1.0f, e);
+            ss = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                ss = fmaf(v[k], v[k], ss);
+            ss = sum_across<P>(ss);
+        }
+    }
+    const float n = sqrtf(ss);
+    // u = H(D x) / (sqrt(d) n); zero rows get u = 0
+    const float inv = ss > 0.0f ? 1.0f / sqrtf((float)D * ss) : 0.0f;
+    apply_signs(v, smask);
+    fwht_row<P>(v, sub);
+    uint32_t w[BITS];
+#pragma unroll
+    for (int j = 0; j < BITS; j++)
+        w[j] = 0u;
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        put_index<BITS>(w, k, bucketize(v[k] * inv, lut));
+    if (valid) {
+        store_words<BITS>(dst_row + sub * 4 * BITS, w);
+        if (sub == 0)
+            *dst_norm = n * nscale;
+    }
+}
+
+struct EncodeSide {
+    const void *src;
+    uint8_t *packed;
+    float *norms;
+    CodeTable code;
+};
+
+struct EncodeParams {
+    EncodeSide side[2];
+    int64_t n_rows;
+    uint32_t signs[8];
+};
+
+template <int D, typename T, int BITS>
+__device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t n_rows,
+                                                   uint32_t smask, const float2 *lut)
+{
+    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    constexpr int RB = D * BITS / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % P, rig = lane / P;
+    const T *src = static_cast<const T *>(s.src);
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows;
+         base += (int64_t)gridDim.x * RPB) {
+        const int64_t row = base + wave * RPW + rig;
+        const bool valid = row < n_rows;
+        const int64_t r = valid ? row : 0;
+        encode_row<D, BITS, T>(src + r * D + sub * kCPL, valid, sub, smask, lut,
+                               s.packed + r * RB, s.norms + r);
+    }
+}
+
+// blockIdx.y selects the side (0 = first non-NULL side, 1 = second)
+template <int D, typename T>
+__global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
+{
+    __shared__ float2 lut[kLutBins];
+    const EncodeSide &s = p.side[blockIdx.y];
+    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
+    __syncthreads();
+    const int sub = (threadIdx.x & 63) % Shape<D>::P;
+    const uint32_t smask = p.signs[sub];
+    switch (s.code.bits) {
+    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, smask, lut); break;
+    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, smask, lut); break;
+    default: encode_contig_loop<D, T, 4>(s, p.n_rows, smask, lut); break;
+    }
+}
+
+// ----------------------------------------------------------------- append
+
+constexpr int kMaxAppendLayers = 48;
+
+struct AppendSide {
+    const void *src[kMaxAppendLayers];
+    uint8_t *packed[kMaxAppendLayers];
+    float *norms[kMaxAppendLayers];
+    CodeTable code;
+};
+
+struct AppendParams {
+    AppendSide side[2];
+    int n_layers;     // layers in this launch (all of head_dim D)
+    int bh;           // batch * n_kv_heads
+    int window;
+    int slot;         // pos % window
+    uint32_t signs[8];
+};
+
+template <int D, typename T, int BITS>
+__device__ __forceinline__ void append_loop(const AppendSide &s, const AppendParams &p,
+                                            uint32_t smask, const float2 *lut)
+{
+    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    constexpr int RB = D * BITS / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % P, rig = lane / P;
+    const int64_t n_rows = (int64_t)p.n_layers * p.bh;
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows;
+         base += (int64_t)gridDim.x * RPB) {
+        const int64_t row = base + wave * RPW + rig;
+        const bool valid = row < n_rows;
+        const int64_t r = valid ? row : 0;
+        const int li = (int)(r / p.bh), j = (int)(r % p.bh);
+        const T *src = static_cast<const T *>(s.src[li]) + (int64_t)j * D + sub * kCPL;
+        const int64_t dst = (int64_t)j * p.window + p.slot;
+        encode_row<D, BITS, T>(src, valid, sub, smask, lut, s.packed[li] + dst * RB,
+                               s.norms[li] + dst);
+    }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
+{
+    __shared__ float2 lut[kLutBins];
+    const AppendSide &s = p.side[blockIdx.y];
+    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
+    __syncthreads();
+    const int sub = (threadIdx.x & 63) % Shape<D>::P;
+    const uint32_t smask = p.signs[sub];
+    switch (s.code.bits) {
+    case 2: append_loop<D, T, 2>(s, p, smask, lut); break;
+    case 3: append_loop<D, T, 3>(s, p, smask, lut); break;
+    default: append_loop<D, T, 4>(s, p, smask, lut); break;
+    }
+}
+
+// ----------------------------------------------------------------- decode
+
+struct DecodeParams {
+    const uint8_t *packed;
+    const float *norms;
+    float *out;
+    int64_t n_rows;
+    float cent[16];
+    uint32_t signs[8];
+};
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeParams p)
+{
+    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    constexpr int RB = D * BITS / 8;
+    __shared__ float cent[16];
+    if (threadIdx.x < 16)
+        cent[threadIdx.x] = p.cent[threadIdx.x];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % P, rig = lane / P;
+    const uint32_t smask = p.signs[sub];
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows;
+         base += (int64_t)gridDim.x * RPB) {
+        const int64_t row = base + wave * RPW + rig;
+        const bool valid = row < p.n_rows;
+        const int64_t r = valid ? row : 0;
+        uint32_t w[BITS];
+        load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
+        const float n = p.norms[r];
+        float v[kCPL];
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            v[k] = cent[get_index<BITS>(w, k)];
+        fwht_row<P>(v, sub);
+        const float sc = n * inv_sqrt_d;
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            v[k] *= sc;
+        apply_signs(v, smask);
+        if (valid)
+            store_slice(p.out + r * D + sub * kCPL, v);
+    }
+}
+
+// ----------------------------------------------------------------- rotate
+
+struct RotateParams {
+    const void *in;
+    float *out;
+    int64_t n_rows;
+    int inverse;
+    uint32_t signs[8];
+};
+
+template <int D, typename T>
+__global__ __launch_bounds__(kBlock) void rotate_kernel(RotateParams p)
+{
+    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane % P, rig = lane / P;
+    const uint32_t smask = p.signs[sub];
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const T *in = static_cast<const T *>(p.in);
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows;
+         base += (int64_t)gridDim.x * RPB) {
+        const int64_t row = base + wave * RPW + rig;
+        const bool valid = row < p.n_rows;
+        const int64_t r = valid ? row : 0;
+        float v[kCPL];
+        load_slice(in + r * D + sub * kCPL, v);
+        if (!p.inverse)
+            apply_signs(v, smask);
+        fwht_row<P>(v, sub);
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            v[k] *= inv_sqrt_d;
+        if (p.inverse)
+            apply_signs(v, smask);
+        if (valid)
+            store_slice(p.out + r * D + sub * kCPL, v);
+    }
+}
+
+// ------------------------------------------------------------ host helpers
+
+int device_cus()
+{
+    static std::mutex mu;
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+unsigned grid_for(int64_t n_rows, int rows_per_block)
+{
+    const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
+    const int64_t cap = (int64_t)device_cus() * 16;
+    return (unsigned)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// d supported by the device kernels, else the status to return
+int check_d(int d, const char *fn)
+{
+    if (d == 64 || d == 128 || d == 256)
+        return TQ_OK;
+    if (tq::is_pow2(d) && d >= 2 && d <= (1 << 20))
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device kernels take d in {64, 128, 256}");
+    return tq::fail(TQ_EINVAL, std::string(fn) + ": d must be a power of two");
+}
+
+int check_bits(int bits, const char *fn)
+{
+    if (bits >= 2 && bits <= 4)
+        return TQ_OK;
+    if (bits == 1)
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device kernels take bits in {2, 3, 4}");
+    return tq::fail(TQ_EINVAL, std::string(fn) + ": bits must be in 1..4");
+}
+
+// boundaries for the device table; checks that no widened bin holds two
+int code_table(int d, int bits, CodeTable *t, const char *fn)
+{
+    tq_codebook cb;
+    int rc = tq::get_codebook(d, bits, TQ_BETA_HALF_D, &cb);
+    if (rc != TQ_OK)
+        return rc;
+    t->bits = bits;
+    for (int j = 0; j < 15; j++)
+        t->bnd[j] = j < cb.levels - 1 ? cb.boundaries[j] : 0.0f;
+    for (int j = 0; j + 1 < cb.levels - 1; j++)
+        if (cb.boundaries[j + 1] - cb.boundaries[j] <= 1.0f / kLutScale + 2.0f * kLutSlack)
+            return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": codebook boundaries too close for the bucketize table");
+    return TQ_OK;
+}
+
+int launch_status(const char *fn)
+{
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return tq::fail(TQ_EHIP, std::string(fn) + ": " + hipGetErrorString(e));
+    return TQ_OK;
+}
+
+int injected(const char *fn)
+{
+    if (tq::take_injected_launch_failure())
+        return tq::fail(TQ_EHIP, std::string(fn) + ": injected launch failure (TQ_TEST_FAIL_LAUNCH)");
+    return TQ_OK;
+}
+
+template <typename T>
+void launch_encode(int d, const EncodeParams &p, int sides, hipStream_t st)
+{
+    dim3 block(kBlock);
+    switch (d) {
+    case 64: hipLaunchKernelGGL((encode_kernel<64, T>), dim3(grid_for(p.n_rows, Shape<64>::RPB), sides), block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((encode_kernel<128, T>), dim3(grid_for(p.n_rows, Shape<128>::RPB), sides), block, 0, st, p); break;
+    default: hipLaunchKernelGGL((encode_kernel<256, T>), dim3(grid_for(p.n_rows, Shape<256>::RPB), sides), block, 0, st, p); break;
+    }
+}
+
+template <typename T>
+void launch_append(int d, const AppendParams &p, int sides, hipStream_t st)
+{
+    dim3 block(kBlock);
+    const int64_t rows = (int64_t)p.n_layers * p.bh;
+    switch (d) {
+    case 64: hipLaunchKernelGGL((append_kernel<64, T>), dim3(grid_for(rows, Shape<64>::RPB), sides), block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((append_kernel<128, T>), dim3(grid_for(rows, Shape<128>::RPB), sides), block, 0, st, p); break;
+    default: hipLaunchKernelGGL((append_kernel<256, T>), dim3(grid_for(rows, Shape<256>::RPB), sides), block, 0, st, p); break;
+    }
+}
+
+template <int D>
+void launch_decode_d(int bits, const DecodeParams &p, hipStream_t st)
+{
+    dim3 grid(grid_for(p.n_rows, Shape<D>::RPB)), block(kBlock);
+    switch (bits) {
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, st, p); break;
+    }
+}
+
+template <typename T>
+void launch_rotate(int d, const RotateParams &p, hipStream_t st)
+{
+    dim3 block(kBlock);
+    switch (d) {
+    case 64: hipLaunchKernelGGL((rotate_kernel<64, T>), dim3(grid_for(p.n_rows, Shape<64>::RPB)), block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((rotate_kernel<128, T>), dim3(grid_for(p.n_rows, Shape<128>::RPB)), block, 0, st, p); break;
+    default: hipLaunchKernelGGL((rotate_kernel<256, T>), dim3(grid_for(p.n_rows, Shape<256>::RPB)), block, 0, st, p); break;
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ C entry points
+
+extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint64_t seed,
+                         int inverse, float *out, void *stream)
+{
+    static const char *fn = "tq_rotate";
+    tq::clear_error();
+    if (dtype != TQ_F32 && dtype != TQ_BF16)
+        return tq::fail(TQ_EINVAL, "tq_rotate: unknown dtype");
+    if (n_rows < 0)
+        return tq::fail(TQ_EINVAL, "tq_rotate: n_rows < 0");
+    int rc = check_d(d, fn);
+    if (rc != TQ_OK)
+        return rc;
+    if (n_rows == 0)
+        return TQ_OK;
+    if (!in || !out)
+        return tq::fail(TQ_EINVAL, "tq_rotate: NULL buffer");
+    if (!aligned(in, 16) || !aligned(out, 16))
+        return tq::fail(TQ_EINVAL, "tq_rotate: buffers must be 16-byte aligned");
+    if ((rc = injected(fn)) != TQ_OK)
+        return rc;
+    RotateParams p;
+    p.in = in;
+    p.out = out;
+    p.n_rows = n_rows;
+    p.inverse = inverse ? 1 : 0;
+    tq::sign_words(d, seed, p.signs);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == TQ_F32)
+        launch_rotate<float>(d, p, st);
+    else
+        launch_rotate<uint16_t>(d, p, st);
+    return launch_status(fn);
+}
+
+extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int64_t n_rows,
+                         int d, int bits_k, int bits_v, uint64_t seed, uint8_t *k_packed,
+                         float *k_norms, uint8_t *v_packed, float *v_norms, void *stream)
+{
+    static const char *fn = "tq_encode";
+    tq::clear_error();
+    if (dtype != TQ_F32 && dtype != TQ_BF16)
+        return tq::fail(TQ_EINVAL, "tq_encode: unknown dtype");
+    if (n_rows < 0)
+        return tq::fail(TQ_EINVAL, "tq_encode: n_rows < 0");
+    if (!k_rows && !v_rows)
+        return tq::fail(TQ_EINVAL, "tq_encode: both k_rows and v_rows are NULL");
+    int rc = check_d(d, fn);
+    if (rc != TQ_OK)
+        return rc;
+    EncodeParams p;
+    int sides = 0;
+    const void *src[2] = {k_rows, v_rows};
+    uint8_t *pk[2] = {k_packed, v_packed};
+    float *nm[2] = {k_norms, v_norms};
+    int bits[2] = {bits_k, bits_v};
+    for (int s = 0; s < 2; s++) {
+        if (!src[s])
+            continue;
+        if ((rc = check_bits(bits[s], fn)) != TQ_OK)
+            return rc;
+        if (!pk[s] || !nm[s])
+            return tq::fail(TQ_EINVAL, "tq_encode: NULL output buffer for a non-NULL input");
+        if (!aligned(src[s], 16) || !aligned(pk[s], 16) || !aligned(nm[s], 4))
+            return tq::fail(TQ_EINVAL, "tq_encode: misaligned buffer (rows and packed need 16 bytes, norms 4)");
+        EncodeSide &e = p.side[sides++];
+        e.src = src[s];
+        e.packed = pk[s];
+        e.norms = nm[s];
+        if ((rc = code_table(d, bits[s], &e.code, fn)) != TQ_OK)
+            return rc;
+    }
+    if (n_rows == 0)
+        return TQ_OK;
+    if ((rc = injected(fn)) != TQ_OK)
+        return rc;
+    p.n_rows = n_rows;
+    tq::sign_words(d, seed, p.signs);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == TQ_F32)
+        launch_encode<float>(d, p, sides, st);
+    else
+        launch_encode<uint16_t>(d, p, sides, st);
+    return launch_status(fn);
+}
+
+extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
+                         int bits, uint64_t seed, float *out, void *stream)
+{
+    static const char *fn = "tq_decode";
+    tq::clear_error();
+    if (n_rows < 0)
+        return tq::fail(TQ_EINVAL, "tq_decode: n_rows < 0");
+    int rc = check_d(d, fn);
+    if (rc != TQ_OK)
+        return rc;
+    if ((rc = check_bits(bits, fn)) != TQ_OK)
+        return rc;
+    if (n_rows == 0)
+        return TQ_OK;
+    if (!packed || !norms || !out)
+        return tq::fail(TQ_EINVAL, "tq_decode: NULL buffer");
+    if (!aligned(packed, 16) || !aligned(out, 16) || !aligned(norms, 4))
+        return tq::fail(TQ_EINVAL, "tq_decode: misaligned buffer (packed and out need 16 bytes, norms 4)");
+    if ((rc = injected(fn)) != TQ_OK)
+        return rc;
+    tq_codebook cb;
+    if ((rc = tq::get_codebook(d, bits, TQ_BETA_HALF_D, &cb)) != TQ_OK)
+        return rc;
+    DecodeParams p;
+    p.packed = packed;
+    p.norms = norms;
+    p.out = out;
+    p.n_rows = n_rows;
+    for (int j = 0; j < 16; j++)
+        p.cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
+    tq::sign_words(d, seed, p.signs);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (d) {
+    case 64: launch_decode_d<64>(bits, p, st); break;
+    case 128: launch_decode_d<128>(bits, p, st); break;
+    default: launch_decode_d<256>(bits, p, st); break;
+    }
+    return launch_status(fn);
+}
+
+extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *const *k_new,
+                             const void *const *v_new, int dtype, int64_t pos, void *stream)
+{
+    static const char *fn = "tq_append_row";
+    tq::clear_error();
+    if (!c)
+        return tq::fail(TQ_EINVAL, "tq_append_row: cache is NULL");
+    if (dtype != TQ_F32 && dtype != TQ_BF16)
+        return tq::fail(TQ_EINVAL, "tq_append_row: unknown dtype");
+    if (c->n_layers < 1 || c->n_layers > TQ_MAX_LAYERS || c->batch < 0 || c->n_kv_heads < 0 ||
+        c->window < 1 || !c->head_dim || !c->k_packed || !c->k_norms || !c->v_packed ||
+        !c->v_norms)
+        return tq::fail(TQ_EINVAL, "tq_append_row: invalid cache descriptor");
+    if (layer < -1 || layer >= c->n_layers)
+        return tq::fail(TQ_EINVAL, "tq_append_row: layer out of range");
+    if (pos < 0)
+        return tq::fail(TQ_EINVAL, "tq_append_row: pos < 0");
+    if (!k_new || !v_new)
+        return tq::fail(TQ_EINVAL, "tq_append_row: k_new / v_new is NULL");
+    int rc;
+    if ((rc = check_bits(c->bits_k, fn)) != TQ_OK || (rc = check_bits(c->bits_v, fn)) != TQ_OK)
+        return rc;
+    const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->n_layers : layer + 1;
+    for (int l = l0; l < l1; l++) {
+        const int i = l - l0;
+        if ((rc = check_d(c->head_dim[l], fn)) != TQ_OK)
+            return rc;
+        if (!k_new[i] || !v_new[i] || !c->k_packed[l] || !c->k_norms[l] || !c->v_packed[l] ||
+            !c->v_norms[l])
+            return tq::fail(TQ_EINVAL, "tq_append_row: NULL layer buffer");
+        if (!aligned(k_new[i], 16) || !aligned(v_new[i], 16) || !aligned(c->k_packed[l], 16) ||
+            !aligned(c->v_packed[l], 16) || !aligned(c->k_norms[l], 4) || !aligned(c->v_norms[l], 4))
+            return tq::fail(TQ_EINVAL, "tq_append_row: misaligned layer buffer");
+    }
+    const int bh = c->batch * c->n_kv_heads;
+    if (bh == 0)
+        return TQ_OK;
+    if ((rc = injected(fn)) != TQ_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int slot = (int)(pos % c->window);
+    // one launch per distinct head_dim (and per kMaxAppendLayers layers)
+    const int dims[3] = {64, 128, 256};
+    for (int di = 0; di < 3; di++) {
+        const int d = dims[di];
+        AppendParams p;
+        p.bh = bh;
+        p.window = c->window;
+        p.slot = slot;
+        tq::sign_words(d, c->seed, p.signs);
+        if ((rc = code_table(d, c->bits_k, &p.side[0].code, fn)) != TQ_OK ||
+            (rc = code_table(d, c->bits_v, &p.side[1].code, fn)) != TQ_OK)
+            return rc;
+        p.n_layers = 0;
+        for (int l = l0; l <= l1; l++) {
+            const bool flush = (l == l1) || (p.n_layers == kMaxAppendLayers);
+            if (flush && p.n_layers > 0) {
+                if (dtype == TQ_F32)
+                    launch_append<float>(d, p, 2, st);
+                else
+                    launch_append<uint16_t>(d, p, 2, st);
+                if ((rc = launch_status(fn)) != TQ_OK)
+                    return rc;
+                p.n_layers = 0;
+            }
+            if (l == l1)
+                break;
+            if (c->head_dim[l] != d)
+                continue;
+            const int i = l - l0, n = p.n_layers++;
+            p.side[0].src[n] = k_new[i];
+            p.side[0].packed[n] = c->k_packed[l];
+            p.side[0].norms[n] = c->k_norms[l];
+            p.side[1].src[n] = v_new[i];
+            p.side[1].packed[n] = c->v_packed[l];
+            p.side[1].norms[n] = c->v_norms[l];
+        }
+    }
+    return TQ_OK;
+}

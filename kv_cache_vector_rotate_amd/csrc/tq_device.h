@@ -1,0 +1,263 @@
+// Device building blocks shared by the codec and attention kernels (gfx950,
+// wave64).
+//
+// Row layout in registers: a row of D coordinates is held by P = D / 32
+// neighbouring lanes of one wavefront, 32 consecutive coordinates per lane
+// (lane `sub` of the group holds coordinates [32*sub, 32*sub + 32)).  A wave
+// therefore carries 64 / P rows at once: 8 rows of 256, 16 rows of 128 or 32
+// rows of 64 coordinates (Shape<D>).  Each lane loads and stores one
+// contiguous slice, so global accesses are contiguous per lane and per row.
+//
+// Walsh-Hadamard transform ("TurboQuant KV Cache Compression — Spec",
+// "Hadamard Transform Detail": Sylvester butterflies over log2(d) stages):
+// the five stages over coordinate bits 0..4 run inside a lane on registers;
+// the stages over bits 5.. pair lane `sub` with lane `sub ^ m` and run with
+// DPP quad permutes (m = 1, 2) or ds_swizzle xor (m = 4, 8), never through
+// LDS memory.  A butterfly keeps (a + b) in the lower lane and (a - b) in the
+// upper lane of the pair, exactly as the in-lane stages do.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tqd {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCPL = 32;          // coordinates per lane
+constexpr int kBlock = 256;       // threads per workgroup (4 waves)
+
+// Bucketize table: the unit interval of u is cut into kLutBins equal bins of
+// width 1/128 over [-1.0625, 1.0625) (|u| <= 1 for every finite row, up to
+// rounding).  Bin i stores the number of boundaries below its (slightly
+// widened) left edge and the single boundary that may fall inside it, so
+// idx(u) = base + (u > boundary_in_bin).  The host checks that boundaries are
+// further apart than a widened bin, so a bin never holds two.
+constexpr int kLutBins = 272;
+constexpr float kLutScale = 128.0f;   // bins per unit of u
+constexpr float kLutOffset = 136.0f;  // bin of u = 0 is 136
+constexpr float kLutSlack = 1e-5f;    // widening of each bin, in units of u
+
+template <int D>
+struct Shape {
+    static constexpr int P = D / kCPL;        // lanes per row
+    static constexpr int RPW = 64 / P;        // rows per wave
+    static constexpr int RPB = RPW * (kBlock / 64);  // rows per workgroup pass
+};
+
+// value of lane (lane ^ M) within the wave, for M in {1, 2, 4, 8, 16}
+template <int M>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    int x = __float_as_int(v);
+    if constexpr (M == 1)
+        x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    else if constexpr (M == 2)
+        x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    else if constexpr (M == 4)
+        x = __builtin_amdgcn_ds_swizzle(x, 0x101F);             // and 0x1f, xor 4
+    else if constexpr (M == 8)
+        x = __builtin_amdgcn_ds_swizzle(x, 0x201F);             // and 0x1f, xor 8
+    else
+        x = __builtin_amdgcn_ds_swizzle(x, 0x401F);             // and 0x1f, xor 16
+    return __int_as_float(x);
+}
+
+template <int P>
+__device__ __forceinline__ float sum_across(float x)
+{
+    if constexpr (P > 1) x += lane_xor<1>(x);
+    if constexpr (P > 2) x += lane_xor<2>(x);
+    if constexpr (P > 4) x += lane_xor<4>(x);
+    if constexpr (P > 8) x += lane_xor<8>(x);
+    if constexpr (P > 16) x += lane_xor<16>(x);
+    return x;
+}
+
+template <int P>
+__device__ __forceinline__ float max_across(float x)
+{
+    if constexpr (P > 1) x = fmaxf(x, lane_xor<1>(x));
+    if constexpr (P > 2) x = fmaxf(x, lane_xor<2>(x));
+    if constexpr (P > 4) x = fmaxf(x, lane_xor<4>(x));
+    if constexpr (P > 8) x = fmaxf(x, lane_xor<8>(x));
+    if constexpr (P > 16) x = fmaxf(x, lane_xor<16>(x));
+    return x;
+}
+
+// in-lane stages (coordinate bits 0..4), unnormalised
+__device__ __forceinline__ void fwht_lane(float (&v)[kCPL])
+{
+#pragma unroll
+    for (int h = 1; h < kCPL; h *= 2) {
+#pragma unroll
+        for (int i = 0; i < kCPL; i++) {
+            if ((i & h) == 0) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
+template <int M>
+__device__ __forceinline__ void fwht_cross_stage(float (&v)[kCPL], int sub)
+{
+    // lower lane of the pair: a + b; upper lane: a - b = partner - own
+    const float sg = (sub & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kCPL; i++)
+        v[i] = fmaf(sg, v[i], lane_xor<M>(v[i]));
+}
+
+// full unnormalised transform of a row held by P lanes
+template <int P>
+__device__ __forceinline__ void fwht_row(float (&v)[kCPL], int sub)
+{
+    fwht_lane(v);
+    if constexpr (P > 1) fwht_cross_stage<1>(v, sub);
+    if constexpr (P > 2) fwht_cross_stage<2>(v, sub);
+    if constexpr (P > 4) fwht_cross_stage<4>(v, sub);
+    if constexpr (P > 8) fwht_cross_stage<8>(v, sub);
+}
+
+// negate coordinate k when bit k of mask is set (sign diagonal D)
+__device__ __forceinline__ void apply_signs(float (&v)[kCPL], uint32_t mask)
+{
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        v[k] = __uint_as_float(__float_as_uint(v[k]) ^ ((mask << (31 - k)) & 0x80000000u));
+}
+
+// ---------------------------------------------------------------- row I/O
+
+__device__ __forceinline__ void load_slice(const float *p, float (&v)[kCPL])
+{
+    const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        f32x4 t = __builtin_nontemporal_load(q + j);
+        v[4 * j + 0] = t.x;
+        v[4 * j + 1] = t.y;
+        v[4 * j + 2] = t.z;
+        v[4 * j + 3] = t.w;
+    }
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits
+__device__ __forceinline__ void load_slice(const uint16_t *p, float (&v)[kCPL])
+{
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < kCPL / 8; j++) {
+        u32x4 t = __builtin_nontemporal_load(q + j);
+        uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            v[8 * j + 2 * m] = __uint_as_float(w[m] << 16);
+            v[8 * j + 2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_slice(float *p, const float (&v)[kCPL])
+{
+    f32x4 *q = reinterpret_cast<f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        f32x4 t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        __builtin_nontemporal_store(t, q + j);
+    }
+}
+
+// ------------------------------------------------------------ bit packing
+// Index k of a lane's slice occupies bits [k*BITS, (k+1)*BITS) of the lane's
+// BITS 32-bit words (little-endian), which is the row's bitstream restricted
+// to that slice: the slice starts at bit 32*BITS*sub of the row, a multiple
+// of 32.
+
+template <int BITS>
+__device__ __forceinline__ void put_index(uint32_t (&w)[BITS], int k, uint32_t idx)
+{
+    const int bit = k * BITS, word = bit >> 5, off = bit & 31;
+    w[word] |= idx << off;
+    if (off + BITS > 32)
+        w[word + 1] |= idx >> (32 - off);
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t get_index(const uint32_t (&w)[BITS], int k)
+{
+    const int bit = k * BITS, word = bit >> 5, off = bit & 31;
+    uint32_t v = w[word] >> off;
+    if (off + BITS > 32)
+        v |= w[word + 1] << (32 - off);
+    return v & ((1u << BITS) - 1u);
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_words(uint8_t *p, const uint32_t (&w)[BITS])
+{
+    if constexpr (BITS == 4) {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    } else {
+        uint32_t *q = reinterpret_cast<uint32_t *>(p);
+#pragma unroll
+        for (int j = 0; j < BITS; j++)
+            q[j] = w[j];
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[BITS])
+{
+    if constexpr (BITS == 4) {
+        uint4 t = *reinterpret_cast<const uint4 *>(p);
+        w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+    } else if constexpr (BITS == 2) {
+        uint2 t = *reinterpret_cast<const uint2 *>(p);
+        w[0] = t.x; w[1] = t.y;
+    } else {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+        for (int j = 0; j < BITS; j++)
+            w[j] = q[j];
+    }
+}
+
+// ----------------------------------------------------------- bucketize
+
+// Fill the bucketize table from the (levels - 1) boundaries.  Every thread of
+// the block takes part; the caller synchronises afterwards.
+__device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbnd)
+{
+    for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) {
+        const float lo = (float)(i - (int)kLutOffset) * (1.0f / kLutScale) - kLutSlack;
+        const float hi = (float)(i + 1 - (int)kLutOffset) * (1.0f / kLutScale) + kLutSlack;
+        int base = 0;
+        float inside = __builtin_huge_valf();
+        for (int j = 0; j < nbnd; j++) {
+            const float b = bnd[j];
+            if (b < lo)
+                base++;
+            else if (b <= hi && inside == __builtin_huge_valf())
+                inside = b;
+        }
+        lut[i] = make_float2(inside, __int_as_float(base));
+    }
+}
+
+// idx = #{j : b_j < u}, via the table
+__device__ __forceinline__ uint32_t bucketize(float u, const float2 *lut)
+{
+    float g = fmaf(u, kLutScale, kLutOffset);
+    g = fminf(fmaxf(g, 0.0f), (float)(kLutBins - 1));  // also maps NaN to bin 0
+    const float2 e = lut[(int)g];
+    return (uint32_t)__float_as_int(e.y) + (u > e.x ? 1u : 0u);
+}
+
+}  // namespace tqd

@@ -1,0 +1,78 @@
+"""Comparison helpers for the GPU-vs-oracle parity tests.
+
+Tolerances (the task's contract for this codec, restated):
+  * packed indices: bit-exact, except at coordinates whose normalised value u
+    (oracle, fp64) lies within 1e-6 of a decision boundary; such mismatches
+    are counted and must be at most 1e-5 of all coordinates;
+  * norms: |n_gpu - n_oracle| <= 1e-5 * n_oracle;
+  * decoded rows (compared on identical packed input, so index flips cannot
+    leak in): max_i |x_gpu - x_oracle| <= 1e-5 * ||x_oracle||_2 per row;
+  * attention outputs: within 2e-3 absolute (fp32 accumulation).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BAND = 1e-6
+BAND_FRACTION = 1e-5
+NORM_RTOL = 1e-5
+DECODE_RTOL = 1e-5
+ATTN_ATOL = 2e-3
+
+
+def unpack_rows(packed: np.ndarray, d: int, bits: int) -> np.ndarray:
+    """Indices [n, d] from packed rows [n, d*bits/8] (little-endian bitstream)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8).reshape(-1, d * bits // 8)
+    b = np.unpackbits(p, axis=1, bitorder="little").reshape(p.shape[0], d, bits)
+    return (b.astype(np.uint16) << np.arange(bits, dtype=np.uint16)).sum(-1).astype(np.uint8)
+
+
+def check_indices(gpu_packed, orc_packed, u, d, bits, boundaries, total_coords=None):
+    """Returns (mismatches, in_band_mismatches); raises if a mismatch lies
+    outside the band or the in-band count exceeds the allowed fraction."""
+    ig = unpack_rows(gpu_packed, d, bits)
+    io = unpack_rows(orc_packed, d, bits)
+    mism = ig != io
+    n_mism = int(mism.sum())
+    if n_mism:
+        b = np.asarray(boundaries, np.float64)
+        dist = np.abs(np.asarray(u, np.float64)[..., None] - b).min(-1)
+        outside = mism & (dist > BAND)
+        assert not outside.any(), (
+            f"{int(outside.sum())} index mismatches outside the 1e-6 band; first at "
+            f"{np.argwhere(outside)[:3].tolist()}")
+    total = total_coords if total_coords is not None else ig.size
+    assert n_mism <= BAND_FRACTION * total + 1e-12, f"{n_mism} in-band mismatches of {total}"
+    return n_mism
+
+
+def check_norms(gpu, orc):
+    gpu = np.asarray(gpu, np.float64)
+    orc = np.asarray(orc, np.float64)
+    err = np.abs(gpu - orc)
+    ok = err <= NORM_RTOL * np.abs(orc)
+    assert ok.all(), f"norm mismatch at {np.argwhere(~ok)[:3].ravel().tolist()}: " \
+                     f"{gpu[~ok][:3]} vs {orc[~ok][:3]}"
+
+
+def check_decoded(gpu, orc):
+    gpu = np.asarray(gpu, np.float64)
+    orc = np.asarray(orc, np.float64)
+    d = orc.shape[-1]
+    gpu = gpu.reshape(-1, d)
+    orc = orc.reshape(-1, d)
+    err = np.abs(gpu - orc).max(axis=1)
+    lim = DECODE_RTOL * np.linalg.norm(orc, axis=1)
+    ok = err <= lim
+    assert ok.all(), f"decode mismatch rows {np.argwhere(~ok)[:3].ravel().tolist()}: " \
+                     f"err {err[~ok][:3]} limit {lim[~ok][:3]}"
+    return float((err / np.maximum(np.linalg.norm(orc, axis=1), 1e-30)).max())
+
+
+def check_attention(gpu, orc):
+    gpu = np.asarray(gpu, np.float64)
+    orc = np.asarray(orc, np.float64)
+    err = np.abs(gpu - orc).max()
+    assert err <= ATTN_ATOL, f"attention max abs error {err}"
+    rel = np.linalg.norm(gpu - orc) / max(np.linalg.norm(orc), 1e-30)
+    return float(err), float(rel)

@@ -1,0 +1,187 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+its host-side pieces agree with the oracle, and argument validation and the
+HIP-error path behave as the header states.  No kernel is launched."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def tq():
+    import kv_cache_vector_rotate_amd as tq
+    tq.lib()
+    return tq
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(tq):
+    names = _declared_functions()
+    assert "tq_encode" in names and "tq_attn_decode" in names
+    L = ctypes.CDLL(tq.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+    from kv_cache_vector_rotate_amd import _abi
+    assert sorted(_abi.EXPORTS) == names
+
+
+def test_version_and_row_bytes(tq):
+    assert "gfx950" in tq.tq_version()
+    for d in (64, 128, 256):
+        for b in (2, 3, 4):
+            assert tq.tq_packed_row_bytes(d, b) == d * b // 8
+    assert tq.tq_packed_row_bytes(96, 3) == 36
+    assert tq.tq_packed_row_bytes(0, 4) == 0 and tq.tq_packed_row_bytes(64, 9) == 0
+
+
+@pytest.mark.parametrize("d", [2, 64, 128, 256, 1024])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(tq, orc, d, bits):
+    """Library (incomplete-beta continued fraction) vs oracle (quadrature):
+    independent computations of the same Lloyd-Max fixed point; float tables
+    equal or at most 1 ulp apart."""
+    cb = tq.tq_codebook_init(d, bits)
+    cf, bf = orc.codebook_float(d, bits)
+    assert cb["levels"] == 1 << bits
+    for a, b in ((cb["centroids"], cf), (cb["boundaries"], bf)):
+        ua = a.view(np.int32).astype(np.int64)
+        ub = b.view(np.int32).astype(np.int64)
+        assert np.all(np.abs(ua - ub) <= 1), (a, b)
+    assert cb["boundaries"][(1 << bits) // 2 - 1] == 0.0
+    # distortion: E[X^2] - sum P c^2 under the Beta density; compare with a
+    # direct quadrature of the squared error (scipy)
+    import scipy.integrate
+    import scipy.stats
+    if d >= 4:
+        a = d / 2
+        c = cb["centroids"].astype(np.float64)
+        edges = np.concatenate([[-1.0], cb["boundaries"].astype(np.float64), [1.0]])
+        f = lambda x: scipy.stats.beta.pdf((x + 1) / 2, a, a) / 2
+        tot = sum(scipy.integrate.quad(lambda x: (x - c[j]) ** 2 * f(x), edges[j], edges[j + 1],
+                                       epsabs=1e-15, limit=200)[0] for j in range(len(c)))
+        assert abs(cb["distortion_per_coord"] - tot) < 1e-9 + 1e-6 * tot
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_gaussian_density_codebook(tq, orc, bits):
+    cb = tq.tq_codebook_init(128, bits, tq.TQ_GAUSS_1_OVER_D)
+    cf, _ = orc.codebook_float(128, bits, orc.GAUSS)
+    assert np.all(np.abs(cb["centroids"].view(np.int32).astype(np.int64)
+                         - cf.view(np.int32).astype(np.int64)) <= 1)
+
+
+def test_signs_match_oracle(tq, orc):
+    for seed in (0, 1, 42, 2 ** 63 + 5):
+        assert np.array_equal(tq.tq_signs(256, seed), orc.signs(seed, 256))
+    assert np.array_equal(tq.tq_signs(64, 42), orc.signs(42, 256)[:64])
+
+
+def test_codebook_and_sign_validation(tq):
+    with pytest.raises(tq.TqError) as e:
+        tq.tq_codebook_init(96, 3)
+    assert e.value.status == tq.TQ_EINVAL and "power of two" in str(e.value)
+    for d, b in ((1, 2), (128, 0), (128, 5), (1 << 21, 2)):
+        with pytest.raises(tq.TqError):
+            tq.tq_codebook_init(d, b)
+    with pytest.raises(tq.TqError):
+        tq.tq_codebook_init(128, 2, 7)
+    L = tq.lib()
+    assert L.tq_signs(0, 1, None) == tq.TQ_EINVAL
+
+
+def _c(v):
+    return ctypes.c_void_p(v)
+
+
+def test_encode_decode_validation_without_launch(tq):
+    """Every rejected argument is rejected before any HIP call (no GPU here)."""
+    L = tq.lib()
+    A = _c(4096)          # fake, 16-byte aligned pointers: never dereferenced
+    N = _c(8192)
+    assert L.tq_encode(None, None, 0, 10, 128, 4, 2, 42, A, N, A, N, None) == tq.TQ_EINVAL
+    assert "both" in tq.tq_last_error()
+    assert L.tq_encode(A, None, 7, 10, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 96, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 512, 4, 2, 42, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 128, 1, 2, 42, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 128, 5, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, -1, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(_c(4100), None, 0, 10, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert "aligned" in tq.tq_last_error()
+    assert L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, None, N, None, None, None) == tq.TQ_EINVAL
+    # n_rows == 0 succeeds and launches nothing
+    assert L.tq_encode(A, A, 1, 0, 128, 4, 2, 42, A, N, A, N, None) == tq.TQ_OK
+    assert L.tq_decode(A, N, 0, 128, 4, 42, A, None) == tq.TQ_OK
+    assert L.tq_decode(A, N, 5, 128, 1, 42, A, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_decode(None, N, 5, 128, 4, 42, A, None) == tq.TQ_EINVAL
+    assert L.tq_rotate(A, 0, 0, 128, 42, 0, A, None) == tq.TQ_OK
+    assert L.tq_rotate(A, 0, 3, 100, 42, 0, A, None) == tq.TQ_EINVAL
+
+
+def _desc(tq, n_layers=2, batch=2, n_kv=2, window=8, head_dim=128, bk=4, bv=2):
+    from kv_cache_vector_rotate_amd import _abi
+    hd = (ctypes.c_int32 * n_layers)(*([head_dim] * n_layers))
+    ptrs = [(ctypes.c_void_p * n_layers)(*([4096 * (i + 1)] * n_layers)) for i in range(4)]
+    d = _abi.TqCacheDesc(n_layers, batch, n_kv, window, bk, bv, 42,
+                         ctypes.cast(hd, ctypes.c_void_p),
+                         *[ctypes.cast(p, ctypes.c_void_p) for p in ptrs])
+    d._keep = (hd, ptrs)
+    return d
+
+
+def test_cache_and_attention_validation(tq):
+    L = tq.lib()
+    d = _desc(tq)
+    A = _c(4096)
+    arr = (ctypes.c_void_p * 2)(4096, 4096)
+    assert L.tq_append_row(None, -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
+    assert L.tq_append_row(ctypes.byref(d), 2, arr, arr, 0, 0, None) == tq.TQ_EINVAL
+    assert L.tq_append_row(ctypes.byref(d), -1, arr, arr, 0, -1, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 3, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert "multiple" in tq.tq_last_error()
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 6, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, A, A, 16, None) == tq.TQ_EINVAL
+    assert "workspace" in tq.tq_last_error()
+    ws = L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5)
+    # 2 sequences x 4 query heads x 1 chunk x (128 + 4) floats
+    assert ws == 2 * 4 * 1 * 132 * 4
+    assert L.tq_attn_workspace_bytes(ctypes.byref(d), 5, 4, 5) == 0
+    d2 = _desc(tq, head_dim=96)
+    assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    d3 = _desc(tq, bk=1)
+    assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+
+
+def test_injected_hip_error_path():
+    """TQ_TEST_FAIL_LAUNCH=1 makes the next launch report TQ_EHIP without
+    launching; the following call is unaffected (one shot)."""
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import kv_cache_vector_rotate_amd as tq
+L = tq.lib()
+A = ctypes.c_void_p(4096); N = ctypes.c_void_p(8192)
+rc = L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, A, N, None, None, None)
+msg = tq.tq_last_error()
+rc2 = L.tq_decode(None, N, 5, 128, 4, 42, A, None)
+print(rc, rc2, msg)
+""" % ROOT
+    env = dict(os.environ, TQ_TEST_FAIL_LAUNCH="1", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    rc, rc2, msg = r.stdout.split(" ", 2)
+    assert int(rc) == -3 and "injected" in msg
+    assert int(rc2) == -1

@@ -1,0 +1,106 @@
+"""GPU parity of the append-only ring cache (tq_append_row) and of decoding
+the whole window, against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kvgen
+from _parity import check_decoded, check_indices, check_norms
+
+pytestmark = pytest.mark.gpu
+SEED = 42
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_rotate_amd as tq
+    tq.lib()
+    return tq
+
+
+def _check_slot(orc, rows, packed, norms, d, bits):
+    op, on, u = orc.encode(rows.astype(np.float32), d, bits, SEED, want_u=True)
+    _, bnd = orc.codebook_float(d, bits)
+    check_norms(norms, on)
+    check_indices(packed, op, u, d, bits, bnd)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_append_ring_small_mixed_head_dims(tq, orc, dtype):
+    """3 layers (head_dim 256, 64, 256), batch 3, 2 KV heads, window 5;
+    appends positions 0..11 (the ring wraps twice), all layers per call; the
+    cache must hold exactly the last `window` rows of every (layer, seq, head)
+    and untouched slots must stay as they were."""
+    hd = [256, 64, 256]
+    B, H, W, bk, bv = 3, 2, 5, 4, 3
+    cache = tq.TQCache(3, B, H, W, hd, bk, bv, SEED)
+    hist = {}
+    for pos in range(12):
+        ks = [kvgen.unit_dirs_lognormal((B, H, d), 1000 * pos + l, "cuda").to(dtype)
+              for l, d in enumerate(hd)]
+        vs = [kvgen.unit_dirs_lognormal((B, H, d), 5000 + 1000 * pos + l, "cuda").to(dtype)
+              for l, d in enumerate(hd)]
+        tq.tq_append_row(cache, -1, ks, vs, pos)
+        hist[pos % W] = (ks, vs)
+        if pos == 2:
+            # slots 3, 4 never written yet: still zero
+            assert torch.count_nonzero(cache.k_norms[0][:, :, 3:]).item() == 0
+    torch.cuda.synchronize()
+    for slot, (ks, vs) in hist.items():
+        for l, d in enumerate(hd):
+            for x, bits, pk, nm in ((ks[l], bk, cache.k_packed[l], cache.k_norms[l]),
+                                    (vs[l], bv, cache.v_packed[l], cache.v_norms[l])):
+                rows = x.float().cpu().numpy().reshape(B * H, d)
+                _check_slot(orc, rows, pk[:, :, slot].cpu().numpy().reshape(B * H, -1),
+                            nm[:, :, slot].cpu().numpy().reshape(-1), d, bits)
+
+
+def test_append_single_layer(tq, orc):
+    B, H, W, d = 2, 4, 7, 128
+    cache = tq.TQCache(2, B, H, W, d, 4, 2, SEED)
+    k = kvgen.normal((B, H, d), 1, "cuda")
+    v = kvgen.normal((B, H, d), 2, "cuda")
+    tq.tq_append_row(cache, 1, k, v, 9)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(cache.k_norms[0]).item() == 0
+    slot = 9 % W
+    _check_slot(orc, k.cpu().numpy().reshape(-1, d),
+                cache.k_packed[1][:, :, slot].cpu().numpy().reshape(B * H, -1),
+                cache.k_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 4)
+    _check_slot(orc, v.cpu().numpy().reshape(-1, d),
+                cache.v_packed[1][:, :, slot].cpu().numpy().reshape(B * H, -1),
+                cache.v_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 2)
+
+
+def test_config2_gemma_shaped_step_full_size_sampled(tq, orc):
+    """34 layers, 4 KV heads, head_dim 256, window 512, batch 64, K4/V4, fp32
+    rows with random directions and lognormal(0, 0.5) norms.  Prefill fills
+    the window (one encode per layer), then one step appends a row to every
+    layer at pos 512 (slot 0) and decodes the whole window of every layer."""
+    NL, B, H, W, d = 34, 64, 4, 512, 256
+    cache = tq.TQCache(NL, B, H, W, d, 4, 4, SEED)
+    rng = np.random.default_rng(2)
+    for l in range(NL):
+        k = kvgen.unit_dirs_lognormal((B, H, W, d), 10 + l, "cuda")
+        v = kvgen.unit_dirs_lognormal((B, H, W, d), 100 + l, "cuda")
+        tq.tq_encode(k, v, 4, 4, SEED, cache.k_packed[l], cache.k_norms[l], cache.v_packed[l],
+                     cache.v_norms[l])
+    ks = [kvgen.unit_dirs_lognormal((B, H, d), 300 + l, "cuda") for l in range(NL)]
+    vs = [kvgen.unit_dirs_lognormal((B, H, d), 400 + l, "cuda") for l in range(NL)]
+    tq.tq_append_row(cache, -1, ks, vs, W)
+    out = torch.empty(B, H, W, d, device="cuda")
+    for l in rng.choice(NL, 3, replace=False):
+        for x, pk, nm in ((ks[l], cache.k_packed[l], cache.k_norms[l]),
+                          (vs[l], cache.v_packed[l], cache.v_norms[l])):
+            _check_slot(orc, x.cpu().numpy().reshape(-1, d),
+                        pk[:, :, 0].cpu().numpy().reshape(B * H, -1),
+                        nm[:, :, 0].cpu().numpy().reshape(-1), d, 4)
+            tq.tq_decode(pk, nm, d, 4, SEED, out=out)
+            torch.cuda.synchronize()
+            sel = rng.choice(B * H * W, 2048, replace=False)
+            gp = pk.reshape(-1, d // 2)[torch.from_numpy(sel).cuda()].cpu().numpy()
+            gn = nm.reshape(-1)[torch.from_numpy(sel).cuda()].cpu().numpy()
+            gx = out.reshape(-1, d)[torch.from_numpy(sel).cuda()].cpu().numpy()
+            check_decoded(gx, orc.decode(gp, gn, d, 4, SEED))

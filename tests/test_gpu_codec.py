@@ -1,0 +1,197 @@
+"""GPU parity of rotate / encode / decode against the fp64 oracle.
+
+Every case calls the HIP kernels through the C ABI (via the thin binding) and
+compares element by element with the oracle on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvgen
+from _parity import (check_decoded, check_indices, check_norms, unpack_rows)
+
+pytestmark = pytest.mark.gpu
+SEED = 42
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_vector_rotate_amd as tq
+    tq.lib()
+    return tq
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
+
+
+def _encode_check(tq, orc, x, d, bits, density_seed=SEED):
+    """Encode x (device, [n, d]) on the GPU, compare with the oracle; returns
+    (gpu packed, gpu norms)."""
+    kp, kn, _, _ = tq.tq_encode(x, None, bits, 2, density_seed)
+    torch.cuda.synchronize()
+    xh = _np(x).reshape(-1, d).astype(np.float32)
+    op, on, u = orc.encode(xh, d, bits, density_seed, want_u=True)
+    _, bnd = orc.codebook_float(d, bits)
+    gp, gn = kp.cpu().numpy().reshape(-1, d * bits // 8), kn.cpu().numpy().reshape(-1)
+    check_norms(gn, on)
+    check_indices(gp, op, u, d, bits, bnd)
+    return gp, gn
+
+
+def test_config1_round_trip_full(tq, orc):
+    """4096 rows x 128, fp32 N(0,1), K4, seed 42: encode, decode, cosine."""
+    d, bits = 128, 4
+    x = kvgen.normal((4096, d), 1, "cuda")
+    gp, gn = _encode_check(tq, orc, x, d, bits)
+    kp = torch.from_numpy(gp).cuda()
+    kn = torch.from_numpy(gn).cuda()
+    xd = tq.tq_decode(kp, kn, d, bits, SEED).cpu().numpy()
+    check_decoded(xd, orc.decode(gp, gn, d, bits, SEED))
+    xs = _np(x)
+    cos = (xd * xs).sum(1) / np.linalg.norm(xd, axis=1) / np.linalg.norm(xs, axis=1)
+    assert cos.min() >= 0.88
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_encode_decode_all_bits_ragged(tq, orc, d, dtype):
+    """K and V in one launch with different bit widths; row counts that leave
+    a ragged tail in the last workgroup pass."""
+    n = 1000 + 37
+    k = kvgen.normal((n, d), 11 + d, "cuda", dtype)
+    v = kvgen.normal((n, d), 12 + d, "cuda", dtype) * 3.0
+    for bk, bv in ((4, 2), (3, 3), (2, 4)):
+        kp, kn, vp, vn = tq.tq_encode(k, v, bk, bv, SEED)
+        torch.cuda.synchronize()
+        for x, bits, p, nm in ((k, bk, kp, kn), (v, bv, vp, vn)):
+            xh = _np(x).astype(np.float32)
+            op, on, u = orc.encode(xh, d, bits, SEED, want_u=True)
+            _, bnd = orc.codebook_float(d, bits)
+            gp, gn = p.cpu().numpy(), nm.cpu().numpy()
+            check_norms(gn, on)
+            check_indices(gp, op, u, d, bits, bnd)
+            xd = tq.tq_decode(p, nm, d, bits, SEED).cpu().numpy()
+            check_decoded(xd, orc.decode(gp, gn, d, bits, SEED))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotate_forward_inverse(tq, orc, d):
+    x = kvgen.normal((333, d), 5, "cuda")
+    y = tq.tq_rotate(x, SEED).cpu().numpy()
+    yo = orc.rotate(_np(x).astype(np.float64), SEED)
+    assert np.abs(y - yo).max() <= 1e-6 * np.abs(yo).max()
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(_np(x), axis=1), rtol=1e-5)
+    xb = tq.tq_rotate(torch.from_numpy(y).cuda(), SEED, inverse=True).cpu().numpy()
+    assert np.abs(xb - _np(x)).max() <= 1e-5
+    xi = orc.unrotate(_np(x).astype(np.float64), SEED)
+    yi = tq.tq_rotate(x, SEED, inverse=True).cpu().numpy()
+    assert np.abs(yi - xi).max() <= 1e-6 * np.abs(xi).max()
+    xb16 = x.to(torch.bfloat16)
+    y16 = tq.tq_rotate(xb16, SEED).cpu().numpy()
+    yo16 = orc.rotate(_np(xb16).astype(np.float64), SEED)
+    assert np.abs(y16 - yo16).max() <= 1e-6 * np.abs(yo16).max()
+
+
+def test_edge_rows(tq, orc):
+    """Zero, constant, tiny, huge and single-spike rows; power-of-two scale
+    invariance on the device."""
+    d, bits = 128, 4
+    rng = np.random.default_rng(3)
+    base = rng.standard_normal((8, d)).astype(np.float32)
+    rows = [np.zeros(d, np.float32), np.ones(d, np.float32), -np.ones(d, np.float32),
+            np.eye(d, dtype=np.float32)[5] * 7.0, base[0] * np.float32(1e-30),
+            base[1] * np.float32(1e30), base[2] * np.float32(2.0 ** -126),
+            base[3] * np.float32(3e-41)]
+    x = torch.from_numpy(np.stack(rows + list(base))).cuda()
+    gp, gn = _encode_check(tq, orc, x, d, bits)
+    L = 1 << bits
+    assert gn[0] == 0 and np.all(unpack_rows(gp[:1], d, bits) == L // 2 - 1)
+    xd = tq.tq_decode(torch.from_numpy(gp).cuda(), torch.from_numpy(gn).cuda(), d, bits,
+                      SEED).cpu().numpy()
+    assert np.all(xd[0] == 0)
+    finite = np.isfinite(gn) & (gn > 1e-30) & (gn < 1e30)
+    check_decoded(xd[finite], orc.decode(gp[finite], gn[finite], d, bits, SEED))
+    # constant row: the sign-first order spreads it; round trip keeps cos >= 0.88
+    c = (xd[1] @ rows[1]) / np.linalg.norm(xd[1]) / np.linalg.norm(rows[1])
+    assert c >= 0.88
+    # exact power-of-two scaling leaves the indices unchanged
+    for k in (-90, -20, 20, 90):
+        xs = torch.from_numpy(base * np.float32(2.0 ** k)).cuda()
+        sp, sn, _, _ = tq.tq_encode(xs, None, bits, 2, SEED)
+        assert np.array_equal(sp.cpu().numpy(), gp[8:])
+        assert np.array_equal(sn.cpu().numpy(), gn[8:] * np.float32(2.0 ** k))
+
+
+def test_empty_and_single_row(tq, orc):
+    d = 128
+    x = torch.empty(0, d, device="cuda")
+    kp, kn, _, _ = tq.tq_encode(x, None, 4, 2, SEED)
+    assert kp.numel() == 0 and kn.numel() == 0
+    one = kvgen.normal((1, d), 9, "cuda")
+    _encode_check(tq, orc, one, d, 4)
+
+
+def test_determinism(tq):
+    d = 256
+    x = kvgen.normal((5000, d), 17, "cuda", torch.bfloat16)
+    a = tq.tq_encode(x, x, 3, 2, SEED)
+    b = tq.tq_encode(x, x, 3, 2, SEED)
+    for s, t in zip(a, b):
+        assert torch.equal(s, t)
+    da = tq.tq_decode(a[0], a[1], d, 3, SEED)
+    db = tq.tq_decode(b[0], b[1], d, 3, SEED)
+    assert torch.equal(da, db)
+
+
+def test_config3_bulk_prefill_full_size_sampled(tq, orc):
+    """32 layers x 8 KV heads x 32768 tokens x 128, bf16 AR(1) rho 0.6 with 4
+    outlier channels (x8) per head, K4/V2 in one launch -- the bench's launch
+    -- compared on 4096 sampled rows per side."""
+    L, H, T, d = 32, 8, 32768, 128
+    k = kvgen.ar1_outliers((L, H, T, d), 3, "cuda")
+    v = kvgen.ar1_outliers((L, H, T, d), 103, "cuda")
+    kp, kn, vp, vn = tq.tq_encode(k, v, 4, 2, SEED)
+    torch.cuda.synchronize()
+    n = L * H * T
+    rows = np.sort(np.random.default_rng(3).choice(n, 4096, replace=False))
+    ridx = torch.from_numpy(rows).cuda()
+    for x, bits, p, nm in ((k, 4, kp, kn), (v, 2, vp, vn)):
+        xs = x.reshape(n, d)[ridx].float().cpu().numpy()
+        op, on, u = orc.encode(xs, d, bits, SEED, want_u=True)
+        _, bnd = orc.codebook_float(d, bits)
+        gp = p.reshape(n, -1)[ridx].cpu().numpy()
+        gn = nm.reshape(n)[ridx].cpu().numpy()
+        check_norms(gn, on)
+        check_indices(gp, op, u, d, bits, bnd)
+
+
+def test_config5_long_context_codec_sampled(tq, orc):
+    """K3/V2, one sequence, 131072 tokens, 8 KV heads, head_dim 64 and 256,
+    bf16 Student-t(3): encode and decode per layer (two layers of each head_dim
+    here), compared on sampled rows."""
+    T, H = 131072, 8
+    rng = np.random.default_rng(5)
+    for li, d in enumerate((64, 256, 64, 256)):
+        k = kvgen.student_t((H, T, d), 500 + li, device="cuda")
+        v = kvgen.student_t((H, T, d), 600 + li, device="cuda")
+        kp, kn, vp, vn = tq.tq_encode(k, v, 3, 2, SEED)
+        n = H * T
+        rows = np.sort(rng.choice(n, 2048, replace=False))
+        ridx = torch.from_numpy(rows).cuda()
+        for x, bits, p, nm in ((k, 3, kp, kn), (v, 2, vp, vn)):
+            xs = x.reshape(n, d)[ridx].float().cpu().numpy()
+            op, on, u = orc.encode(xs, d, bits, SEED, want_u=True)
+            _, bnd = orc.codebook_float(d, bits)
+            gp = p.reshape(n, -1)[ridx].cpu().numpy()
+            gn = nm.reshape(n)[ridx].cpu().numpy()
+            check_norms(gn, on)
+            check_indices(gp, op, u, d, bits, bnd)
+            out = tq.tq_decode(p, nm, d, bits, SEED)
+            xd = out.reshape(n, d)[ridx].cpu().numpy()
+            check_decoded(xd, orc.decode(gp, gn, d, bits, SEED))
+            del out
+        del k, v, kp, kn, vp, vn
