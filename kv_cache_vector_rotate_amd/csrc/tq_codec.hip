@@ -59,7 +59,8 @@ __device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int s
     // Rows whose sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or
     // non-finite) are rescaled by an exact power of two first; indices are
     // invariant under such scaling and the norm is scaled back.
-    float nscale = 1.0f;
+    // (ldexpf per element: 2^-e itself is not representable for e < -126)
+    int nexp = 0;
     if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
         float m = 0.0f;
 #pragma unroll
@@ -67,13 +68,10 @@ __device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int s
             m = fmaxf(m, fabsf(v[k]));
         m = max_across<P>(m);
         if (m > 0.0f && m <= FLT_MAX) {
-            int e;
-            (void)frexpf(m, &e);
-            const float sc = ldexpf(1.0f, -e);
+            (void)frexpf(m, &nexp);
 #pragma unroll
             for (int k = 0; k < kCPL; k++)
-                v[k] *= sc;
-            nscale = ldexpf(1.0f, e);
+                v[k] = ldexpf(v[k], -nexp);
             ss = 0.0f;
 #pragma unroll
             for (int k = 0; k < kCPL; k++)
@@ -96,7 +94,7 @@ __device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int s
     if (valid) {
         store_words<BITS>(dst_row + sub * 4 * BITS, w);
         if (sub == 0)
-            *dst_norm = n * nscale;
+            *dst_norm = ldexpf(n, nexp);
     }
 }
 
@@ -465,11 +463,13 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         return tq::fail(TQ_EINVAL, "tq_encode: unknown dtype");
     if (n_rows < 0)
         return tq::fail(TQ_EINVAL, "tq_encode: n_rows < 0");
-    if (!k_rows && !v_rows)
-        return tq::fail(TQ_EINVAL, "tq_encode: both k_rows and v_rows are NULL");
     int rc = check_d(d, fn);
     if (rc != TQ_OK)
         return rc;
+    if (n_rows == 0)
+        return TQ_OK;  // nothing to do; buffers may be NULL
+    if (!k_rows && !v_rows)
+        return tq::fail(TQ_EINVAL, "tq_encode: both k_rows and v_rows are NULL");
     EncodeParams p;
     int sides = 0;
     const void *src[2] = {k_rows, v_rows};
@@ -492,8 +492,6 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         if ((rc = code_table(d, bits[s], &e.code, fn)) != TQ_OK)
             return rc;
     }
-    if (n_rows == 0)
-        return TQ_OK;
     if ((rc = injected(fn)) != TQ_OK)
         return rc;
     p.n_rows = n_rows;

@@ -120,8 +120,9 @@ def test_encode_decode_validation_without_launch(tq):
     assert L.tq_encode(_c(4100), None, 0, 10, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
     assert "aligned" in tq.tq_last_error()
     assert L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, None, N, None, None, None) == tq.TQ_EINVAL
-    # n_rows == 0 succeeds and launches nothing
+    # n_rows == 0 succeeds and launches nothing, NULL buffers included
     assert L.tq_encode(A, A, 1, 0, 128, 4, 2, 42, A, N, A, N, None) == tq.TQ_OK
+    assert L.tq_encode(None, None, 1, 0, 128, 4, 2, 42, None, None, None, None, None) == tq.TQ_OK
     assert L.tq_decode(A, N, 0, 128, 4, 42, A, None) == tq.TQ_OK
     assert L.tq_decode(A, N, 5, 128, 1, 42, A, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_decode(None, N, 5, 128, 4, 42, A, None) == tq.TQ_EINVAL
