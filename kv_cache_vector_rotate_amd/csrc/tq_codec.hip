@@ -35,32 +35,25 @@ struct CodeTable {
 };
 
 // One row: norm, sign, rotate, normalise, bucketize, pack.  `valid` false
-// lanes compute on zeros and store nothing.  The caller has built the
-// bucketize table `lut` for BITS.
+// lanes compute on zeros and store nothing.  `key` addresses the bucketize
+// table built for BITS.
 template <int D, int BITS, typename T>
-__device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int sub,
-                                           uint32_t smask, const float2 *lut,
+__device__ __forceinline__ void encode_row(const RawSlice<T> &raw, bool valid, int sub,
+                                           const SignMasks<T> &sm, uint32_t key,
                                            uint8_t *dst_row, float *dst_norm)
 {
     constexpr int P = Shape<D>::P;
     float v[kCPL];
-    if (valid) {
-        load_slice(src_slice, v);
-    } else {
-#pragma unroll
-        for (int k = 0; k < kCPL; k++)
-            v[k] = 0.0f;
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kCPL; k++)
-        ss = fmaf(v[k], v[k], ss);
+    float ss;
+    convert_signed(raw, sm.xm, v, ss);  // invalid lanes carry a zeroed slice
     ss = sum_across<P>(ss);
     // Rows whose sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or
-    // non-finite) are rescaled by an exact power of two first; indices are
-    // invariant under such scaling and the norm is scaled back.
-    // (ldexpf per element: 2^-e itself is not representable for e < -126)
+    // non-finite) are rescaled by an exact power of two first (ldexpf per
+    // element: 2^-e is not representable for e < -126); indices do not change
+    // under such scaling and the norm is scaled back.  Non-finite rows are
+    // encoded as the zero row (their stored norm is not finite).
     int nexp = 0;
+    float nbad = 0.0f;
     if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
         float m = 0.0f;
 #pragma unroll
@@ -77,12 +70,17 @@ __device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int s
             for (int k = 0; k < kCPL; k++)
                 ss = fmaf(v[k], v[k], ss);
             ss = sum_across<P>(ss);
+        } else if (!(m <= FLT_MAX)) {
+            nbad = ss + m;  // inf or NaN
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                v[k] = 0.0f;
+            ss = 0.0f;
         }
     }
     const float n = sqrtf(ss);
     // u = H(D x) / (sqrt(d) n); zero rows get u = 0
     const float inv = ss > 0.0f ? 1.0f / sqrtf((float)D * ss) : 0.0f;
-    apply_signs(v, smask);
     fwht_row<P>(v, sub);
     uint32_t w[BITS];
 #pragma unroll
@@ -90,11 +88,11 @@ __device__ __forceinline__ void encode_row(const T *src_slice, bool valid, int s
         w[j] = 0u;
 #pragma unroll
     for (int k = 0; k < kCPL; k++)
-        put_index<BITS>(w, k, bucketize(v[k] * inv, lut));
+        put_index<BITS>(w, k, bucketize(v[k] * inv, key));
     if (valid) {
         store_words<BITS>(dst_row + sub * 4 * BITS, w);
         if (sub == 0)
-            *dst_norm = ldexpf(n, nexp);
+            *dst_norm = nbad != 0.0f ? nbad : ldexpf(n, nexp);
     }
 }
 
@@ -113,20 +111,33 @@ struct EncodeParams {
 
 template <int D, typename T, int BITS>
 __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t n_rows,
-                                                   uint32_t smask, const float2 *lut)
+                                                   const SignMasks<T> &sm, uint32_t key)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % P, rig = lane / P;
     const T *src = static_cast<const T *>(s.src);
-    for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows;
-         base += (int64_t)gridDim.x * RPB) {
-        const int64_t row = base + wave * RPW + rig;
+    const int64_t stride = (int64_t)gridDim.x * RPB;
+    int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + rig;
+    RawSlice<T> cur;
+    if (row < n_rows)
+        load_raw(src + row * D + sub * kCPL, cur);
+    else
+        zero_raw(cur);
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows; base += stride) {
+        // issue the next pass's loads before transforming this one
+        const int64_t nrow = row + stride;
+        RawSlice<T> nxt;
+        if (nrow < n_rows)
+            load_raw(src + nrow * D + sub * kCPL, nxt);
+        else
+            zero_raw(nxt);
         const bool valid = row < n_rows;
         const int64_t r = valid ? row : 0;
-        encode_row<D, BITS, T>(src + r * D + sub * kCPL, valid, sub, smask, lut,
-                               s.packed + r * RB, s.norms + r);
+        encode_row<D, BITS, T>(cur, valid, sub, sm, key, s.packed + r * RB, s.norms + r);
+        cur = nxt;
+        row = nrow;
     }
 }
 
@@ -139,11 +150,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
     __syncthreads();
     const int sub = (threadIdx.x & 63) % Shape<D>::P;
-    const uint32_t smask = p.signs[sub];
+    const SignMasks<T> sm(p.signs[sub]);
+    const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, smask, lut); break;
-    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, smask, lut); break;
-    default: encode_contig_loop<D, T, 4>(s, p.n_rows, smask, lut); break;
+    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, sm, key); break;
+    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, sm, key); break;
+    default: encode_contig_loop<D, T, 4>(s, p.n_rows, sm, key); break;
     }
 }
 
@@ -169,7 +181,7 @@ struct AppendParams {
 
 template <int D, typename T, int BITS>
 __device__ __forceinline__ void append_loop(const AppendSide &s, const AppendParams &p,
-                                            uint32_t smask, const float2 *lut)
+                                            const SignMasks<T> &sm, uint32_t key)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
@@ -184,7 +196,12 @@ __device__ __forceinline__ void append_loop(const AppendSide &s, const AppendPar
         const int li = (int)(r / p.bh), j = (int)(r % p.bh);
         const T *src = static_cast<const T *>(s.src[li]) + (int64_t)j * D + sub * kCPL;
         const int64_t dst = (int64_t)j * p.window + p.slot;
-        encode_row<D, BITS, T>(src, valid, sub, smask, lut, s.packed[li] + dst * RB,
+        RawSlice<T> raw;
+        if (valid)
+            load_raw(src, raw);
+        else
+            zero_raw(raw);
+        encode_row<D, BITS, T>(raw, valid, sub, sm, key, s.packed[li] + dst * RB,
                                s.norms[li] + dst);
     }
 }
@@ -197,11 +214,12 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
     build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
     __syncthreads();
     const int sub = (threadIdx.x & 63) % Shape<D>::P;
-    const uint32_t smask = p.signs[sub];
+    const SignMasks<T> sm(p.signs[sub]);
+    const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: append_loop<D, T, 2>(s, p, smask, lut); break;
-    case 3: append_loop<D, T, 3>(s, p, smask, lut); break;
-    default: append_loop<D, T, 4>(s, p, smask, lut); break;
+    case 2: append_loop<D, T, 2>(s, p, sm, key); break;
+    case 3: append_loop<D, T, 3>(s, p, sm, key); break;
+    default: append_loop<D, T, 4>(s, p, sm, key); break;
     }
 }
 
@@ -222,6 +240,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeParams p)
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
     __shared__ float cent[16];
+    __shared__ __attribute__((aligned(16))) float stage[kBlock / 64][kStageFloats];
     if (threadIdx.x < 16)
         cent[threadIdx.x] = p.cent[threadIdx.x];
     __syncthreads();
@@ -229,14 +248,26 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeParams p)
     const int sub = lane % P, rig = lane / P;
     const uint32_t smask = p.signs[sub];
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows;
-         base += (int64_t)gridDim.x * RPB) {
-        const int64_t row = base + wave * RPW + rig;
-        const bool valid = row < p.n_rows;
-        const int64_t r = valid ? row : 0;
-        uint32_t w[BITS];
+    const int64_t stride = (int64_t)gridDim.x * RPB;
+    int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + rig;
+    uint32_t w[BITS];
+    float n;
+    {
+        const int64_t r = row < p.n_rows ? row : 0;
         load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
-        const float n = p.norms[r];
+        n = p.norms[r];
+    }
+    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows; base += stride) {
+        const int64_t row0 = base + wave * RPW;
+        // next pass's packed words and norm, issued before this pass's work
+        const int64_t nrow = row + stride;
+        uint32_t wn[BITS];
+        float nn;
+        {
+            const int64_t r = nrow < p.n_rows ? nrow : 0;
+            load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, wn);
+            nn = p.norms[r];
+        }
         float v[kCPL];
 #pragma unroll
         for (int k = 0; k < kCPL; k++)
@@ -247,8 +278,14 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeParams p)
         for (int k = 0; k < kCPL; k++)
             v[k] *= sc;
         apply_signs(v, smask);
-        if (valid)
-            store_slice(p.out + r * D + sub * kCPL, v);
+        const int64_t left = (p.n_rows - row0) * D;
+        if (left > 0)
+            store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, left);
+#pragma unroll
+        for (int j = 0; j < BITS; j++)
+            w[j] = wn[j];
+        n = nn;
+        row = nrow;
     }
 }
 
@@ -271,9 +308,11 @@ __global__ __launch_bounds__(kBlock) void rotate_kernel(RotateParams p)
     const uint32_t smask = p.signs[sub];
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
     const T *in = static_cast<const T *>(p.in);
+    __shared__ __attribute__((aligned(16))) float stage[kBlock / 64][kStageFloats];
     for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows;
          base += (int64_t)gridDim.x * RPB) {
-        const int64_t row = base + wave * RPW + rig;
+        const int64_t row0 = base + wave * RPW;
+        const int64_t row = row0 + rig;
         const bool valid = row < p.n_rows;
         const int64_t r = valid ? row : 0;
         float v[kCPL];
@@ -286,8 +325,9 @@ __global__ __launch_bounds__(kBlock) void rotate_kernel(RotateParams p)
             v[k] *= inv_sqrt_d;
         if (p.inverse)
             apply_signs(v, smask);
-        if (valid)
-            store_slice(p.out + r * D + sub * kCPL, v);
+        const int64_t left = (p.n_rows - row0) * D;
+        if (left > 0)
+            store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, left);
     }
 }
 

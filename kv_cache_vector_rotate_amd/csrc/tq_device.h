@@ -20,24 +20,33 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tqd {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kCPL = 32;          // coordinates per lane
 constexpr int kBlock = 256;       // threads per workgroup (4 waves)
 
-// Bucketize table: the unit interval of u is cut into kLutBins equal bins of
-// width 1/128 over [-1.0625, 1.0625) (|u| <= 1 for every finite row, up to
-// rounding).  Bin i stores the number of boundaries below its (slightly
-// widened) left edge and the single boundary that may fall inside it, so
-// idx(u) = base + (u > boundary_in_bin).  The host checks that boundaries are
-// further apart than a widened bin, so a bin never holds two.
-constexpr int kLutBins = 272;
-constexpr float kLutScale = 128.0f;   // bins per unit of u
-constexpr float kLutOffset = 136.0f;  // bin of u = 0 is 136
-constexpr float kLutSlack = 1e-5f;    // widening of each bin, in units of u
+// Bucketize table.  u is mapped to bin round(128 u) + 136 by one fma whose
+// float result lands in [2^23, 2^24) (unit spacing), so the bin is the low
+// bits of the float and the table address is one shift-add of those bits.
+// Bin i covers u in [(i - 136.5)/128, (i - 135.5)/128); |u| <= 1 up to
+// rounding for every finite row, so bins 0..271 are the ones reached and
+// the table has slack bins on both ends.  Entry i holds the number of
+// boundaries below its (slightly widened) lower edge and the single boundary
+// that may fall inside it, so idx(u) = base + (u > boundary_in_bin).  The
+// host checks that boundaries are further apart than a widened bin, so a bin
+// never holds two.
+constexpr int kLutBins = 280;
+constexpr float kLutScale = 128.0f;        // bins per unit of u
+constexpr int kLutZero = 136;              // bin of u = 0
+constexpr float kLutMagic = 12583048.0f;   // 1.5 * 2^23 + 136
+constexpr uint32_t kLutMagicBits = 0x4B400000u;  // bits of 1.5 * 2^23
+constexpr float kLutSlack = 1e-5f;         // widening of each bin, in units of u
 
 template <int D>
 struct Shape {
@@ -172,6 +181,43 @@ __device__ __forceinline__ void store_slice(float *p, const float (&v)[kCPL])
     }
 }
 
+// A wave's P-lane row groups cover 64 * 32 consecutive floats of a row-major
+// [rows][D] array (lane l holds floats [32 l, 32 l + 32) of the wave's
+// region).  Storing that straight from registers sends 16 bytes to each of 64
+// different cache lines per instruction; instead the region is passed through
+// a per-wave LDS buffer (rows padded by 4 floats) and written back so that
+// each store instruction covers 1 KiB contiguously.  `valid_floats` limits the
+// stores to the rows that exist.  Wave-local: no workgroup barrier.
+constexpr int kStageStride = kCPL + 4;                 // floats per lane in LDS
+constexpr int kStageFloats = 64 * kStageStride;        // per wave
+
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void store_region_coalesced(float *region, const float (&v)[kCPL],
+                                                       float *stage, int lane,
+                                                       int64_t valid_floats)
+{
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        f32x4 t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        *reinterpret_cast<f32x4 *>(stage + lane * kStageStride + 4 * j) = t;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        const int e = 64 * j + lane;  // float4 index inside the region
+        const f32x4 t = *reinterpret_cast<const f32x4 *>(stage + (e >> 3) * kStageStride + 4 * (e & 7));
+        if ((int64_t)e * 4 < valid_floats)
+            __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(region) + e);
+    }
+    wave_lds_fence();
+}
+
 // ------------------------------------------------------------ bit packing
 // Index k of a lane's slice occupies bits [k*BITS, (k+1)*BITS) of the lane's
 // BITS 32-bit words (little-endian), which is the row's bitstream restricted
@@ -231,13 +277,19 @@ __device__ __forceinline__ void load_words(const uint8_t *p, uint32_t (&w)[BITS]
 
 // ----------------------------------------------------------- bucketize
 
+// LDS byte address of a pointer into LDS
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // Fill the bucketize table from the (levels - 1) boundaries.  Every thread of
 // the block takes part; the caller synchronises afterwards.
 __device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbnd)
 {
     for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) {
-        const float lo = (float)(i - (int)kLutOffset) * (1.0f / kLutScale) - kLutSlack;
-        const float hi = (float)(i + 1 - (int)kLutOffset) * (1.0f / kLutScale) + kLutSlack;
+        const float lo = ((float)(i - kLutZero) - 0.5f) * (1.0f / kLutScale) - kLutSlack;
+        const float hi = ((float)(i - kLutZero) + 0.5f) * (1.0f / kLutScale) + kLutSlack;
         int base = 0;
         float inside = __builtin_huge_valf();
         for (int j = 0; j < nbnd; j++) {
@@ -251,13 +303,124 @@ __device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbn
     }
 }
 
-// idx = #{j : b_j < u}, via the table
-__device__ __forceinline__ uint32_t bucketize(float u, const float2 *lut)
+// Base for bucketize(): LDS address of the table minus the magic offset.
+__device__ __forceinline__ uint32_t lut_key(const float2 *lut)
 {
-    float g = fmaf(u, kLutScale, kLutOffset);
-    g = fminf(fmaxf(g, 0.0f), (float)(kLutBins - 1));  // also maps NaN to bin 0
-    const float2 e = lut[(int)g];
+    return lds_address(lut) - (kLutMagicBits << 3);
+}
+
+// idx = #{j : b_j < u} for finite |u| <= 1.09
+__device__ __forceinline__ uint32_t bucketize(float u, uint32_t key)
+{
+    const float g = fmaf(u, kLutScale, kLutMagic);
+    const uint32_t a = (__float_as_uint(g) << 3) + key;
+    const f32x2 e = *reinterpret_cast<const __attribute__((address_space(3))) f32x2 *>(
+        (uintptr_t)a);
     return (uint32_t)__float_as_int(e.y) + (u > e.x ? 1u : 0u);
 }
+
+// ------------------------------------------------------- signed row loads
+// The sign diagonal is applied while loading, as an xor of the sign bits.
+// For bf16 one mask per 32-bit word covers two coordinates (bits 15 and 31).
+
+// per-lane xor masks for a lane's 32 coordinates (bit k of `mask` = coord k)
+__device__ __forceinline__ void sign_masks_bf16(uint32_t mask, uint32_t (&xm)[kCPL / 2])
+{
+#pragma unroll
+    for (int m = 0; m < kCPL / 2; m++)
+        xm[m] = (((mask >> (2 * m)) & 1u) << 15) | (((mask >> (2 * m + 1)) & 1u) << 31);
+}
+
+__device__ __forceinline__ void sign_masks_f32(uint32_t mask, uint32_t (&xm)[kCPL])
+{
+#pragma unroll
+    for (int k = 0; k < kCPL; k++)
+        xm[k] = ((mask >> k) & 1u) << 31;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Raw slice of one lane (loaded ahead of use to keep loads in flight while
+// the previous row is being transformed).
+template <typename T>
+struct RawSlice;
+template <>
+struct RawSlice<uint16_t> {
+    u32x4 q[kCPL / 8];
+};
+template <>
+struct RawSlice<float> {
+    f32x4 q[kCPL / 4];
+};
+
+template <typename T>
+__device__ __forceinline__ void load_raw(const T *p, RawSlice<T> &r)
+{
+    using V = typename std::remove_reference<decltype(r.q[0])>::type;
+    const V *q = reinterpret_cast<const V *>(p);
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(r.q) / sizeof(r.q[0])); j++)
+        r.q[j] = __builtin_nontemporal_load(q + j);
+}
+
+template <typename T>
+__device__ __forceinline__ void zero_raw(RawSlice<T> &r)
+{
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(r.q) / sizeof(r.q[0])); j++)
+        r.q[j] = 0;
+}
+
+// bf16 slice -> sign-flipped fp32 values and their sum of squares (the sum
+// of squares uses the bf16 dot-product instruction, fp32 accumulate)
+__device__ __forceinline__ void convert_signed(const RawSlice<uint16_t> &r,
+                                               const uint32_t (&xm)[kCPL / 2],
+                                               float (&v)[kCPL], float &ss)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCPL / 8; j++) {
+        const uint32_t w[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const bf16x2_t h = __builtin_bit_cast(bf16x2_t, w[m]);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(h, h, acc, false);
+            const uint32_t s = w[m] ^ xm[4 * j + m];
+            v[8 * j + 2 * m] = __uint_as_float(s << 16);
+            v[8 * j + 2 * m + 1] = __uint_as_float(s & 0xFFFF0000u);
+        }
+    }
+    ss = acc;
+}
+
+__device__ __forceinline__ void convert_signed(const RawSlice<float> &r,
+                                               const uint32_t (&xm)[kCPL],
+                                               float (&v)[kCPL], float &ss)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        const float x[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            acc = fmaf(x[m], x[m], acc);
+            v[4 * j + m] = __uint_as_float(__float_as_uint(x[m]) ^ xm[4 * j + m]);
+        }
+    }
+    ss = acc;
+}
+
+template <typename T>
+struct SignMasks;
+template <>
+struct SignMasks<uint16_t> {
+    uint32_t xm[kCPL / 2];
+    __device__ __forceinline__ explicit SignMasks(uint32_t mask) { sign_masks_bf16(mask, xm); }
+};
+template <>
+struct SignMasks<float> {
+    uint32_t xm[kCPL];
+    __device__ __forceinline__ explicit SignMasks(uint32_t mask) { sign_masks_f32(mask, xm); }
+};
 
 }  // namespace tqd
