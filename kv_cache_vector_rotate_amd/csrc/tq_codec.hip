@@ -159,6 +159,262 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     }
 }
 
+// ------------------------------------------- encode, 64 coordinates per lane
+// For bf16 rows of d in {64, 128} each lane produces 64 output coordinates
+// of one row: with d = 64 a lane owns a row; with d = 128 lanes l and l + 32
+// share row l, lane l + 32 producing the second half of the outputs.  Every
+// lane thus works on the same coordinate indices and the sign diagonal is
+// wave-uniform; it is folded into the butterflies: writing the signed input
+// as s_i x_i and carrying one sign per block, merging blocks [j, j+h) and
+// [j+h, j+2h) (signs s_j and s_{j+h}) gives
+//   a' = s_j (a + r b),  b' = s_j (a - r b),   r = s_j s_{j+h},
+// so a butterfly is two fmas with a uniform r (a scalar register) and every
+// output carries the single sign s_0, which joins 1/||x||.  For d = 128 the
+// stage across the two halves goes first (the stages commute): lane l forms
+// x_k + r_k x_{k+64}, lane l + 32 forms x_k - r_k x_{k+64} (its minus sign
+// applied as an xor on the bf16 words), after which both lanes carry the
+// signs s_0..s_63 and run the same six remaining stages.
+// Global memory is read and written through a per-wave LDS stage so that
+// every load and store instruction covers whole 128-byte lines.
+
+constexpr int kPiece = 128;            // bytes of 64 bf16 coordinates
+constexpr int kPieceStride = kPiece + 16;
+constexpr int kRowStage = 64 * kPieceStride;  // per wave
+
+struct EncodeRowsParams {
+    EncodeSide side[2];
+    int64_t n_rows;
+    uint32_t rbits[4];  // butterfly signs r in the order used (d - 1 bits; 1 = -1)
+    float s0;           // sign carried by every output
+};
+
+// r as a float from the packed bits (uniform: scalar instructions)
+__device__ __forceinline__ float butterfly_sign(const uint32_t (&rb)[4], int i)
+{
+    return __uint_as_float(0x3F800000u | (((rb[i >> 5] >> (i & 31)) & 1u) << 31));
+}
+
+template <int D, int BITS>
+__device__ __forceinline__ void encode_rows_loop(const EncodeSide s, const int64_t n_rows,
+                                                 const uint32_t (&rb)[4], const float s0,
+                                                 uint32_t key, uint8_t *stg)
+{
+    constexpr int NH = D / 64;                 // lanes per row
+    constexpr int RPW = 64 / NH;               // rows per wave
+    constexpr int CB = D * 2;                  // input bytes per row (bf16)
+    constexpr int RB = D * BITS / 8;           // packed bytes per row
+    constexpr int HB = 64 * BITS / 8;          // packed bytes per lane
+    constexpr int NWL = 2 * BITS;              // packed words per lane
+    constexpr int G = HB % 16 == 0 ? 16 : 8;   // store granule (divides HB)
+    constexpr int CROSS = NH - 1;              // signs used by the stage across halves
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane % RPW, half = lane / RPW;
+    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * RPW;
+    const uint8_t *src = static_cast<const uint8_t *>(s.src);
+    const uint32_t flip = half ? 0x80008000u : 0u;
+
+    for (int64_t row0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * RPW; row0 < n_rows;
+         row0 += stride) {
+        const int nvalid = (int)min<int64_t>(RPW, n_rows - row0);
+        // ---- stage the group (8 KiB): 128-byte piece pc of row r at slot pc*RPW + r
+        {
+            u32x4 t[8];
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const int c = 8 * q + (lane >> 3);  // 128-byte chunk of the group
+                if (c / NH < nvalid)
+                    t[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        src + row0 * CB + c * kPiece + (lane & 7) * 16));
+                else
+                    t[q] = 0;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                const int c = 8 * q + (lane >> 3);
+                *reinterpret_cast<u32x4 *>(stg + ((c % NH) * RPW + c / NH) * kPieceStride +
+                                           (lane & 7) * 16) = t[q];
+            }
+        }
+        wave_lds_fence();
+        const uint8_t *sa = stg + row * kPieceStride;              // coordinates 0..63
+        const uint8_t *sb = stg + (RPW + row) * kPieceStride;      // 64..127 (d = 128)
+        // ---- read, convert; sum of squares of this lane's input half
+        float v[64];
+        float ss = 0.0f, mx = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const u32x4 wa = *reinterpret_cast<const u32x4 *>(sa + m * 16);
+            const uint32_t aa[4] = {wa.x, wa.y, wa.z, wa.w};
+            if constexpr (NH == 1) {
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    const bf16x2_t hv = __builtin_bit_cast(bf16x2_t, aa[c]);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(hv, hv, ss, false);
+                    v[8 * m + 2 * c] = __uint_as_float(aa[c] << 16);
+                    v[8 * m + 2 * c + 1] = __uint_as_float(aa[c] & 0xFFFF0000u);
+                }
+            } else {
+                const u32x4 wb = *reinterpret_cast<const u32x4 *>(sb + m * 16);
+                const uint32_t bw[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    const uint32_t own = half ? bw[c] : aa[c];
+                    const bf16x2_t hv = __builtin_bit_cast(bf16x2_t, own);
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(hv, hv, ss, false);
+                    const uint32_t bb = bw[c] ^ flip;
+#pragma unroll
+                    for (int hh = 0; hh < 2; hh++) {
+                        const int k = 8 * m + 2 * c + hh;
+                        const float xa = __uint_as_float(hh ? (aa[c] & 0xFFFF0000u) : (aa[c] << 16));
+                        const float xb = __uint_as_float(hh ? (bb & 0xFFFF0000u) : (bb << 16));
+                        v[k] = fmaf(butterfly_sign(rb, k), xb, xa);
+                    }
+                }
+            }
+        }
+        if constexpr (NH == 2)
+            ss += __shfl_xor(ss, 32);
+        // Rows whose sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or
+        // non-finite) get an exact power-of-two rescale of the transformed
+        // values; rows holding Inf or NaN encode as the zero row and store a
+        // non-finite norm.
+        int nexp = 0;
+        bool bad = false;
+        if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
+            // largest magnitude of the row (both halves)
+#pragma unroll
+            for (int m = 0; m < 8; m++)
+#pragma unroll
+                for (int pc = 0; pc < NH; pc++) {
+                    const u32x4 w4 = *reinterpret_cast<const u32x4 *>((pc ? sb : sa) + m * 16);
+                    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int c = 0; c < 4; c++)
+                        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(ww[c] << 16)),
+                                             fabsf(__uint_as_float(ww[c] & 0xFFFF0000u))));
+                }
+            if (!(mx <= FLT_MAX)) {
+                bad = true;
+            } else if (mx > 0.0f) {
+                (void)frexpf(mx, &nexp);
+                ss = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 8; m++)
+#pragma unroll
+                    for (int pc = 0; pc < NH; pc++) {
+                        const u32x4 w4 = *reinterpret_cast<const u32x4 *>((pc ? sb : sa) + m * 16);
+                        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                        for (int c = 0; c < 4; c++) {
+                            const float x0 = ldexpf(__uint_as_float(ww[c] << 16), -nexp);
+                            const float x1 = ldexpf(__uint_as_float(ww[c] & 0xFFFF0000u), -nexp);
+                            ss = fmaf(x0, x0, ss);
+                            ss = fmaf(x1, x1, ss);
+                        }
+                    }
+#pragma unroll
+                for (int k = 0; k < 64; k++)
+                    v[k] = ldexpf(v[k], -nexp);
+            }
+        }
+        const float n = sqrtf(ss);
+        const float inv = ss > 0.0f ? s0 / sqrtf((float)D * ss) : 0.0f;
+        // ---- remaining stages; the last one is fused with bucketize/pack
+        uint32_t w[NWL];
+#pragma unroll
+        for (int q = 0; q < NWL; q++)
+            w[q] = 0u;
+        int off = 64 * CROSS;
+#pragma unroll
+        for (int h = 1; h < 32; h *= 2) {
+#pragma unroll
+            for (int j = 0; j < 64; j += 2 * h) {
+                const float rr = butterfly_sign(rb, off + j / (2 * h));
+#pragma unroll
+                for (int i = j; i < j + h; i++) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = fmaf(rr, b, a);
+                    v[i + h] = fmaf(-rr, b, a);
+                }
+            }
+            off += 64 / (2 * h);
+        }
+        const float rl = butterfly_sign(rb, off);
+        const float sc = bad ? 0.0f : inv;   // bad rows: u = 0 (the zero-row code)
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            const float a = v[i], b = v[i + 32];
+            const uint32_t i0 = bucketize(fmaf(rl, b, a) * sc, key);
+            const uint32_t i1 = bucketize(fmaf(-rl, b, a) * sc, key);
+#pragma unroll
+            for (int t2 = 0; t2 < 2; t2++) {
+                const int k = t2 ? i + 32 : i;
+                const uint32_t idx = t2 ? i1 : i0;
+                const int bit = k * BITS, wd = bit >> 5, sh = bit & 31;
+                w[wd] |= idx << sh;
+                if (sh + BITS > 32)
+                    w[wd + 1] |= idx >> (32 - sh);
+            }
+        }
+        if (half == 0 && row < nvalid)
+            s.norms[row0 + row] = bad ? ss : ldexpf(n, nexp);
+        wave_lds_fence();
+        // ---- packed rows through LDS, then whole-line stores
+        constexpr int PS = HB + 16;  // padded stride of a lane's packed bytes
+        const int chunk = row * NH + half;  // lane's packed bytes sit at chunk * HB
+#pragma unroll
+        for (int q = 0; q < NWL; q++)
+            *reinterpret_cast<uint32_t *>(stg + chunk * PS + 4 * q) = w[q];
+        wave_lds_fence();
+        uint8_t *dst = s.packed + row0 * RB;
+#pragma unroll
+        for (int q = 0; q < (64 * HB + 64 * G - 1) / (64 * G); q++) {
+            const int e = 64 * q + lane;          // granule index in the region
+            if (e * G < nvalid * RB) {
+                const int owner = (e * G) / HB, o = (e * G) % HB;
+                if constexpr (G == 16) {
+                    const u32x4 t = *reinterpret_cast<const u32x4 *>(stg + owner * PS + o);
+                    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst) + e);
+                } else {
+                    const uint2 t = *reinterpret_cast<const uint2 *>(stg + owner * PS + o);
+                    reinterpret_cast<uint2 *>(dst)[e] = t;
+                }
+            }
+        }
+        wave_lds_fence();
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void encode_rows_side(const EncodeSide s, const int64_t n_rows,
+                                                 const uint32_t (&rb)[4], const float s0,
+                                                 float2 *lut, uint8_t *stg)
+{
+    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
+    __syncthreads();
+    const uint32_t key = lut_key(lut);
+    switch (s.code.bits) {
+    case 2: encode_rows_loop<D, 2>(s, n_rows, rb, s0, key, stg); break;
+    case 3: encode_rows_loop<D, 3>(s, n_rows, rb, s0, key, stg); break;
+    default: encode_rows_loop<D, 4>(s, n_rows, rb, s0, key, stg); break;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
+void encode_rows_kernel(EncodeRowsParams p)
+{
+    __shared__ float2 lut[kLutBins];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][kRowStage];
+    // the side is chosen by a uniform branch: indexing the kernel argument
+    // struct with blockIdx.y would copy it to scratch memory
+    const uint32_t rb[4] = {p.rbits[0], p.rbits[1], p.rbits[2], p.rbits[3]};
+    if (blockIdx.y == 0)
+        encode_rows_side<D>(p.side[0], p.n_rows, rb, p.s0, lut, stage[threadIdx.x >> 6]);
+    else
+        encode_rows_side<D>(p.side[1], p.n_rows, rb, p.s0, lut, stage[threadIdx.x >> 6]);
+}
+
 // ----------------------------------------------------------------- append
 
 constexpr int kMaxAppendLayers = 48;
@@ -410,6 +666,62 @@ int injected(const char *fn)
     return TQ_OK;
 }
 
+// butterfly signs for the row-per-lane encode, in the order the kernel uses:
+// for d = 128 first the 64 signs s_k s_{k+64} of the stage across halves, then
+// (for both d) the stages h = 1, 2, .., 32 over the first 64 signs
+void fill_row_signs(int d, uint64_t seed, EncodeRowsParams &q)
+{
+    int8_t s[128];
+    tq_signs(d, seed, s);
+    for (int w = 0; w < 4; w++)
+        q.rbits[w] = 0u;
+    int off = 0;
+    auto put = [&](int i, int sign) {
+        if (sign < 0)
+            q.rbits[i >> 5] |= 1u << (i & 31);
+    };
+    if (d == 128) {
+        for (int k = 0; k < 64; k++)
+            put(off + k, s[k] * s[k + 64]);
+        off += 64;
+    }
+    for (int h = 1; h < 64; h *= 2) {
+        for (int m = 0; m < 64 / (2 * h); m++)
+            put(off + m, s[2 * h * m] * s[2 * h * m + h]);
+        off += 64 / (2 * h);
+    }
+    q.s0 = (float)s[0];
+}
+
+// workgroups of `kern` that fit on one CU at once (queried once per kernel)
+template <typename K>
+int resident_blocks(K kern)
+{
+    static int v = 0;
+    if (v == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0) != hipSuccess || n < 1)
+            n = 1;
+        v = n;
+    }
+    return v;
+}
+
+template <int D>
+void launch_encode_rows_d(const EncodeRowsParams &q, int sides, hipStream_t st)
+{
+    auto kern = encode_rows_kernel<D>;
+    const int rpw = 64 / (D / 64);  // rows per wave
+    const int64_t groups = (q.n_rows + rpw - 1) / rpw;
+    const int64_t need = (groups + kBlock / 64 - 1) / (kBlock / 64);
+    // the resident workgroups (split between the sides), each looping
+    int64_t cap = (int64_t)device_cus() * resident_blocks(kern) / sides;
+    if (cap < 1)
+        cap = 1;
+    dim3 grid((unsigned)(need < cap ? need : cap), sides), block(kBlock);
+    hipLaunchKernelGGL(kern, grid, block, 0, st, q);
+}
+
 template <typename T>
 void launch_encode(int d, const EncodeParams &p, int sides, hipStream_t st)
 {
@@ -535,8 +847,20 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
     if ((rc = injected(fn)) != TQ_OK)
         return rc;
     p.n_rows = n_rows;
-    tq::sign_words(d, seed, p.signs);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dtype == TQ_BF16 && d <= 128) {
+        EncodeRowsParams q;
+        q.side[0] = p.side[0];
+        q.side[1] = p.side[1];
+        q.n_rows = n_rows;
+        fill_row_signs(d, seed, q);
+        if (d == 64)
+            launch_encode_rows_d<64>(q, sides, st);
+        else
+            launch_encode_rows_d<128>(q, sides, st);
+        return launch_status(fn);
+    }
+    tq::sign_words(d, seed, p.signs);
     if (dtype == TQ_F32)
         launch_encode<float>(d, p, sides, st);
     else
