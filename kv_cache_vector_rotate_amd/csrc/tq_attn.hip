@@ -119,6 +119,8 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     constexpr int RS = D + 4;
     static_assert(kTile == kBlock, "one tile row per thread in the softmax step");
     static_assert(kTile % RPB == 0, "tile covered by whole passes");
+    constexpr int NIT = kTile / RPB;            // row passes per tile
+    constexpr int CH = NIT < 8 ? NIT : 8;       // passes loaded together
 
     __shared__ float2 tabK[NPK];
     __shared__ float2 tabV[NPV];
@@ -176,35 +178,44 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     const int t_end = min(p.T, t_begin + p.chunk_len);
 
     for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        // ---- scores of the tile
+        // ---- scores of the tile; each chunk's loads are all issued before
+        // its arithmetic so that several rows per lane are in flight
 #pragma unroll 1
-        for (int it = 0; it < kTile / RPB; it++) {
-            const int tl = it * RPB + wave * RPW + rig;
-            const int t = t0 + tl;
-            const bool valid = t < t_end;
-            const int64_t row = rowbase + (valid ? t : t_begin);
-            const uint64_t bits = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
-            const float n = p.kn[row];
-            float s[G];
+        for (int it0 = 0; it0 < NIT; it0 += CH) {
+            uint64_t kb[CH];
+            float kn[CH];
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                s[h] = 0.0f;
-#pragma unroll
-            for (int m = 0; m < CPL / 2; m++) {
-                const float2 c = tabK[(bits >> (2 * BK * m)) & (NPK - 1)];
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    s[h] = fmaf(qr[h][2 * m], c.x, s[h]);
-                    s[h] = fmaf(qr[h][2 * m + 1], c.y, s[h]);
-                }
+            for (int c = 0; c < CH; c++) {
+                const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
+                const int64_t row = rowbase + (t < t_end ? t : t_begin);
+                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
+                kn[c] = p.kn[row];
             }
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                s[h] = sum_across<P>(s[h]);
-            if (sub == 0) {
+            for (int c = 0; c < CH; c++) {
+                const int tl = (it0 + c) * RPB + wave * RPW + rig;
+                float s[G];
 #pragma unroll
                 for (int h = 0; h < G; h++)
-                    sc[tl][h] = valid ? s[h] * n : -__builtin_huge_valf();
+                    s[h] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < CPL / 2; m++) {
+                    const float2 cc = tabK[(kb[c] >> (2 * BK * m)) & (NPK - 1)];
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        s[h] = fmaf(qr[h][2 * m], cc.x, s[h]);
+                        s[h] = fmaf(qr[h][2 * m + 1], cc.y, s[h]);
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    s[h] = sum_across<P>(s[h]);
+                if (sub == 0) {
+                    const bool valid = t0 + tl < t_end;
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        sc[tl][h] = valid ? s[h] * kn[c] : -__builtin_huge_valf();
+                }
             }
         }
         __syncthreads();
@@ -241,24 +252,31 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
             for (int k = 0; k < CPL; k++)
                 acc[h][k] *= fac[h];
 #pragma unroll 1
-        for (int it = 0; it < kTile / RPB; it++) {
-            const int tl = it * RPB + wave * RPW + rig;
-            const int t = t0 + tl;
-            const bool valid = t < t_end;
-            const int64_t row = rowbase + (valid ? t : t_begin);
-            const uint64_t bits = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-            const float nv = valid ? p.vn[row] : 0.0f;
-            float w[G];
+        for (int it0 = 0; it0 < NIT; it0 += CH) {
+            uint64_t vb[CH];
+            float vn[CH];
 #pragma unroll
-            for (int h = 0; h < G; h++)
-                w[h] = sc[tl][h] * nv;
+            for (int c = 0; c < CH; c++) {
+                const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
+                const int64_t row = rowbase + (t < t_end ? t : t_begin);
+                vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+                vn[c] = t < t_end ? p.vn[row] : 0.0f;
+            }
 #pragma unroll
-            for (int m = 0; m < CPL / 2; m++) {
-                const float2 c = tabV[(bits >> (2 * BV * m)) & (NPV - 1)];
+            for (int c = 0; c < CH; c++) {
+                const int tl = (it0 + c) * RPB + wave * RPW + rig;
+                float w[G];
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    acc[h][2 * m] = fmaf(w[h], c.x, acc[h][2 * m]);
-                    acc[h][2 * m + 1] = fmaf(w[h], c.y, acc[h][2 * m + 1]);
+                for (int h = 0; h < G; h++)
+                    w[h] = sc[tl][h] * vn[c];
+#pragma unroll
+                for (int m = 0; m < CPL / 2; m++) {
+                    const float2 cc = tabV[(vb[c] >> (2 * BV * m)) & (NPV - 1)];
+#pragma unroll
+                    for (int h = 0; h < G; h++) {
+                        acc[h][2 * m] = fmaf(w[h], cc.x, acc[h][2 * m]);
+                        acc[h][2 * m + 1] = fmaf(w[h], cc.y, acc[h][2 * m + 1]);
+                    }
                 }
             }
         }
