@@ -13,6 +13,8 @@
  *             dequantize / attention), Integration Points (circular
  *             addressing pos % max_seq), Hadamard Transform Detail,
  *             Optimization: Fused dequant-dot.
+ *   [Atlas]   "CITATIONS" (TurboQuant+ integration notes): Prior art item 4
+ *             (N(0, 1/d) codebooks).
  *   [KVC]     "Implementation specification: TurboAngle and TurboQuant-style
  *             KV compression": Core implementation contract (rows [B, d],
  *             power-of-two d, K and V may use different codecs).
@@ -30,8 +32,8 @@
  *     a buffer starts at byte r * tq_packed_row_bytes(d, bits); index i of a
  *     row occupies bits [i*bits, (i+1)*bits) of the row's little-endian
  *     bitstream (3-bit rows are dense: 8 indices per 3 bytes).
- *   - Alignment: fp32/bf16 row buffers and norm buffers 4-byte aligned;
- *     packed buffers 16-byte aligned.  Misaligned pointers -> TQ_EINVAL.
+ *   - Alignment: fp32/bf16 row buffers and packed buffers 16-byte aligned;
+ *     norm buffers 4-byte aligned.  Misaligned pointers -> TQ_EINVAL.
  *   - Device kernels accept d in {64, 128, 256} and bits in {2, 3, 4};
  *     other valid values return TQ_EUNSUPPORTED.
  *   - n_rows == 0 (or an empty context) succeeds and launches nothing.
@@ -59,7 +61,7 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 /* Coordinate density a codebook is optimised for.
  *   TQ_BETA_HALF_D    Beta(d/2, d/2) mapped to [-1, 1]: [Foundry] Step 2.
- *   TQ_GAUSS_1_OVER_D N(0, 1/d): [Atlas citations page] "Prior art" item 4.
+ *   TQ_GAUSS_1_OVER_D N(0, 1/d): [Atlas] "Prior art" item 4.
  * Every call below other than tq_codebook_init_density uses TQ_BETA_HALF_D. */
 typedef enum { TQ_BETA_HALF_D = 0, TQ_GAUSS_1_OVER_D = 1 } tq_density;
 

@@ -159,225 +159,283 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     }
 }
 
-// ------------------------------------------- encode, 64 coordinates per lane
-// For bf16 rows of d in {64, 128} each lane produces 64 output coordinates
-// of one row: with d = 64 a lane owns a row; with d = 128 lanes l and l + 32
-// share row l, lane l + 32 producing the second half of the outputs.  Every
-// lane thus works on the same coordinate indices and the sign diagonal is
-// wave-uniform; it is folded into the butterflies: writing the signed input
-// as s_i x_i and carrying one sign per block, merging blocks [j, j+h) and
-// [j+h, j+2h) (signs s_j and s_{j+h}) gives
-//   a' = s_j (a + r b),  b' = s_j (a - r b),   r = s_j s_{j+h},
-// so a butterfly is two fmas with a uniform r (a scalar register) and every
-// output carries the single sign s_0, which joins 1/||x||.  For d = 128 the
-// stage across the two halves goes first (the stages commute): lane l forms
-// x_k + r_k x_{k+64}, lane l + 32 forms x_k - r_k x_{k+64} (its minus sign
-// applied as an xor on the bf16 words), after which both lanes carry the
-// signs s_0..s_63 and run the same six remaining stages.
-// Global memory is read and written through a per-wave LDS stage so that
-// every load and store instruction covers whole 128-byte lines.
+// --------------------------------------------- encode, one lane per row
+// For bf16 rows of d in {64, 128} lane l of a wave owns row l of a 64-row
+// group.  The rows of the group are staged in LDS (whole-line global loads,
+// the next group's loads in flight while this one is transformed), and each
+// lane reads its own row from there.
+//
+// The first Hadamard stage (across the halves of the row, h = d/2) takes the
+// raw bf16 words: with P = (x_k, x_{k+d/2}) packed from two words by a byte
+// permute and Q = (s_k, +-s_{k+d/2}) the bf16 sign pair, the bf16 dot product
+// instruction gives s_k x_k +- s_{k+d/2} x_{k+d/2} exactly rounded to fp32:
+// sign, conversion and the first stage in one instruction.  The Q words are
+// the same for every row and are read from LDS.  The remaining stages are
+// plain fp32 add/sub; the last one is fused with the scaling to
+// T = 128 u = 128 y / ||x||, which feeds the bucketize table directly.  With
+// d = 128 a lane makes two passes of 64 outputs (coordinates 0..63, then
+// 64..127), each reading the staged row again.
+//
+// The sum of squares uses the same dot product on the raw words.  Rows whose
+// sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or non-finite) take
+// an exact power-of-two rescale of the input instead; rows holding Inf or NaN
+// encode as the zero row and store a non-finite norm.
 
-constexpr int kPiece = 128;            // bytes of 64 bf16 coordinates
-constexpr int kPieceStride = kPiece + 16;
-constexpr int kRowStage = 64 * kPieceStride;  // per wave
-
-struct EncodeRowsParams {
+struct EncodeLaneParams {
     EncodeSide side[2];
     int64_t n_rows;
-    uint32_t rbits[4];  // butterfly signs r in the order used (d - 1 bits; 1 = -1)
-    float s0;           // sign carried by every output
+    uint32_t sbits[4];  // sign bits of the diagonal (bit k set: s_k = -1)
 };
 
-// r as a float from the packed bits (uniform: scalar instructions)
-__device__ __forceinline__ float butterfly_sign(const uint32_t (&rb)[4], int i)
+template <int NWORDS>
+__device__ __forceinline__ void put_bits(uint32_t (&w)[NWORDS], int bit, int nbits, uint32_t idx)
 {
-    return __uint_as_float(0x3F800000u | (((rb[i >> 5] >> (i & 31)) & 1u) << 31));
+    const int wd = bit >> 5, sh = bit & 31;
+    w[wd] |= idx << sh;
+    if (sh + nbits > 32)
+        w[wd + 1] |= idx >> (32 - sh);
+}
+
+// bucketize on T = 128 u against a table built with boundary scale 128
+__device__ __forceinline__ uint32_t bucketize_t(float t, uint32_t key)
+{
+    const float g = t + kLutMagic;
+    const uint32_t a = (__float_as_uint(g) << 3) + key;
+    const f32x2 e = *reinterpret_cast<const __attribute__((address_space(3))) f32x2 *>(
+        (uintptr_t)a);
+    return (uint32_t)__float_as_int(e.y) + (t > e.x ? 1u : 0u);
+}
+
+__device__ __forceinline__ u32x4 lds_u32x4(uint32_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)addr);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// First two stages of pass `pass` for one lane's staged row, from the raw
+// bf16 words: A = (x_{2j}, x_{2j+1}) and B = (x_{2j+d/2}, x_{2j+1+d/2}).  The
+// stage across halves (h = d/2) and the stage h = 1 give
+//   y_{2j}   = s_{2j} x_{2j} + s_{2j+1} x_{2j+1} + sigma (s' x' + s'' x'')
+//   y_{2j+1} = s_{2j} x_{2j} - s_{2j+1} x_{2j+1} + sigma (s' x' - s'' x'')
+// (primes: the partners d/2 further on), i.e. two bf16 dot products each
+// against sign pairs.  sigma = +1 gives output coordinates 0..d/2-1, sigma =
+// -1 the rest.  The sign pairs are the same for every row and sit in LDS:
+// qt[4 (32 s + j) + {0,1,2,3}] = (s_{2j}, s_{2j+1}), (s_{2j}, -s_{2j+1}),
+// sigma (s', s''), sigma (s', -s'') with s = 0 for sigma = +1, 1 for -1.
+//   d = 128: pass p gives v[k] = output 64 p + k, k < 64.
+//   d = 64:  one pass; v[k] = output k for both signs of sigma.
+template <int D>
+__device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, int pass,
+                                            float (&v)[64])
+{
+    constexpr int HB = D;  // bytes of half a row
+#pragma unroll
+    for (int m = 0; m < HB / 16; m++) {
+        const u32x4 wa = *reinterpret_cast<const u32x4 *>(row + 16 * m);
+        const u32x4 wb = *reinterpret_cast<const u32x4 *>(row + HB + 16 * m);
+        const uint32_t a[4] = {wa.x, wa.y, wa.z, wa.w};
+        const uint32_t b[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int j = 4 * m + c;
+            const bf16x2_t A = as_bf16x2(a[c]), B = as_bf16x2(b[c]);
+            const int s0 = D == 128 ? pass : 0;
+            const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * s0 + j));
+            const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
+            const float e0 = __builtin_amdgcn_fdot2_f32_bf16(A, as_bf16x2(q[0]), 0.0f, false);
+            const float e1 = __builtin_amdgcn_fdot2_f32_bf16(A, as_bf16x2(q[1]), 0.0f, false);
+            v[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(q[2]), e0, false);
+            v[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(q[3]), e1, false);
+            if constexpr (D == 64) {
+                const u32x4 r4 = lds_u32x4(qaddr + 16 * (32 + j));
+                v[32 + 2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(r4.z), e0, false);
+                v[33 + 2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(r4.w), e1, false);
+            }
+        }
+        if (m & 1)
+            __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Sum of squares of a staged bf16 row (products exact, fp32 sums).
+template <int D>
+__device__ __forceinline__ float row_sumsq(const uint8_t *row)
+{
+    float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 2 * D / 16; m++) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 16 * m);
+        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; c += 2) {
+            ss0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xw[c]), as_bf16x2(xw[c]), ss0, false);
+            ss1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xw[c + 1]), as_bf16x2(xw[c + 1]), ss1, false);
+        }
+    }
+    return ss0 + ss1;
 }
 
 template <int D, int BITS>
-__device__ __forceinline__ void encode_rows_loop(const EncodeSide s, const int64_t n_rows,
-                                                 const uint32_t (&rb)[4], const float s0,
-                                                 uint32_t key, uint8_t *stg)
+__device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64_t n_rows,
+                                                 const uint32_t key, uint8_t *stg,
+                                                 const uint32_t *qt)
 {
-    constexpr int NH = D / 64;                 // lanes per row
-    constexpr int RPW = 64 / NH;               // rows per wave
-    constexpr int CB = D * 2;                  // input bytes per row (bf16)
-    constexpr int RB = D * BITS / 8;           // packed bytes per row
-    constexpr int HB = 64 * BITS / 8;          // packed bytes per lane
-    constexpr int NWL = 2 * BITS;              // packed words per lane
-    constexpr int G = HB % 16 == 0 ? 16 : 8;   // store granule (divides HB)
-    constexpr int CROSS = NH - 1;              // signs used by the stage across halves
+    constexpr int NP = D / 64;            // passes of 64 outputs
+    constexpr int CB = 2 * D;             // input bytes per row
+    constexpr int SR = CB + 16;           // LDS stride of a staged row
+    constexpr int NCH = 64 * CB / 1024;   // 1 KiB chunks per group
+    constexpr int RPC = 1024 / CB;        // rows per chunk
+    constexpr int LPR = 64 / RPC;         // lanes per row within a chunk
+    constexpr int RB = D * BITS / 8;      // packed bytes per row
+    constexpr int NW = D * BITS / 32;     // packed words per row
+    constexpr int NWP = 2 * BITS;         // packed words per pass
+    constexpr int HL = D / 4;             // half-width of the last stage
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row = lane % RPW, half = lane / RPW;
-    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * RPW;
+    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
     const uint8_t *src = static_cast<const uint8_t *>(s.src);
-    const uint32_t flip = half ? 0x80008000u : 0u;
+    const int crow = lane / LPR, cbyte = (lane % LPR) * 16;
+    const uint8_t *mine = stg + lane * SR;
+    // the sign-pair table's LDS address as an opaque register value: its reads
+    // then take base + immediate offset instead of one materialised address each
+    uint32_t qaddr = lds_address(qt);
+    asm volatile("" : "+v"(qaddr));
 
-    for (int64_t row0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * RPW; row0 < n_rows;
-         row0 += stride) {
-        const int nvalid = (int)min<int64_t>(RPW, n_rows - row0);
-        // ---- stage the group (8 KiB): 128-byte piece pc of row r at slot pc*RPW + r
-        {
-            u32x4 t[8];
+    int64_t g0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 64;
+    u32x4 pf[NCH];
 #pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const int c = 8 * q + (lane >> 3);  // 128-byte chunk of the group
-                if (c / NH < nvalid)
-                    t[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                        src + row0 * CB + c * kPiece + (lane & 7) * 16));
-                else
-                    t[q] = 0;
-            }
+    for (int c = 0; c < NCH; c++)
+        pf[c] = g0 + c * RPC + crow < n_rows
+                    ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + g0 * CB + c * 1024) + lane)
+                    : u32x4{0u, 0u, 0u, 0u};
+    for (; g0 < n_rows; g0 += stride) {
+        const int nvalid = (int)min<int64_t>(64, n_rows - g0);
 #pragma unroll
-            for (int q = 0; q < 8; q++) {
-                const int c = 8 * q + (lane >> 3);
-                *reinterpret_cast<u32x4 *>(stg + ((c % NH) * RPW + c / NH) * kPieceStride +
-                                           (lane & 7) * 16) = t[q];
-            }
-        }
+        for (int c = 0; c < NCH; c++)
+            *reinterpret_cast<u32x4 *>(stg + (c * RPC + crow) * SR + cbyte) = pf[c];
         wave_lds_fence();
-        const uint8_t *sa = stg + row * kPieceStride;              // coordinates 0..63
-        const uint8_t *sb = stg + (RPW + row) * kPieceStride;      // 64..127 (d = 128)
-        // ---- read, convert; sum of squares of this lane's input half
-        float v[64];
-        float ss = 0.0f, mx = 0.0f;
+        {
+            const int64_t gn = g0 + stride;
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const u32x4 wa = *reinterpret_cast<const u32x4 *>(sa + m * 16);
-            const uint32_t aa[4] = {wa.x, wa.y, wa.z, wa.w};
-            if constexpr (NH == 1) {
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const bf16x2_t hv = __builtin_bit_cast(bf16x2_t, aa[c]);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(hv, hv, ss, false);
-                    v[8 * m + 2 * c] = __uint_as_float(aa[c] << 16);
-                    v[8 * m + 2 * c + 1] = __uint_as_float(aa[c] & 0xFFFF0000u);
-                }
-            } else {
-                const u32x4 wb = *reinterpret_cast<const u32x4 *>(sb + m * 16);
-                const uint32_t bw[4] = {wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const uint32_t own = half ? bw[c] : aa[c];
-                    const bf16x2_t hv = __builtin_bit_cast(bf16x2_t, own);
-                    ss = __builtin_amdgcn_fdot2_f32_bf16(hv, hv, ss, false);
-                    const uint32_t bb = bw[c] ^ flip;
-#pragma unroll
-                    for (int hh = 0; hh < 2; hh++) {
-                        const int k = 8 * m + 2 * c + hh;
-                        const float xa = __uint_as_float(hh ? (aa[c] & 0xFFFF0000u) : (aa[c] << 16));
-                        const float xb = __uint_as_float(hh ? (bb & 0xFFFF0000u) : (bb << 16));
-                        v[k] = fmaf(butterfly_sign(rb, k), xb, xa);
-                    }
-                }
-            }
+            for (int c = 0; c < NCH; c++)
+                pf[c] = gn + c * RPC + crow < n_rows
+                            ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + gn * CB + c * 1024) + lane)
+                            : u32x4{0u, 0u, 0u, 0u};
         }
-        if constexpr (NH == 2)
-            ss += __shfl_xor(ss, 32);
-        // Rows whose sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or
-        // non-finite) get an exact power-of-two rescale of the transformed
-        // values; rows holding Inf or NaN encode as the zero row and store a
-        // non-finite norm.
+        uint32_t w[NW];
+#pragma unroll
+        for (int q = 0; q < NW; q++)
+            w[q] = 0u;
+        float t = 0.0f, nstore = 0.0f;
         int nexp = 0;
         bool bad = false;
-        if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
-            // largest magnitude of the row (both halves)
+        {
+            float ss = row_sumsq<D>(mine);
+            if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
+                // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
+                // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
+                // first stage below then runs on it unchanged
+                uint8_t *rw = stg + lane * SR;
+                float mx = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 8; m++)
-#pragma unroll
-                for (int pc = 0; pc < NH; pc++) {
-                    const u32x4 w4 = *reinterpret_cast<const u32x4 *>((pc ? sb : sa) + m * 16);
-                    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+                for (int m = 0; m < CB / 16; m++) {
+                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(rw + 16 * m);
+                    const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
                     for (int c = 0; c < 4; c++)
-                        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(ww[c] << 16)),
-                                             fabsf(__uint_as_float(ww[c] & 0xFFFF0000u))));
+                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
                 }
-            if (!(mx <= FLT_MAX)) {
-                bad = true;
-            } else if (mx > 0.0f) {
-                (void)frexpf(mx, &nexp);
+                bad = !(mx <= FLT_MAX);
+                if (!bad && mx > 0.0f)
+                    (void)frexpf(mx, &nexp);
                 ss = 0.0f;
 #pragma unroll
-                for (int m = 0; m < 8; m++)
+                for (int m = 0; m < CB / 16; m++) {
+                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(rw + 16 * m);
+                    uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-                    for (int pc = 0; pc < NH; pc++) {
-                        const u32x4 w4 = *reinterpret_cast<const u32x4 *>((pc ? sb : sa) + m * 16);
-                        const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                        for (int c = 0; c < 4; c++) {
-                            const float x0 = ldexpf(__uint_as_float(ww[c] << 16), -nexp);
-                            const float x1 = ldexpf(__uint_as_float(ww[c] & 0xFFFF0000u), -nexp);
-                            ss = fmaf(x0, x0, ss);
-                            ss = fmaf(x1, x1, ss);
-                        }
+                    for (int c = 0; c < 4; c++) {
+                        // exact for normal results; parts below 2^-126 of the
+                        // largest magnitude may round, far under fp32 precision
+                        const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
+                        const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
+                        ss = fmaf(x0, x0, ss);
+                        ss = fmaf(x1, x1, ss);
+                        xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
                     }
-#pragma unroll
-                for (int k = 0; k < 64; k++)
-                    v[k] = ldexpf(v[k], -nexp);
-            }
-        }
-        const float n = sqrtf(ss);
-        const float inv = ss > 0.0f ? s0 / sqrtf((float)D * ss) : 0.0f;
-        // ---- remaining stages; the last one is fused with bucketize/pack
-        uint32_t w[NWL];
-#pragma unroll
-        for (int q = 0; q < NWL; q++)
-            w[q] = 0u;
-        int off = 64 * CROSS;
-#pragma unroll
-        for (int h = 1; h < 32; h *= 2) {
-#pragma unroll
-            for (int j = 0; j < 64; j += 2 * h) {
-                const float rr = butterfly_sign(rb, off + j / (2 * h));
-#pragma unroll
-                for (int i = j; i < j + h; i++) {
-                    const float a = v[i], b = v[i + h];
-                    v[i] = fmaf(rr, b, a);
-                    v[i + h] = fmaf(-rr, b, a);
+                    *reinterpret_cast<u32x4 *>(rw + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
                 }
+                if (bad)
+                    ss = mx;  // stored as the norm: not finite
             }
-            off += 64 / (2 * h);
+            t = (ss > 0.0f && !bad) ? 128.0f / sqrtf((float)D * ss) : 0.0f;
+            nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);
         }
-        const float rl = butterfly_sign(rb, off);
-        const float sc = bad ? 0.0f : inv;   // bad rows: u = 0 (the zero-row code)
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            const float a = v[i], b = v[i + 32];
-            const uint32_t i0 = bucketize(fmaf(rl, b, a) * sc, key);
-            const uint32_t i1 = bucketize(fmaf(-rl, b, a) * sc, key);
+        for (int pass = 0; pass < NP; pass++) {
+            float v[64];
+            // reread the row in every pass rather than keep it in registers
+            wave_lds_fence();
+            first_stage<D>(mine, qaddr, pass, v);
+            // remaining stages but the last (h = 1 is part of the first)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; t2++) {
-                const int k = t2 ? i + 32 : i;
-                const uint32_t idx = t2 ? i1 : i0;
-                const int bit = k * BITS, wd = bit >> 5, sh = bit & 31;
-                w[wd] |= idx << sh;
-                if (sh + BITS > 32)
-                    w[wd + 1] |= idx >> (32 - sh);
-            }
+            for (int h = 2; h < HL; h *= 2)
+#pragma unroll
+                for (int j = 0; j < 64; j += 2 * h)
+#pragma unroll
+                    for (int i = j; i < j + h; i++) {
+                        const float a = v[i], b = v[i + h];
+                        v[i] = a + b;
+                        v[i + h] = a - b;
+                    }
+            // last stage, scaled to T = 128 u, bucketized and packed; in
+            // groups of 16 outputs so that the table reads in flight stay few
+#pragma unroll
+            for (int j = 0; j < 64; j += 2 * HL)
+#pragma unroll
+                for (int i = j; i < j + HL; i++) {
+                    const float bt = v[i + HL] * t;
+                    const float ta = fmaf(v[i], t, bt);
+                    const float tb = fmaf(v[i], t, -bt);
+                    put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
+                    put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
+                    if ((i & 7) == 7)
+                        __builtin_amdgcn_sched_barrier(0);
+                }
+            // keep the passes in order: this pass's words are complete here
+            // (otherwise the whole pass can be sunk below the next pass's loads)
+#pragma unroll
+            for (int q = 0; q < NWP; q++)
+                asm volatile("" ::"v"(w[NWP * pass + q]));
         }
-        if (half == 0 && row < nvalid)
-            s.norms[row0 + row] = bad ? ss : ldexpf(n, nexp);
-        wave_lds_fence();
-        // ---- packed rows through LDS, then whole-line stores
-        constexpr int PS = HB + 16;  // padded stride of a lane's packed bytes
-        const int chunk = row * NH + half;  // lane's packed bytes sit at chunk * HB
+        if (lane < nvalid)
+            *as_global(s.norms + g0 + lane) = nstore;
+        wave_lds_fence();  // every lane is done with the staged rows
+        // packed rows, densely (the group's global layout), then whole-line stores
+        if constexpr (RB % 16 == 0) {
 #pragma unroll
-        for (int q = 0; q < NWL; q++)
-            *reinterpret_cast<uint32_t *>(stg + chunk * PS + 4 * q) = w[q];
-        wave_lds_fence();
-        uint8_t *dst = s.packed + row0 * RB;
+            for (int q = 0; q < NW / 4; q++)
+                *reinterpret_cast<u32x4 *>(stg + lane * RB + 16 * q) =
+                    u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+        } else {
 #pragma unroll
-        for (int q = 0; q < (64 * HB + 64 * G - 1) / (64 * G); q++) {
-            const int e = 64 * q + lane;          // granule index in the region
-            if (e * G < nvalid * RB) {
-                const int owner = (e * G) / HB, o = (e * G) % HB;
-                if constexpr (G == 16) {
-                    const u32x4 t = *reinterpret_cast<const u32x4 *>(stg + owner * PS + o);
-                    __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(dst) + e);
-                } else {
-                    const uint2 t = *reinterpret_cast<const uint2 *>(stg + owner * PS + o);
-                    reinterpret_cast<uint2 *>(dst)[e] = t;
+            for (int q = 0; q < NW / 2; q++)
+                *reinterpret_cast<uint2 *>(stg + lane * RB + 8 * q) = make_uint2(w[2 * q], w[2 * q + 1]);
+        }
+        wave_lds_fence();
+        {
+            const int bytes = nvalid * RB;
+            __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + g0 * RB);
+#pragma unroll
+            for (int q = 0; q < (64 * RB + 1023) / 1024; q++) {
+                const int e = 64 * q + lane;  // 16-byte granule of the group's packed rows
+                if (16 * e + 16 <= bytes) {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + 16 * e);
+                    __builtin_nontemporal_store(x, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
+                } else if (16 * e < bytes) {  // an 8-byte tail (RB is a multiple of 8)
+                    *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(dst + 16 * e) =
+                        *reinterpret_cast<const u32x2 *>(stg + 16 * e);
                 }
             }
         }
@@ -386,33 +444,46 @@ __device__ __forceinline__ void encode_rows_loop(const EncodeSide s, const int64
 }
 
 template <int D>
-__device__ __forceinline__ void encode_rows_side(const EncodeSide s, const int64_t n_rows,
-                                                 const uint32_t (&rb)[4], const float s0,
-                                                 float2 *lut, uint8_t *stg)
+__device__ __forceinline__ void encode_lane_side(const EncodeSide s, const int64_t n_rows,
+                                                 float2 *lut, uint8_t *stg, const uint32_t *qt)
 {
-    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
+    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1, kLutScale);
     __syncthreads();
     const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: encode_rows_loop<D, 2>(s, n_rows, rb, s0, key, stg); break;
-    case 3: encode_rows_loop<D, 3>(s, n_rows, rb, s0, key, stg); break;
-    default: encode_rows_loop<D, 4>(s, n_rows, rb, s0, key, stg); break;
+    case 2: encode_lane_loop<D, 2>(s, n_rows, key, stg, qt); break;
+    case 3: encode_lane_loop<D, 3>(s, n_rows, key, stg, qt); break;
+    default: encode_lane_loop<D, 4>(s, n_rows, key, stg, qt); break;
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
-void encode_rows_kernel(EncodeRowsParams p)
+void encode_lane_kernel(EncodeLaneParams p)
 {
     __shared__ float2 lut[kLutBins];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][kRowStage];
+    __shared__ __attribute__((aligned(16))) uint32_t qt[256];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][64 * (2 * D + 16)];
+    static_assert(kBlock == 256, "one sign-pair word per thread");
+    // bf16 sign pairs of the first two stages (layout at first_stage)
+    {
+        const int i = threadIdx.x, sg = i >> 7, j = (i >> 2) & 31, form = i & 3;
+        const uint32_t w0 = p.sbits[0], w1 = p.sbits[1], w2 = p.sbits[2], w3 = p.sbits[3];
+        auto neg = [&](int k) -> uint32_t {  // 1 if s_k = -1
+            const uint32_t w = k < 32 ? w0 : k < 64 ? w1 : k < 96 ? w2 : w3;
+            return (w >> (k & 31)) & 1u;
+        };
+        const int k = (form < 2 ? 0 : D / 2) + 2 * j;
+        const uint32_t lo = neg(k) ^ (form < 2 ? 0u : (uint32_t)sg);
+        const uint32_t hi = neg(k + 1) ^ (form & 1u) ^ (form < 2 ? 0u : (uint32_t)sg);
+        qt[i] = (0x3F80u | (lo << 15)) | ((0x3F80u | (hi << 15)) << 16);
+    }
     // the side is chosen by a uniform branch: indexing the kernel argument
     // struct with blockIdx.y would copy it to scratch memory
-    const uint32_t rb[4] = {p.rbits[0], p.rbits[1], p.rbits[2], p.rbits[3]};
     if (blockIdx.y == 0)
-        encode_rows_side<D>(p.side[0], p.n_rows, rb, p.s0, lut, stage[threadIdx.x >> 6]);
+        encode_lane_side<D>(p.side[0], p.n_rows, lut, stage[threadIdx.x >> 6], qt);
     else
-        encode_rows_side<D>(p.side[1], p.n_rows, rb, p.s0, lut, stage[threadIdx.x >> 6]);
+        encode_lane_side<D>(p.side[1], p.n_rows, lut, stage[threadIdx.x >> 6], qt);
 }
 
 // ----------------------------------------------------------------- append
@@ -666,33 +737,6 @@ int injected(const char *fn)
     return TQ_OK;
 }
 
-// butterfly signs for the row-per-lane encode, in the order the kernel uses:
-// for d = 128 first the 64 signs s_k s_{k+64} of the stage across halves, then
-// (for both d) the stages h = 1, 2, .., 32 over the first 64 signs
-void fill_row_signs(int d, uint64_t seed, EncodeRowsParams &q)
-{
-    int8_t s[128];
-    tq_signs(d, seed, s);
-    for (int w = 0; w < 4; w++)
-        q.rbits[w] = 0u;
-    int off = 0;
-    auto put = [&](int i, int sign) {
-        if (sign < 0)
-            q.rbits[i >> 5] |= 1u << (i & 31);
-    };
-    if (d == 128) {
-        for (int k = 0; k < 64; k++)
-            put(off + k, s[k] * s[k + 64]);
-        off += 64;
-    }
-    for (int h = 1; h < 64; h *= 2) {
-        for (int m = 0; m < 64 / (2 * h); m++)
-            put(off + m, s[2 * h * m] * s[2 * h * m + h]);
-        off += 64 / (2 * h);
-    }
-    q.s0 = (float)s[0];
-}
-
 // workgroups of `kern` that fit on one CU at once (queried once per kernel)
 template <typename K>
 int resident_blocks(K kern)
@@ -708,11 +752,10 @@ int resident_blocks(K kern)
 }
 
 template <int D>
-void launch_encode_rows_d(const EncodeRowsParams &q, int sides, hipStream_t st)
+void launch_encode_lane_d(const EncodeLaneParams &q, int sides, hipStream_t st)
 {
-    auto kern = encode_rows_kernel<D>;
-    const int rpw = 64 / (D / 64);  // rows per wave
-    const int64_t groups = (q.n_rows + rpw - 1) / rpw;
+    auto kern = encode_lane_kernel<D>;
+    const int64_t groups = (q.n_rows + 63) / 64;  // 64 rows per wave
     const int64_t need = (groups + kBlock / 64 - 1) / (kBlock / 64);
     // the resident workgroups (split between the sides), each looping
     int64_t cap = (int64_t)device_cus() * resident_blocks(kern) / sides;
@@ -849,15 +892,17 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
     p.n_rows = n_rows;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == TQ_BF16 && d <= 128) {
-        EncodeRowsParams q;
+        EncodeLaneParams q;
         q.side[0] = p.side[0];
         q.side[1] = p.side[1];
         q.n_rows = n_rows;
-        fill_row_signs(d, seed, q);
+        for (int w = 0; w < 4; w++)
+            q.sbits[w] = 0u;
+        tq::sign_words(d, seed, q.sbits);
         if (d == 64)
-            launch_encode_rows_d<64>(q, sides, st);
+            launch_encode_lane_d<64>(q, sides, st);
         else
-            launch_encode_rows_d<128>(q, sides, st);
+            launch_encode_lane_d<128>(q, sides, st);
         return launch_status(fn);
     }
     tq::sign_words(d, seed, p.signs);

@@ -27,6 +27,7 @@ namespace tqd {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kCPL = 32;          // coordinates per lane
 constexpr int kBlock = 256;       // threads per workgroup (4 waves)
@@ -284,8 +285,11 @@ __device__ __forceinline__ uint32_t lds_address(const void *p)
 }
 
 // Fill the bucketize table from the (levels - 1) boundaries.  Every thread of
-// the block takes part; the caller synchronises afterwards.
-__device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbnd)
+// the block takes part; the caller synchronises afterwards.  The stored
+// boundary is multiplied by `bscale` (a power of two: 1 for tables looked up
+// with u, kLutScale for tables looked up with 128 u).
+__device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbnd,
+                                          float bscale = 1.0f)
 {
     for (int i = threadIdx.x; i < kLutBins; i += blockDim.x) {
         const float lo = ((float)(i - kLutZero) - 0.5f) * (1.0f / kLutScale) - kLutSlack;
@@ -299,7 +303,7 @@ __device__ __forceinline__ void build_lut(float2 *lut, const float *bnd, int nbn
             else if (b <= hi && inside == __builtin_huge_valf())
                 inside = b;
         }
-        lut[i] = make_float2(inside, __int_as_float(base));
+        lut[i] = make_float2(inside * bscale, __int_as_float(base));
     }
 }
 
@@ -339,6 +343,19 @@ __device__ __forceinline__ void sign_masks_f32(uint32_t mask, uint32_t (&xm)[kCP
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// A pointer to device memory as a global-address-space pointer (plain global
+// loads and stores instead of flat ones).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T *as_global(T *p)
+{
+    return (__attribute__((address_space(1))) T *)p;
+}
+
+// Reinterpret a 32-bit word as two bf16 (taken by value: __builtin_bit_cast
+// applied directly to an element of an ext_vector_type value reads element 0
+// with this compiler).
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2_t, w); }
 
 // Raw slice of one lane (loaded ahead of use to keep loads in flight while
 // the previous row is being transformed).
