@@ -557,63 +557,53 @@ struct DecodeParams {
     const float *norms;
     float *out;
     int64_t n_rows;
+    int64_t row_base;  // first row of this launch
     float cent[16];
     uint32_t signs[8];
 };
 
+// One wave per workgroup, one pass of RPW rows per wave, and one launch (or
+// a few, for grids beyond the launch limit) covering all rows: short-lived
+// workgroups keep the write stream in few DRAM pages at a time, which a
+// persistent grid-stride loop does not.  The packed words and the norm are
+// both requested before either is used (one memory round trip, not two).
+constexpr int kDecodeBlock = 64;
+
 template <int D, int BITS>
-__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
 {
-    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW;
     constexpr int RB = D * BITS / 8;
     __shared__ float cent[16];
-    __shared__ __attribute__((aligned(16))) float stage[kBlock / 64][kStageFloats];
+    __shared__ __attribute__((aligned(16))) float stage[kStageFloats];
     if (threadIdx.x < 16)
         cent[threadIdx.x] = p.cent[threadIdx.x];
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const int sub = lane % P, rig = lane / P;
+    const int64_t row0 = p.row_base + (int64_t)blockIdx.x * RPW;
+    if (row0 >= p.n_rows)
+        return;
     const uint32_t smask = p.signs[sub];
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const int64_t stride = (int64_t)gridDim.x * RPB;
-    int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + rig;
     uint32_t w[BITS];
     float n;
     {
-        const int64_t r = row < p.n_rows ? row : 0;
+        const int64_t row = row0 + rig;
+        const int64_t r = row < p.n_rows ? row : row0;
         load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
         n = p.norms[r];
     }
-    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows; base += stride) {
-        const int64_t row0 = base + wave * RPW;
-        // next pass's packed words and norm, issued before this pass's work
-        const int64_t nrow = row + stride;
-        uint32_t wn[BITS];
-        float nn;
-        {
-            const int64_t r = nrow < p.n_rows ? nrow : 0;
-            load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, wn);
-            nn = p.norms[r];
-        }
-        float v[kCPL];
+    float v[kCPL];
 #pragma unroll
-        for (int k = 0; k < kCPL; k++)
-            v[k] = cent[get_index<BITS>(w, k)];
-        fwht_row<P>(v, sub);
-        const float sc = n * inv_sqrt_d;
+    for (int k = 0; k < kCPL; k++)
+        v[k] = cent[get_index<BITS>(w, k)];
+    fwht_row<P>(v, sub);
+    const float sc = n * (1.0f / sqrtf((float)D));
 #pragma unroll
-        for (int k = 0; k < kCPL; k++)
-            v[k] *= sc;
-        apply_signs(v, smask);
-        const int64_t left = (p.n_rows - row0) * D;
-        if (left > 0)
-            store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, left);
-#pragma unroll
-        for (int j = 0; j < BITS; j++)
-            w[j] = wn[j];
-        n = nn;
-        row = nrow;
-    }
+    for (int k = 0; k < kCPL; k++)
+        v[k] *= sc;
+    apply_signs(v, smask);
+    store_region_coalesced(p.out + row0 * D, v, stage, lane, (p.n_rows - row0) * D);
 }
 
 // ----------------------------------------------------------------- rotate
@@ -622,6 +612,7 @@ struct RotateParams {
     const void *in;
     float *out;
     int64_t n_rows;
+    int64_t row_base;  // first row of this launch
     int inverse;
     uint32_t signs[8];
 };
@@ -630,32 +621,27 @@ template <int D, typename T>
 __global__ __launch_bounds__(kBlock) void rotate_kernel(RotateParams p)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
+    __shared__ __attribute__((aligned(16))) float stage[kBlock / 64][kStageFloats];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % P, rig = lane / P;
+    const int64_t row0 = p.row_base + (int64_t)blockIdx.x * RPB + wave * RPW;
+    if (row0 >= p.n_rows)
+        return;
+    const int64_t row = row0 + rig;
+    const int64_t r = row < p.n_rows ? row : row0;
     const uint32_t smask = p.signs[sub];
+    float v[kCPL];
+    load_slice(static_cast<const T *>(p.in) + r * D + sub * kCPL, v);
+    if (!p.inverse)
+        apply_signs(v, smask);
+    fwht_row<P>(v, sub);
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const T *in = static_cast<const T *>(p.in);
-    __shared__ __attribute__((aligned(16))) float stage[kBlock / 64][kStageFloats];
-    for (int64_t base = (int64_t)blockIdx.x * RPB; base < p.n_rows;
-         base += (int64_t)gridDim.x * RPB) {
-        const int64_t row0 = base + wave * RPW;
-        const int64_t row = row0 + rig;
-        const bool valid = row < p.n_rows;
-        const int64_t r = valid ? row : 0;
-        float v[kCPL];
-        load_slice(in + r * D + sub * kCPL, v);
-        if (!p.inverse)
-            apply_signs(v, smask);
-        fwht_row<P>(v, sub);
 #pragma unroll
-        for (int k = 0; k < kCPL; k++)
-            v[k] *= inv_sqrt_d;
-        if (p.inverse)
-            apply_signs(v, smask);
-        const int64_t left = (p.n_rows - row0) * D;
-        if (left > 0)
-            store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, left);
-    }
+    for (int k = 0; k < kCPL; k++)
+        v[k] *= inv_sqrt_d;
+    if (p.inverse)
+        apply_signs(v, smask);
+    store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, (p.n_rows - row0) * D);
 }
 
 // ------------------------------------------------------------ host helpers
@@ -683,6 +669,20 @@ unsigned grid_for(int64_t n_rows, int rows_per_block)
     const int64_t need = (n_rows + rows_per_block - 1) / rows_per_block;
     const int64_t cap = (int64_t)device_cus() * 16;
     return (unsigned)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+// One workgroup per `rpb` rows, in launches of at most kMaxGrid workgroups:
+// calls launch(grid, first_row) for each.
+constexpr int64_t kMaxGrid = 1 << 30;
+
+template <typename F>
+void launch_all(int64_t n_rows, int rpb, F launch)
+{
+    const int64_t per = kMaxGrid * rpb;
+    for (int64_t first = 0; first < n_rows; first += per) {
+        const int64_t rows = n_rows - first < per ? n_rows - first : per;
+        launch(dim3((unsigned)((rows + rpb - 1) / rpb)), first);
+    }
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -789,25 +789,33 @@ void launch_append(int d, const AppendParams &p, int sides, hipStream_t st)
 }
 
 template <int D>
-void launch_decode_d(int bits, const DecodeParams &p, hipStream_t st)
+void launch_decode_d(int bits, const DecodeParams &p0, hipStream_t st)
 {
-    dim3 grid(grid_for(p.n_rows, Shape<D>::RPB)), block(kBlock);
-    switch (bits) {
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, st, p); break;
-    }
+    launch_all(p0.n_rows, Shape<D>::RPW, [&](dim3 grid, int64_t first) {
+        DecodeParams p = p0;
+        p.row_base = first;
+        const dim3 block(kDecodeBlock);
+        switch (bits) {
+        case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, st, p); break;
+        }
+    });
 }
 
 template <typename T>
-void launch_rotate(int d, const RotateParams &p, hipStream_t st)
+void launch_rotate(int d, const RotateParams &p0, hipStream_t st)
 {
-    dim3 block(kBlock);
-    switch (d) {
-    case 64: hipLaunchKernelGGL((rotate_kernel<64, T>), dim3(grid_for(p.n_rows, Shape<64>::RPB)), block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((rotate_kernel<128, T>), dim3(grid_for(p.n_rows, Shape<128>::RPB)), block, 0, st, p); break;
-    default: hipLaunchKernelGGL((rotate_kernel<256, T>), dim3(grid_for(p.n_rows, Shape<256>::RPB)), block, 0, st, p); break;
-    }
+    const int rpb = d == 64 ? Shape<64>::RPB : d == 128 ? Shape<128>::RPB : Shape<256>::RPB;
+    launch_all(p0.n_rows, rpb, [&](dim3 grid, int64_t first) {
+        RotateParams p = p0;
+        p.row_base = first;
+        switch (d) {
+        case 64: hipLaunchKernelGGL((rotate_kernel<64, T>), grid, dim3(kBlock), 0, st, p); break;
+        case 128: hipLaunchKernelGGL((rotate_kernel<128, T>), grid, dim3(kBlock), 0, st, p); break;
+        default: hipLaunchKernelGGL((rotate_kernel<256, T>), grid, dim3(kBlock), 0, st, p); break;
+        }
+    });
 }
 
 }  // namespace

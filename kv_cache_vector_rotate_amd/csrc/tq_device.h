@@ -344,6 +344,18 @@ __device__ __forceinline__ void sign_masks_f32(uint32_t mask, uint32_t (&xm)[kCP
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// a[i] for a lane-varying i < N from a uniform array (kernel arguments): a
+// select chain on scalar values rather than an indexed load
+template <int N>
+__device__ __forceinline__ uint32_t pick(const uint32_t *a, int i)
+{
+    uint32_t v = a[0];
+#pragma unroll
+    for (int j = 1; j < N; j++)
+        v = i == j ? a[j] : v;
+    return v;
+}
+
 // A pointer to device memory as a global-address-space pointer (plain global
 // loads and stores instead of flat ones).
 template <typename T>
