@@ -32,6 +32,7 @@ namespace {
 struct CodeTable {
     float bnd[15];
     int bits;
+    float istep;  // 2 bits: 1 / (128 b) for the boundaries (-b, 0, b); else 0
 };
 
 // One row: norm, sign, rotate, normalise, bucketize, pack.  `valid` false
@@ -191,7 +192,7 @@ template <int NWORDS>
 __device__ __forceinline__ void put_bits(uint32_t (&w)[NWORDS], int bit, int nbits, uint32_t idx)
 {
     const int wd = bit >> 5, sh = bit & 31;
-    w[wd] |= idx << sh;
+    w[wd] = lshl_or(idx, sh, w[wd]);
     if (sh + nbits > 32)
         w[wd + 1] |= idx >> (32 - sh);
 }
@@ -222,8 +223,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // (primes: the partners d/2 further on), i.e. two bf16 dot products each
 // against sign pairs.  sigma = +1 gives output coordinates 0..d/2-1, sigma =
 // -1 the rest.  The sign pairs are the same for every row and sit in LDS:
-// qt[4 (32 s + j) + {0,1,2,3}] = (s_{2j}, s_{2j+1}), (s_{2j}, -s_{2j+1}),
-// sigma (s', s''), sigma (s', -s'') with s = 0 for sigma = +1, 1 for -1.
+// word 4 (32 g + j) + {0,1,2,3} of the table is (s_{2j}, s_{2j+1}),
+// (s_{2j}, -s_{2j+1}), sigma (s', s''), sigma (s', -s'') with g = 0 for sigma
+// = +1 and g = 1 for -1; `qaddr` is the table's LDS byte address.
 //   d = 128: pass p gives v[k] = output 64 p + k, k < 64.
 //   d = 64:  one pass; v[k] = output k for both signs of sigma.
 template <int D>
@@ -240,18 +242,14 @@ __device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, 
 #pragma unroll
         for (int c = 0; c < 4; c++) {
             const int j = 4 * m + c;
-            const bf16x2_t A = as_bf16x2(a[c]), B = as_bf16x2(b[c]);
-            const int s0 = D == 128 ? pass : 0;
-            const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * s0 + j));
-            const uint32_t q[4] = {q4.x, q4.y, q4.z, q4.w};
-            const float e0 = __builtin_amdgcn_fdot2_f32_bf16(A, as_bf16x2(q[0]), 0.0f, false);
-            const float e1 = __builtin_amdgcn_fdot2_f32_bf16(A, as_bf16x2(q[1]), 0.0f, false);
-            v[2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(q[2]), e0, false);
-            v[2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(q[3]), e1, false);
+            const int g = D == 128 ? pass : 0;
+            const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * g + j));
             if constexpr (D == 64) {
                 const u32x4 r4 = lds_u32x4(qaddr + 16 * (32 + j));
-                v[32 + 2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(r4.z), e0, false);
-                v[33 + 2 * j] = __builtin_amdgcn_fdot2_f32_bf16(B, as_bf16x2(r4.w), e1, false);
+                dot2_quad(a[c], b[c], q4.x, q4.y, q4.z, q4.w, r4.z, r4.w, v[2 * j],
+                          v[2 * j + 1], v[32 + 2 * j], v[33 + 2 * j]);
+            } else {
+                dot2_pair(a[c], b[c], q4.x, q4.y, q4.z, q4.w, v[2 * j], v[2 * j + 1]);
             }
         }
         if (m & 1)
@@ -259,13 +257,13 @@ __device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, 
     }
 }
 
-// Sum of squares of a staged bf16 row (products exact, fp32 sums).
-template <int D>
+// Sum of squares of NB bytes of a staged bf16 row (products exact, fp32 sums).
+template <int NB>
 __device__ __forceinline__ float row_sumsq(const uint8_t *row)
 {
     float ss0 = 0.0f, ss1 = 0.0f;
 #pragma unroll
-    for (int m = 0; m < 2 * D / 16; m++) {
+    for (int m = 0; m < NB / 16; m++) {
         const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 16 * m);
         const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -287,7 +285,7 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
     constexpr int SR = CB + 16;           // LDS stride of a staged row
     constexpr int NCH = 64 * CB / 1024;   // 1 KiB chunks per group
     constexpr int RPC = 1024 / CB;        // rows per chunk
-    constexpr int LPR = 64 / RPC;         // lanes per row within a chunk
+    constexpr int LPC = 64 / RPC;         // lanes per row within a chunk
     constexpr int RB = D * BITS / 8;      // packed bytes per row
     constexpr int NW = D * BITS / 32;     // packed words per row
     constexpr int NWP = 2 * BITS;         // packed words per pass
@@ -295,8 +293,8 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
     const uint8_t *src = static_cast<const uint8_t *>(s.src);
-    const int crow = lane / LPR, cbyte = (lane % LPR) * 16;
-    const uint8_t *mine = stg + lane * SR;
+    const int crow = lane / LPC, cbyte = (lane % LPC) * 16;
+    uint8_t *mine = stg + lane * SR;
     // the sign-pair table's LDS address as an opaque register value: its reads
     // then take base + immediate offset instead of one materialised address each
     uint32_t qaddr = lds_address(qt);
@@ -328,19 +326,18 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
         for (int q = 0; q < NW; q++)
             w[q] = 0u;
         float t = 0.0f, nstore = 0.0f;
-        int nexp = 0;
-        bool bad = false;
         {
-            float ss = row_sumsq<D>(mine);
+            float ss = row_sumsq<CB>(mine);
+            int nexp = 0;
+            bool bad = false;
             if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
                 // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
                 // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
                 // first stage below then runs on it unchanged
-                uint8_t *rw = stg + lane * SR;
                 float mx = 0.0f;
 #pragma unroll
                 for (int m = 0; m < CB / 16; m++) {
-                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(rw + 16 * m);
+                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
                     const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
                     for (int c = 0; c < 4; c++)
@@ -352,7 +349,7 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
                 ss = 0.0f;
 #pragma unroll
                 for (int m = 0; m < CB / 16; m++) {
-                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(rw + 16 * m);
+                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
                     uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
                     for (int c = 0; c < 4; c++) {
@@ -364,7 +361,7 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
                         ss = fmaf(x1, x1, ss);
                         xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
                     }
-                    *reinterpret_cast<u32x4 *>(rw + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
+                    *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
                 }
                 if (bad)
                     ss = mx;  // stored as the norm: not finite
@@ -389,25 +386,50 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
                         v[i] = a + b;
                         v[i + h] = a - b;
                     }
-            // last stage, scaled to T = 128 u, bucketized and packed; in
-            // groups of 16 outputs so that the table reads in flight stay few
+            if constexpr (BITS == 2) {
+                // boundaries -b, 0, b are equally spaced: with T' = u / b the
+                // index #{boundaries < u} is 1 - clamp(floor(-T'), -2, 1); the
+                // words collect sum c 4^k and take 0x55..55 - that at the end
+                const float t2 = t * s.code.istep;
 #pragma unroll
-            for (int j = 0; j < 64; j += 2 * HL)
+                for (int j = 0; j < 64; j += 2 * HL)
 #pragma unroll
-                for (int i = j; i < j + HL; i++) {
-                    const float bt = v[i + HL] * t;
-                    const float ta = fmaf(v[i], t, bt);
-                    const float tb = fmaf(v[i], t, -bt);
-                    put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
-                    put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
-                    if ((i & 7) == 7)
-                        __builtin_amdgcn_sched_barrier(0);
-                }
+                    for (int i = j; i < j + HL; i++) {
+                        const float bt = v[i + HL] * t2;
+                        const float ta = fmaf(v[i], t2, bt);
+                        const float tb = fmaf(v[i], t2, -bt);
+                        const int ca = min(max(floor_neg_i32(ta), -2), 1);
+                        const int cb = min(max(floor_neg_i32(tb), -2), 1);
+                        const int ka = 64 * pass + i, kb = ka + HL;
+                        w[ka >> 4] = lshl_add((uint32_t)ca, 2 * (ka & 15), w[ka >> 4]);
+                        w[kb >> 4] = lshl_add((uint32_t)cb, 2 * (kb & 15), w[kb >> 4]);
+                    }
+            } else {
+                // last stage, scaled to T = 128 u, bucketized and packed; in
+                // groups of 16 outputs so that the table reads in flight stay few
+#pragma unroll
+                for (int j = 0; j < 64; j += 2 * HL)
+#pragma unroll
+                    for (int i = j; i < j + HL; i++) {
+                        const float bt = v[i + HL] * t;
+                        const float ta = fmaf(v[i], t, bt);
+                        const float tb = fmaf(v[i], t, -bt);
+                        put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
+                        put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
+                        if ((i & 7) == 7)
+                            __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
             // keep the passes in order: this pass's words are complete here
             // (otherwise the whole pass can be sunk below the next pass's loads)
 #pragma unroll
             for (int q = 0; q < NWP; q++)
                 asm volatile("" ::"v"(w[NWP * pass + q]));
+        }
+        if constexpr (BITS == 2) {
+#pragma unroll
+            for (int q = 0; q < NW; q++)
+                w[q] = 0x55555555u - w[q];
         }
         if (lane < nvalid)
             *as_global(s.norms + g0 + lane) = nstore;
@@ -421,7 +443,7 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64
         } else {
 #pragma unroll
             for (int q = 0; q < NW / 2; q++)
-                *reinterpret_cast<uint2 *>(stg + lane * RB + 8 * q) = make_uint2(w[2 * q], w[2 * q + 1]);
+                *reinterpret_cast<u32x2 *>(stg + lane * RB + 8 * q) = u32x2{w[2 * q], w[2 * q + 1]};
         }
         wave_lds_fence();
         {
@@ -719,6 +741,13 @@ int code_table(int d, int bits, CodeTable *t, const char *fn)
     for (int j = 0; j + 1 < cb.levels - 1; j++)
         if (cb.boundaries[j + 1] - cb.boundaries[j] <= 1.0f / kLutScale + 2.0f * kLutSlack)
             return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": codebook boundaries too close for the bucketize table");
+    t->istep = 0.0f;
+    if (bits == 2) {
+        // the three boundaries are -b, 0, b (the codebook is symmetric)
+        if (!(cb.boundaries[1] == 0.0f && cb.boundaries[0] == -cb.boundaries[2] && cb.boundaries[2] > 0.0f))
+            return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": 2-bit codebook is not symmetric");
+        t->istep = 1.0f / (kLutScale * cb.boundaries[2]);
+    }
     return TQ_OK;
 }
 

@@ -344,6 +344,67 @@ __device__ __forceinline__ void sign_masks_f32(uint32_t mask, uint32_t (&xm)[kCP
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Packed-bf16 dot products in their three-operand form (the compiler only
+// emits the two-operand form, whose accumulator doubles as destination and
+// needs a copy or a zeroing move first):
+//   e0 = A.q0, e1 = A.q1, y0 = B.q2 + e0, y1 = B.q3 + e1,
+// each product exact and each sum rounded once to fp32.  A result of this
+// instruction needs three wait states before a different vector instruction
+// reads it; the compiler cannot see into the asm, so the block ends with
+// them (a chained read as the accumulator of the same instruction needs none).
+__device__ __forceinline__ void dot2_pair(uint32_t A, uint32_t B, uint32_t q0, uint32_t q1,
+                                          uint32_t q2, uint32_t q3, float &y0, float &y1)
+{
+    float e0, e1;
+    asm("v_dot2_f32_bf16 %0, %4, %6, 0\n\t"
+        "v_dot2_f32_bf16 %1, %4, %7, 0\n\t"
+        "v_dot2_f32_bf16 %2, %5, %8, %0\n\t"
+        "v_dot2_f32_bf16 %3, %5, %9, %1\n\t"
+        "s_nop 2"
+        : "=&v"(e0), "=&v"(e1), "=&v"(y0), "=v"(y1)
+        : "v"(A), "v"(B), "v"(q0), "v"(q1), "v"(q2), "v"(q3));
+}
+
+// The same with a second pair sharing e0 and e1: y2 = B.r2 + e0, y3 = B.r3 + e1.
+__device__ __forceinline__ void dot2_quad(uint32_t A, uint32_t B, uint32_t q0, uint32_t q1,
+                                          uint32_t q2, uint32_t q3, uint32_t r2, uint32_t r3,
+                                          float &y0, float &y1, float &y2, float &y3)
+{
+    float e0, e1;
+    asm("v_dot2_f32_bf16 %0, %6, %8, 0\n\t"
+        "v_dot2_f32_bf16 %1, %6, %9, 0\n\t"
+        "v_dot2_f32_bf16 %2, %7, %10, %0\n\t"
+        "v_dot2_f32_bf16 %3, %7, %11, %1\n\t"
+        "v_dot2_f32_bf16 %4, %7, %12, %0\n\t"
+        "v_dot2_f32_bf16 %5, %7, %13, %1\n\t"
+        "s_nop 2"
+        : "=&v"(e0), "=&v"(e1), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=v"(y3)
+        : "v"(A), "v"(B), "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(r2), "v"(r3));
+}
+
+// (a << sh) | b and (a << sh) + b as single instructions (the compiler tends
+// to split them into a shift and a three-input or/add)
+__device__ __forceinline__ uint32_t lshl_or(uint32_t a, uint32_t sh, uint32_t b)
+{
+    uint32_t r;
+    asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(sh), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t sh, uint32_t b)
+{
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(sh), "v"(b));
+    return r;
+}
+
+// floor(-x) as int32 (one instruction; the compiler emits floor and convert)
+__device__ __forceinline__ int floor_neg_i32(float x)
+{
+    int r;
+    asm("v_cvt_flr_i32_f32_e64 %0, -%1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // a[i] for a lane-varying i < N from a uniform array (kernel arguments): a
 // select chain on scalar values rather than an indexed load
 template <int N>
@@ -355,6 +416,9 @@ __device__ __forceinline__ uint32_t pick(const uint32_t *a, int i)
         v = i == j ? a[j] : v;
     return v;
 }
+
+// cache policy of streaming buffer loads: non-temporal
+constexpr int kCpolNT = 2;
 
 // A pointer to device memory as a global-address-space pointer (plain global
 // loads and stores instead of flat ones).
