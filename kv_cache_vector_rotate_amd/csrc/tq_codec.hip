@@ -275,215 +275,237 @@ __device__ __forceinline__ float row_sumsq(const uint8_t *row)
     return ss0 + ss1;
 }
 
-template <int D, int BITS>
-__device__ __forceinline__ void encode_lane_loop(const EncodeSide s, const int64_t n_rows,
-                                                 const uint32_t key, uint8_t *stg,
-                                                 const uint32_t *qt)
+// The 64 rows of a group starting at row g0 of `src`: chunk c of lane l is
+// bytes [1024 c + 16 l, +16) of the group (rows past n_rows read as zeros).
+template <int D>
+__device__ __forceinline__ void load_group(const uint8_t *src, int64_t g0, int64_t n_rows,
+                                           int lane, u32x4 (&pf)[64 * 2 * D / 1024])
 {
-    constexpr int NP = D / 64;            // passes of 64 outputs
-    constexpr int CB = 2 * D;             // input bytes per row
-    constexpr int SR = CB + 16;           // LDS stride of a staged row
-    constexpr int NCH = 64 * CB / 1024;   // 1 KiB chunks per group
-    constexpr int RPC = 1024 / CB;        // rows per chunk
-    constexpr int LPC = 64 / RPC;         // lanes per row within a chunk
-    constexpr int RB = D * BITS / 8;      // packed bytes per row
-    constexpr int NW = D * BITS / 32;     // packed words per row
-    constexpr int NWP = 2 * BITS;         // packed words per pass
-    constexpr int HL = D / 4;             // half-width of the last stage
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
-    const uint8_t *src = static_cast<const uint8_t *>(s.src);
-    const int crow = lane / LPC, cbyte = (lane % LPC) * 16;
-    uint8_t *mine = stg + lane * SR;
-    // the sign-pair table's LDS address as an opaque register value: its reads
-    // then take base + immediate offset instead of one materialised address each
-    uint32_t qaddr = lds_address(qt);
-    asm volatile("" : "+v"(qaddr));
-
-    int64_t g0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 64;
-    u32x4 pf[NCH];
+    constexpr int CB = 2 * D, NCH = 64 * CB / 1024, RPC = 1024 / CB, LPC = 64 / RPC;
+    const int crow = lane / LPC;
 #pragma unroll
     for (int c = 0; c < NCH; c++)
         pf[c] = g0 + c * RPC + crow < n_rows
                     ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + g0 * CB + c * 1024) + lane)
                     : u32x4{0u, 0u, 0u, 0u};
-    for (; g0 < n_rows; g0 += stride) {
-        const int nvalid = (int)min<int64_t>(64, n_rows - g0);
+}
+
+// The group's rows from registers into this wave's LDS stage (row stride SR).
+template <int D>
+__device__ __forceinline__ void stage_group(const u32x4 (&pf)[64 * 2 * D / 1024], uint8_t *stg,
+                                            int lane)
+{
+    constexpr int CB = 2 * D, SR = CB + 16, NCH = 64 * CB / 1024, RPC = 1024 / CB,
+                  LPC = 64 / RPC;
+    const int crow = lane / LPC, cbyte = (lane % LPC) * 16;
 #pragma unroll
-        for (int c = 0; c < NCH; c++)
-            *reinterpret_cast<u32x4 *>(stg + (c * RPC + crow) * SR + cbyte) = pf[c];
-        wave_lds_fence();
-        {
-            const int64_t gn = g0 + stride;
+    for (int c = 0; c < NCH; c++)
+        *reinterpret_cast<u32x4 *>(stg + (c * RPC + crow) * SR + cbyte) = pf[c];
+    wave_lds_fence();
+}
+
+// Encode the staged group of 64 rows starting at row g0 for one side.
+template <int D, int BITS>
+__device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t g0,
+                                             const int64_t n_rows, const uint32_t key,
+                                             uint8_t *stg, const uint32_t qaddr)
+{
+    constexpr int NP = D / 64;            // passes of 64 outputs
+    constexpr int CB = 2 * D;             // input bytes per row
+    constexpr int SR = CB + 16;           // LDS stride of a staged row
+    constexpr int RB = D * BITS / 8;      // packed bytes per row
+    constexpr int NW = D * BITS / 32;     // packed words per row
+    constexpr int NWP = 2 * BITS;         // packed words per pass
+    constexpr int HL = D / 4;             // half-width of the last stage
+    const int lane = threadIdx.x & 63;
+    uint8_t *mine = stg + lane * SR;
+    const int nvalid = (int)min<int64_t>(64, n_rows - g0);
+    uint32_t w[NW];
 #pragma unroll
-            for (int c = 0; c < NCH; c++)
-                pf[c] = gn + c * RPC + crow < n_rows
-                            ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + gn * CB + c * 1024) + lane)
-                            : u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < NW; q++)
+        w[q] = 0u;
+    float t = 0.0f, nstore = 0.0f;
+    {
+        float ss = row_sumsq<CB>(mine);
+        int nexp = 0;
+        bool bad = false;
+        if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
+            // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
+            // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
+            // first stage below then runs on it unchanged
+            float mx = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CB / 16; m++) {
+                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
+                const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
+            }
+            bad = !(mx <= FLT_MAX);
+            if (!bad && mx > 0.0f)
+                (void)frexpf(mx, &nexp);
+            ss = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CB / 16; m++) {
+                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
+                uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    // exact for normal results; parts below 2^-126 of the
+                    // largest magnitude may round, far under fp32 precision
+                    const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
+                    const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
+                    ss = fmaf(x0, x0, ss);
+                    ss = fmaf(x1, x1, ss);
+                    xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
+                }
+                *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
+            }
+            if (bad)
+                ss = mx;  // stored as the norm: not finite
         }
-        uint32_t w[NW];
+        t = (ss > 0.0f && !bad) ? 128.0f / sqrtf((float)D * ss) : 0.0f;
+        nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; pass++) {
+        float v[64];
+        // reread the row in every pass rather than keep it in registers
+        wave_lds_fence();
+        first_stage<D>(mine, qaddr, pass, v);
+        // remaining stages but the last (h = 1 is part of the first)
+#pragma unroll
+        for (int h = 2; h < HL; h *= 2)
+#pragma unroll
+            for (int j = 0; j < 64; j += 2 * h)
+#pragma unroll
+                for (int i = j; i < j + h; i++) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+        if constexpr (BITS == 2) {
+            // boundaries -b, 0, b are equally spaced: with T' = u / b the
+            // index #{boundaries < u} is 1 - clamp(floor(-T'), -2, 1); the
+            // words collect sum c 4^k and take 0x55..55 - that at the end
+            const float t2 = t * s.code.istep;
+#pragma unroll
+            for (int j = 0; j < 64; j += 2 * HL)
+#pragma unroll
+                for (int i = j; i < j + HL; i++) {
+                    const float bt = v[i + HL] * t2;
+                    const float ta = fmaf(v[i], t2, bt);
+                    const float tb = fmaf(v[i], t2, -bt);
+                    const int ca = min(max(floor_neg_i32(ta), -2), 1);
+                    const int cb = min(max(floor_neg_i32(tb), -2), 1);
+                    const int ka = 64 * pass + i, kb = ka + HL;
+                    w[ka >> 4] = lshl_add((uint32_t)ca, 2 * (ka & 15), w[ka >> 4]);
+                    w[kb >> 4] = lshl_add((uint32_t)cb, 2 * (kb & 15), w[kb >> 4]);
+                }
+        } else {
+            // last stage, scaled to T = 128 u, bucketized and packed; in
+            // groups of 16 outputs so that the table reads in flight stay few
+#pragma unroll
+            for (int j = 0; j < 64; j += 2 * HL)
+#pragma unroll
+                for (int i = j; i < j + HL; i++) {
+                    const float bt = v[i + HL] * t;
+                    const float ta = fmaf(v[i], t, bt);
+                    const float tb = fmaf(v[i], t, -bt);
+                    put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
+                    put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
+                    if ((i & 7) == 7)
+                        __builtin_amdgcn_sched_barrier(0);
+                }
+        }
+        // keep the passes in order: this pass's words are complete here
+        // (otherwise the whole pass can be sunk below the next pass's loads)
+#pragma unroll
+        for (int q = 0; q < NWP; q++)
+            asm volatile("" ::"v"(w[NWP * pass + q]));
+    }
+    if constexpr (BITS == 2) {
 #pragma unroll
         for (int q = 0; q < NW; q++)
-            w[q] = 0u;
-        float t = 0.0f, nstore = 0.0f;
-        {
-            float ss = row_sumsq<CB>(mine);
-            int nexp = 0;
-            bool bad = false;
-            if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
-                // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
-                // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
-                // first stage below then runs on it unchanged
-                float mx = 0.0f;
-#pragma unroll
-                for (int m = 0; m < CB / 16; m++) {
-                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                    const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                    for (int c = 0; c < 4; c++)
-                        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
-                }
-                bad = !(mx <= FLT_MAX);
-                if (!bad && mx > 0.0f)
-                    (void)frexpf(mx, &nexp);
-                ss = 0.0f;
-#pragma unroll
-                for (int m = 0; m < CB / 16; m++) {
-                    const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                    uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                    for (int c = 0; c < 4; c++) {
-                        // exact for normal results; parts below 2^-126 of the
-                        // largest magnitude may round, far under fp32 precision
-                        const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
-                        const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
-                        ss = fmaf(x0, x0, ss);
-                        ss = fmaf(x1, x1, ss);
-                        xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
-                    }
-                    *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
-                }
-                if (bad)
-                    ss = mx;  // stored as the norm: not finite
-            }
-            t = (ss > 0.0f && !bad) ? 128.0f / sqrtf((float)D * ss) : 0.0f;
-            nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);
-        }
-#pragma unroll
-        for (int pass = 0; pass < NP; pass++) {
-            float v[64];
-            // reread the row in every pass rather than keep it in registers
-            wave_lds_fence();
-            first_stage<D>(mine, qaddr, pass, v);
-            // remaining stages but the last (h = 1 is part of the first)
-#pragma unroll
-            for (int h = 2; h < HL; h *= 2)
-#pragma unroll
-                for (int j = 0; j < 64; j += 2 * h)
-#pragma unroll
-                    for (int i = j; i < j + h; i++) {
-                        const float a = v[i], b = v[i + h];
-                        v[i] = a + b;
-                        v[i + h] = a - b;
-                    }
-            if constexpr (BITS == 2) {
-                // boundaries -b, 0, b are equally spaced: with T' = u / b the
-                // index #{boundaries < u} is 1 - clamp(floor(-T'), -2, 1); the
-                // words collect sum c 4^k and take 0x55..55 - that at the end
-                const float t2 = t * s.code.istep;
-#pragma unroll
-                for (int j = 0; j < 64; j += 2 * HL)
-#pragma unroll
-                    for (int i = j; i < j + HL; i++) {
-                        const float bt = v[i + HL] * t2;
-                        const float ta = fmaf(v[i], t2, bt);
-                        const float tb = fmaf(v[i], t2, -bt);
-                        const int ca = min(max(floor_neg_i32(ta), -2), 1);
-                        const int cb = min(max(floor_neg_i32(tb), -2), 1);
-                        const int ka = 64 * pass + i, kb = ka + HL;
-                        w[ka >> 4] = lshl_add((uint32_t)ca, 2 * (ka & 15), w[ka >> 4]);
-                        w[kb >> 4] = lshl_add((uint32_t)cb, 2 * (kb & 15), w[kb >> 4]);
-                    }
-            } else {
-                // last stage, scaled to T = 128 u, bucketized and packed; in
-                // groups of 16 outputs so that the table reads in flight stay few
-#pragma unroll
-                for (int j = 0; j < 64; j += 2 * HL)
-#pragma unroll
-                    for (int i = j; i < j + HL; i++) {
-                        const float bt = v[i + HL] * t;
-                        const float ta = fmaf(v[i], t, bt);
-                        const float tb = fmaf(v[i], t, -bt);
-                        put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
-                        put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
-                        if ((i & 7) == 7)
-                            __builtin_amdgcn_sched_barrier(0);
-                    }
-            }
-            // keep the passes in order: this pass's words are complete here
-            // (otherwise the whole pass can be sunk below the next pass's loads)
-#pragma unroll
-            for (int q = 0; q < NWP; q++)
-                asm volatile("" ::"v"(w[NWP * pass + q]));
-        }
-        if constexpr (BITS == 2) {
-#pragma unroll
-            for (int q = 0; q < NW; q++)
-                w[q] = 0x55555555u - w[q];
-        }
-        if (lane < nvalid)
-            *as_global(s.norms + g0 + lane) = nstore;
-        wave_lds_fence();  // every lane is done with the staged rows
-        // packed rows, densely (the group's global layout), then whole-line stores
-        if constexpr (RB % 16 == 0) {
-#pragma unroll
-            for (int q = 0; q < NW / 4; q++)
-                *reinterpret_cast<u32x4 *>(stg + lane * RB + 16 * q) =
-                    u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
-        } else {
-#pragma unroll
-            for (int q = 0; q < NW / 2; q++)
-                *reinterpret_cast<u32x2 *>(stg + lane * RB + 8 * q) = u32x2{w[2 * q], w[2 * q + 1]};
-        }
-        wave_lds_fence();
-        {
-            const int bytes = nvalid * RB;
-            __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + g0 * RB);
-#pragma unroll
-            for (int q = 0; q < (64 * RB + 1023) / 1024; q++) {
-                const int e = 64 * q + lane;  // 16-byte granule of the group's packed rows
-                if (16 * e + 16 <= bytes) {
-                    const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + 16 * e);
-                    __builtin_nontemporal_store(x, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
-                } else if (16 * e < bytes) {  // an 8-byte tail (RB is a multiple of 8)
-                    *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(dst + 16 * e) =
-                        *reinterpret_cast<const u32x2 *>(stg + 16 * e);
-                }
-            }
-        }
-        wave_lds_fence();
+            w[q] = 0x55555555u - w[q];
     }
+    if (lane < nvalid)
+        *as_global(s.norms + g0 + lane) = nstore;
+    wave_lds_fence();  // every lane is done with the staged rows
+    // packed rows, densely (the group's global layout), then whole-line stores
+    if constexpr (RB % 16 == 0) {
+#pragma unroll
+        for (int q = 0; q < NW / 4; q++)
+            *reinterpret_cast<u32x4 *>(stg + lane * RB + 16 * q) =
+                u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+    } else {
+#pragma unroll
+        for (int q = 0; q < NW / 2; q++)
+            *reinterpret_cast<u32x2 *>(stg + lane * RB + 8 * q) = u32x2{w[2 * q], w[2 * q + 1]};
+    }
+    wave_lds_fence();
+    {
+        const int bytes = nvalid * RB;
+        __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + g0 * RB);
+#pragma unroll
+        for (int q = 0; q < (64 * RB + 1023) / 1024; q++) {
+            const int e = 64 * q + lane;  // 16-byte granule of the group's packed rows
+            if (16 * e + 16 <= bytes) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + 16 * e);
+                __builtin_nontemporal_store(x, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
+            } else if (16 * e < bytes) {  // an 8-byte tail (RB is a multiple of 8)
+                *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(dst + 16 * e) =
+                    *reinterpret_cast<const u32x2 *>(stg + 16 * e);
+            }
+        }
+    }
+    wave_lds_fence();
 }
 
-template <int D>
-__device__ __forceinline__ void encode_lane_side(const EncodeSide s, const int64_t n_rows,
-                                                 float2 *lut, uint8_t *stg, const uint32_t *qt)
+// Persistent loop over groups; with two sides (B1 > 0) each wave encodes
+// group g of the first side, then group g of the second, so that every wave
+// carries the same work whatever the bit widths.  The next group's loads are
+// issued before the current one is transformed.
+template <int D, int B0, int B1>
+__device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const EncodeSide &s1,
+                                                 const int64_t n_rows, const uint32_t key0,
+                                                 const uint32_t key1, uint8_t *stg,
+                                                 const uint32_t *qt)
 {
-    build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1, kLutScale);
-    __syncthreads();
-    const uint32_t key = lut_key(lut);
-    switch (s.code.bits) {
-    case 2: encode_lane_loop<D, 2>(s, n_rows, key, stg, qt); break;
-    case 3: encode_lane_loop<D, 3>(s, n_rows, key, stg, qt); break;
-    default: encode_lane_loop<D, 4>(s, n_rows, key, stg, qt); break;
+    constexpr int NCH = 64 * 2 * D / 1024;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
+    const uint8_t *src0 = static_cast<const uint8_t *>(s0.src);
+    const uint8_t *src1 = static_cast<const uint8_t *>(s1.src);
+    // the sign-pair table's LDS address as an opaque register value: its reads
+    // then take base + immediate offset instead of one materialised address each
+    uint32_t qaddr = lds_address(qt);
+    asm volatile("" : "+v"(qaddr));
+    int64_t g0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 64;
+    u32x4 pf[NCH];
+    load_group<D>(src0, g0, n_rows, lane, pf);
+    for (; g0 < n_rows; g0 += stride) {
+        stage_group<D>(pf, stg, lane);
+        if constexpr (B1 > 0)
+            load_group<D>(src1, g0, n_rows, lane, pf);
+        else
+            load_group<D>(src0, g0 + stride, n_rows, lane, pf);
+        encode_group<D, B0>(s0, g0, n_rows, key0, stg, qaddr);
+        if constexpr (B1 > 0) {
+            stage_group<D>(pf, stg, lane);
+            load_group<D>(src0, g0 + stride, n_rows, lane, pf);
+            encode_group<D, B1>(s1, g0, n_rows, key1, stg, qaddr);
+        }
     }
 }
 
-template <int D>
+template <int D, int B0, int B1>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
 void encode_lane_kernel(EncodeLaneParams p)
 {
-    __shared__ float2 lut[kLutBins];
+    __shared__ float2 lut0[kLutBins];
+    __shared__ float2 lut1[kLutBins];
     __shared__ __attribute__((aligned(16))) uint32_t qt[256];
     __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][64 * (2 * D + 16)];
     static_assert(kBlock == 256, "one sign-pair word per thread");
@@ -500,12 +522,13 @@ void encode_lane_kernel(EncodeLaneParams p)
         const uint32_t hi = neg(k + 1) ^ (form & 1u) ^ (form < 2 ? 0u : (uint32_t)sg);
         qt[i] = (0x3F80u | (lo << 15)) | ((0x3F80u | (hi << 15)) << 16);
     }
-    // the side is chosen by a uniform branch: indexing the kernel argument
-    // struct with blockIdx.y would copy it to scratch memory
-    if (blockIdx.y == 0)
-        encode_lane_side<D>(p.side[0], p.n_rows, lut, stage[threadIdx.x >> 6], qt);
-    else
-        encode_lane_side<D>(p.side[1], p.n_rows, lut, stage[threadIdx.x >> 6], qt);
+    if constexpr (B0 != 2)
+        build_lut(lut0, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
+    if constexpr (B1 > 2)
+        build_lut(lut1, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
+    __syncthreads();
+    encode_lane_loop<D, B0, B1>(p.side[0], p.side[1], p.n_rows, lut_key(lut0), lut_key(lut1),
+                                stage[threadIdx.x >> 6], qt);
 }
 
 // ----------------------------------------------------------------- append
@@ -766,32 +789,60 @@ int injected(const char *fn)
     return TQ_OK;
 }
 
-// workgroups of `kern` that fit on one CU at once (queried once per kernel)
+// workgroups of `kern` that fit on one CU at once (queried once per kernel
+// and device)
 template <typename K>
 int resident_blocks(K kern)
 {
-    static int v = 0;
-    if (v == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0) != hipSuccess || n < 1)
-            n = 1;
-        v = n;
+    static std::mutex mu;
+    static const void *keys[64];
+    static int vals[64];
+    static int nkeys = 0;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const void *key = reinterpret_cast<const void *>(kern);
+    std::lock_guard<std::mutex> lk(mu);
+    for (int i = 0; i < nkeys; i++)
+        if (keys[i] == key && vals[i] >> 16 == dev)
+            return vals[i] & 0xFFFF;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0) != hipSuccess || n < 1)
+        n = 1;
+    if (nkeys < 64) {
+        keys[nkeys] = key;
+        vals[nkeys++] = (dev << 16) | (n & 0xFFFF);
     }
-    return v;
+    return n;
 }
 
-template <int D>
-void launch_encode_lane_d(const EncodeLaneParams &q, int sides, hipStream_t st)
+template <int D, int B0, int B1>
+void launch_encode_lane_k(const EncodeLaneParams &q, hipStream_t st)
 {
-    auto kern = encode_lane_kernel<D>;
+    auto kern = encode_lane_kernel<D, B0, B1>;
     const int64_t groups = (q.n_rows + 63) / 64;  // 64 rows per wave
     const int64_t need = (groups + kBlock / 64 - 1) / (kBlock / 64);
-    // the resident workgroups (split between the sides), each looping
-    int64_t cap = (int64_t)device_cus() * resident_blocks(kern) / sides;
+    // the resident workgroups, each looping over groups
+    int64_t cap = (int64_t)device_cus() * resident_blocks(kern);
     if (cap < 1)
         cap = 1;
-    dim3 grid((unsigned)(need < cap ? need : cap), sides), block(kBlock);
-    hipLaunchKernelGGL(kern, grid, block, 0, st, q);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(need < cap ? need : cap)), dim3(kBlock), 0, st, q);
+}
+
+// sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
+template <int D>
+void launch_encode_lane_d(const EncodeLaneParams &q, int b0, int b1, hipStream_t st)
+{
+    switch (b0 * 10 + b1) {
+    case 40: launch_encode_lane_k<D, 4, 0>(q, st); break;
+    case 30: launch_encode_lane_k<D, 3, 0>(q, st); break;
+    case 20: launch_encode_lane_k<D, 2, 0>(q, st); break;
+    case 44: launch_encode_lane_k<D, 4, 4>(q, st); break;
+    case 43: launch_encode_lane_k<D, 4, 3>(q, st); break;
+    case 42: launch_encode_lane_k<D, 4, 2>(q, st); break;
+    case 33: launch_encode_lane_k<D, 3, 3>(q, st); break;
+    case 32: launch_encode_lane_k<D, 3, 2>(q, st); break;
+    default: launch_encode_lane_k<D, 2, 2>(q, st); break;
+    }
 }
 
 template <typename T>
@@ -932,14 +983,21 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         EncodeLaneParams q;
         q.side[0] = p.side[0];
         q.side[1] = p.side[1];
+        if (sides == 2 && q.side[1].code.bits > q.side[0].code.bits) {
+            q.side[0] = p.side[1];
+            q.side[1] = p.side[0];
+        }
+        const int b0 = q.side[0].code.bits, b1 = sides == 2 ? q.side[1].code.bits : 0;
+        if (sides == 1)
+            q.side[1] = q.side[0];  // unused
         q.n_rows = n_rows;
         for (int w = 0; w < 4; w++)
             q.sbits[w] = 0u;
         tq::sign_words(d, seed, q.sbits);
         if (d == 64)
-            launch_encode_lane_d<64>(q, sides, st);
+            launch_encode_lane_d<64>(q, b0, b1, st);
         else
-            launch_encode_lane_d<128>(q, sides, st);
+            launch_encode_lane_d<128>(q, b0, b1, st);
         return launch_status(fn);
     }
     tq::sign_words(d, seed, p.signs);
