@@ -197,14 +197,13 @@ __device__ __forceinline__ void put_bits(uint32_t (&w)[NWORDS], int bit, int nbi
         w[wd + 1] |= idx >> (32 - sh);
 }
 
-// bucketize on T = 128 u against a table built with boundary scale 128
-__device__ __forceinline__ uint32_t bucketize_t(float t, uint32_t key)
+// The table entry (boundary inside the bin, count below it) for T = 128 u,
+// from a table built with boundary scale 128
+__device__ __forceinline__ f32x2 lut_entry(float t, uint32_t key)
 {
     const float g = t + kLutMagic;
     const uint32_t a = (__float_as_uint(g) << 3) + key;
-    const f32x2 e = *reinterpret_cast<const __attribute__((address_space(3))) f32x2 *>(
-        (uintptr_t)a);
-    return (uint32_t)__float_as_int(e.y) + (t > e.x ? 1u : 0u);
+    return *reinterpret_cast<const __attribute__((address_space(3))) f32x2 *>((uintptr_t)a);
 }
 
 __device__ __forceinline__ u32x4 lds_u32x4(uint32_t addr)
@@ -252,8 +251,6 @@ __device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, 
                 dot2_pair(a[c], b[c], q4.x, q4.y, q4.z, q4.w, v[2 * j], v[2 * j + 1]);
             }
         }
-        if (m & 1)
-            __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -282,12 +279,18 @@ __device__ __forceinline__ void load_group(const uint8_t *src, int64_t g0, int64
                                            int lane, u32x4 (&pf)[64 * 2 * D / 1024])
 {
     constexpr int CB = 2 * D, NCH = 64 * CB / 1024, RPC = 1024 / CB, LPC = 64 / RPC;
-    const int crow = lane / LPC;
+    const u32x4 *gp = reinterpret_cast<const u32x4 *>(src + g0 * CB) + lane;
+    if (g0 + 64 <= n_rows) {  // a whole group (uniform branch): no per-lane checks
 #pragma unroll
-    for (int c = 0; c < NCH; c++)
-        pf[c] = g0 + c * RPC + crow < n_rows
-                    ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + g0 * CB + c * 1024) + lane)
-                    : u32x4{0u, 0u, 0u, 0u};
+        for (int c = 0; c < NCH; c++)
+            pf[c] = __builtin_nontemporal_load(gp + 64 * c);
+    } else {
+        const int crow = lane / LPC;
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+            pf[c] = g0 + c * RPC + crow < n_rows ? __builtin_nontemporal_load(gp + 64 * c)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // The group's rows from registers into this wave's LDS stage (row stride SR).
@@ -397,26 +400,35 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
                     const float bt = v[i + HL] * t2;
                     const float ta = fmaf(v[i], t2, bt);
                     const float tb = fmaf(v[i], t2, -bt);
-                    const int ca = min(max(floor_neg_i32(ta), -2), 1);
-                    const int cb = min(max(floor_neg_i32(tb), -2), 1);
                     const int ka = 64 * pass + i, kb = ka + HL;
-                    w[ka >> 4] = lshl_add((uint32_t)ca, 2 * (ka & 15), w[ka >> 4]);
-                    w[kb >> 4] = lshl_add((uint32_t)cb, 2 * (kb & 15), w[kb >> 4]);
+                    pack_c2(ta, tb, 2 * (ka & 15), 2 * (kb & 15), w[ka >> 4], w[kb >> 4]);
                 }
         } else {
-            // last stage, scaled to T = 128 u, bucketized and packed; in
-            // groups of 16 outputs so that the table reads in flight stay few
+            // last stage, scaled to T = 128 u, bucketized and packed, four
+            // outputs at a time
 #pragma unroll
             for (int j = 0; j < 64; j += 2 * HL)
 #pragma unroll
-                for (int i = j; i < j + HL; i++) {
-                    const float bt = v[i + HL] * t;
-                    const float ta = fmaf(v[i], t, bt);
-                    const float tb = fmaf(v[i], t, -bt);
-                    put_bits(w, (64 * pass + i) * BITS, BITS, bucketize_t(ta, key));
-                    put_bits(w, (64 * pass + i + HL) * BITS, BITS, bucketize_t(tb, key));
-                    if ((i & 7) == 7)
-                        __builtin_amdgcn_sched_barrier(0);
+                for (int i = j; i < j + HL; i += 2) {
+                    float tt[4], bb[4];
+                    uint32_t base[4], idx[4];
+                    const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        const float bt = v[i + h + HL] * t;
+                        tt[h] = fmaf(v[i + h], t, bt);
+                        tt[h + 2] = fmaf(v[i + h], t, -bt);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const f32x2 e = lut_entry(tt[q], key);
+                        bb[q] = e.x;
+                        base[q] = __float_as_uint(e.y);
+                    }
+                    bucket_add4(tt, bb, base, idx);
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        put_bits(w, (64 * pass + k[q]) * BITS, BITS, idx[q]);
                 }
         }
         // keep the passes in order: this pass's words are complete here

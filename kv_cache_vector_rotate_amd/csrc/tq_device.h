@@ -382,6 +382,28 @@ __device__ __forceinline__ void dot2_quad(uint32_t A, uint32_t B, uint32_t q0, u
         : "v"(A), "v"(B), "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(r2), "v"(r3));
 }
 
+// idx_k = base_k + (t_k > b_k) for four outputs.  Each compare writes its own
+// scalar register pair, so no compare waits for the previous add (the
+// compiler puts every compare in VCC, and a compare's result must be two wait
+// states old before an add reads it as carry; here each is at least three).
+__device__ __forceinline__ void bucket_add4(const float (&t)[4], const float (&b)[4],
+                                            const uint32_t (&base)[4], uint32_t (&idx)[4])
+{
+    uint64_t m0, m1, m2, m3;
+    asm("v_cmp_gt_f32_e64 %4, %8, %12\n\t"
+        "v_cmp_gt_f32_e64 %5, %9, %13\n\t"
+        "v_cmp_gt_f32_e64 %6, %10, %14\n\t"
+        "v_cmp_gt_f32_e64 %7, %11, %15\n\t"
+        "v_addc_co_u32_e64 %0, %4, %16, 0, %4\n\t"
+        "v_addc_co_u32_e64 %1, %5, %17, 0, %5\n\t"
+        "v_addc_co_u32_e64 %2, %6, %18, 0, %6\n\t"
+        "v_addc_co_u32_e64 %3, %7, %19, 0, %7"
+        : "=&v"(idx[0]), "=&v"(idx[1]), "=&v"(idx[2]), "=v"(idx[3]), "=&s"(m0), "=&s"(m1),
+          "=&s"(m2), "=&s"(m3)
+        : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]),
+          "v"(b[3]), "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]));
+}
+
 // (a << sh) | b and (a << sh) + b as single instructions (the compiler tends
 // to split them into a shift and a three-input or/add)
 __device__ __forceinline__ uint32_t lshl_or(uint32_t a, uint32_t sh, uint32_t b)
@@ -397,12 +419,21 @@ __device__ __forceinline__ uint32_t lshl_add(uint32_t a, uint32_t sh, uint32_t b
     return r;
 }
 
-// floor(-x) as int32 (one instruction; the compiler emits floor and convert)
-__device__ __forceinline__ int floor_neg_i32(float x)
+// 2-bit packing step for two outputs: wa += c_a << sa, wb += c_b << sb with
+// c = clamp(floor(-t), -2, 1) (three instructions per output; the compiler
+// emits floor and convert separately)
+__device__ __forceinline__ void pack_c2(float ta, float tb, uint32_t sa, uint32_t sb_, uint32_t &wa,
+                                        uint32_t &wb)
 {
-    int r;
-    asm("v_cvt_flr_i32_f32_e64 %0, -%1" : "=v"(r) : "v"(x));
-    return r;
+    uint32_t ca, cb;
+    asm("v_cvt_flr_i32_f32_e64 %0, -%4\n\t"
+        "v_cvt_flr_i32_f32_e64 %1, -%5\n\t"
+        "v_med3_i32 %0, %0, -2, 1\n\t"
+        "v_med3_i32 %1, %1, -2, 1\n\t"
+        "v_lshl_add_u32 %2, %0, %6, %2\n\t"
+        "v_lshl_add_u32 %3, %1, %7, %3"
+        : "=&v"(ca), "=&v"(cb), "+v"(wa), "+v"(wb)
+        : "v"(ta), "v"(tb), "i"(sa), "i"(sb_));
 }
 
 // a[i] for a lane-varying i < N from a uniform array (kernel arguments): a
