@@ -238,17 +238,23 @@ __device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, 
         const u32x4 wb = *reinterpret_cast<const u32x4 *>(row + HB + 16 * m);
         const uint32_t a[4] = {wa.x, wa.y, wa.z, wa.w};
         const uint32_t b[4] = {wb.x, wb.y, wb.z, wb.w};
+        if constexpr (D == 64) {
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int j = 4 * m + c;
-            const int g = D == 128 ? pass : 0;
-            const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * g + j));
-            if constexpr (D == 64) {
+            for (int c = 0; c < 4; c++) {
+                const int j = 4 * m + c;
+                const u32x4 q4 = lds_u32x4(qaddr + 16 * j);
                 const u32x4 r4 = lds_u32x4(qaddr + 16 * (32 + j));
                 dot2_quad(a[c], b[c], q4.x, q4.y, q4.z, q4.w, r4.z, r4.w, v[2 * j],
                           v[2 * j + 1], v[32 + 2 * j], v[33 + 2 * j]);
-            } else {
-                dot2_pair(a[c], b[c], q4.x, q4.y, q4.z, q4.w, v[2 * j], v[2 * j + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; c += 2) {
+                const int j = 4 * m + c;
+                const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * pass + j));
+                const u32x4 q5 = lds_u32x4(qaddr + 16 * (32 * pass + j + 1));
+                dot2_pair2(a[c], b[c], q4, a[c + 1], b[c + 1], q5, v[2 * j], v[2 * j + 1],
+                           v[2 * j + 2], v[2 * j + 3]);
             }
         }
     }

@@ -352,17 +352,25 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // instruction needs three wait states before a different vector instruction
 // reads it; the compiler cannot see into the asm, so the block ends with
 // them (a chained read as the accumulator of the same instruction needs none).
-__device__ __forceinline__ void dot2_pair(uint32_t A, uint32_t B, uint32_t q0, uint32_t q1,
-                                          uint32_t q2, uint32_t q3, float &y0, float &y1)
+// Two such steps in one block (one trailing wait for both): (A, B, q) ->
+// (y0, y1) and (A', B', q') -> (z0, z1).
+__device__ __forceinline__ void dot2_pair2(uint32_t A, uint32_t B, const u32x4 &q, uint32_t A2,
+                                           uint32_t B2, const u32x4 &q2, float &y0, float &y1,
+                                           float &z0, float &z1)
 {
-    float e0, e1;
-    asm("v_dot2_f32_bf16 %0, %4, %6, 0\n\t"
-        "v_dot2_f32_bf16 %1, %4, %7, 0\n\t"
-        "v_dot2_f32_bf16 %2, %5, %8, %0\n\t"
-        "v_dot2_f32_bf16 %3, %5, %9, %1\n\t"
+    float e0, e1, f0, f1;
+    asm("v_dot2_f32_bf16 %0, %8, %12, 0\n\t"
+        "v_dot2_f32_bf16 %1, %8, %13, 0\n\t"
+        "v_dot2_f32_bf16 %2, %10, %16, 0\n\t"
+        "v_dot2_f32_bf16 %3, %10, %17, 0\n\t"
+        "v_dot2_f32_bf16 %4, %9, %14, %0\n\t"
+        "v_dot2_f32_bf16 %5, %9, %15, %1\n\t"
+        "v_dot2_f32_bf16 %6, %11, %18, %2\n\t"
+        "v_dot2_f32_bf16 %7, %11, %19, %3\n\t"
         "s_nop 2"
-        : "=&v"(e0), "=&v"(e1), "=&v"(y0), "=v"(y1)
-        : "v"(A), "v"(B), "v"(q0), "v"(q1), "v"(q2), "v"(q3));
+        : "=&v"(e0), "=&v"(e1), "=&v"(f0), "=&v"(f1), "=&v"(y0), "=&v"(y1), "=&v"(z0), "=v"(z1)
+        : "v"(A), "v"(B), "v"(A2), "v"(B2), "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w),
+          "v"(q2.x), "v"(q2.y), "v"(q2.z), "v"(q2.w));
 }
 
 // The same with a second pair sharing e0 and e1: y2 = B.r2 + e0, y3 = B.r3 + e1.
