@@ -613,6 +613,11 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
 /* Attention                                                           */
 /* ------------------------------------------------------------------ */
 
+/* Positions per block of the sparse-V reference maximum (a reading: the
+ * pages gate on the running maximum of an online softmax and leave its
+ * blocking open). */
+#define ORC_SPARSE_V_BLOCK 256
+
 /* Softmax attention of n_q query heads over T cached rows, plain definition:
  *   khat_t, vhat_t = decode of the stored K, V rows (fp64, not rounded)
  *   score_t = scale * <q, khat_t>,  p = softmax(score) (max subtracted)
@@ -620,9 +625,13 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
  * Query head h reads KV head g = h / (n_q / n_kv) (contiguous groups;
  * reading).  q[n_q][d] are the query values (bf16 inputs arrive converted
  * exactly).  Cache rows are [n_kv][T] with row strides of one packed row.
- * sparse_v_threshold > 0 drops rows whose normalised weight p_t is below the
- * threshold from the V sum (the page's "sparse V" gate; the kept weights are
- * not renormalised); 0 disables it. */
+ * sparse_v_threshold > 0 gates the V sum ([Atlas] "Sparse V dequant"): a
+ * row's V contributes only if its exponent relative to the running maximum
+ * exceeds the threshold, here taken against a fixed reference, the largest
+ * score of the row's aligned block of ORC_SPARSE_V_BLOCK positions:
+ *   keep_t = exp(score_t - max_{t' in block(t)} score_t') > threshold;
+ * gated rows still count in the softmax denominator (their V is zero, the
+ * kept weights are not renormalised).  0 disables the gate. */
 int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
                   const float *k_norms, const uint8_t *v_packed,
                   const float *v_norms, int n_kv, int T, int d, int bits_k,
@@ -666,10 +675,21 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
             double *oh = out + (size_t)h * d;
             for (int i = 0; i < d; i++)
                 oh[i] = 0.0;
+            double eb = 0.0;  /* largest exp(score - m) of the current block */
             for (int t = 0; t < T; t++) {
                 double p = sc[t] / denom;
-                if (sparse_v_threshold > 0.0 && p < sparse_v_threshold)
-                    continue;
+                if (sparse_v_threshold > 0.0) {
+                    /* sc holds exp(score - m); the block's largest is exp(mb - m) */
+                    if (t % ORC_SPARSE_V_BLOCK == 0) {
+                        int b1 = t + ORC_SPARSE_V_BLOCK < T ? t + ORC_SPARSE_V_BLOCK : T;
+                        eb = 0.0;
+                        for (int u = t; u < b1; u++)
+                            if (sc[u] > eb)
+                                eb = sc[u];
+                    }
+                    if (!(sc[t] / eb > sparse_v_threshold))
+                        continue;
+                }
                 for (int i = 0; i < d; i++)
                     oh[i] += p * V[(size_t)t * d + i];
             }

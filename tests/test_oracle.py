@@ -360,6 +360,8 @@ def test_attention_quality_matches_pages_table(orc, bk, bv, want):
 
 
 def test_attention_sparse_v_gate(orc):
+    """One block (T <= 256): the gate reduces to p_t / max_t p_t > threshold,
+    checked against scipy's softmax; gated rows stay in the denominator."""
     d, n_kv, T = 64, 1, 40
     K, V, kp, kn, vp, vn = _cache(orc, n_kv, T, d, 4, 4, 8, kscale=3.0)
     q = (np.random.default_rng(9).standard_normal((1, d)) * 3).astype(np.float32)
@@ -368,6 +370,36 @@ def test_attention_sparse_v_gate(orc):
     Kh = orc.decode(kp, kn, d, 4, 42, f64=True)
     Vh = orc.decode(vp, vn, d, 4, 42, f64=True)
     p = scipy.special.softmax(0.2 * Kh @ q[0].astype(np.float64))
-    keep = p >= thr
+    keep = p / p.max() > thr
     assert 0 < keep.sum() < T
     np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-13)
+    # threshold 0 is the plain definition
+    o0 = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 4, 42, 0.2, sparse_v_threshold=0.0)
+    np.testing.assert_allclose(o0[0], p @ Vh, atol=1e-13)
+
+
+def test_attention_sparse_v_gate_per_block(orc):
+    """Rows are gated against the largest score of their own aligned block of
+    256 positions, not the global one: with one dominant row in block 0, every
+    row of block 1 (each with global weight far below the threshold) still
+    contributes, while block 0 keeps only its dominant row."""
+    d, n_kv, T = 64, 1, 512
+    K, V, kp, kn, vp, vn = _cache(orc, n_kv, T, d, 4, 4, 10)
+    kn = kn.copy()
+    kn[3] *= 60.0  # row 3 dominates everything by far
+    Kh = orc.decode(kp, kn, d, 4, 42, f64=True)
+    Vh = orc.decode(vp, vn, d, 4, 42, f64=True)
+    q = np.zeros((1, d), np.float32)
+    q[0, :] = Kh[3] / np.linalg.norm(Kh[3])
+    scale = 1.0 / float(np.abs(Kh[256:] @ q[0].astype(np.float64)).max())  # block 1 spread <= 2
+    s = scale * Kh @ q[0].astype(np.float64)
+    p = scipy.special.softmax(s)
+    assert p[256:].max() < 1e-6
+    thr = 1e-3
+    o = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 4, 42, scale, sparse_v_threshold=thr)
+    keep = np.zeros(T, bool)
+    for b0 in (0, 256):
+        e = np.exp(s[b0:b0 + 256] - s[b0:b0 + 256].max())
+        keep[b0:b0 + 256] = e > thr
+    assert keep[256:].sum() > 10 and keep[:256].sum() < 256
+    np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-15, rtol=1e-10)
