@@ -217,6 +217,14 @@ def main():
     at = sorted(a.elapsed_time(b) * 1e3 for a, b in aev)
     attn_us = sum(at) / len(at)
     ab = attn_bytes(B4, HQ4, HKV4, D4, T4, BK4, BV4)
+    # the same launch with the sparse-V gate at 1e-3 (N(0,1) keys: few rows gated)
+    for i, (a, b) in enumerate(aev):
+        a.record()
+        tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws, sparse_v=1e-3)
+        b.record()
+    torch.cuda.synchronize()
+    ats = [a.elapsed_time(b) * 1e3 for a, b in aev]
+    attn_sparse_us = sum(ats) / len(ats)
 
     res = {
         "metric": METRIC,
@@ -249,6 +257,7 @@ def main():
             "median_us": round(at[len(at) // 2], 2), "min_us": round(at[0], 2),
             "alg_bytes": ab, "GB_s": round(ab / attn_us / 1e3, 1),
             "pct_hbm_peak": round(100 * ab / attn_us / 1e3 / HBM_PEAK_GBS, 2),
+            "sparse_v_1e-3_us": round(attn_sparse_us, 2),
         },
         "roofline": {
             "bound": "hbm", "kernel": dom,

@@ -177,11 +177,17 @@ size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
  * h / (n_q_heads / n_kv_heads); n_q_heads must be a multiple of n_kv_heads
  * with a ratio of 1, 2, 4 or 8.  Context = slots [0, min(ctx_len, window)).
  * scale <= 0 selects 1/sqrt(d).  out: [batch][n_q_heads][d] fp32 (device).
+ * sparse_v_threshold in [0, 1): 0 disables the gate; otherwise the V row of
+ * slot t contributes only where exp(score_t - m) > sparse_v_threshold, m the
+ * largest score among slots [256 floor(t/256), +256) of the same query head
+ * ([Atlas] "Sparse V dequant": V of rows with a negligible weight relative
+ * to the running maximum is neither loaded nor decoded); gated rows stay in
+ * the softmax denominator.  Invalid (negative, >= 1 or NaN) -> TQ_EINVAL.
  * workspace: device buffer of at least tq_attn_workspace_bytes(...) bytes,
  * 16-byte aligned; its contents need no initialisation.  ctx_len >= 1. */
 int tq_attn_decode(const tq_cache_desc *cache, int layer, const uint16_t *q_bf16,
-                   int n_q_heads, int64_t ctx_len, float scale, float *out,
-                   void *workspace, size_t ws_bytes, void *stream);
+                   int n_q_heads, int64_t ctx_len, float scale, float sparse_v_threshold,
+                   float *out, void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

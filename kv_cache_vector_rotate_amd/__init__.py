@@ -208,8 +208,9 @@ def tq_attn_workspace_bytes(cache: TQCache, layer: int, n_q_heads: int, ctx_len:
 
 
 def tq_attn_decode(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int, scale: float = 0.0,
-                   out=None, workspace=None, stream=None):
-    """q: bf16 [batch, n_q_heads, d]; returns fp32 [batch, n_q_heads, d]."""
+                   out=None, workspace=None, stream=None, sparse_v: float = 0.0):
+    """q: bf16 [batch, n_q_heads, d]; returns fp32 [batch, n_q_heads, d].
+    sparse_v: the sparse-V gate threshold (0 = off)."""
     n_q = q.shape[-2]
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
@@ -217,7 +218,8 @@ def tq_attn_decode(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int, sc
     if workspace is None:
         workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
     _check(lib().tq_attn_decode(ctypes.byref(cache.desc), layer, _dev(q, "q", torch.bfloat16), n_q,
-                                ctx_len, ctypes.c_float(scale), _dev(out, "out", torch.float32),
+                                ctx_len, ctypes.c_float(scale), ctypes.c_float(sparse_v),
+                                _dev(out, "out", torch.float32),
                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream)), "tq_attn_decode")
     return out

@@ -73,7 +73,7 @@ def lib():
         L.tq_append_row.argtypes = [P, i32, P, P, i32, i64, P]
         L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64]
         L.tq_attn_workspace_bytes.restype = sz
-        L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, P, P, sz, P]
+        L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P, sz, P]
         for name in ("tq_codebook_init", "tq_codebook_init_density", "tq_signs", "tq_rotate",
                      "tq_encode", "tq_decode", "tq_append_row", "tq_attn_decode"):
             getattr(L, name).restype = i32

@@ -48,6 +48,7 @@ struct AttnParams {
     float *out;               // [B][Hq][D]
     int Hq, Hkv, window, T, n_chunks, chunk_len;
     float qscale;             // scale * log2(e) / sqrt(D)
+    float gate_log2;          // sparse-V gate: log2(threshold), -inf when off
     float centK[16];
     float centV[16];
     uint32_t signs[8];
@@ -240,9 +241,12 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
             const float mnew = fmaxf(m_run[h], mt);
             fac[h] = exp2f(m_run[h] - mnew);
             m_run[h] = mnew;
-            const float pr = exp2f(sc[tid][h] - mnew);
+            const float s_t = sc[tid][h];
+            const float pr = exp2f(s_t - mnew);
             l_part[h] = l_part[h] * fac[h] + pr;
-            sc[tid][h] = pr;
+            // sparse V: the row's V counts only if exp(s - tile max) > threshold
+            // (tiles are aligned 256-slot blocks); it stays in the denominator
+            sc[tid][h] = s_t - mt > p.gate_log2 ? pr : 0.0f;
         }
         __syncthreads();
         // ---- V sum of the tile (rotated domain)
@@ -257,10 +261,21 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
             float vn[CH];
 #pragma unroll
             for (int c = 0; c < CH; c++) {
-                const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
-                const int64_t row = rowbase + (t < t_end ? t : t_begin);
-                vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-                vn[c] = t < t_end ? p.vn[row] : 0.0f;
+                const int tl = (it0 + c) * RPB + wave * RPW + rig;
+                const int t = t0 + tl;
+                // rows with no weight (past the context, or gated by sparse V)
+                // are neither loaded nor decoded
+                bool need = false;
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    need |= sc[tl][h] != 0.0f;
+                vb[c] = 0;
+                vn[c] = 0.0f;
+                if (need) {
+                    const int64_t row = rowbase + t;
+                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+                    vn[c] = p.vn[row];
+                }
             }
 #pragma unroll
             for (int c = 0; c < CH; c++) {
@@ -458,14 +473,17 @@ extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int
 }
 
 extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
-                              int n_q_heads, int64_t ctx_len, float scale, float *out,
-                              void *workspace, size_t ws_bytes, void *stream)
+                              int n_q_heads, int64_t ctx_len, float scale,
+                              float sparse_v_threshold, float *out, void *workspace,
+                              size_t ws_bytes, void *stream)
 {
     static const char *fn = "tq_attn_decode";
     tq::clear_error();
     int rc = check_cache(c, layer, fn);
     if (rc != TQ_OK)
         return rc;
+    if (!(sparse_v_threshold >= 0.0f && sparse_v_threshold < 1.0f))
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: sparse_v_threshold must be in [0, 1)");
     if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
         return tq::fail(TQ_EINVAL, "tq_attn_decode: n_q_heads must be a positive multiple of n_kv_heads");
     const int G = n_q_heads / c->n_kv_heads;
@@ -519,6 +537,7 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     p.chunk_len = s.chunk_len;
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)d);
     p.qscale = sc * kLog2e / sqrtf((float)d);
+    p.gate_log2 = sparse_v_threshold > 0.0f ? log2f(sparse_v_threshold) : -__builtin_huge_valf();
     for (int j = 0; j < 16; j++) {
         p.centK[j] = j < ck.levels ? ck.centroids[j] : 0.0f;
         p.centV[j] = j < cv.levels ? cv.centroids[j] : 0.0f;

@@ -149,20 +149,23 @@ def test_cache_and_attention_validation(tq):
     assert L.tq_append_row(None, -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
     assert L.tq_append_row(ctypes.byref(d), 2, arr, arr, 0, 0, None) == tq.TQ_EINVAL
     assert L.tq_append_row(ctypes.byref(d), -1, arr, arr, 0, -1, None) == tq.TQ_EINVAL
-    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 3, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 3, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
     assert "multiple" in tq.tq_last_error()
-    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 6, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
-    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
-    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, A, A, 16, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 6, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 0, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, 0.0, A, A, 16, None) == tq.TQ_EINVAL
     assert "workspace" in tq.tq_last_error()
     ws = L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5)
     # 2 sequences x 4 query heads x 1 chunk x (128 + 4) floats
     assert ws == 2 * 4 * 1 * 132 * 4
     assert L.tq_attn_workspace_bytes(ctypes.byref(d), 5, 4, 5) == 0
+    for bad in (-0.1, 1.0, float("nan")):
+        assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, bad, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert "sparse_v" in tq.tq_last_error()
     d2 = _desc(tq, head_dim=96)
-    assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
     d3 = _desc(tq, bk=1)
-    assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
 
 
 def test_injected_hip_error_path():

@@ -34,7 +34,7 @@ def _fill(tq, cache, layer, seed, kscale=1.0, dist="normal"):
                  cache.k_norms[layer], cache.v_packed[layer], cache.v_norms[layer])
 
 
-def _oracle(orc, cache, layer, q, b, heads, T, scale):
+def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
     """Oracle output for sequence b, the given query heads, context slots [0, T)."""
     d = cache.head_dim[layer]
     G = q.shape[1] // cache.n_kv_heads
@@ -47,7 +47,7 @@ def _oracle(orc, cache, layer, q, b, heads, T, scale):
         vn = cache.v_norms[layer][b, g, :T].cpu().numpy()
         qh = q[b, h:h + 1].float().cpu().numpy()
         out[h] = orc.attention(qh, kp, kn, vp, vn, 1, T, d, cache.bits_k, cache.bits_v, SEED,
-                               scale)[0]
+                               scale, sparse_v_threshold=sparse_v)[0]
     return out
 
 
@@ -129,3 +129,41 @@ def test_config5_long_context_attention_sampled(tq, orc):
         ref = _oracle(orc, cache, l, q, 0, (1, 6), T, 1 / math.sqrt(d))
         for h in (1, 6):
             check_attention(o[0, h], ref[h])
+
+
+@pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 3, 2), (256, 2, 4, 1)])
+def test_attention_sparse_v(tq, orc, d, bk, bv, G):
+    """Sparse-V gate (threshold 1e-3) against the oracle's rule, on a peaked
+    softmax over several 256-slot blocks and a ragged last block; a large
+    fraction of the rows is gated."""
+    B, Hkv, T = 2, 2, 1100
+    Hq = Hkv * G
+    cache = tq.TQCache(1, B, Hkv, T, d, bk, bv, SEED)
+    _fill(tq, cache, 0, 80 + d, kscale=6.0)
+    q = (kvgen.normal((B, Hq, d), 81 + d, "cuda") * 2.0).to(torch.bfloat16)
+    scale = 0.5
+    o = tq.tq_attn_decode(cache, 0, q, T, scale=scale, sparse_v=1e-3).cpu().numpy()
+    o0 = tq.tq_attn_decode(cache, 0, q, T, scale=scale).cpu().numpy()
+    for b in range(B):
+        ref = _oracle(orc, cache, 0, q, b, range(Hq), T, scale, sparse_v=1e-3)
+        for h in range(Hq):
+            check_attention(o[b, h], ref[h])
+    # the gate changes the result (rows were dropped) but only slightly
+    assert np.abs(o - o0).max() > 0
+    assert np.abs(o - o0).max() < 0.05
+
+
+def test_config4_attention_sparse_v_sampled(tq, orc):
+    """The bench's attention launch with the sparse-V gate at 1e-3, sampled."""
+    B, Hq, Hkv, d, T = 32, 32, 8, 128, 16384
+    cache = tq.TQCache(1, B, Hkv, T, d, 4, 2, SEED)
+    _fill(tq, cache, 0, 4)
+    q = kvgen.normal((B, Hq, d), 44, "cuda", torch.bfloat16)
+    o = tq.tq_attn_decode(cache, 0, q, T, sparse_v=1e-3).cpu().numpy()
+    rng = np.random.default_rng(5)
+    for b in rng.choice(B, 3, replace=False):
+        g = int(rng.integers(Hkv))
+        heads = range(g * 4, g * 4 + 4)
+        ref = _oracle(orc, cache, 0, q, int(b), heads, T, 1 / math.sqrt(d), sparse_v=1e-3)
+        for h in heads:
+            check_attention(o[b, h], ref[h])
