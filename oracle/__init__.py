@@ -42,9 +42,10 @@ def lib():
         i32, i64, u64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
         L.orc_splitmix64_stream.argtypes = [u64, i32, P]
         L.orc_signs.argtypes = [u64, i32, P]
+        L.orc_signs2.argtypes = [u64, i32, P, P]
         L.orc_fwht.argtypes = [P, i32]
-        L.orc_rotate.argtypes = [P, i32, P, P]
-        L.orc_unrotate.argtypes = [P, i32, P, P]
+        L.orc_rotate.argtypes = [P, i32, P, P, P]
+        L.orc_unrotate.argtypes = [P, i32, P, P, P]
         L.orc_pack.argtypes = [P, i32, i32, P]
         L.orc_unpack.argtypes = [P, i32, i32, P]
         L.orc_codebook.argtypes = [i32, i32, i32, P, P, P]
@@ -53,17 +54,17 @@ def lib():
         L.orc_sphere_mse.argtypes = [i32, i32, P, P]
         L.orc_sphere_mse.restype = f64
         L.orc_codebook_float.argtypes = [i32, i32, i32, P, P]
-        L.orc_encode.argtypes = [P, i64, i32, i32, i32, u64, P, P, P]
+        L.orc_encode.argtypes = [P, i64, i32, i32, i32, i32, u64, P, P, P]
         L.orc_encode.restype = i32
-        L.orc_decode.argtypes = [P, P, i64, i32, i32, i32, u64, P]
+        L.orc_decode.argtypes = [P, P, i64, i32, i32, i32, i32, u64, P]
         L.orc_decode.restype = i32
-        L.orc_decode_f64.argtypes = [P, P, i64, i32, i32, i32, u64, P]
+        L.orc_decode_f64.argtypes = [P, P, i64, i32, i32, i32, i32, u64, P]
         L.orc_decode_f64.restype = i32
         L.orc_attention.argtypes = [P, i32, P, P, P, P, i32, i32, i32, i32, i32,
-                                    i32, u64, f64, f64, P]
+                                    i32, i32, u64, f64, f64, P]
         L.orc_attention.restype = i32
         L.orc_attention_rotated.argtypes = [P, i32, P, P, P, P, i32, i32, i32,
-                                            i32, i32, i32, u64, f64, P]
+                                            i32, i32, i32, i32, u64, f64, P]
         L.orc_attention_rotated.restype = i32
         _lib = L
     return _lib
@@ -89,29 +90,45 @@ def signs(seed: int, d: int) -> np.ndarray:
     return out
 
 
+def signs2(seed: int, d: int):
+    """(s1, s2): the sign vectors before and after the butterfly."""
+    s1 = np.zeros(d, np.int8)
+    s2 = np.zeros(d, np.int8)
+    lib().orc_signs2(seed, d, _p(s1), _p(s2))
+    return s1, s2
+
+
+def _rotation_signs(seed: int, d: int, two_sided: bool):
+    if two_sided:
+        return signs2(seed, d)
+    return signs(seed, d), None
+
+
 def fwht(x) -> np.ndarray:
     x = _c(x, np.float64).copy()
     lib().orc_fwht(_p(x), x.shape[-1])
     return x
 
 
-def rotate(x, seed: int) -> np.ndarray:
+def rotate(x, seed: int, two_sided: bool = False) -> np.ndarray:
     x = _c(x, np.float64)
     d = x.shape[-1]
-    s = signs(seed, d)
+    s, s2 = _rotation_signs(seed, d, two_sided)
     y = np.empty_like(x)
     for r in range(x.reshape(-1, d).shape[0]):
-        lib().orc_rotate(_p(x.reshape(-1, d)[r]), d, _p(s), _p(y.reshape(-1, d)[r]))
+        lib().orc_rotate(_p(x.reshape(-1, d)[r]), d, _p(s), None if s2 is None else _p(s2),
+                         _p(y.reshape(-1, d)[r]))
     return y
 
 
-def unrotate(y, seed: int) -> np.ndarray:
+def unrotate(y, seed: int, two_sided: bool = False) -> np.ndarray:
     y = _c(y, np.float64)
     d = y.shape[-1]
-    s = signs(seed, d)
+    s, s2 = _rotation_signs(seed, d, two_sided)
     x = np.empty_like(y)
     for r in range(y.reshape(-1, d).shape[0]):
-        lib().orc_unrotate(_p(y.reshape(-1, d)[r]), d, _p(s), _p(x.reshape(-1, d)[r]))
+        lib().orc_unrotate(_p(y.reshape(-1, d)[r]), d, _p(s), None if s2 is None else _p(s2),
+                           _p(x.reshape(-1, d)[r]))
     return x
 
 
@@ -166,7 +183,8 @@ def codebook_float(d: int, bits: int, density: int = BETA):
     return cf, bf[: L - 1]
 
 
-def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False):
+def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False,
+           two_sided: bool = False):
     """x: float32 [n, d] (bf16 callers convert exactly first).
     Returns packed uint8 [n, d*bits/8], norms float32 [n] (and u fp64 [n, d])."""
     x = _c(x, np.float32).reshape(-1, d)
@@ -174,7 +192,7 @@ def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False):
     packed = np.zeros((n, d * bits // 8), np.uint8)
     norms = np.zeros(n, np.float32)
     u = np.zeros((n, d), np.float64) if want_u else None
-    rc = lib().orc_encode(_p(x), n, d, bits, density, seed, _p(packed), _p(norms),
+    rc = lib().orc_encode(_p(x), n, d, bits, density, int(two_sided), seed, _p(packed), _p(norms),
                           _p(u) if want_u else None)
     if rc != 0:
         raise RuntimeError(f"orc_encode -> {rc}")
@@ -182,23 +200,26 @@ def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False):
 
 
 def decode(packed, norms, d: int, bits: int, seed: int, density: int = BETA,
-           f64: bool = False):
+           f64: bool = False, two_sided: bool = False):
     packed = _c(packed, np.uint8).reshape(-1, d * bits // 8)
     norms = _c(norms, np.float32).reshape(-1)
     n = packed.shape[0]
     if f64:
         out = np.zeros((n, d), np.float64)
-        rc = lib().orc_decode_f64(_p(packed), _p(norms), n, d, bits, density, seed, _p(out))
+        rc = lib().orc_decode_f64(_p(packed), _p(norms), n, d, bits, density, int(two_sided),
+                                  seed, _p(out))
     else:
         out = np.zeros((n, d), np.float32)
-        rc = lib().orc_decode(_p(packed), _p(norms), n, d, bits, density, seed, _p(out))
+        rc = lib().orc_decode(_p(packed), _p(norms), n, d, bits, density, int(two_sided),
+                              seed, _p(out))
     if rc != 0:
         raise RuntimeError(f"orc_decode -> {rc}")
     return out
 
 
 def attention(q, k_packed, k_norms, v_packed, v_norms, n_kv, T, d, bits_k, bits_v,
-              seed, scale, density=BETA, sparse_v_threshold=0.0, rotated=False):
+              seed, scale, density=BETA, sparse_v_threshold=0.0, rotated=False,
+              two_sided=False):
     """One sequence: q [n_q, d] float32; cache rows [n_kv, T]. Returns fp64 [n_q, d]."""
     q = _c(q, np.float32).reshape(-1, d)
     n_q = q.shape[0]
@@ -211,10 +232,11 @@ def attention(q, k_packed, k_norms, v_packed, v_norms, n_kv, T, d, bits_k, bits_
     out = np.zeros((n_q, d), np.float64)
     if rotated:
         rc = lib().orc_attention_rotated(_p(q), n_q, _p(kp), _p(kn), _p(vp), _p(vn), n_kv,
-                                         T, d, bits_k, bits_v, density, seed, scale, _p(out))
+                                         T, d, bits_k, bits_v, density, int(two_sided), seed,
+                                         scale, _p(out))
     else:
         rc = lib().orc_attention(_p(q), n_q, _p(kp), _p(kn), _p(vp), _p(vn), n_kv, T, d,
-                                 bits_k, bits_v, density, seed, scale,
+                                 bits_k, bits_v, density, int(two_sided), seed, scale,
                                  sparse_v_threshold, _p(out))
     if rc != 0:
         raise RuntimeError(f"orc_attention -> {rc}")

@@ -21,6 +21,8 @@
  *   orc_rotate     [Foundry] "As-Built Notes" item 1 (signs before the
  *                  Hadamard: y = H (D x) / sqrt(d)); [KVC] "TurboAngle
  *                  reference path" steps 1-2 (D then orthonormal H).
+ *                  Optional second sign vector after the Hadamard: [Atlas]
+ *                  "Two-sided Rademacher signs in WHT" (orc_signs2).
  *   orc_codebook   [Foundry] "Step 2: Lloyd-Max Scalar Quantization" and
  *                  "Codebook Generation" (Lloyd iteration on Beta(d/2, d/2)
  *                  mapped to [-1, 1]); [Atlas] "Prior art" item 4 for the
@@ -85,6 +87,34 @@ void orc_signs(uint64_t seed, int d, int8_t *out)
     }
 }
 
+/* Two-sided rotation ([Atlas] "Two-sided Rademacher signs in WHT": one sign
+ * vector before the butterfly and another after it).  The page does not
+ * print the two vectors; reading: s1 is the one-sided vector above (outputs
+ * 0..d-1) and s2 takes the next d outputs of the same stream (d..2d-1). */
+void orc_signs2(uint64_t seed, int d, int8_t *s1, int8_t *s2)
+{
+    int8_t *all = (int8_t *)malloc((size_t)2 * d);
+    orc_signs(seed, 2 * d, all);
+    memcpy(s1, all, (size_t)d);
+    memcpy(s2, all + d, (size_t)d);
+    free(all);
+}
+
+/* The sign vectors a codec call uses: s always, s2 only when two_sided
+ * (else *s2 = NULL).  Both are malloc'd; free with free(). */
+static void orc_rotation_signs(uint64_t seed, int d, int two_sided, int8_t **s,
+                               int8_t **s2)
+{
+    *s = (int8_t *)malloc((size_t)d);
+    *s2 = NULL;
+    if (two_sided) {
+        *s2 = (int8_t *)malloc((size_t)d);
+        orc_signs2(seed, d, *s, *s2);
+    } else {
+        orc_signs(seed, d, *s);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Rotation                                                            */
 /* ------------------------------------------------------------------ */
@@ -105,8 +135,10 @@ void orc_fwht(double *x, int d)
     }
 }
 
-/* Forward rotation y = H (s .* x) / sqrt(d). */
-void orc_rotate(const double *x, int d, const int8_t *s, double *y)
+/* Forward rotation y = H (s .* x) / sqrt(d), and with a second sign vector
+ * s2 (not NULL) y = s2 .* H (s .* x) / sqrt(d). */
+void orc_rotate(const double *x, int d, const int8_t *s, const int8_t *s2,
+                double *y)
 {
     double inv = 1.0 / sqrt((double)d);
     for (int i = 0; i < d; i++)
@@ -114,16 +146,20 @@ void orc_rotate(const double *x, int d, const int8_t *s, double *y)
     orc_fwht(y, d);
     for (int i = 0; i < d; i++)
         y[i] *= inv;
+    if (s2)
+        for (int i = 0; i < d; i++)
+            y[i] *= (double)s2[i];
 }
 
 /* Inverse rotation x = s .* (H y) / sqrt(d): H/sqrt(d) is symmetric and
  * orthogonal, so it is its own inverse, and D is its own inverse; the order
- * is the reverse of the forward one. */
-void orc_unrotate(const double *y, int d, const int8_t *s, double *x)
+ * is the reverse of the forward one.  With s2: x = s .* H (s2 .* y) / sqrt(d). */
+void orc_unrotate(const double *y, int d, const int8_t *s, const int8_t *s2,
+                  double *x)
 {
     double inv = 1.0 / sqrt((double)d);
     for (int i = 0; i < d; i++)
-        x[i] = y[i];
+        x[i] = s2 ? (double)s2[i] * y[i] : y[i];
     orc_fwht(x, d);
     for (int i = 0; i < d; i++)
         x[i] = (double)s[i] * x[i] * inv;
@@ -490,7 +526,8 @@ int orc_codebook_float(int d, int bits, int density, float *cf, float *bf)
  *   n   = ||x||_2 of the input row, stored as float         (reading: the
  *         norm of the input row, not of the rotated one; equal in exact
  *         arithmetic)
- *   y   = H (s .* x) / sqrt(d)
+ *   y   = H (s .* x) / sqrt(d), or s2 .* H (s .* x) / sqrt(d) when
+ *         two_sided ([Atlas] "Two-sided Rademacher signs in WHT")
  *   u   = y / n, and u = 0 when n = 0                        (reading)
  *   idx = #{ j : b_j < u }  with b_j the float boundaries    (a u exactly on
  *         a boundary takes the lower cell; reading)
@@ -499,7 +536,8 @@ int orc_codebook_float(int d, int bits, int density, float *cf, float *bf)
  * u_out, when not NULL, receives u[n_rows][d] (for boundary-band accounting).
  * Returns 0 or a negative error. */
 int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
-               uint64_t seed, uint8_t *packed, float *norms, double *u_out)
+               int two_sided, uint64_t seed, uint8_t *packed, float *norms,
+               double *u_out)
 {
     if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4)
         return -3;
@@ -510,11 +548,11 @@ int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
         return -1;
     int L = 1 << bits;
     int row_bytes = d * bits / 8;
-    int8_t *s = (int8_t *)malloc((size_t)d);
+    int8_t *s, *s2;
     double *xr = (double *)malloc(sizeof(double) * d);
     double *y = (double *)malloc(sizeof(double) * d);
     uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_signs(seed, d, s);
+    orc_rotation_signs(seed, d, two_sided, &s, &s2);
     for (int64_t r = 0; r < n_rows; r++) {
         const float *xrow = x + r * d;
         double ss = 0.0;
@@ -523,7 +561,7 @@ int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
             ss += xr[i] * xr[i];
         }
         double n = sqrt(ss);
-        orc_rotate(xr, d, s, y);
+        orc_rotate(xr, d, s, s2, y);
         for (int i = 0; i < d; i++) {
             double u = n > 0.0 ? y[i] / n : 0.0;
             if (u_out)
@@ -538,27 +576,29 @@ int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
         norms[r] = (float)n;
     }
     free(s);
+    free(s2);
     free(xr);
     free(y);
     free(idx);
     return 0;
 }
 
-/* Decode one row into fp64: yhat = n * c[idx], xhat = s .* H yhat / sqrt(d). */
+/* Decode one row into fp64: yhat = n * c[idx], xhat = s .* H yhat / sqrt(d)
+ * (s .* H (s2 .* yhat) / sqrt(d) with a second sign vector). */
 static void orc_decode_row_f64(const uint8_t *packed_row, float norm, int d,
                                int bits, const orc_cb_entry *cb,
-                               const int8_t *s, uint8_t *idx, double *yh,
-                               double *out)
+                               const int8_t *s, const int8_t *s2, uint8_t *idx,
+                               double *yh, double *out)
 {
     orc_unpack(packed_row, d, bits, idx);
     for (int i = 0; i < d; i++)
         yh[i] = (double)norm * (double)cb->cf[idx[i]];
-    orc_unrotate(yh, d, s, out);
+    orc_unrotate(yh, d, s, s2, out);
 }
 
 /* Decode rows to float (rounded once from fp64). */
 int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
-               int bits, int density, uint64_t seed, float *out)
+               int bits, int density, int two_sided, uint64_t seed, float *out)
 {
     if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4 ||
         (d * bits) % 8 != 0)
@@ -567,18 +607,19 @@ int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
     if (!cb)
         return -1;
     int row_bytes = d * bits / 8;
-    int8_t *s = (int8_t *)malloc((size_t)d);
+    int8_t *s, *s2;
     double *yh = (double *)malloc(sizeof(double) * d);
     double *xo = (double *)malloc(sizeof(double) * d);
     uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_signs(seed, d, s);
+    orc_rotation_signs(seed, d, two_sided, &s, &s2);
     for (int64_t r = 0; r < n_rows; r++) {
-        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s,
+        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s, s2,
                            idx, yh, xo);
         for (int i = 0; i < d; i++)
             out[r * d + i] = (float)xo[i];
     }
     free(s);
+    free(s2);
     free(yh);
     free(xo);
     free(idx);
@@ -587,7 +628,8 @@ int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
 
 /* Same, but keeps fp64 output (used by the attention definition). */
 int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
-                   int d, int bits, int density, uint64_t seed, double *out)
+                   int d, int bits, int density, int two_sided, uint64_t seed,
+                   double *out)
 {
     if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4 ||
         (d * bits) % 8 != 0)
@@ -596,14 +638,15 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
     if (!cb)
         return -1;
     int row_bytes = d * bits / 8;
-    int8_t *s = (int8_t *)malloc((size_t)d);
+    int8_t *s, *s2;
     double *yh = (double *)malloc(sizeof(double) * d);
     uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_signs(seed, d, s);
+    orc_rotation_signs(seed, d, two_sided, &s, &s2);
     for (int64_t r = 0; r < n_rows; r++)
-        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s,
+        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s, s2,
                            idx, yh, out + r * d);
     free(s);
+    free(s2);
     free(yh);
     free(idx);
     return 0;
@@ -635,8 +678,8 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
 int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
                   const float *k_norms, const uint8_t *v_packed,
                   const float *v_norms, int n_kv, int T, int d, int bits_k,
-                  int bits_v, int density, uint64_t seed, double scale,
-                  double sparse_v_threshold, double *out)
+                  int bits_v, int density, int two_sided, uint64_t seed,
+                  double scale, double sparse_v_threshold, double *out)
 {
     if (n_kv <= 0 || n_q % n_kv != 0 || T < 1)
         return -3;
@@ -650,11 +693,11 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
     int rc = 0;
     for (int g = 0; g < n_kv && rc == 0; g++) {
         rc = orc_decode_f64(k_packed + (size_t)g * T * kb, k_norms + (size_t)g * T,
-                            T, d, bits_k, density, seed, K);
+                            T, d, bits_k, density, two_sided, seed, K);
         if (rc == 0)
             rc = orc_decode_f64(v_packed + (size_t)g * T * vb,
                                 v_norms + (size_t)g * T, T, d, bits_v, density,
-                                seed, V);
+                                two_sided, seed, V);
         for (int hh = 0; hh < G && rc == 0; hh++) {
             int h = g * G + hh;
             const float *qh = q + (size_t)h * d;
@@ -703,12 +746,13 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
 
 /* The same attention evaluated in the rotated domain: q' = H (s .* q)/sqrt(d),
  * score_t = scale * n_t <q', c_K[idx_t]>, o' = sum_t p_t n^V_t c_V[idx^V_t],
- * o = s .* H o' / sqrt(d).  Equal to orc_attention up to rounding. */
+ * o = s .* H o' / sqrt(d) (the rotation and its inverse take the second sign
+ * vector when two_sided).  Equal to orc_attention up to rounding. */
 int orc_attention_rotated(const float *q, int n_q, const uint8_t *k_packed,
                           const float *k_norms, const uint8_t *v_packed,
                           const float *v_norms, int n_kv, int T, int d,
-                          int bits_k, int bits_v, int density, uint64_t seed,
-                          double scale, double *out)
+                          int bits_k, int bits_v, int density, int two_sided,
+                          uint64_t seed, double scale, double *out)
 {
     if (n_kv <= 0 || n_q % n_kv != 0 || T < 1)
         return -3;
@@ -718,18 +762,18 @@ int orc_attention_rotated(const float *q, int n_q, const uint8_t *k_packed,
         return -1;
     int G = n_q / n_kv;
     int kb = d * bits_k / 8, vb = d * bits_v / 8;
-    int8_t *s = (int8_t *)malloc((size_t)d);
+    int8_t *s, *s2;
     double *qd = (double *)malloc(sizeof(double) * d);
     double *qr = (double *)malloc(sizeof(double) * d);
     double *orot = (double *)malloc(sizeof(double) * d);
     double *sc = (double *)malloc(sizeof(double) * (size_t)T);
     uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_signs(seed, d, s);
+    orc_rotation_signs(seed, d, two_sided, &s, &s2);
     for (int h = 0; h < n_q; h++) {
         int g = h / G;
         for (int i = 0; i < d; i++)
             qd[i] = (double)q[(size_t)h * d + i];
-        orc_rotate(qd, d, s, qr);
+        orc_rotate(qd, d, s, s2, qr);
         double m = -INFINITY;
         for (int t = 0; t < T; t++) {
             size_t row = (size_t)g * T + t;
@@ -755,9 +799,10 @@ int orc_attention_rotated(const float *q, int n_q, const uint8_t *k_packed,
             for (int i = 0; i < d; i++)
                 orot[i] += w * (double)cbv->cf[idx[i]];
         }
-        orc_unrotate(orot, d, s, out + (size_t)h * d);
+        orc_unrotate(orot, d, s, s2, out + (size_t)h * d);
     }
     free(s);
+    free(s2);
     free(qd);
     free(qr);
     free(orot);

@@ -403,3 +403,143 @@ def test_attention_sparse_v_gate_per_block(orc):
         keep[b0:b0 + 256] = e > thr
     assert keep[256:].sum() > 10 and keep[:256].sum() < 256
     np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-15, rtol=1e-10)
+
+
+# --------------------------------------------------------------------------
+# two-sided signs and the N(0, 1/d) density
+
+def _two_sided_dense(orc, d, seed=42):
+    """(S2 H S1, S1 H S2) from scipy's Sylvester Hadamard and the two sign
+    vectors."""
+    s1, s2 = (v.astype(np.float64) for v in orc.signs2(seed, d))
+    H = scipy.linalg.hadamard(d) / math.sqrt(d)
+    return np.diag(s2) @ H @ np.diag(s1), np.diag(s1) @ H @ np.diag(s2)
+
+
+def test_two_sided_signs_are_the_next_outputs(orc):
+    d = 128
+    raw = orc.splitmix64_stream(42, 2 * d)
+    top = np.where(raw >> np.uint64(63), -1, 1).astype(np.int8)
+    s1, s2 = orc.signs2(42, d)
+    assert np.array_equal(s1, top[:d]) and np.array_equal(s2, top[d:])
+    assert np.array_equal(s1, orc.signs(42, d))
+    assert not np.array_equal(s1, s2)
+    s1b, s2b = orc.signs2(42, 64)
+    assert np.array_equal(s1b, s1[:64]) and np.array_equal(s2b, top[64:128])
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_two_sided_rotation_dense_and_inverse(orc, d):
+    R, Rinv = _two_sided_dense(orc, d)
+    x = np.random.default_rng(d + 3).standard_normal((7, d))
+    y = orc.rotate(x, 42, two_sided=True)
+    np.testing.assert_allclose(y, x @ R.T, atol=1e-12)
+    assert np.abs(y - orc.rotate(x, 42)).max() > 1e-3      # not the one-sided map
+    # (S2 H S1)(S1 H S2) = I: the inverse takes the signs in the other order
+    np.testing.assert_allclose(R @ Rinv, np.eye(d), atol=1e-12)
+    np.testing.assert_allclose(orc.unrotate(y, 42, two_sided=True), x, atol=1e-12)
+    np.testing.assert_allclose(orc.unrotate(np.eye(d), 42, two_sided=True), Rinv.T,
+                               atol=1e-12)
+    # inner products survive (what attention in the rotated domain relies on)
+    z = np.random.default_rng(d + 4).standard_normal((7, d))
+    np.testing.assert_allclose((orc.rotate(z, 42, two_sided=True) * y).sum(1),
+                               (z * x).sum(1), rtol=1e-11)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 3), (128, 4), (256, 4)])
+def test_two_sided_encode_flips_cells_where_s2_is_negative(orc, d, bits):
+    L = 1 << bits
+    x = _rand_rows(300, d, 6)
+    p1, n1 = orc.encode(x, d, bits, 42)
+    p2, n2, u2 = orc.encode(x, d, bits, 42, want_u=True, two_sided=True)
+    assert np.array_equal(n1, n2)
+    _, s2 = orc.signs2(42, d)
+    i1 = np.stack([orc.unpack(r, d, bits) for r in p1]).astype(int)
+    i2 = np.stack([orc.unpack(r, d, bits) for r in p2]).astype(int)
+    c, b, _ = orc.codebook(d, bits)
+    away = np.abs(u2[..., None] - b[None, None, :]).min(-1) > 1e-6
+    assert away.mean() > 0.999
+    # the codebook is symmetric: negating a coordinate mirrors its cell
+    want = np.where(s2[None, :] < 0, L - 1 - i1, i1)
+    assert np.array_equal(i2[away], want[away])
+    assert (s2 < 0).any() and not np.array_equal(i1, i2)
+    R, _ = _two_sided_dense(orc, d)
+    nrm = np.linalg.norm(x.astype(np.float64), axis=1)
+    np.testing.assert_allclose(u2 * nrm[:, None], x.astype(np.float64) @ R.T, atol=1e-12)
+    nearest = np.abs(u2[..., None] - c[None, None, :]).argmin(-1)
+    assert np.array_equal(i2[away], nearest[away])
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 4), (256, 3)])
+def test_two_sided_decode_equals_dense_inverse(orc, d, bits):
+    x = _rand_rows(20, d, 3)
+    p, n = orc.encode(x, d, bits, 42, two_sided=True)
+    cf, _ = orc.codebook_float(d, bits)
+    _, Rinv = _two_sided_dense(orc, d)
+    idx = np.stack([orc.unpack(r, d, bits) for r in p])
+    yh = n[:, None].astype(np.float64) * cf[idx].astype(np.float64)
+    want = yh @ Rinv.T
+    np.testing.assert_allclose(orc.decode(p, n, d, bits, 42, f64=True, two_sided=True), want,
+                               atol=1e-12)
+    np.testing.assert_array_equal(orc.decode(p, n, d, bits, 42, two_sided=True),
+                                  want.astype(np.float32))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_gauss_density_is_scaled_normal_lloyd(orc, d, bits):
+    # N(0, 1/d) is N(0, 1) scaled by 1/sqrt(d): its Lloyd-Max levels are
+    # scipy's normal Lloyd-Max levels over sqrt(d), at every d
+    cg, bg, _ = orc.codebook(d, bits, orc.GAUSS)
+    np.testing.assert_allclose(cg * math.sqrt(d), _gauss_lloyd_scipy(bits), atol=1e-9)
+    np.testing.assert_allclose(bg, 0.5 * (cg[1:] + cg[:-1]), atol=1e-15)
+    cf, bf = orc.codebook_float(d, bits, orc.GAUSS)
+    L = 1 << bits
+    assert np.array_equal(cf, -cf[::-1]) and np.array_equal(bf, -bf[::-1])
+    assert bf[L // 2 - 1] == 0.0
+    np.testing.assert_allclose(cf, cg, rtol=1e-7)
+    # Beta(d/2, d/2) has variance 1/(d+1): its levels sit slightly inside
+    cb, _, _ = orc.codebook(d, bits)
+    assert np.all(np.abs(cb) < np.abs(cg))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_gauss_density_roundtrip_mse_matches_sphere_closed_form(orc, bits):
+    # encode and decode both take the N(0, 1/d) table: the round-trip error of
+    # uniform directions equals the sphere closed form for that table
+    d, n = 128, 6000
+    x = _rand_rows(n, d, 300 + bits).astype(np.float64)
+    p, nr = orc.encode(x.astype(np.float32), d, bits, 42, density=orc.GAUSS, two_sided=True)
+    xh = orc.decode(p, nr, d, bits, 42, density=orc.GAUSS, f64=True, two_sided=True)
+    nrm = np.linalg.norm(x, axis=1, keepdims=True)
+    err = ((x / nrm - xh / nr[:, None].astype(np.float64)) ** 2).sum(1)
+    c, b, _ = orc.codebook(d, bits, orc.GAUSS)
+    want = orc.sphere_mse(d, bits, c, b)
+    se = err.std(ddof=1) / math.sqrt(n)
+    assert abs(err.mean() - want) < 4 * se, (err.mean(), want, se)
+    # decode reads the N(0, 1/d) centroids (dense inverse on the float table)
+    cf, _ = orc.codebook_float(d, bits, orc.GAUSS)
+    _, Rinv = _two_sided_dense(orc, d)
+    idx = np.stack([orc.unpack(r, d, bits) for r in p[:50]])
+    yh = nr[:50, None].astype(np.float64) * cf[idx].astype(np.float64)
+    np.testing.assert_allclose(xh[:50], yh @ Rinv.T, atol=1e-12)
+
+
+def test_two_sided_attention_definition_and_rotated_identity(orc):
+    d, n_kv, G, T = 64, 2, 2, 40
+    rng = np.random.default_rng(17)
+    K = rng.standard_normal((n_kv * T, d)).astype(np.float32)
+    V = rng.standard_normal((n_kv * T, d)).astype(np.float32)
+    kw = dict(density=orc.GAUSS, two_sided=True)
+    kp, kn = orc.encode(K, d, 4, 42, **kw)
+    vp, vn = orc.encode(V, d, 3, 42, **kw)
+    q = rng.standard_normal((n_kv * G, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    o = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 3, 42, scale, **kw)
+    orot = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 3, 42, scale, rotated=True, **kw)
+    np.testing.assert_allclose(orot, o, atol=1e-12)
+    Kh = orc.decode(kp, kn, d, 4, 42, f64=True, **kw).reshape(n_kv, T, d)
+    Vh = orc.decode(vp, vn, d, 3, 42, f64=True, **kw).reshape(n_kv, T, d)
+    for h in range(n_kv * G):
+        p = scipy.special.softmax(scale * Kh[h // G] @ q[h].astype(np.float64))
+        np.testing.assert_allclose(o[h], p @ Vh[h // G], atol=1e-12)
