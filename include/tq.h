@@ -14,7 +14,8 @@
  *             addressing pos % max_seq), Hadamard Transform Detail,
  *             Optimization: Fused dequant-dot.
  *   [Atlas]   "CITATIONS" (TurboQuant+ integration notes): Prior art item 4
- *             (N(0, 1/d) codebooks).
+ *             (N(0, 1/d) codebooks); "Two-sided Rademacher signs in WHT";
+ *             "N(0, 1/d) codebook replacement"; "Sparse V dequant".
  *   [KVC]     "Implementation specification: TurboAngle and TurboQuant-style
  *             KV compression": Core implementation contract (rows [B, d],
  *             power-of-two d, K and V may use different codecs).
@@ -61,9 +62,24 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 /* Coordinate density a codebook is optimised for.
  *   TQ_BETA_HALF_D    Beta(d/2, d/2) mapped to [-1, 1]: [Foundry] Step 2.
- *   TQ_GAUSS_1_OVER_D N(0, 1/d): [Atlas] "Prior art" item 4.
- * Every call below other than tq_codebook_init_density uses TQ_BETA_HALF_D. */
+ *   TQ_GAUSS_1_OVER_D N(0, 1/d): [Atlas] "Prior art" item 4 and "N(0, 1/d)
+ *                     codebook replacement".
+ * The codec calls below select the density with TQ_FLAG_GAUSS_1_OVER_D. */
 typedef enum { TQ_BETA_HALF_D = 0, TQ_GAUSS_1_OVER_D = 1 } tq_density;
+
+/* Option bits (`flags` of tq_rotate / tq_encode / tq_decode and of
+ * tq_cache_desc).  0 = the default codec: Beta(d/2, d/2) codebooks and the
+ * one-sided rotation H (D x) / sqrt(d).  Other bits -> TQ_EINVAL.
+ *   TQ_FLAG_GAUSS_1_OVER_D  codebooks for N(0, 1/d) instead of Beta(d/2, d/2).
+ *   TQ_FLAG_TWO_SIDED       rotation S2 H (S1 x) / sqrt(d), inverse
+ *                           S1 H (S2 y) / sqrt(d) ([Atlas] "Two-sided
+ *                           Rademacher signs in WHT").  S1 is the one-sided
+ *                           diagonal (SplitMix64 outputs 0..d-1 of the seed);
+ *                           S2 takes outputs d..2d-1 of the same stream, i.e.
+ *                           S2 = entries d..2d-1 of tq_signs(2d, seed).
+ * Rows encoded with some flags decode correctly only with the same flags. */
+#define TQ_FLAG_GAUSS_1_OVER_D 1u
+#define TQ_FLAG_TWO_SIDED 2u
 
 /* Lloyd-Max scalar quantiser for one (d, bits, density), in units of a
  * unit-norm coordinate ([Foundry] Step 2's fa_tq_codebook, plus d, density
@@ -108,9 +124,11 @@ size_t tq_packed_row_bytes(int d, int bits);
  * Forward (inverse == 0): out = H (D x) / sqrt(d)   ([Foundry] As-Built 1).
  * Inverse (inverse != 0): out = D (H x) / sqrt(d)    ([Foundry] Hadamard
  * Transform Detail: H/sqrt(d) and D are each their own inverse).
+ * With TQ_FLAG_TWO_SIDED: S2 H (S1 x) / sqrt(d) and S1 H (S2 x) / sqrt(d);
+ * TQ_FLAG_GAUSS_1_OVER_D has no effect here.
  * in: [n_rows][d] of `dtype` (device); out: [n_rows][d] fp32 (device). */
 int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint64_t seed,
-              int inverse, float *out, void *stream);
+              uint32_t flags, int inverse, float *out, void *stream);
 
 /* Encode K and/or V rows ([Foundry] Steps 1-3 with As-Built 2; [KVC] K and V
  * may use different bit widths).  Per row x: n = ||x||_2 (fp32, stored),
@@ -119,16 +137,20 @@ int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint64_t seed,
  * k_rows / v_rows: [n_rows][d] of `dtype` (device); either side may be NULL
  * (its outputs are then ignored) but not both.
  * k_packed: [n_rows][d*bits_k/8], k_norms: [n_rows] (device, written).
- * Same for v_*.  One kernel launch covers both sides. */
+ * Same for v_*.  One kernel launch covers both sides.  `flags` selects the
+ * codebook density and the rotation (TQ_FLAG_*; u then uses S2 H S1). */
 int tq_encode(const void *k_rows, const void *v_rows, int dtype, int64_t n_rows,
-              int d, int bits_k, int bits_v, uint64_t seed, uint8_t *k_packed,
-              float *k_norms, uint8_t *v_packed, float *v_norms, void *stream);
+              int d, int bits_k, int bits_v, uint64_t seed, uint32_t flags,
+              uint8_t *k_packed, float *k_norms, uint8_t *v_packed, float *v_norms,
+              void *stream);
 
 /* Decode ([Foundry] Step 2 lookup, then the inverse rotation):
- * out = D H (n * c[idx]) / sqrt(d), fp32 [n_rows][d] (device).
+ * out = D H (n * c[idx]) / sqrt(d), fp32 [n_rows][d] (device); with
+ * TQ_FLAG_TWO_SIDED out = S1 H (S2 n c[idx]) / sqrt(d).  `flags` must be the
+ * ones the rows were encoded with.
  * packed: [n_rows][d*bits/8], norms: [n_rows] (device, read). */
 int tq_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
-              int bits, uint64_t seed, float *out, void *stream);
+              int bits, uint64_t seed, uint32_t flags, float *out, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Ring-buffer KV cache ([Foundry] API "Cache" and Integration Points:
@@ -146,6 +168,7 @@ typedef struct {
     int32_t window;           /* ring slots per (sequence, head) */
     int32_t bits_k, bits_v;
     uint64_t seed;            /* sign seed shared by K, V and q */
+    uint32_t flags;           /* TQ_FLAG_* for every layer, K and V */
     const int32_t *head_dim;  /* host array [n_layers] */
     uint8_t *const *k_packed; /* host array [n_layers] of device pointers */
     float *const *k_norms;

@@ -16,15 +16,15 @@ import torch
 
 from . import _abi
 from ._abi import (TQ_BETA_HALF_D, TQ_BF16, TQ_EHIP, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_F32,
-                   TQ_GAUSS_1_OVER_D, TQ_MAX_LAYERS, TQ_OK, TqCodebook, TqError, lib,
-                   library_path)
+                   TQ_FLAG_GAUSS_1_OVER_D, TQ_FLAG_TWO_SIDED, TQ_GAUSS_1_OVER_D, TQ_MAX_LAYERS,
+                   TQ_OK, TqCodebook, TqError, lib, library_path)
 
 __all__ = [
     "TqError", "TQCache", "lib", "library_path", "tq_codebook_init", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
     "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
     "TQ_F32", "TQ_BF16", "TQ_BETA_HALF_D", "TQ_GAUSS_1_OVER_D", "TQ_OK", "TQ_EINVAL",
-    "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS",
+    "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS", "TQ_FLAG_GAUSS_1_OVER_D", "TQ_FLAG_TWO_SIDED",
 ]
 
 _DTYPES = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
@@ -85,13 +85,15 @@ def tq_packed_row_bytes(d: int, bits: int) -> int:
     return int(lib().tq_packed_row_bytes(d, bits))
 
 
-def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, stream=None):
-    """Rotation only: out = H(D x)/sqrt(d) (or D H x / sqrt(d) when inverse)."""
+def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, stream=None,
+              flags: int = 0):
+    """Rotation only: out = H(D x)/sqrt(d) (or D H x / sqrt(d) when inverse);
+    S2 H S1 and S1 H S2 with TQ_FLAG_TWO_SIDED."""
     d = x.shape[-1]
     n = x.numel() // d if d else 0
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    _check(lib().tq_rotate(_dev(x, "x"), _DTYPES[x.dtype], n, d, ctypes.c_uint64(seed),
+    _check(lib().tq_rotate(_dev(x, "x"), _DTYPES[x.dtype], n, d, ctypes.c_uint64(seed), flags,
                            1 if inverse else 0, _dev(out, "out", torch.float32), _stream(stream)),
            "tq_rotate")
     return out
@@ -99,7 +101,7 @@ def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, strea
 
 def tq_encode(k: torch.Tensor | None, v: torch.Tensor | None, bits_k: int, bits_v: int,
               seed: int, k_packed=None, k_norms=None, v_packed=None, v_norms=None,
-              stream=None):
+              stream=None, flags: int = 0):
     """Encode K and/or V rows ([..., d], fp32 or bf16) in one launch.
     Returns (k_packed, k_norms, v_packed, v_norms) with None for a missing side."""
     ref = k if k is not None else v
@@ -128,12 +130,13 @@ def tq_encode(k: torch.Tensor | None, v: torch.Tensor | None, bits_k: int, bits_
         args += [_dev(x, "rows"), _dev(pk, "packed", torch.uint8), _dev(nm, "norms", torch.float32)]
         outs += [pk, nm]
     _check(lib().tq_encode(args[0], args[3], dt, n, d, bits_k, bits_v, ctypes.c_uint64(seed),
-                           args[1], args[2], args[4], args[5], _stream(stream)), "tq_encode")
+                           flags, args[1], args[2], args[4], args[5], _stream(stream)),
+           "tq_encode")
     return tuple(outs)
 
 
 def tq_decode(packed: torch.Tensor, norms: torch.Tensor, d: int, bits: int, seed: int,
-              out=None, stream=None):
+              out=None, stream=None, flags: int = 0):
     n = norms.numel()
     rb = tq_packed_row_bytes(d, bits)
     if packed.numel() != n * rb:
@@ -143,8 +146,8 @@ def tq_decode(packed: torch.Tensor, norms: torch.Tensor, d: int, bits: int, seed
     if out.numel() != n * d:
         raise ValueError("tq_decode: out has the wrong size")
     _check(lib().tq_decode(_dev(packed, "packed", torch.uint8), _dev(norms, "norms", torch.float32),
-                           n, d, bits, ctypes.c_uint64(seed), _dev(out, "out", torch.float32),
-                           _stream(stream)), "tq_decode")
+                           n, d, bits, ctypes.c_uint64(seed), flags,
+                           _dev(out, "out", torch.float32), _stream(stream)), "tq_decode")
     return out
 
 
@@ -156,12 +159,13 @@ class TQCache:
     descriptor holds host arrays of their device pointers."""
 
     def __init__(self, n_layers, batch, n_kv_heads, window, head_dim, bits_k, bits_v,
-                 seed=42, device="cuda"):
+                 seed=42, device="cuda", flags=0):
         hd = [head_dim] * n_layers if isinstance(head_dim, int) else list(head_dim)
         if len(hd) != n_layers:
             raise ValueError("head_dim list must have n_layers entries")
         self.n_layers, self.batch, self.n_kv_heads, self.window = n_layers, batch, n_kv_heads, window
         self.head_dim, self.bits_k, self.bits_v, self.seed = hd, bits_k, bits_v, seed
+        self.flags = flags
         self.k_packed, self.k_norms, self.v_packed, self.v_norms = [], [], [], []
         for d in hd:
             self.k_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bits_k),
@@ -181,7 +185,7 @@ class TQCache:
         self._vn = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.v_norms])
         self.desc = _abi.TqCacheDesc(
             n, self.batch, self.n_kv_heads, self.window, self.bits_k, self.bits_v, self.seed,
-            ctypes.cast(self._hd, ctypes.c_void_p), ctypes.cast(self._kp, ctypes.c_void_p),
+            self.flags, ctypes.cast(self._hd, ctypes.c_void_p), ctypes.cast(self._kp, ctypes.c_void_p),
             ctypes.cast(self._kn, ctypes.c_void_p), ctypes.cast(self._vp, ctypes.c_void_p),
             ctypes.cast(self._vn, ctypes.c_void_p))
 

@@ -10,6 +10,7 @@ _LIB_PATH = os.path.join(PKG, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP = 0, -1, -2, -3
 TQ_F32, TQ_BF16 = 0, 1
 TQ_BETA_HALF_D, TQ_GAUSS_1_OVER_D = 0, 1
+TQ_FLAG_GAUSS_1_OVER_D, TQ_FLAG_TWO_SIDED = 1, 2
 TQ_MAX_LAYERS = 256
 
 # every symbol include/tq.h declares
@@ -36,7 +37,7 @@ class TqCacheDesc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32), ("seed", ctypes.c_uint64),
-                ("head_dim", ctypes.c_void_p), ("k_packed", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32), ("head_dim", ctypes.c_void_p), ("k_packed", ctypes.c_void_p),
                 ("k_norms", ctypes.c_void_p), ("v_packed", ctypes.c_void_p),
                 ("v_norms", ctypes.c_void_p)]
 
@@ -67,9 +68,10 @@ def lib():
         L.tq_signs.argtypes = [i32, u64, P]
         L.tq_packed_row_bytes.argtypes = [i32, i32]
         L.tq_packed_row_bytes.restype = sz
-        L.tq_rotate.argtypes = [P, i32, i64, i32, u64, i32, P, P]
-        L.tq_encode.argtypes = [P, P, i32, i64, i32, i32, i32, u64, P, P, P, P, P]
-        L.tq_decode.argtypes = [P, P, i64, i32, i32, u64, P, P]
+        u32 = ctypes.c_uint32
+        L.tq_rotate.argtypes = [P, i32, i64, i32, u64, u32, i32, P, P]
+        L.tq_encode.argtypes = [P, P, i32, i64, i32, i32, i32, u64, u32, P, P, P, P, P]
+        L.tq_decode.argtypes = [P, P, i64, i32, i32, u64, u32, P, P]
         L.tq_append_row.argtypes = [P, i32, P, P, i32, i64, P]
         L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64]
         L.tq_attn_workspace_bytes.restype = sz

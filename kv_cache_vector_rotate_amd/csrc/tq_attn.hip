@@ -52,6 +52,7 @@ struct AttnParams {
     float centK[16];
     float centV[16];
     uint32_t signs[8];
+    uint32_t signs2[8];       // second diagonal (two-sided rotation), else zero
 };
 
 template <int M>
@@ -138,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     for (int i = tid; i < NPV; i += kBlock)
         tabV[i] = make_float2(p.centV[i & ((1 << BV) - 1)], p.centV[i >> BV]);
 
-    // q' = H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV head
+    // q' = S2 H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV
+    // head (S2 = identity for the one-sided rotation)
     if (wave == 0) {
         constexpr int P2 = D / kCPL;
         const int sub2 = lane % P2, r2 = lane / P2;
@@ -147,6 +149,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
         load_slice(p.q + ((int64_t)b * p.Hq + h) * D + sub2 * kCPL, v);
         apply_signs(v, p.signs[sub2]);
         fwht_row<P2>(v, sub2);
+        apply_signs(v, p.signs2[sub2]);
         if (r2 < G) {
 #pragma unroll
             for (int k = 0; k < kCPL; k++)
@@ -379,6 +382,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p)
             o[4 * j + 3] = fmaf(w, t.w, o[4 * j + 3]);
         }
     }
+    apply_signs(o, p.signs2[sub]);
     fwht_row<P>(o, sub);
     const float sc = 1.0f / (L * sqrtf((float)D));
 #pragma unroll
@@ -399,7 +403,7 @@ int check_cache(const tq_cache_desc *c, int layer, const char *fn)
         return tq::fail(TQ_EINVAL, std::string(fn) + ": invalid cache descriptor");
     if (layer < 0 || layer >= c->n_layers)
         return tq::fail(TQ_EINVAL, std::string(fn) + ": layer out of range");
-    return TQ_OK;
+    return tq::check_flags(c->flags, fn);
 }
 
 struct Split {
@@ -517,8 +521,8 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     if (tq::take_injected_launch_failure())
         return tq::fail(TQ_EHIP, "tq_attn_decode: injected launch failure (TQ_TEST_FAIL_LAUNCH)");
     tq_codebook ck, cv;
-    if ((rc = tq::get_codebook(d, c->bits_k, TQ_BETA_HALF_D, &ck)) != TQ_OK ||
-        (rc = tq::get_codebook(d, c->bits_v, TQ_BETA_HALF_D, &cv)) != TQ_OK)
+    if ((rc = tq::get_codebook(d, c->bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
+        (rc = tq::get_codebook(d, c->bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
         return rc;
     Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
     AttnParams p;
@@ -543,6 +547,7 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
         p.centV[j] = j < cv.levels ? cv.centroids[j] : 0.0f;
     }
     tq::sign_words(d, c->seed, p.signs);
+    tq::sign_words2(d, c->seed, c->flags, p.signs2);
     dim3 grid((unsigned)s.n_chunks, (unsigned)c->n_kv_heads, (unsigned)c->batch);
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (d) {

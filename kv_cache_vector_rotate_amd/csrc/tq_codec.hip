@@ -40,7 +40,7 @@ struct CodeTable {
 // table built for BITS.
 template <int D, int BITS, typename T>
 __device__ __forceinline__ void encode_row(const RawSlice<T> &raw, bool valid, int sub,
-                                           const SignMasks<T> &sm, uint32_t key,
+                                           const SignMasks<T> &sm, uint32_t s2, uint32_t key,
                                            uint8_t *dst_row, float *dst_norm)
 {
     constexpr int P = Shape<D>::P;
@@ -80,9 +80,12 @@ __device__ __forceinline__ void encode_row(const RawSlice<T> &raw, bool valid, i
         }
     }
     const float n = sqrtf(ss);
-    // u = H(D x) / (sqrt(d) n); zero rows get u = 0
+    // u = H(D x) / (sqrt(d) n) (S2 H (D x) / (sqrt(d) n) with the second
+    // diagonal of the two-sided rotation); zero rows get u = 0
     const float inv = ss > 0.0f ? 1.0f / sqrtf((float)D * ss) : 0.0f;
     fwht_row<P>(v, sub);
+    if (s2 != 0u)
+        apply_signs(v, s2);
     uint32_t w[BITS];
 #pragma unroll
     for (int j = 0; j < BITS; j++)
@@ -108,11 +111,13 @@ struct EncodeParams {
     EncodeSide side[2];
     int64_t n_rows;
     uint32_t signs[8];
+    uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
 
 template <int D, typename T, int BITS>
 __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t n_rows,
-                                                   const SignMasks<T> &sm, uint32_t key)
+                                                   const SignMasks<T> &sm, uint32_t s2,
+                                                   uint32_t key)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
@@ -136,7 +141,7 @@ __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t 
             zero_raw(nxt);
         const bool valid = row < n_rows;
         const int64_t r = valid ? row : 0;
-        encode_row<D, BITS, T>(cur, valid, sub, sm, key, s.packed + r * RB, s.norms + r);
+        encode_row<D, BITS, T>(cur, valid, sub, sm, s2, key, s.packed + r * RB, s.norms + r);
         cur = nxt;
         row = nrow;
     }
@@ -152,11 +157,12 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     __syncthreads();
     const int sub = (threadIdx.x & 63) % Shape<D>::P;
     const SignMasks<T> sm(p.signs[sub]);
+    const uint32_t s2 = p.signs2[sub];
     const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, sm, key); break;
-    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, sm, key); break;
-    default: encode_contig_loop<D, T, 4>(s, p.n_rows, sm, key); break;
+    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, sm, s2, key); break;
+    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, sm, s2, key); break;
+    default: encode_contig_loop<D, T, 4>(s, p.n_rows, sm, s2, key); break;
     }
 }
 
@@ -182,11 +188,24 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
 // an exact power-of-two rescale of the input instead; rows holding Inf or NaN
 // encode as the zero row and store a non-finite norm.
 
+struct SignBits {
+    uint32_t w[4];  // bit k of w[k / 32] set: coordinate k is negated
+};
+
 struct EncodeLaneParams {
     EncodeSide side[2];
     int64_t n_rows;
     uint32_t sbits[4];  // sign bits of the diagonal (bit k set: s_k = -1)
+    SignBits s2;        // second diagonal of the two-sided rotation
 };
+
+// t negated when output coordinate k carries a -1 of the second diagonal (k
+// is a compile-time index once the loops are unrolled, and the words are
+// uniform: the mask is scalar work, the xor one vector instruction)
+__device__ __forceinline__ float flip_by(float t, const SignBits &s2, int k)
+{
+    return __uint_as_float(__float_as_uint(t) ^ ((s2.w[k >> 5] << (31 - (k & 31))) & 0x80000000u));
+}
 
 template <int NWORDS>
 __device__ __forceinline__ void put_bits(uint32_t (&w)[NWORDS], int bit, int nbits, uint32_t idx)
@@ -314,10 +333,11 @@ __device__ __forceinline__ void stage_group(const u32x4 (&pf)[64 * 2 * D / 1024]
 }
 
 // Encode the staged group of 64 rows starting at row g0 for one side.
-template <int D, int BITS>
+template <int D, int BITS, bool S2>
 __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t g0,
                                              const int64_t n_rows, const uint32_t key,
-                                             uint8_t *stg, const uint32_t qaddr)
+                                             uint8_t *stg, const uint32_t qaddr,
+                                             const SignBits &s2)
 {
     constexpr int NP = D / 64;            // passes of 64 outputs
     constexpr int CB = 2 * D;             // input bytes per row
@@ -404,9 +424,13 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
 #pragma unroll
                 for (int i = j; i < j + HL; i++) {
                     const float bt = v[i + HL] * t2;
-                    const float ta = fmaf(v[i], t2, bt);
-                    const float tb = fmaf(v[i], t2, -bt);
+                    float ta = fmaf(v[i], t2, bt);
+                    float tb = fmaf(v[i], t2, -bt);
                     const int ka = 64 * pass + i, kb = ka + HL;
+                    if constexpr (S2) {
+                        ta = flip_by(ta, s2, ka);
+                        tb = flip_by(tb, s2, kb);
+                    }
                     pack_c2(ta, tb, 2 * (ka & 15), 2 * (kb & 15), w[ka >> 4], w[kb >> 4]);
                 }
         } else {
@@ -424,6 +448,11 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
                         const float bt = v[i + h + HL] * t;
                         tt[h] = fmaf(v[i + h], t, bt);
                         tt[h + 2] = fmaf(v[i + h], t, -bt);
+                    }
+                    if constexpr (S2) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++)
+                            tt[q] = flip_by(tt[q], s2, 64 * pass + k[q]);
                     }
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
@@ -485,11 +514,11 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
 // group g of the first side, then group g of the second, so that every wave
 // carries the same work whatever the bit widths.  The next group's loads are
 // issued before the current one is transformed.
-template <int D, int B0, int B1>
+template <int D, int B0, int B1, bool S2>
 __device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const EncodeSide &s1,
                                                  const int64_t n_rows, const uint32_t key0,
                                                  const uint32_t key1, uint8_t *stg,
-                                                 const uint32_t *qt)
+                                                 const uint32_t *qt, const SignBits &s2)
 {
     constexpr int NCH = 64 * 2 * D / 1024;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -509,16 +538,16 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const Enc
             load_group<D>(src1, g0, n_rows, lane, pf);
         else
             load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-        encode_group<D, B0>(s0, g0, n_rows, key0, stg, qaddr);
+        encode_group<D, B0, S2>(s0, g0, n_rows, key0, stg, qaddr, s2);
         if constexpr (B1 > 0) {
             stage_group<D>(pf, stg, lane);
             load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-            encode_group<D, B1>(s1, g0, n_rows, key1, stg, qaddr);
+            encode_group<D, B1, S2>(s1, g0, n_rows, key1, stg, qaddr, s2);
         }
     }
 }
 
-template <int D, int B0, int B1>
+template <int D, int B0, int B1, bool S2>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
 void encode_lane_kernel(EncodeLaneParams p)
 {
@@ -545,8 +574,8 @@ void encode_lane_kernel(EncodeLaneParams p)
     if constexpr (B1 > 2)
         build_lut(lut1, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
     __syncthreads();
-    encode_lane_loop<D, B0, B1>(p.side[0], p.side[1], p.n_rows, lut_key(lut0), lut_key(lut1),
-                                stage[threadIdx.x >> 6], qt);
+    encode_lane_loop<D, B0, B1, S2>(p.side[0], p.side[1], p.n_rows, lut_key(lut0),
+                                    lut_key(lut1), stage[threadIdx.x >> 6], qt, p.s2);
 }
 
 // ----------------------------------------------------------------- append
@@ -567,11 +596,12 @@ struct AppendParams {
     int window;
     int slot;         // pos % window
     uint32_t signs[8];
+    uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
 
 template <int D, typename T, int BITS>
 __device__ __forceinline__ void append_loop(const AppendSide &s, const AppendParams &p,
-                                            const SignMasks<T> &sm, uint32_t key)
+                                            const SignMasks<T> &sm, uint32_t s2, uint32_t key)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
@@ -591,7 +621,7 @@ __device__ __forceinline__ void append_loop(const AppendSide &s, const AppendPar
             load_raw(src, raw);
         else
             zero_raw(raw);
-        encode_row<D, BITS, T>(raw, valid, sub, sm, key, s.packed[li] + dst * RB,
+        encode_row<D, BITS, T>(raw, valid, sub, sm, s2, key, s.packed[li] + dst * RB,
                                s.norms[li] + dst);
     }
 }
@@ -605,11 +635,12 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
     __syncthreads();
     const int sub = (threadIdx.x & 63) % Shape<D>::P;
     const SignMasks<T> sm(p.signs[sub]);
+    const uint32_t s2 = p.signs2[sub];
     const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: append_loop<D, T, 2>(s, p, sm, key); break;
-    case 3: append_loop<D, T, 3>(s, p, sm, key); break;
-    default: append_loop<D, T, 4>(s, p, sm, key); break;
+    case 2: append_loop<D, T, 2>(s, p, sm, s2, key); break;
+    case 3: append_loop<D, T, 3>(s, p, sm, s2, key); break;
+    default: append_loop<D, T, 4>(s, p, sm, s2, key); break;
     }
 }
 
@@ -623,6 +654,11 @@ struct DecodeParams {
     int64_t row_base;  // first row of this launch
     float cent[16];
     uint32_t signs[8];
+    // packed-row xor mask: all bits of index i set where the second diagonal
+    // of the two-sided rotation is -1 (else zero).  The centroid table is
+    // exactly symmetric, c[L-1-k] = -c[k], so flipping the index bits is the
+    // exact negation of n c[idx].
+    uint32_t flip[32];
 };
 
 // One wave per workgroup, one pass of RPW rows per wave, and one launch (or
@@ -656,6 +692,9 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
         load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
         n = p.norms[r];
     }
+#pragma unroll
+    for (int j = 0; j < BITS; j++)
+        w[j] ^= p.flip[sub * BITS + j];
     float v[kCPL];
 #pragma unroll
     for (int k = 0; k < kCPL; k++)
@@ -678,6 +717,7 @@ struct RotateParams {
     int64_t row_base;  // first row of this launch
     int inverse;
     uint32_t signs[8];
+    uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
 
 template <int D, typename T>
@@ -692,18 +732,17 @@ __global__ __launch_bounds__(kBlock) void rotate_kernel(RotateParams p)
         return;
     const int64_t row = row0 + rig;
     const int64_t r = row < p.n_rows ? row : row0;
-    const uint32_t smask = p.signs[sub];
+    const uint32_t smask = p.signs[sub], s2 = p.signs2[sub];
     float v[kCPL];
     load_slice(static_cast<const T *>(p.in) + r * D + sub * kCPL, v);
-    if (!p.inverse)
-        apply_signs(v, smask);
+    // forward S2 H S1, inverse S1 H S2 (S2 = identity when one-sided)
+    apply_signs(v, p.inverse ? s2 : smask);
     fwht_row<P>(v, sub);
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 #pragma unroll
     for (int k = 0; k < kCPL; k++)
         v[k] *= inv_sqrt_d;
-    if (p.inverse)
-        apply_signs(v, smask);
+    apply_signs(v, p.inverse ? smask : s2);
     store_region_coalesced(p.out + row0 * D, v, stage[wave], lane, (p.n_rows - row0) * D);
 }
 
@@ -770,10 +809,10 @@ int check_bits(int bits, const char *fn)
 }
 
 // boundaries for the device table; checks that no widened bin holds two
-int code_table(int d, int bits, CodeTable *t, const char *fn)
+int code_table(int d, int bits, int density, CodeTable *t, const char *fn)
 {
     tq_codebook cb;
-    int rc = tq::get_codebook(d, bits, TQ_BETA_HALF_D, &cb);
+    int rc = tq::get_codebook(d, bits, density, &cb);
     if (rc != TQ_OK)
         return rc;
     t->bits = bits;
@@ -790,6 +829,26 @@ int code_table(int d, int bits, CodeTable *t, const char *fn)
         t->istep = 1.0f / (kLutScale * cb.boundaries[2]);
     }
     return TQ_OK;
+}
+
+// The decode kernel's packed-row xor mask (DecodeParams::flip): the packed
+// row (LSB-first bitstream) of indices L-1 where the second diagonal is -1,
+// 0 elsewhere; all zero for the one-sided rotation.
+void flip_words(int d, int bits, uint64_t seed, uint32_t flags, uint32_t *flip)
+{
+    uint32_t s2[8];
+    tq::sign_words2(d, seed, flags, s2);
+    for (int j = 0; j < 32; j++)
+        flip[j] = 0u;
+    const uint32_t all = (1u << bits) - 1u;
+    for (int i = 0; i < d; i++) {
+        if (!((s2[i / 32] >> (i % 32)) & 1u))
+            continue;
+        const int bit = i * bits, wd = bit / 32, sh = bit % 32;
+        flip[wd] |= all << sh;
+        if (sh + bits > 32)
+            flip[wd + 1] |= all >> (32 - sh);
+    }
 }
 
 int launch_status(const char *fn)
@@ -833,10 +892,10 @@ int resident_blocks(K kern)
     return n;
 }
 
-template <int D, int B0, int B1>
+template <int D, int B0, int B1, bool S2>
 void launch_encode_lane_k(const EncodeLaneParams &q, hipStream_t st)
 {
-    auto kern = encode_lane_kernel<D, B0, B1>;
+    auto kern = encode_lane_kernel<D, B0, B1, S2>;
     const int64_t groups = (q.n_rows + 63) / 64;  // 64 rows per wave
     const int64_t need = (groups + kBlock / 64 - 1) / (kBlock / 64);
     // the resident workgroups, each looping over groups
@@ -847,19 +906,19 @@ void launch_encode_lane_k(const EncodeLaneParams &q, hipStream_t st)
 }
 
 // sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
-template <int D>
+template <int D, bool S2>
 void launch_encode_lane_d(const EncodeLaneParams &q, int b0, int b1, hipStream_t st)
 {
     switch (b0 * 10 + b1) {
-    case 40: launch_encode_lane_k<D, 4, 0>(q, st); break;
-    case 30: launch_encode_lane_k<D, 3, 0>(q, st); break;
-    case 20: launch_encode_lane_k<D, 2, 0>(q, st); break;
-    case 44: launch_encode_lane_k<D, 4, 4>(q, st); break;
-    case 43: launch_encode_lane_k<D, 4, 3>(q, st); break;
-    case 42: launch_encode_lane_k<D, 4, 2>(q, st); break;
-    case 33: launch_encode_lane_k<D, 3, 3>(q, st); break;
-    case 32: launch_encode_lane_k<D, 3, 2>(q, st); break;
-    default: launch_encode_lane_k<D, 2, 2>(q, st); break;
+    case 40: launch_encode_lane_k<D, 4, 0, S2>(q, st); break;
+    case 30: launch_encode_lane_k<D, 3, 0, S2>(q, st); break;
+    case 20: launch_encode_lane_k<D, 2, 0, S2>(q, st); break;
+    case 44: launch_encode_lane_k<D, 4, 4, S2>(q, st); break;
+    case 43: launch_encode_lane_k<D, 4, 3, S2>(q, st); break;
+    case 42: launch_encode_lane_k<D, 4, 2, S2>(q, st); break;
+    case 33: launch_encode_lane_k<D, 3, 3, S2>(q, st); break;
+    case 32: launch_encode_lane_k<D, 3, 2, S2>(q, st); break;
+    default: launch_encode_lane_k<D, 2, 2, S2>(q, st); break;
     }
 }
 
@@ -921,7 +980,7 @@ void launch_rotate(int d, const RotateParams &p0, hipStream_t st)
 // ------------------------------------------------------------ C entry points
 
 extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint64_t seed,
-                         int inverse, float *out, void *stream)
+                         uint32_t flags, int inverse, float *out, void *stream)
 {
     static const char *fn = "tq_rotate";
     tq::clear_error();
@@ -929,8 +988,10 @@ extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint6
         return tq::fail(TQ_EINVAL, "tq_rotate: unknown dtype");
     if (n_rows < 0)
         return tq::fail(TQ_EINVAL, "tq_rotate: n_rows < 0");
-    int rc = check_d(d, fn);
+    int rc = tq::check_flags(flags, fn);
     if (rc != TQ_OK)
+        return rc;
+    if ((rc = check_d(d, fn)) != TQ_OK)
         return rc;
     if (n_rows == 0)
         return TQ_OK;
@@ -946,6 +1007,7 @@ extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint6
     p.n_rows = n_rows;
     p.inverse = inverse ? 1 : 0;
     tq::sign_words(d, seed, p.signs);
+    tq::sign_words2(d, seed, flags, p.signs2);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == TQ_F32)
         launch_rotate<float>(d, p, st);
@@ -955,8 +1017,9 @@ extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint6
 }
 
 extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int64_t n_rows,
-                         int d, int bits_k, int bits_v, uint64_t seed, uint8_t *k_packed,
-                         float *k_norms, uint8_t *v_packed, float *v_norms, void *stream)
+                         int d, int bits_k, int bits_v, uint64_t seed, uint32_t flags,
+                         uint8_t *k_packed, float *k_norms, uint8_t *v_packed, float *v_norms,
+                         void *stream)
 {
     static const char *fn = "tq_encode";
     tq::clear_error();
@@ -964,8 +1027,10 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         return tq::fail(TQ_EINVAL, "tq_encode: unknown dtype");
     if (n_rows < 0)
         return tq::fail(TQ_EINVAL, "tq_encode: n_rows < 0");
-    int rc = check_d(d, fn);
+    int rc = tq::check_flags(flags, fn);
     if (rc != TQ_OK)
+        return rc;
+    if ((rc = check_d(d, fn)) != TQ_OK)
         return rc;
     if (n_rows == 0)
         return TQ_OK;  // nothing to do; buffers may be NULL
@@ -990,7 +1055,7 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         e.src = src[s];
         e.packed = pk[s];
         e.norms = nm[s];
-        if ((rc = code_table(d, bits[s], &e.code, fn)) != TQ_OK)
+        if ((rc = code_table(d, bits[s], tq::density_of(flags), &e.code, fn)) != TQ_OK)
             return rc;
     }
     if ((rc = injected(fn)) != TQ_OK)
@@ -1010,15 +1075,20 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
             q.side[1] = q.side[0];  // unused
         q.n_rows = n_rows;
         for (int w = 0; w < 4; w++)
-            q.sbits[w] = 0u;
+            q.sbits[w] = q.s2.w[w] = 0u;
         tq::sign_words(d, seed, q.sbits);
+        tq::sign_words2(d, seed, flags, q.s2.w);
+        const bool two = (flags & TQ_FLAG_TWO_SIDED) != 0;
         if (d == 64)
-            launch_encode_lane_d<64>(q, b0, b1, st);
+            two ? launch_encode_lane_d<64, true>(q, b0, b1, st)
+                : launch_encode_lane_d<64, false>(q, b0, b1, st);
         else
-            launch_encode_lane_d<128>(q, b0, b1, st);
+            two ? launch_encode_lane_d<128, true>(q, b0, b1, st)
+                : launch_encode_lane_d<128, false>(q, b0, b1, st);
         return launch_status(fn);
     }
     tq::sign_words(d, seed, p.signs);
+    tq::sign_words2(d, seed, flags, p.signs2);
     if (dtype == TQ_F32)
         launch_encode<float>(d, p, sides, st);
     else
@@ -1027,14 +1097,16 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
 }
 
 extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
-                         int bits, uint64_t seed, float *out, void *stream)
+                         int bits, uint64_t seed, uint32_t flags, float *out, void *stream)
 {
     static const char *fn = "tq_decode";
     tq::clear_error();
     if (n_rows < 0)
         return tq::fail(TQ_EINVAL, "tq_decode: n_rows < 0");
-    int rc = check_d(d, fn);
+    int rc = tq::check_flags(flags, fn);
     if (rc != TQ_OK)
+        return rc;
+    if ((rc = check_d(d, fn)) != TQ_OK)
         return rc;
     if ((rc = check_bits(bits, fn)) != TQ_OK)
         return rc;
@@ -1047,8 +1119,11 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
     if ((rc = injected(fn)) != TQ_OK)
         return rc;
     tq_codebook cb;
-    if ((rc = tq::get_codebook(d, bits, TQ_BETA_HALF_D, &cb)) != TQ_OK)
+    if ((rc = tq::get_codebook(d, bits, tq::density_of(flags), &cb)) != TQ_OK)
         return rc;
+    for (int j = 0; j < cb.levels; j++)
+        if (cb.centroids[cb.levels - 1 - j] != -cb.centroids[j])
+            return tq::fail(TQ_EUNSUPPORTED, "tq_decode: codebook is not symmetric");
     DecodeParams p;
     p.packed = packed;
     p.norms = norms;
@@ -1057,6 +1132,7 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
     for (int j = 0; j < 16; j++)
         p.cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
     tq::sign_words(d, seed, p.signs);
+    flip_words(d, bits, seed, flags, p.flip);
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (d) {
     case 64: launch_decode_d<64>(bits, p, st); break;
@@ -1083,6 +1159,8 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
         return tq::fail(TQ_EINVAL, "tq_append_row: layer out of range");
     if (pos < 0)
         return tq::fail(TQ_EINVAL, "tq_append_row: pos < 0");
+    if (tq::check_flags(c->flags, fn) != TQ_OK)
+        return TQ_EINVAL;
     if (!k_new || !v_new)
         return tq::fail(TQ_EINVAL, "tq_append_row: k_new / v_new is NULL");
     int rc;
@@ -1116,8 +1194,10 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
         p.window = c->window;
         p.slot = slot;
         tq::sign_words(d, c->seed, p.signs);
-        if ((rc = code_table(d, c->bits_k, &p.side[0].code, fn)) != TQ_OK ||
-            (rc = code_table(d, c->bits_v, &p.side[1].code, fn)) != TQ_OK)
+        tq::sign_words2(d, c->seed, c->flags, p.signs2);
+        const int dens = tq::density_of(c->flags);
+        if ((rc = code_table(d, c->bits_k, dens, &p.side[0].code, fn)) != TQ_OK ||
+            (rc = code_table(d, c->bits_v, dens, &p.side[1].code, fn)) != TQ_OK)
             return rc;
         p.n_layers = 0;
         for (int l = l0; l <= l1; l++) {

@@ -77,6 +77,28 @@ void sign_words(int d, uint64_t seed, uint32_t *words)
             words[i / 32] |= 1u << (i % 32);
 }
 
+void sign_words2(int d, uint64_t seed, uint32_t flags, uint32_t *words)
+{
+    int nw = (d + 31) / 32;
+    for (int w = 0; w < nw; w++)
+        words[w] = 0;
+    if (!(flags & TQ_FLAG_TWO_SIDED))
+        return;
+    uint64_t s = seed;
+    for (int i = 0; i < d; i++)
+        (void)splitmix64_next(s);
+    for (int i = 0; i < d; i++)
+        if (splitmix64_next(s) >> 63)
+            words[i / 32] |= 1u << (i % 32);
+}
+
+int check_flags(uint32_t flags, const char *fn)
+{
+    if (flags & ~(TQ_FLAG_GAUSS_1_OVER_D | TQ_FLAG_TWO_SIDED))
+        return fail(TQ_EINVAL, std::string(fn) + ": unknown flag bits");
+    return TQ_OK;
+}
+
 // ------------------------------------------------------------- codebook
 
 // Continued fraction of I_x(a, b) (valid for x < (a+1)/(a+b+2)).

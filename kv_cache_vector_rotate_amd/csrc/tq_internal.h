@@ -21,6 +21,19 @@ int get_codebook(int d, int bits, int density, tq_codebook *out);
 // when coordinate i is negated.  d <= 256 for device use.
 void sign_words(int d, uint64_t seed, uint32_t *words /* d/32 rounded up */);
 
+// The second diagonal of the two-sided rotation (S2: stream outputs d..2d-1),
+// same layout; all zero unless `flags` has TQ_FLAG_TWO_SIDED.
+void sign_words2(int d, uint64_t seed, uint32_t flags, uint32_t *words);
+
+// Codebook density selected by `flags`.
+inline int density_of(uint32_t flags)
+{
+    return (flags & TQ_FLAG_GAUSS_1_OVER_D) ? TQ_GAUSS_1_OVER_D : TQ_BETA_HALF_D;
+}
+
+// TQ_OK, or TQ_EINVAL (with a message naming fn) for unknown option bits.
+int check_flags(uint32_t flags, const char *fn);
+
 bool is_pow2(int64_t v);
 
 // Test-only fault injection: when the environment variable TQ_TEST_FAIL_LAUNCH

@@ -109,32 +109,42 @@ def test_encode_decode_validation_without_launch(tq):
     L = tq.lib()
     A = _c(4096)          # fake, 16-byte aligned pointers: never dereferenced
     N = _c(8192)
-    assert L.tq_encode(None, None, 0, 10, 128, 4, 2, 42, A, N, A, N, None) == tq.TQ_EINVAL
+    assert L.tq_encode(None, None, 0, 10, 128, 4, 2, 42, 0, A, N, A, N, None) == tq.TQ_EINVAL
     assert "both" in tq.tq_last_error()
-    assert L.tq_encode(A, None, 7, 10, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
-    assert L.tq_encode(A, None, 0, 10, 96, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
-    assert L.tq_encode(A, None, 0, 10, 512, 4, 2, 42, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
-    assert L.tq_encode(A, None, 0, 10, 128, 1, 2, 42, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
-    assert L.tq_encode(A, None, 0, 10, 128, 5, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
-    assert L.tq_encode(A, None, 0, -1, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
-    assert L.tq_encode(_c(4100), None, 0, 10, 128, 4, 2, 42, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 7, 10, 128, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 96, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 512, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 128, 1, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 128, 5, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, -1, 128, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(_c(4100), None, 0, 10, 128, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
     assert "aligned" in tq.tq_last_error()
-    assert L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, None, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, 0, None, N, None, None, None) == tq.TQ_EINVAL
     # n_rows == 0 succeeds and launches nothing, NULL buffers included
-    assert L.tq_encode(A, A, 1, 0, 128, 4, 2, 42, A, N, A, N, None) == tq.TQ_OK
-    assert L.tq_encode(None, None, 1, 0, 128, 4, 2, 42, None, None, None, None, None) == tq.TQ_OK
-    assert L.tq_decode(A, N, 0, 128, 4, 42, A, None) == tq.TQ_OK
-    assert L.tq_decode(A, N, 5, 128, 1, 42, A, None) == tq.TQ_EUNSUPPORTED
-    assert L.tq_decode(None, N, 5, 128, 4, 42, A, None) == tq.TQ_EINVAL
-    assert L.tq_rotate(A, 0, 0, 128, 42, 0, A, None) == tq.TQ_OK
-    assert L.tq_rotate(A, 0, 3, 100, 42, 0, A, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, A, 1, 0, 128, 4, 2, 42, 0, A, N, A, N, None) == tq.TQ_OK
+    assert L.tq_encode(None, None, 1, 0, 128, 4, 2, 42, 0, None, None, None, None, None) == tq.TQ_OK
+    assert L.tq_decode(A, N, 0, 128, 4, 42, 0, A, None) == tq.TQ_OK
+    assert L.tq_decode(A, N, 5, 128, 1, 42, 0, A, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_decode(None, N, 5, 128, 4, 42, 0, A, None) == tq.TQ_EINVAL
+    assert L.tq_rotate(A, 0, 0, 128, 42, 0, 0, A, None) == tq.TQ_OK
+    assert L.tq_rotate(A, 0, 3, 100, 42, 0, 0, A, None) == tq.TQ_EINVAL
+    # option bits: the two known ones pass validation, any other is rejected
+    for fn, args in (("tq_encode", lambda f: (A, None, 0, 0, 128, 4, 2, 42, f, A, N, None, None,
+                                              None)),
+                     ("tq_decode", lambda f: (A, N, 0, 128, 4, 42, f, A, None)),
+                     ("tq_rotate", lambda f: (A, 0, 0, 128, 42, f, 0, A, None))):
+        for f in (0, 1, 2, 3):
+            assert getattr(L, fn)(*args(f)) == tq.TQ_OK
+        for f in (4, 8, 0x80000000):
+            assert getattr(L, fn)(*args(f)) == tq.TQ_EINVAL
+            assert "flag" in tq.tq_last_error()
 
 
-def _desc(tq, n_layers=2, batch=2, n_kv=2, window=8, head_dim=128, bk=4, bv=2):
+def _desc(tq, n_layers=2, batch=2, n_kv=2, window=8, head_dim=128, bk=4, bv=2, flags=0):
     from kv_cache_vector_rotate_amd import _abi
     hd = (ctypes.c_int32 * n_layers)(*([head_dim] * n_layers))
     ptrs = [(ctypes.c_void_p * n_layers)(*([4096 * (i + 1)] * n_layers)) for i in range(4)]
-    d = _abi.TqCacheDesc(n_layers, batch, n_kv, window, bk, bv, 42,
+    d = _abi.TqCacheDesc(n_layers, batch, n_kv, window, bk, bv, 42, flags,
                          ctypes.cast(hd, ctypes.c_void_p),
                          *[ctypes.cast(p, ctypes.c_void_p) for p in ptrs])
     d._keep = (hd, ptrs)
@@ -166,6 +176,11 @@ def test_cache_and_attention_validation(tq):
     assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
     d3 = _desc(tq, bk=1)
     assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    d4 = _desc(tq, flags=4)
+    assert L.tq_attn_decode(ctypes.byref(d4), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    assert "flag" in tq.tq_last_error()
+    assert L.tq_append_row(ctypes.byref(d4), -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
+    assert "flag" in tq.tq_last_error()
 
 
 def test_injected_hip_error_path():
@@ -177,9 +192,9 @@ sys.path.insert(0, %r)
 import kv_cache_vector_rotate_amd as tq
 L = tq.lib()
 A = ctypes.c_void_p(4096); N = ctypes.c_void_p(8192)
-rc = L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, A, N, None, None, None)
+rc = L.tq_encode(A, None, 0, 10, 128, 4, 2, 42, 0, A, N, None, None, None)
 msg = tq.tq_last_error()
-rc2 = L.tq_decode(None, N, 5, 128, 4, 42, A, None)
+rc2 = L.tq_decode(None, N, 5, 128, 4, 42, 0, A, None)
 print(rc, rc2, msg)
 """ % ROOT
     env = dict(os.environ, TQ_TEST_FAIL_LAUNCH="1", HIP_VISIBLE_DEVICES="")

@@ -31,7 +31,8 @@ def _fill(tq, cache, layer, seed, kscale=1.0, dist="normal"):
         k = kvgen.student_t((B, H, W, d), seed, device="cuda") * kscale
         v = kvgen.student_t((B, H, W, d), seed + 1, device="cuda")
     tq.tq_encode(k, v, cache.bits_k, cache.bits_v, SEED, cache.k_packed[layer],
-                 cache.k_norms[layer], cache.v_packed[layer], cache.v_norms[layer])
+                 cache.k_norms[layer], cache.v_packed[layer], cache.v_norms[layer],
+                 flags=cache.flags)
 
 
 def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
@@ -47,7 +48,9 @@ def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
         vn = cache.v_norms[layer][b, g, :T].cpu().numpy()
         qh = q[b, h:h + 1].float().cpu().numpy()
         out[h] = orc.attention(qh, kp, kn, vp, vn, 1, T, d, cache.bits_k, cache.bits_v, SEED,
-                               scale, sparse_v_threshold=sparse_v)[0]
+                               scale, sparse_v_threshold=sparse_v,
+                               density=orc.GAUSS if cache.flags & 1 else orc.BETA,
+                               two_sided=bool(cache.flags & 2))[0]
     return out
 
 
@@ -167,3 +170,24 @@ def test_config4_attention_sparse_v_sampled(tq, orc):
         ref = _oracle(orc, cache, 0, q, int(b), heads, T, 1 / math.sqrt(d), sparse_v=1e-3)
         for h in heads:
             check_attention(o[b, h], ref[h])
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 3, 2), (256, 2, 4, 1)])
+def test_attention_flags(tq, orc, d, bk, bv, G, flags):
+    """N(0, 1/d) codebooks and the two-sided rotation: the cache written with
+    the flags, q rotated and the output rotated back with the same ones."""
+    B, Hkv, T = 2, 2, 1100
+    cache = tq.TQCache(1, B, Hkv, T, d, bk, bv, SEED, flags=flags)
+    _fill(tq, cache, 0, 40 + d + flags)
+    q = kvgen.normal((B, Hkv * G, d), 41 + flags, "cuda", torch.bfloat16)
+    o = tq.tq_attn_decode(cache, 0, q, T).cpu().numpy()
+    for b in range(B):
+        ref = _oracle(orc, cache, 0, q, b, range(Hkv * G), T, 1 / math.sqrt(d))
+        for h in range(Hkv * G):
+            check_attention(o[b, h], ref[h])
+    # with the gate on as well
+    o = tq.tq_attn_decode(cache, 0, q, T, sparse_v=1e-2).cpu().numpy()
+    ref = _oracle(orc, cache, 0, q, 1, range(Hkv * G), T, 1 / math.sqrt(d), sparse_v=1e-2)
+    for h in range(Hkv * G):
+        check_attention(o[1, h], ref[h])

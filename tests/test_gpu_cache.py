@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import kvgen
-from _parity import check_decoded, check_indices, check_norms
+from _parity import BandTally, check_decoded, check_indices, check_norms
 
 pytestmark = pytest.mark.gpu
 SEED = 42
@@ -20,22 +20,26 @@ def tq():
     return tq
 
 
-def _check_slot(orc, rows, packed, norms, d, bits):
-    op, on, u = orc.encode(rows.astype(np.float32), d, bits, SEED, want_u=True)
-    _, bnd = orc.codebook_float(d, bits)
+def _check_slot(orc, rows, packed, norms, d, bits, flags=0, tally=None):
+    density = orc.GAUSS if flags & 1 else orc.BETA
+    op, on, u = orc.encode(rows.astype(np.float32), d, bits, SEED, want_u=True,
+                           density=density, two_sided=bool(flags & 2))
+    _, bnd = orc.codebook_float(d, bits, density)
     check_norms(norms, on)
-    check_indices(packed, op, u, d, bits, bnd)
+    check_indices(packed, op, u, d, bits, bnd, tally=tally)
 
 
+@pytest.mark.parametrize("flags", [0, 3])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_append_ring_small_mixed_head_dims(tq, orc, dtype):
+def test_append_ring_small_mixed_head_dims(tq, orc, dtype, flags):
     """3 layers (head_dim 256, 64, 256), batch 3, 2 KV heads, window 5;
     appends positions 0..11 (the ring wraps twice), all layers per call; the
     cache must hold exactly the last `window` rows of every (layer, seq, head)
-    and untouched slots must stay as they were."""
+    and untouched slots must stay as they were.  flags 3: N(0, 1/d) codebooks
+    and the two-sided rotation."""
     hd = [256, 64, 256]
     B, H, W, bk, bv = 3, 2, 5, 4, 3
-    cache = tq.TQCache(3, B, H, W, hd, bk, bv, SEED)
+    cache = tq.TQCache(3, B, H, W, hd, bk, bv, SEED, flags=flags)
     hist = {}
     for pos in range(12):
         ks = [kvgen.unit_dirs_lognormal((B, H, d), 1000 * pos + l, "cuda").to(dtype)
@@ -48,13 +52,15 @@ def test_append_ring_small_mixed_head_dims(tq, orc, dtype):
             # slots 3, 4 never written yet: still zero
             assert torch.count_nonzero(cache.k_norms[0][:, :, 3:]).item() == 0
     torch.cuda.synchronize()
+    tally = BandTally()
     for slot, (ks, vs) in hist.items():
         for l, d in enumerate(hd):
             for x, bits, pk, nm in ((ks[l], bk, cache.k_packed[l], cache.k_norms[l]),
                                     (vs[l], bv, cache.v_packed[l], cache.v_norms[l])):
                 rows = x.float().cpu().numpy().reshape(B * H, d)
                 _check_slot(orc, rows, pk[:, :, slot].cpu().numpy().reshape(B * H, -1),
-                            nm[:, :, slot].cpu().numpy().reshape(-1), d, bits)
+                            nm[:, :, slot].cpu().numpy().reshape(-1), d, bits, flags, tally)
+    tally.check()
 
 
 def test_append_single_layer(tq, orc):
@@ -66,12 +72,14 @@ def test_append_single_layer(tq, orc):
     torch.cuda.synchronize()
     assert torch.count_nonzero(cache.k_norms[0]).item() == 0
     slot = 9 % W
+    tally = BandTally()
     _check_slot(orc, k.cpu().numpy().reshape(-1, d),
                 cache.k_packed[1][:, :, slot].cpu().numpy().reshape(B * H, -1),
-                cache.k_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 4)
+                cache.k_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 4, tally=tally)
     _check_slot(orc, v.cpu().numpy().reshape(-1, d),
                 cache.v_packed[1][:, :, slot].cpu().numpy().reshape(B * H, -1),
-                cache.v_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 2)
+                cache.v_norms[1][:, :, slot].cpu().numpy().reshape(-1), d, 2, tally=tally)
+    tally.check()
 
 
 def test_config2_gemma_shaped_step_full_size_sampled(tq, orc):
@@ -91,12 +99,13 @@ def test_config2_gemma_shaped_step_full_size_sampled(tq, orc):
     vs = [kvgen.unit_dirs_lognormal((B, H, d), 400 + l, "cuda") for l in range(NL)]
     tq.tq_append_row(cache, -1, ks, vs, W)
     out = torch.empty(B, H, W, d, device="cuda")
+    tally = BandTally()
     for l in rng.choice(NL, 3, replace=False):
         for x, pk, nm in ((ks[l], cache.k_packed[l], cache.k_norms[l]),
                           (vs[l], cache.v_packed[l], cache.v_norms[l])):
             _check_slot(orc, x.cpu().numpy().reshape(-1, d),
                         pk[:, :, 0].cpu().numpy().reshape(B * H, -1),
-                        nm[:, :, 0].cpu().numpy().reshape(-1), d, 4)
+                        nm[:, :, 0].cpu().numpy().reshape(-1), d, 4, tally=tally)
             tq.tq_decode(pk, nm, d, 4, SEED, out=out)
             torch.cuda.synchronize()
             sel = rng.choice(B * H * W, 2048, replace=False)
@@ -104,3 +113,4 @@ def test_config2_gemma_shaped_step_full_size_sampled(tq, orc):
             gn = nm.reshape(-1)[torch.from_numpy(sel).cuda()].cpu().numpy()
             gx = out.reshape(-1, d)[torch.from_numpy(sel).cuda()].cpu().numpy()
             check_decoded(gx, orc.decode(gp, gn, d, 4, SEED))
+    tally.check()

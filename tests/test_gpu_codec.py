@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import kvgen
-from _parity import (check_decoded, check_indices, check_norms, unpack_rows)
+from _parity import (BandTally, check_decoded, check_indices, check_norms, unpack_rows)
 
 pytestmark = pytest.mark.gpu
 SEED = 42
@@ -62,6 +62,7 @@ def test_encode_decode_all_bits_ragged(tq, orc, d, dtype):
     """K and V in one launch with different bit widths; row counts that leave
     a ragged tail in the last workgroup pass."""
     n = 1000 + 37
+    tally = BandTally()
     k = kvgen.normal((n, d), 11 + d, "cuda", dtype)
     v = kvgen.normal((n, d), 12 + d, "cuda", dtype) * 3.0
     for bk, bv in ((4, 2), (3, 3), (2, 4)):
@@ -73,9 +74,10 @@ def test_encode_decode_all_bits_ragged(tq, orc, d, dtype):
             _, bnd = orc.codebook_float(d, bits)
             gp, gn = p.cpu().numpy(), nm.cpu().numpy()
             check_norms(gn, on)
-            check_indices(gp, op, u, d, bits, bnd)
+            check_indices(gp, op, u, d, bits, bnd, tally=tally)
             xd = tq.tq_decode(p, nm, d, bits, SEED).cpu().numpy()
             check_decoded(xd, orc.decode(gp, gn, d, bits, SEED))
+    tally.check()
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
@@ -159,6 +161,7 @@ def test_config3_bulk_prefill_full_size_sampled(tq, orc):
     n = L * H * T
     rows = np.sort(np.random.default_rng(3).choice(n, 4096, replace=False))
     ridx = torch.from_numpy(rows).cuda()
+    tally = BandTally()
     for x, bits, p, nm in ((k, 4, kp, kn), (v, 2, vp, vn)):
         xs = x.reshape(n, d)[ridx].float().cpu().numpy()
         op, on, u = orc.encode(xs, d, bits, SEED, want_u=True)
@@ -166,7 +169,8 @@ def test_config3_bulk_prefill_full_size_sampled(tq, orc):
         gp = p.reshape(n, -1)[ridx].cpu().numpy()
         gn = nm.reshape(n)[ridx].cpu().numpy()
         check_norms(gn, on)
-        check_indices(gp, op, u, d, bits, bnd)
+        check_indices(gp, op, u, d, bits, bnd, tally=tally)
+    tally.check()
 
 
 def test_config5_long_context_codec_sampled(tq, orc):
@@ -175,6 +179,7 @@ def test_config5_long_context_codec_sampled(tq, orc):
     here), compared on sampled rows."""
     T, H = 131072, 8
     rng = np.random.default_rng(5)
+    tally = BandTally()
     for li, d in enumerate((64, 256, 64, 256)):
         k = kvgen.student_t((H, T, d), 500 + li, device="cuda")
         v = kvgen.student_t((H, T, d), 600 + li, device="cuda")
@@ -189,9 +194,89 @@ def test_config5_long_context_codec_sampled(tq, orc):
             gp = p.reshape(n, -1)[ridx].cpu().numpy()
             gn = nm.reshape(n)[ridx].cpu().numpy()
             check_norms(gn, on)
-            check_indices(gp, op, u, d, bits, bnd)
+            check_indices(gp, op, u, d, bits, bnd, tally=tally)
             out = tq.tq_decode(p, nm, d, bits, SEED)
             xd = out.reshape(n, d)[ridx].cpu().numpy()
             check_decoded(xd, orc.decode(gp, gn, d, bits, SEED))
             del out
         del k, v, kp, kn, vp, vn
+    tally.check()
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_encode_decode_flags(tq, orc, d, dtype, flags):
+    """N(0, 1/d) codebooks (flag 1) and the two-sided rotation (flag 2): every
+    bit width on both sides of one launch (the one-lane-per-row kernel for
+    bf16 d <= 128, the lane-slice kernel otherwise), then decode."""
+    density = orc.GAUSS if flags & 1 else orc.BETA
+    two = bool(flags & 2)
+    n = 4096 + 29
+    tally = BandTally()
+    k = kvgen.normal((n, d), 31 + d + flags, "cuda", dtype)
+    v = kvgen.normal((n, d), 32 + d + flags, "cuda", dtype) * 2.0
+    for bk, bv in ((4, 2), (3, 3), (2, 4)):
+        kp, kn, vp, vn = tq.tq_encode(k, v, bk, bv, SEED, flags=flags)
+        torch.cuda.synchronize()
+        for x, bits, p, nm in ((k, bk, kp, kn), (v, bv, vp, vn)):
+            xh = _np(x).astype(np.float32)
+            op, on, u = orc.encode(xh, d, bits, SEED, density=density, want_u=True,
+                                   two_sided=two)
+            _, bnd = orc.codebook_float(d, bits, density)
+            gp, gn = p.cpu().numpy(), nm.cpu().numpy()
+            check_norms(gn, on)
+            check_indices(gp, op, u, d, bits, bnd, tally=tally)
+            xd = tq.tq_decode(p, nm, d, bits, SEED, flags=flags).cpu().numpy()
+            check_decoded(xd, orc.decode(gp, gn, d, bits, SEED, density=density,
+                                         two_sided=two))
+    tally.check()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotate_two_sided(tq, orc, d):
+    x = kvgen.normal((333, d), 6, "cuda")
+    xs = _np(x).astype(np.float64)
+    for inverse in (False, True):
+        y = tq.tq_rotate(x, SEED, inverse=inverse, flags=2).cpu().numpy()
+        yo = (orc.unrotate if inverse else orc.rotate)(xs, SEED, two_sided=True)
+        assert np.abs(y - yo).max() <= 1e-6 * np.abs(yo).max()
+    y = tq.tq_rotate(x, SEED, flags=2)
+    xb = tq.tq_rotate(y, SEED, inverse=True, flags=2).cpu().numpy()
+    assert np.abs(xb - xs).max() <= 1e-5
+    # the density bit does not change the rotation
+    assert torch.equal(tq.tq_rotate(x, SEED, flags=3), y)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_edge_rows_two_sided(tq, orc, dtype, bits):
+    """Rows whose rotated coordinates are exactly zero (u = +-0 after the
+    second diagonal), zero rows and spikes, two-sided with both densities."""
+    d = 128
+    e = np.eye(d, dtype=np.float32)
+    rows = [np.zeros(d, np.float32), e[0] + e[1], e[3] - e[7], e[5] * 3.0,
+            e[0] + e[1] + e[2] + e[3], np.ones(d, np.float32)]
+    x = torch.from_numpy(np.stack(rows)).cuda().to(dtype)
+    for flags in (2, 3):
+        density = orc.GAUSS if flags & 1 else orc.BETA
+        kp, kn, _, _ = tq.tq_encode(x, None, bits, 2, SEED, flags=flags)
+        torch.cuda.synchronize()
+        op, on, u = orc.encode(_np(x).astype(np.float32), d, bits, SEED, density=density,
+                               want_u=True, two_sided=True)
+        gp, gn = kp.cpu().numpy(), kn.cpu().numpy()
+        # exact zeros sit on the middle boundary: the two cells next to it are
+        # equally near, and the kernel's fused last stage (a*t + b*t as one
+        # fma over a rounded product) may leave that product's rounding error,
+        # a tiny value of either sign, there; every other index is bit-exact
+        ig, io = unpack_rows(gp, d, bits), unpack_rows(op, d, bits)
+        _, bnd = orc.codebook_float(d, bits, density)
+        away = np.abs(u[..., None] - bnd.astype(np.float64)).min(-1) > 1e-6
+        assert np.array_equal(ig[away], io[away])
+        assert np.all(np.abs(ig[~away].astype(int) - io[~away].astype(int)) <= 1)
+        assert np.array_equal(ig[0], io[0])           # zero row: u = 0 exactly, t = 0
+        check_norms(gn, on)
+        xd = tq.tq_decode(kp, kn, d, bits, SEED, flags=flags).cpu().numpy()
+        assert np.all(xd[0] == 0)
+        check_decoded(xd[1:], orc.decode(gp[1:], gn[1:], d, bits, SEED, density=density,
+                                         two_sided=True))
