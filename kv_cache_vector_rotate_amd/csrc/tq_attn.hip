@@ -109,7 +109,7 @@ __device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *row, int off)
     }
 }
 
-template <int D, int BK, int BV, int G>
+template <int D, int BK, int BV, int G, bool GATE>
 __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
 {
     constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     __shared__ float2 tabV[NPV];
     __shared__ float qs[G][D];
     __shared__ float sc[kTile][G];
+    __shared__ uint32_t keep[GATE ? kTile : 1];  // sparse V: row has a weight
     __shared__ float red[kBlock / 64][G];
     __shared__ float accs[kBlock / 64][G][D];
 
@@ -235,6 +236,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
         }
         __syncthreads();
         float fac[G];
+        bool any = false;
 #pragma unroll
         for (int h = 0; h < G; h++) {
             float mt = red[0][h];
@@ -247,10 +249,19 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
             const float s_t = sc[tid][h];
             const float pr = exp2f(s_t - mnew);
             l_part[h] = l_part[h] * fac[h] + pr;
-            // sparse V: the row's V counts only if exp(s - tile max) > threshold
-            // (tiles are aligned 256-slot blocks); it stays in the denominator
-            sc[tid][h] = s_t - mt > p.gate_log2 ? pr : 0.0f;
+            if constexpr (GATE) {
+                // sparse V: the row's V counts only if exp(s - tile max) >
+                // threshold (tiles are aligned 256-slot blocks); it stays in
+                // the denominator
+                const float wv = s_t - mt > p.gate_log2 ? pr : 0.0f;
+                sc[tid][h] = wv;
+                any |= wv != 0.0f;
+            } else {
+                sc[tid][h] = pr;
+            }
         }
+        if constexpr (GATE)
+            keep[tid] = any ? 1u : 0u;
         __syncthreads();
         // ---- V sum of the tile (rotated domain)
 #pragma unroll
@@ -262,22 +273,29 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
         for (int it0 = 0; it0 < NIT; it0 += CH) {
             uint64_t vb[CH];
             float vn[CH];
+            if constexpr (GATE) {
 #pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int tl = (it0 + c) * RPB + wave * RPW + rig;
-                const int t = t0 + tl;
-                // rows with no weight (past the context, or gated by sparse V)
-                // are neither loaded nor decoded
-                bool need = false;
+                for (int c = 0; c < CH; c++) {
+                    const int tl = (it0 + c) * RPB + wave * RPW + rig;
+                    // rows with no weight (gated by sparse V, or past the
+                    // context) are neither loaded nor decoded
+                    vb[c] = 0;
+                    vn[c] = 0.0f;
+                    if (keep[tl]) {
+                        const int64_t row = rowbase + t0 + tl;
+                        vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+                        vn[c] = p.vn[row];
+                    }
+                }
+            } else {
+                // every load issued at once, before any weight is read (rows
+                // past the context read a valid row and get weight 0)
 #pragma unroll
-                for (int h = 0; h < G; h++)
-                    need |= sc[tl][h] != 0.0f;
-                vb[c] = 0;
-                vn[c] = 0.0f;
-                if (need) {
-                    const int64_t row = rowbase + t;
+                for (int c = 0; c < CH; c++) {
+                    const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
+                    const int64_t row = rowbase + (t < t_end ? t : t_begin);
                     vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-                    vn[c] = p.vn[row];
+                    vn[c] = t < t_end ? p.vn[row] : 0.0f;
                 }
             }
 #pragma unroll
@@ -430,16 +448,27 @@ Split split_for(int batch, int n_kv, int64_t ctx_len, int window)
     return s;
 }
 
-template <int D, int BK, int BV>
-void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+template <int D, int BK, int BV, bool GATE>
+void launch_attn_gate(int G, dim3 grid, const AttnParams &p, hipStream_t st)
 {
     dim3 block(kBlock);
     switch (G) {
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 8>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 1, GATE>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p); break;
     }
+}
+
+// the sparse-V gate is a separate instantiation: the kernel without it is
+// the one that runs when the threshold is 0
+template <int D, int BK, int BV>
+void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+{
+    if (p.gate_log2 > -__builtin_huge_valf())
+        launch_attn_gate<D, BK, BV, true>(G, grid, p, st);
+    else
+        launch_attn_gate<D, BK, BV, false>(G, grid, p, st);
 }
 
 template <int D, int BK>

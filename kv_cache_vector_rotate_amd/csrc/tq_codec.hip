@@ -659,6 +659,7 @@ struct DecodeParams {
     // exactly symmetric, c[L-1-k] = -c[k], so flipping the index bits is the
     // exact negation of n c[idx].
     uint32_t flip[32];
+    int two_sided;  // flip is nonzero
 };
 
 // One wave per workgroup, one pass of RPW rows per wave, and one launch (or
@@ -692,9 +693,11 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
         load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
         n = p.norms[r];
     }
+    if (p.two_sided) {
 #pragma unroll
-    for (int j = 0; j < BITS; j++)
-        w[j] ^= p.flip[sub * BITS + j];
+        for (int j = 0; j < BITS; j++)
+            w[j] ^= p.flip[sub * BITS + j];
+    }
     float v[kCPL];
 #pragma unroll
     for (int k = 0; k < kCPL; k++)
@@ -1133,6 +1136,7 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
         p.cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
     tq::sign_words(d, seed, p.signs);
     flip_words(d, bits, seed, flags, p.flip);
+    p.two_sided = (flags & TQ_FLAG_TWO_SIDED) ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (d) {
     case 64: launch_decode_d<64>(bits, p, st); break;
