@@ -15,7 +15,9 @@
  *             Optimization: Fused dequant-dot.
  *   [Atlas]   "CITATIONS" (TurboQuant+ integration notes): Prior art item 4
  *             (N(0, 1/d) codebooks); "Two-sided Rademacher signs in WHT";
- *             "N(0, 1/d) codebook replacement"; "Sparse V dequant".
+ *             "N(0, 1/d) codebook replacement"; "Sparse V dequant";
+ *             "LA-V7 boundary-V protection" (first and last layers at higher
+ *             precision).
  *   [KVC]     "Implementation specification: TurboAngle and TurboQuant-style
  *             KV compression": Core implementation contract (rows [B, d],
  *             power-of-two d, K and V may use different codecs).
@@ -158,7 +160,9 @@ int tq_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
  * The descriptor is a host struct; every buffer it points to is a caller-
  * owned device allocation.  Layer l holds, for K and for V,
  *   packed [batch][n_kv_heads][window][head_dim[l] * bits / 8] bytes
- *   norms  [batch][n_kv_heads][window] floats.                               */
+ *   norms  [batch][n_kv_heads][window] floats,
+ * with bits the layer's K or V width (layer_bits_k[l] / layer_bits_v[l], or
+ * bits_k / bits_v for every layer when those arrays are NULL).               */
 #define TQ_MAX_LAYERS 256
 
 typedef struct {
@@ -174,11 +178,27 @@ typedef struct {
     float *const *k_norms;
     uint8_t *const *v_packed;
     float *const *v_norms;
+    /* Per-layer bit widths, host arrays [n_layers] in 2..4, or NULL for
+     * bits_k / bits_v on every layer ([Atlas] "LA-V7 boundary-V protection":
+     * boundary layers at a higher precision; [KVC] K and V codecs chosen per
+     * layer).  See tq_layer_bits_boundary. */
+    const int32_t *layer_bits_k;
+    const int32_t *layer_bits_v;
 } tq_cache_desc;
+
+/* Host only.  The boundary-layer policy of [Atlas] "LA-V7 boundary-V
+ * protection" as bit widths: out[l] = bits_boundary for the first and the
+ * last n_boundary layers, bits_inner for the others (n_boundary < 0 selects
+ * the page's default of 2).  out: host array [n_layers].  TQ_EINVAL when
+ * n_layers is outside 1..TQ_MAX_LAYERS, a width is outside 1..4 or out is
+ * NULL. */
+int tq_layer_bits_boundary(int n_layers, int n_boundary, int bits_inner,
+                           int bits_boundary, int32_t *out);
 
 /* Append-only encode of the new K and V rows ([Engine] 6, W3: encode only the
  * new row) into slot pos % window ([Foundry] Integration Points).
- * layer = -1 appends to every layer (one launch per distinct head_dim);
+ * layer = -1 appends to every layer (one launch per distinct (head_dim,
+ * K width, V width));
  * otherwise only that layer.  k_new / v_new are host arrays of device
  * pointers with n_layers entries (layer = -1) or 1 entry; entry i points to
  * [batch][n_kv_heads][head_dim] rows of `dtype`.  pos >= 0. */
@@ -195,7 +215,9 @@ size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
  * "Compressed-domain attention"): q' = H (D q) / sqrt(d) once per head;
  * score_t = scale * n_t <q', c_K[idx_t]>; softmax over t; o' = sum_t p_t
  * n^V_t c_V[idx^V_t]; out = D H o' / sqrt(d).  Equal, up to rounding, to
- * softmax attention over the decoded rows.
+ * softmax attention over the decoded rows.  The cache's flags select the
+ * codebooks and the rotation (S2 H S1 q and S1 H S2 o' when two-sided); the
+ * layer's K and V widths come from the descriptor.
  * q_bf16: [batch][n_q_heads][d] bf16 (device).  Query head h reads KV head
  * h / (n_q_heads / n_kv_heads); n_q_heads must be a multiple of n_kv_heads
  * with a ratio of 1, 2, 4 or 8.  Context = slots [0, min(ctx_len, window)).

@@ -23,6 +23,7 @@ __all__ = [
     "TqError", "TQCache", "lib", "library_path", "tq_codebook_init", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
     "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
+    "tq_layer_bits_boundary",
     "TQ_F32", "TQ_BF16", "TQ_BETA_HALF_D", "TQ_GAUSS_1_OVER_D", "TQ_OK", "TQ_EINVAL",
     "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS", "TQ_FLAG_GAUSS_1_OVER_D", "TQ_FLAG_TWO_SIDED",
 ]
@@ -83,6 +84,16 @@ def tq_signs(d: int, seed: int) -> np.ndarray:
 
 def tq_packed_row_bytes(d: int, bits: int) -> int:
     return int(lib().tq_packed_row_bytes(d, bits))
+
+
+def tq_layer_bits_boundary(n_layers: int, bits_inner: int, bits_boundary: int,
+                           n_boundary: int = -1) -> list:
+    """Per-layer widths: the first and last n_boundary layers (default 2) at
+    bits_boundary, the others at bits_inner."""
+    out = (ctypes.c_int32 * max(n_layers, 1))()
+    _check(lib().tq_layer_bits_boundary(n_layers, n_boundary, bits_inner, bits_boundary, out),
+           "tq_layer_bits_boundary")
+    return list(out[:n_layers])
 
 
 def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, stream=None,
@@ -154,23 +165,29 @@ def tq_decode(packed: torch.Tensor, norms: torch.Tensor, d: int, bits: int, seed
 class TQCache:
     """Ring-buffer compressed KV cache; buffers are torch device tensors.
 
-    Per layer l: k_packed[l] uint8 [batch, n_kv, window, d_l*bits_k/8],
-    k_norms[l] float32 [batch, n_kv, window] (likewise for V).  The C
-    descriptor holds host arrays of their device pointers."""
+    Per layer l: k_packed[l] uint8 [batch, n_kv, window, d_l*bk_l/8],
+    k_norms[l] float32 [batch, n_kv, window] (likewise for V).  head_dim,
+    bits_k and bits_v are one value for every layer or a list per layer.  The
+    C descriptor holds host arrays of their device pointers."""
 
     def __init__(self, n_layers, batch, n_kv_heads, window, head_dim, bits_k, bits_v,
                  seed=42, device="cuda", flags=0):
-        hd = [head_dim] * n_layers if isinstance(head_dim, int) else list(head_dim)
-        if len(hd) != n_layers:
-            raise ValueError("head_dim list must have n_layers entries")
+        def per_layer(v, name):
+            out = [v] * n_layers if isinstance(v, int) else list(v)
+            if len(out) != n_layers:
+                raise ValueError(f"{name} list must have n_layers entries")
+            return out
+        hd = per_layer(head_dim, "head_dim")
         self.n_layers, self.batch, self.n_kv_heads, self.window = n_layers, batch, n_kv_heads, window
         self.head_dim, self.bits_k, self.bits_v, self.seed = hd, bits_k, bits_v, seed
+        self.layer_bits_k, self.layer_bits_v = per_layer(bits_k, "bits_k"), per_layer(bits_v, "bits_v")
+        self._uniform = isinstance(bits_k, int) and isinstance(bits_v, int)
         self.flags = flags
         self.k_packed, self.k_norms, self.v_packed, self.v_norms = [], [], [], []
-        for d in hd:
-            self.k_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bits_k),
+        for d, bk, bv in zip(hd, self.layer_bits_k, self.layer_bits_v):
+            self.k_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bk),
                                              dtype=torch.uint8, device=device))
-            self.v_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bits_v),
+            self.v_packed.append(torch.zeros(batch, n_kv_heads, window, tq_packed_row_bytes(d, bv),
                                              dtype=torch.uint8, device=device))
             self.k_norms.append(torch.zeros(batch, n_kv_heads, window, dtype=torch.float32, device=device))
             self.v_norms.append(torch.zeros(batch, n_kv_heads, window, dtype=torch.float32, device=device))
@@ -183,11 +200,20 @@ class TQCache:
         self._kn = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.k_norms])
         self._vp = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.v_packed])
         self._vn = (ctypes.c_void_p * n)(*[t.data_ptr() for t in self.v_norms])
+        self._lbk = (ctypes.c_int32 * n)(*self.layer_bits_k)
+        self._lbv = (ctypes.c_int32 * n)(*self.layer_bits_v)
+        per = None if self._uniform else (ctypes.cast(self._lbk, ctypes.c_void_p),
+                                          ctypes.cast(self._lbv, ctypes.c_void_p))
         self.desc = _abi.TqCacheDesc(
-            n, self.batch, self.n_kv_heads, self.window, self.bits_k, self.bits_v, self.seed,
-            self.flags, ctypes.cast(self._hd, ctypes.c_void_p), ctypes.cast(self._kp, ctypes.c_void_p),
-            ctypes.cast(self._kn, ctypes.c_void_p), ctypes.cast(self._vp, ctypes.c_void_p),
-            ctypes.cast(self._vn, ctypes.c_void_p))
+            n, self.batch, self.n_kv_heads, self.window, self.layer_bits_k[0],
+            self.layer_bits_v[0], self.seed, self.flags, ctypes.cast(self._hd, ctypes.c_void_p),
+            ctypes.cast(self._kp, ctypes.c_void_p), ctypes.cast(self._kn, ctypes.c_void_p),
+            ctypes.cast(self._vp, ctypes.c_void_p), ctypes.cast(self._vn, ctypes.c_void_p),
+            *(per if per else (None, None)))
+
+    def layer_bits(self, layer: int):
+        """(K width, V width) of a layer."""
+        return self.layer_bits_k[layer], self.layer_bits_v[layer]
 
 
 def tq_append_row(cache: TQCache, layer: int, k_new, v_new, pos: int, stream=None):

@@ -17,7 +17,7 @@ TQ_MAX_LAYERS = 256
 EXPORTS = [
     "tq_last_error", "tq_version", "tq_codebook_init", "tq_codebook_init_density", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
-    "tq_attn_workspace_bytes", "tq_attn_decode",
+    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_layer_bits_boundary",
 ]
 
 
@@ -39,7 +39,8 @@ class TqCacheDesc(ctypes.Structure):
                 ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32), ("seed", ctypes.c_uint64),
                 ("flags", ctypes.c_uint32), ("head_dim", ctypes.c_void_p), ("k_packed", ctypes.c_void_p),
                 ("k_norms", ctypes.c_void_p), ("v_packed", ctypes.c_void_p),
-                ("v_norms", ctypes.c_void_p)]
+                ("v_norms", ctypes.c_void_p), ("layer_bits_k", ctypes.c_void_p),
+                ("layer_bits_v", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,8 +77,10 @@ def lib():
         L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64]
         L.tq_attn_workspace_bytes.restype = sz
         L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P, sz, P]
+        L.tq_layer_bits_boundary.argtypes = [i32, i32, i32, i32, P]
         for name in ("tq_codebook_init", "tq_codebook_init_density", "tq_signs", "tq_rotate",
-                     "tq_encode", "tq_decode", "tq_append_row", "tq_attn_decode"):
+                     "tq_encode", "tq_decode", "tq_append_row", "tq_attn_decode",
+                     "tq_layer_bits_boundary"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

@@ -526,7 +526,8 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     if (!(d == 64 || d == 128 || d == 256))
         return tq::fail(tq::is_pow2(d) ? TQ_EUNSUPPORTED : TQ_EINVAL,
                         "tq_attn_decode: device kernels take head_dim in {64, 128, 256}");
-    for (int bits : {c->bits_k, c->bits_v}) {
+    const int bits_k = tq::layer_bits(c, layer, 0), bits_v = tq::layer_bits(c, layer, 1);
+    for (int bits : {bits_k, bits_v}) {
         if (bits < 1 || bits > 4)
             return tq::fail(TQ_EINVAL, "tq_attn_decode: bits must be in 1..4");
         if (bits == 1)
@@ -550,8 +551,8 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     if (tq::take_injected_launch_failure())
         return tq::fail(TQ_EHIP, "tq_attn_decode: injected launch failure (TQ_TEST_FAIL_LAUNCH)");
     tq_codebook ck, cv;
-    if ((rc = tq::get_codebook(d, c->bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
-        (rc = tq::get_codebook(d, c->bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
+    if ((rc = tq::get_codebook(d, bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
+        (rc = tq::get_codebook(d, bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
         return rc;
     Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
     AttnParams p;
@@ -580,9 +581,9 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     dim3 grid((unsigned)s.n_chunks, (unsigned)c->n_kv_heads, (unsigned)c->batch);
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (d) {
-    case 64: launch_attn_d<64>(c->bits_k, c->bits_v, G, grid, p, st); break;
-    case 128: launch_attn_d<128>(c->bits_k, c->bits_v, G, grid, p, st); break;
-    default: launch_attn_d<256>(c->bits_k, c->bits_v, G, grid, p, st); break;
+    case 64: launch_attn_d<64>(bits_k, bits_v, G, grid, p, st); break;
+    case 128: launch_attn_d<128>(bits_k, bits_v, G, grid, p, st); break;
+    default: launch_attn_d<256>(bits_k, bits_v, G, grid, p, st); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

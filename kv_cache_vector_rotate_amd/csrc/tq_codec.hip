@@ -1168,12 +1168,13 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
     if (!k_new || !v_new)
         return tq::fail(TQ_EINVAL, "tq_append_row: k_new / v_new is NULL");
     int rc;
-    if ((rc = check_bits(c->bits_k, fn)) != TQ_OK || (rc = check_bits(c->bits_v, fn)) != TQ_OK)
-        return rc;
     const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->n_layers : layer + 1;
     for (int l = l0; l < l1; l++) {
         const int i = l - l0;
         if ((rc = check_d(c->head_dim[l], fn)) != TQ_OK)
+            return rc;
+        if ((rc = check_bits(tq::layer_bits(c, l, 0), fn)) != TQ_OK ||
+            (rc = check_bits(tq::layer_bits(c, l, 1), fn)) != TQ_OK)
             return rc;
         if (!k_new[i] || !v_new[i] || !c->k_packed[l] || !c->k_norms[l] || !c->v_packed[l] ||
             !c->v_norms[l])
@@ -1189,10 +1190,17 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int slot = (int)(pos % c->window);
-    // one launch per distinct head_dim (and per kMaxAppendLayers layers)
+    // one launch per distinct (head_dim, K width, V width), and per
+    // kMaxAppendLayers layers of it
     const int dims[3] = {64, 128, 256};
-    for (int di = 0; di < 3; di++) {
-        const int d = dims[di];
+    for (int key = 0; key < 3 * 9; key++) {
+        const int d = dims[key / 9], bk = 2 + (key % 9) / 3, bv = 2 + key % 3;
+        bool used = false;
+        for (int l = l0; l < l1 && !used; l++)
+            used = c->head_dim[l] == d && tq::layer_bits(c, l, 0) == bk &&
+                   tq::layer_bits(c, l, 1) == bv;
+        if (!used)
+            continue;
         AppendParams p;
         p.bh = bh;
         p.window = c->window;
@@ -1200,8 +1208,8 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
         tq::sign_words(d, c->seed, p.signs);
         tq::sign_words2(d, c->seed, c->flags, p.signs2);
         const int dens = tq::density_of(c->flags);
-        if ((rc = code_table(d, c->bits_k, dens, &p.side[0].code, fn)) != TQ_OK ||
-            (rc = code_table(d, c->bits_v, dens, &p.side[1].code, fn)) != TQ_OK)
+        if ((rc = code_table(d, bk, dens, &p.side[0].code, fn)) != TQ_OK ||
+            (rc = code_table(d, bv, dens, &p.side[1].code, fn)) != TQ_OK)
             return rc;
         p.n_layers = 0;
         for (int l = l0; l <= l1; l++) {
@@ -1217,7 +1225,8 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
             }
             if (l == l1)
                 break;
-            if (c->head_dim[l] != d)
+            if (c->head_dim[l] != d || tq::layer_bits(c, l, 0) != bk ||
+                tq::layer_bits(c, l, 1) != bv)
                 continue;
             const int i = l - l0, n = p.n_layers++;
             p.side[0].src[n] = k_new[i];

@@ -314,3 +314,19 @@ extern "C" size_t tq_packed_row_bytes(int d, int bits)
         return 0;
     return ((size_t)d * (size_t)bits + 7) / 8;
 }
+
+extern "C" int tq_layer_bits_boundary(int n_layers, int n_boundary, int bits_inner,
+                                      int bits_boundary, int32_t *out)
+{
+    tq::clear_error();
+    if (n_layers < 1 || n_layers > TQ_MAX_LAYERS)
+        return tq::fail(TQ_EINVAL, "tq_layer_bits_boundary: n_layers outside 1..TQ_MAX_LAYERS");
+    if (bits_inner < 1 || bits_inner > 4 || bits_boundary < 1 || bits_boundary > 4)
+        return tq::fail(TQ_EINVAL, "tq_layer_bits_boundary: bits must be in 1..4");
+    if (!out)
+        return tq::fail(TQ_EINVAL, "tq_layer_bits_boundary: out is NULL");
+    const int nb = n_boundary < 0 ? 2 : n_boundary;  // the page's "auto"
+    for (int l = 0; l < n_layers; l++)
+        out[l] = (l < nb || l >= n_layers - nb) ? bits_boundary : bits_inner;
+    return TQ_OK;
+}

@@ -34,6 +34,14 @@ inline int density_of(uint32_t flags)
 // TQ_OK, or TQ_EINVAL (with a message naming fn) for unknown option bits.
 int check_flags(uint32_t flags, const char *fn);
 
+// Bit width of layer l of a cache, side 0 = K, 1 = V (the per-layer arrays
+// when present, else the uniform widths).
+inline int layer_bits(const tq_cache_desc *c, int l, int side)
+{
+    const int32_t *a = side ? c->layer_bits_v : c->layer_bits_k;
+    return a ? a[l] : (side ? c->bits_v : c->bits_k);
+}
+
 bool is_pow2(int64_t v);
 
 // Test-only fault injection: when the environment variable TQ_TEST_FAIL_LAUNCH

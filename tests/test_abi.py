@@ -140,14 +140,17 @@ def test_encode_decode_validation_without_launch(tq):
             assert "flag" in tq.tq_last_error()
 
 
-def _desc(tq, n_layers=2, batch=2, n_kv=2, window=8, head_dim=128, bk=4, bv=2, flags=0):
+def _desc(tq, n_layers=2, batch=2, n_kv=2, window=8, head_dim=128, bk=4, bv=2, flags=0,
+          layer_bk=None, layer_bv=None):
     from kv_cache_vector_rotate_amd import _abi
     hd = (ctypes.c_int32 * n_layers)(*([head_dim] * n_layers))
     ptrs = [(ctypes.c_void_p * n_layers)(*([4096 * (i + 1)] * n_layers)) for i in range(4)]
+    lb = [None if a is None else (ctypes.c_int32 * n_layers)(*a) for a in (layer_bk, layer_bv)]
     d = _abi.TqCacheDesc(n_layers, batch, n_kv, window, bk, bv, 42, flags,
                          ctypes.cast(hd, ctypes.c_void_p),
-                         *[ctypes.cast(p, ctypes.c_void_p) for p in ptrs])
-    d._keep = (hd, ptrs)
+                         *[ctypes.cast(p, ctypes.c_void_p) for p in ptrs],
+                         *[None if a is None else ctypes.cast(a, ctypes.c_void_p) for a in lb])
+    d._keep = (hd, ptrs, lb)
     return d
 
 
@@ -181,6 +184,38 @@ def test_cache_and_attention_validation(tq):
     assert "flag" in tq.tq_last_error()
     assert L.tq_append_row(ctypes.byref(d4), -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
     assert "flag" in tq.tq_last_error()
+
+
+def test_layer_bits_boundary_policy(tq):
+    assert tq.tq_layer_bits_boundary(10, 2, 4) == [4, 4, 2, 2, 2, 2, 2, 2, 4, 4]
+    assert tq.tq_layer_bits_boundary(10, 3, 4, n_boundary=1) == [4] + [3] * 8 + [4]
+    assert tq.tq_layer_bits_boundary(5, 2, 4, n_boundary=0) == [2] * 5
+    assert tq.tq_layer_bits_boundary(3, 2, 4) == [4, 4, 4]       # boundaries overlap
+    L = tq.lib()
+    out = (ctypes.c_int32 * 4)()
+    for args in ((0, 2, 2, 4), (tq.TQ_MAX_LAYERS + 1, 2, 2, 4), (4, 2, 0, 4), (4, 2, 2, 5)):
+        assert L.tq_layer_bits_boundary(*args, out) == tq.TQ_EINVAL
+    assert L.tq_layer_bits_boundary(4, 2, 2, 4, None) == tq.TQ_EINVAL
+
+
+def test_per_layer_bits_validation(tq):
+    """The descriptor's per-layer widths are what append and attention check
+    (no launch: every case is rejected, or has no rows)."""
+    L = tq.lib()
+    A = _c(4096)
+    arr = (ctypes.c_void_p * 2)(4096, 4096)
+    # uniform widths invalid, per-layer widths valid: the arrays win
+    d = _desc(tq, batch=0, bk=9, bv=9, layer_bk=[4, 3], layer_bv=[2, 2])
+    assert L.tq_append_row(ctypes.byref(d), -1, arr, arr, 0, 0, None) == tq.TQ_OK
+    d = _desc(tq, batch=0, layer_bk=[4, 5], layer_bv=[2, 2])
+    assert L.tq_append_row(ctypes.byref(d), -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
+    assert L.tq_append_row(ctypes.byref(d), 0, arr, arr, 0, 0, None) == tq.TQ_OK
+    d = _desc(tq, batch=0, layer_bk=[4, 4], layer_bv=[2, 1])
+    assert L.tq_append_row(ctypes.byref(d), 1, arr, arr, 0, 0, None) == tq.TQ_EUNSUPPORTED
+    d = _desc(tq, layer_bk=[4, 1], layer_bv=[2, 2])
+    assert L.tq_attn_decode(ctypes.byref(d), 1, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    d = _desc(tq, bk=1, layer_bk=[4, 4], layer_bv=[2, 2], batch=0)
+    assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_OK
 
 
 def test_injected_hip_error_path():

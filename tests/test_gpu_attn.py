@@ -30,7 +30,8 @@ def _fill(tq, cache, layer, seed, kscale=1.0, dist="normal"):
     else:
         k = kvgen.student_t((B, H, W, d), seed, device="cuda") * kscale
         v = kvgen.student_t((B, H, W, d), seed + 1, device="cuda")
-    tq.tq_encode(k, v, cache.bits_k, cache.bits_v, SEED, cache.k_packed[layer],
+    bk, bv = cache.layer_bits(layer)
+    tq.tq_encode(k, v, bk, bv, SEED, cache.k_packed[layer],
                  cache.k_norms[layer], cache.v_packed[layer], cache.v_norms[layer],
                  flags=cache.flags)
 
@@ -47,7 +48,8 @@ def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
         vp = cache.v_packed[layer][b, g, :T].cpu().numpy()
         vn = cache.v_norms[layer][b, g, :T].cpu().numpy()
         qh = q[b, h:h + 1].float().cpu().numpy()
-        out[h] = orc.attention(qh, kp, kn, vp, vn, 1, T, d, cache.bits_k, cache.bits_v, SEED,
+        bk, bv = cache.layer_bits(layer)
+        out[h] = orc.attention(qh, kp, kn, vp, vn, 1, T, d, bk, bv, SEED,
                                scale, sparse_v_threshold=sparse_v,
                                density=orc.GAUSS if cache.flags & 1 else orc.BETA,
                                two_sided=bool(cache.flags & 2))[0]
@@ -191,3 +193,23 @@ def test_attention_flags(tq, orc, d, bk, bv, G, flags):
     ref = _oracle(orc, cache, 0, q, 1, range(Hkv * G), T, 1 / math.sqrt(d), sparse_v=1e-2)
     for h in range(Hkv * G):
         check_attention(o[1, h], ref[h])
+
+
+def test_attention_per_layer_bits(tq, orc):
+    """A cache whose layers have their own K and V widths (boundary layers at
+    4 bits, the others lower) and head_dims: each layer's attention reads
+    its own widths."""
+    hd = [128, 64, 128, 256, 128]
+    bk = [4, 3, 2, 3, 4]
+    bv = tq.tq_layer_bits_boundary(5, 2, 4, n_boundary=1)      # [4, 2, 2, 2, 4]
+    B, Hkv, G, T = 2, 2, 2, 600
+    cache = tq.TQCache(5, B, Hkv, T, hd, bk, bv, SEED, flags=3)
+    for layer in range(5):
+        assert cache.k_packed[layer].shape[-1] == hd[layer] * bk[layer] // 8
+        _fill(tq, cache, layer, 70 + layer)
+    for layer in (0, 2, 3):
+        q = kvgen.normal((B, Hkv * G, hd[layer]), 80 + layer, "cuda", torch.bfloat16)
+        o = tq.tq_attn_decode(cache, layer, q, T).cpu().numpy()
+        ref = _oracle(orc, cache, layer, q, 1, range(Hkv * G), T, 1 / math.sqrt(hd[layer]))
+        for h in range(Hkv * G):
+            check_attention(o[1, h], ref[h])

@@ -114,3 +114,34 @@ def test_config2_gemma_shaped_step_full_size_sampled(tq, orc):
             gx = out.reshape(-1, d)[torch.from_numpy(sel).cuda()].cpu().numpy()
             check_decoded(gx, orc.decode(gp, gn, d, 4, SEED))
     tally.check()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_append_per_layer_bits(tq, orc, dtype):
+    """Layers with their own (head_dim, K width, V width): one append call
+    launches once per distinct triple; every slot matches the oracle at its
+    layer's widths and untouched slots stay zero."""
+    hd = [128, 64, 128, 256, 128, 64]
+    bk = [4, 3, 2, 4, 4, 3]
+    bv = tq.tq_layer_bits_boundary(6, 2, 4)                    # [4, 4, 2, 2, 4, 4]
+    assert bv == [4, 4, 2, 2, 4, 4]
+    B, H, W = 2, 3, 4
+    cache = tq.TQCache(6, B, H, W, hd, bk, bv, SEED)
+    tally = BandTally()
+    for pos in (5, 6):
+        ks = [kvgen.normal((B, H, d), 900 + 10 * pos + l, "cuda").to(dtype) for l, d in enumerate(hd)]
+        vs = [kvgen.normal((B, H, d), 950 + 10 * pos + l, "cuda").to(dtype) for l, d in enumerate(hd)]
+        tq.tq_append_row(cache, -1, ks, vs, pos)
+        torch.cuda.synchronize()
+        slot = pos % W
+        for l, d in enumerate(hd):
+            for x, bits, pk, nm in ((ks[l], bk[l], cache.k_packed[l], cache.k_norms[l]),
+                                    (vs[l], bv[l], cache.v_packed[l], cache.v_norms[l])):
+                assert pk.shape[-1] == d * bits // 8
+                _check_slot(orc, x.float().cpu().numpy().reshape(-1, d),
+                            pk[:, :, slot].cpu().numpy().reshape(B * H, -1),
+                            nm[:, :, slot].cpu().numpy().reshape(-1), d, bits, tally=tally)
+    tally.check()
+    for l in range(6):
+        assert torch.count_nonzero(cache.k_norms[l][:, :, [0, 3]]).item() == 0
+        assert torch.count_nonzero(cache.v_packed[l][:, :, [0, 3]]).item() == 0
