@@ -54,6 +54,8 @@ def lib():
         L.orc_sphere_mse.argtypes = [i32, i32, P, P]
         L.orc_sphere_mse.restype = f64
         L.orc_codebook_float.argtypes = [i32, i32, i32, P, P]
+        L.orc_padded_dim.argtypes = [i32]
+        L.orc_padded_dim.restype = i32
         L.orc_encode.argtypes = [P, i64, i32, i32, i32, i32, u64, P, P, P]
         L.orc_encode.restype = i32
         L.orc_decode.argtypes = [P, P, i64, i32, i32, i32, i32, u64, P]
@@ -183,15 +185,22 @@ def codebook_float(d: int, bits: int, density: int = BETA):
     return cf, bf[: L - 1]
 
 
+def padded_dim(d: int) -> int:
+    """The length rows of d coordinates are rotated and stored at."""
+    return int(lib().orc_padded_dim(d))
+
+
 def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False,
            two_sided: bool = False):
-    """x: float32 [n, d] (bf16 callers convert exactly first).
-    Returns packed uint8 [n, d*bits/8], norms float32 [n] (and u fp64 [n, d])."""
+    """x: float32 [n, d] (bf16 callers convert exactly first).  With
+    dp = padded_dim(d): returns packed uint8 [n, dp*bits/8], norms float32 [n]
+    (and u fp64 [n, dp])."""
     x = _c(x, np.float32).reshape(-1, d)
     n = x.shape[0]
-    packed = np.zeros((n, d * bits // 8), np.uint8)
+    dp = padded_dim(d)
+    packed = np.zeros((n, dp * bits // 8), np.uint8)
     norms = np.zeros(n, np.float32)
-    u = np.zeros((n, d), np.float64) if want_u else None
+    u = np.zeros((n, dp), np.float64) if want_u else None
     rc = lib().orc_encode(_p(x), n, d, bits, density, int(two_sided), seed, _p(packed), _p(norms),
                           _p(u) if want_u else None)
     if rc != 0:
@@ -201,7 +210,7 @@ def encode(x, d: int, bits: int, seed: int, density: int = BETA, want_u=False,
 
 def decode(packed, norms, d: int, bits: int, seed: int, density: int = BETA,
            f64: bool = False, two_sided: bool = False):
-    packed = _c(packed, np.uint8).reshape(-1, d * bits // 8)
+    packed = _c(packed, np.uint8).reshape(-1, padded_dim(d) * bits // 8)
     norms = _c(norms, np.float32).reshape(-1)
     n = packed.shape[0]
     if f64:
@@ -227,7 +236,8 @@ def attention(q, k_packed, k_norms, v_packed, v_norms, n_kv, T, d, bits_k, bits_
     kn = _c(k_norms, np.float32)
     vp = _c(v_packed, np.uint8)
     vn = _c(v_norms, np.float32)
-    assert kp.size == n_kv * T * d * bits_k // 8 and vp.size == n_kv * T * d * bits_v // 8
+    dp = padded_dim(d)
+    assert kp.size == n_kv * T * dp * bits_k // 8 and vp.size == n_kv * T * dp * bits_v // 8
     assert kn.size == n_kv * T and vn.size == n_kv * T
     out = np.zeros((n_q, d), np.float64)
     if rotated:

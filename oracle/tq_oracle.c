@@ -29,6 +29,8 @@
  *                  N(0, 1/d) alternative.
  *   orc_pack       [Foundry] "Step 3: Packing" (LSB-first; dense 3-bit, the
  *                  "8 values into 3 bytes" alternative).
+ *   orc_padded_dim [Foundry] "Hadamard Transform Detail" (a head_dim that is
+ *                  not a power of two is padded to the next one).
  *   orc_encode     [Foundry] "As-Built Notes" item 2 (L2-norm normalisation),
  *                  [Engine] "2.2 Memory contract" (fp32 norm + packed indices
  *                  per head).
@@ -521,58 +523,76 @@ int orc_codebook_float(int d, int bits, int density, float *cf, float *bf)
 /* Encode / decode                                                     */
 /* ------------------------------------------------------------------ */
 
+/* Length a row is rotated and stored at: d itself when it is a power of two,
+ * else the next power of two (reading of [Foundry] Hadamard Transform Detail,
+ * which pads a head_dim that is not a power of two and drops the extra
+ * coordinates: the padded vector is rotated, quantised and stored whole, and
+ * only decode drops coordinates d..d_pad-1, since dropping rotated
+ * coordinates would lose information beyond the quantisation).  0 when d is
+ * out of range. */
+int orc_padded_dim(int d)
+{
+    if (d < 2 || d > (1 << 20))
+        return 0;
+    int p = 1;
+    while (p < d)
+        p *= 2;
+    return p;
+}
+
 /* Encode rows x[n_rows][d] (fp32 values; bf16 inputs arrive converted
- * exactly).  Per row:
+ * exactly).  With dp = orc_padded_dim(d), per row:
+ *   x'  = x followed by dp - d zeros
  *   n   = ||x||_2 of the input row, stored as float         (reading: the
  *         norm of the input row, not of the rotated one; equal in exact
  *         arithmetic)
- *   y   = H (s .* x) / sqrt(d), or s2 .* H (s .* x) / sqrt(d) when
- *         two_sided ([Atlas] "Two-sided Rademacher signs in WHT")
+ *   y   = H (s .* x') / sqrt(dp), or s2 .* H (s .* x') / sqrt(dp) when
+ *         two_sided ([Atlas] "Two-sided Rademacher signs in WHT"); s, s2 and
+ *         the codebook are those of dp
  *   u   = y / n, and u = 0 when n = 0                        (reading)
  *   idx = #{ j : b_j < u }  with b_j the float boundaries    (a u exactly on
  *         a boundary takes the lower cell; reading)
- *   packed = LSB-first bitstream of idx, d*bits/8 bytes (d*bits % 8 == 0 for
- *         the powers of two this oracle accepts with bits in 2..4 and d >= 8).
- * u_out, when not NULL, receives u[n_rows][d] (for boundary-band accounting).
+ *   packed = LSB-first bitstream of the dp indices, dp*bits/8 bytes
+ *         (dp*bits % 8 == 0 for bits in 2..4 and dp >= 8).
+ * u_out, when not NULL, receives u[n_rows][dp] (for boundary-band accounting).
  * Returns 0 or a negative error. */
 int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
                int two_sided, uint64_t seed, uint8_t *packed, float *norms,
                double *u_out)
 {
-    if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4)
+    const int dp = orc_padded_dim(d);
+    if (dp == 0 || bits < 1 || bits > 4 || (dp * bits) % 8 != 0)
         return -3;
-    if ((d * bits) % 8 != 0)
-        return -3;
-    const orc_cb_entry *cb = orc_cb_get(d, bits, density);
+    const orc_cb_entry *cb = orc_cb_get(dp, bits, density);
     if (!cb)
         return -1;
     int L = 1 << bits;
-    int row_bytes = d * bits / 8;
+    int row_bytes = dp * bits / 8;
     int8_t *s, *s2;
-    double *xr = (double *)malloc(sizeof(double) * d);
-    double *y = (double *)malloc(sizeof(double) * d);
-    uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_rotation_signs(seed, d, two_sided, &s, &s2);
+    double *xr = (double *)malloc(sizeof(double) * dp);
+    double *y = (double *)malloc(sizeof(double) * dp);
+    uint8_t *idx = (uint8_t *)malloc((size_t)dp);
+    orc_rotation_signs(seed, dp, two_sided, &s, &s2);
     for (int64_t r = 0; r < n_rows; r++) {
         const float *xrow = x + r * d;
         double ss = 0.0;
-        for (int i = 0; i < d; i++) {
-            xr[i] = (double)xrow[i];
+        for (int i = 0; i < dp; i++) {
+            xr[i] = i < d ? (double)xrow[i] : 0.0;
             ss += xr[i] * xr[i];
         }
         double n = sqrt(ss);
-        orc_rotate(xr, d, s, s2, y);
-        for (int i = 0; i < d; i++) {
+        orc_rotate(xr, dp, s, s2, y);
+        for (int i = 0; i < dp; i++) {
             double u = n > 0.0 ? y[i] / n : 0.0;
             if (u_out)
-                u_out[r * d + i] = u;
+                u_out[r * dp + i] = u;
             int k = 0;
             for (int j = 0; j < L - 1; j++)
                 if ((double)cb->bf[j] < u)
                     k++;
             idx[i] = (uint8_t)k;
         }
-        orc_pack(idx, d, bits, packed + r * row_bytes);
+        orc_pack(idx, dp, bits, packed + r * row_bytes);
         norms[r] = (float)n;
     }
     free(s);
@@ -583,40 +603,49 @@ int orc_encode(const float *x, int64_t n_rows, int d, int bits, int density,
     return 0;
 }
 
-/* Decode one row into fp64: yhat = n * c[idx], xhat = s .* H yhat / sqrt(d)
- * (s .* H (s2 .* yhat) / sqrt(d) with a second sign vector). */
-static void orc_decode_row_f64(const uint8_t *packed_row, float norm, int d,
+/* Decode one row into fp64 at the padded length dp: yhat = n * c[idx],
+ * xhat = s .* H yhat / sqrt(dp) (s .* H (s2 .* yhat) / sqrt(dp) with a second
+ * sign vector). */
+static void orc_decode_row_f64(const uint8_t *packed_row, float norm, int dp,
                                int bits, const orc_cb_entry *cb,
                                const int8_t *s, const int8_t *s2, uint8_t *idx,
                                double *yh, double *out)
 {
-    orc_unpack(packed_row, d, bits, idx);
-    for (int i = 0; i < d; i++)
+    orc_unpack(packed_row, dp, bits, idx);
+    for (int i = 0; i < dp; i++)
         yh[i] = (double)norm * (double)cb->cf[idx[i]];
-    orc_unrotate(yh, d, s, s2, out);
+    orc_unrotate(yh, dp, s, s2, out);
 }
 
-/* Decode rows to float (rounded once from fp64). */
-int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
-               int bits, int density, int two_sided, uint64_t seed, float *out)
+/* Decode rows ([n_rows][dp*bits/8] packed) to [n_rows][d]: the first d of the
+ * dp decoded coordinates, in fp64 (out64) or rounded once to float (out32);
+ * exactly one of the two is not NULL. */
+static int orc_decode_any(const uint8_t *packed, const float *norms,
+                          int64_t n_rows, int d, int bits, int density,
+                          int two_sided, uint64_t seed, float *out32,
+                          double *out64)
 {
-    if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4 ||
-        (d * bits) % 8 != 0)
+    const int dp = orc_padded_dim(d);
+    if (dp == 0 || bits < 1 || bits > 4 || (dp * bits) % 8 != 0)
         return -3;
-    const orc_cb_entry *cb = orc_cb_get(d, bits, density);
+    const orc_cb_entry *cb = orc_cb_get(dp, bits, density);
     if (!cb)
         return -1;
-    int row_bytes = d * bits / 8;
+    int row_bytes = dp * bits / 8;
     int8_t *s, *s2;
-    double *yh = (double *)malloc(sizeof(double) * d);
-    double *xo = (double *)malloc(sizeof(double) * d);
-    uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_rotation_signs(seed, d, two_sided, &s, &s2);
+    double *yh = (double *)malloc(sizeof(double) * dp);
+    double *xo = (double *)malloc(sizeof(double) * dp);
+    uint8_t *idx = (uint8_t *)malloc((size_t)dp);
+    orc_rotation_signs(seed, dp, two_sided, &s, &s2);
     for (int64_t r = 0; r < n_rows; r++) {
-        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s, s2,
+        orc_decode_row_f64(packed + r * row_bytes, norms[r], dp, bits, cb, s, s2,
                            idx, yh, xo);
-        for (int i = 0; i < d; i++)
-            out[r * d + i] = (float)xo[i];
+        for (int i = 0; i < d; i++) {
+            if (out32)
+                out32[r * d + i] = (float)xo[i];
+            else
+                out64[r * d + i] = xo[i];
+        }
     }
     free(s);
     free(s2);
@@ -626,30 +655,20 @@ int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
     return 0;
 }
 
+int orc_decode(const uint8_t *packed, const float *norms, int64_t n_rows, int d,
+               int bits, int density, int two_sided, uint64_t seed, float *out)
+{
+    return orc_decode_any(packed, norms, n_rows, d, bits, density, two_sided,
+                          seed, out, NULL);
+}
+
 /* Same, but keeps fp64 output (used by the attention definition). */
 int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
                    int d, int bits, int density, int two_sided, uint64_t seed,
                    double *out)
 {
-    if (d < 2 || (d & (d - 1)) != 0 || bits < 1 || bits > 4 ||
-        (d * bits) % 8 != 0)
-        return -3;
-    const orc_cb_entry *cb = orc_cb_get(d, bits, density);
-    if (!cb)
-        return -1;
-    int row_bytes = d * bits / 8;
-    int8_t *s, *s2;
-    double *yh = (double *)malloc(sizeof(double) * d);
-    uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_rotation_signs(seed, d, two_sided, &s, &s2);
-    for (int64_t r = 0; r < n_rows; r++)
-        orc_decode_row_f64(packed + r * row_bytes, norms[r], d, bits, cb, s, s2,
-                           idx, yh, out + r * d);
-    free(s);
-    free(s2);
-    free(yh);
-    free(idx);
-    return 0;
+    return orc_decode_any(packed, norms, n_rows, d, bits, density, two_sided,
+                          seed, NULL, out);
 }
 
 /* ------------------------------------------------------------------ */
@@ -667,7 +686,9 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
  *   o = sum_t p_t vhat_t
  * Query head h reads KV head g = h / (n_q / n_kv) (contiguous groups;
  * reading).  q[n_q][d] are the query values (bf16 inputs arrive converted
- * exactly).  Cache rows are [n_kv][T] with row strides of one packed row.
+ * exactly).  Cache rows are [n_kv][T] with row strides of one packed row
+ * (dp*bits/8 bytes, dp = orc_padded_dim(d)); khat, vhat are the d decoded
+ * coordinates.
  * sparse_v_threshold > 0 gates the V sum ([Atlas] "Sparse V dequant"): a
  * row's V contributes only if its exponent relative to the running maximum
  * exceeds the threshold, here taken against a fixed reference, the largest
@@ -684,7 +705,10 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
     if (n_kv <= 0 || n_q % n_kv != 0 || T < 1)
         return -3;
     int G = n_q / n_kv;
-    int kb = d * bits_k / 8, vb = d * bits_v / 8;
+    const int dp = orc_padded_dim(d);
+    if (dp == 0)
+        return -3;
+    int kb = dp * bits_k / 8, vb = dp * bits_v / 8;
     double *K = (double *)malloc(sizeof(double) * (size_t)T * d);
     double *V = (double *)malloc(sizeof(double) * (size_t)T * d);
     double *sc = (double *)malloc(sizeof(double) * (size_t)T);
@@ -744,42 +768,47 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
     return rc;
 }
 
-/* The same attention evaluated in the rotated domain: q' = H (s .* q)/sqrt(d),
- * score_t = scale * n_t <q', c_K[idx_t]>, o' = sum_t p_t n^V_t c_V[idx^V_t],
- * o = s .* H o' / sqrt(d) (the rotation and its inverse take the second sign
- * vector when two_sided).  Equal to orc_attention up to rounding. */
+/* The same attention evaluated in the rotated domain at the padded length
+ * dp: q' = H (s .* q) / sqrt(dp) (q zero-padded), score_t = scale * n_t
+ * <q', c_K[idx_t]>, o' = sum_t p_t n^V_t c_V[idx^V_t], o = the first d of
+ * s .* H o' / sqrt(dp) (the rotation and its inverse take the second sign
+ * vector when two_sided).  Equal to orc_attention up to rounding: the padded
+ * coordinates of q are zero, so <q', c_K> only sees the first d coordinates of
+ * the decoded key. */
 int orc_attention_rotated(const float *q, int n_q, const uint8_t *k_packed,
                           const float *k_norms, const uint8_t *v_packed,
                           const float *v_norms, int n_kv, int T, int d,
                           int bits_k, int bits_v, int density, int two_sided,
                           uint64_t seed, double scale, double *out)
 {
-    if (n_kv <= 0 || n_q % n_kv != 0 || T < 1)
+    const int dp = orc_padded_dim(d);
+    if (n_kv <= 0 || n_q % n_kv != 0 || T < 1 || dp == 0)
         return -3;
-    const orc_cb_entry *cbk = orc_cb_get(d, bits_k, density);
-    const orc_cb_entry *cbv = orc_cb_get(d, bits_v, density);
+    const orc_cb_entry *cbk = orc_cb_get(dp, bits_k, density);
+    const orc_cb_entry *cbv = orc_cb_get(dp, bits_v, density);
     if (!cbk || !cbv)
         return -1;
     int G = n_q / n_kv;
-    int kb = d * bits_k / 8, vb = d * bits_v / 8;
+    int kb = dp * bits_k / 8, vb = dp * bits_v / 8;
     int8_t *s, *s2;
-    double *qd = (double *)malloc(sizeof(double) * d);
-    double *qr = (double *)malloc(sizeof(double) * d);
-    double *orot = (double *)malloc(sizeof(double) * d);
+    double *qd = (double *)malloc(sizeof(double) * dp);
+    double *qr = (double *)malloc(sizeof(double) * dp);
+    double *orot = (double *)malloc(sizeof(double) * dp);
+    double *ofull = (double *)malloc(sizeof(double) * dp);
     double *sc = (double *)malloc(sizeof(double) * (size_t)T);
-    uint8_t *idx = (uint8_t *)malloc((size_t)d);
-    orc_rotation_signs(seed, d, two_sided, &s, &s2);
+    uint8_t *idx = (uint8_t *)malloc((size_t)dp);
+    orc_rotation_signs(seed, dp, two_sided, &s, &s2);
     for (int h = 0; h < n_q; h++) {
         int g = h / G;
-        for (int i = 0; i < d; i++)
-            qd[i] = (double)q[(size_t)h * d + i];
-        orc_rotate(qd, d, s, s2, qr);
+        for (int i = 0; i < dp; i++)
+            qd[i] = i < d ? (double)q[(size_t)h * d + i] : 0.0;
+        orc_rotate(qd, dp, s, s2, qr);
         double m = -INFINITY;
         for (int t = 0; t < T; t++) {
             size_t row = (size_t)g * T + t;
-            orc_unpack(k_packed + row * kb, d, bits_k, idx);
+            orc_unpack(k_packed + row * kb, dp, bits_k, idx);
             double acc = 0.0;
-            for (int i = 0; i < d; i++)
+            for (int i = 0; i < dp; i++)
                 acc += qr[i] * (double)cbk->cf[idx[i]];
             sc[t] = scale * (double)k_norms[row] * acc;
             if (sc[t] > m)
@@ -790,17 +819,20 @@ int orc_attention_rotated(const float *q, int n_q, const uint8_t *k_packed,
             sc[t] = exp(sc[t] - m);
             denom += sc[t];
         }
-        for (int i = 0; i < d; i++)
+        for (int i = 0; i < dp; i++)
             orot[i] = 0.0;
         for (int t = 0; t < T; t++) {
             size_t row = (size_t)g * T + t;
-            orc_unpack(v_packed + row * vb, d, bits_v, idx);
+            orc_unpack(v_packed + row * vb, dp, bits_v, idx);
             double w = sc[t] / denom * (double)v_norms[row];
-            for (int i = 0; i < d; i++)
+            for (int i = 0; i < dp; i++)
                 orot[i] += w * (double)cbv->cf[idx[i]];
         }
-        orc_unrotate(orot, d, s, s2, out + (size_t)h * d);
+        orc_unrotate(orot, dp, s, s2, ofull);
+        for (int i = 0; i < d; i++)
+            out[(size_t)h * d + i] = ofull[i];
     }
+    free(ofull);
     free(s);
     free(s2);
     free(qd);

@@ -543,3 +543,78 @@ def test_two_sided_attention_definition_and_rotated_identity(orc):
     for h in range(n_kv * G):
         p = scipy.special.softmax(scale * Kh[h // G] @ q[h].astype(np.float64))
         np.testing.assert_allclose(o[h], p @ Vh[h // G], atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# head_dim that is not a power of two: padded to the next one
+
+def test_padded_dim(orc):
+    assert [orc.padded_dim(d) for d in (2, 3, 64, 96, 100, 128, 160, 192, 224, 256)] == \
+        [2, 4, 64, 128, 128, 128, 256, 256, 256, 256]
+    assert orc.padded_dim(1 << 20) == 1 << 20
+    assert orc.padded_dim((1 << 20) + 1) == 0 and orc.padded_dim(1) == 0
+
+
+@pytest.mark.parametrize("d,bits", [(96, 4), (160, 3), (96, 2), (224, 4)])
+def test_padded_encode_is_the_zero_padded_row(orc, d, bits):
+    """A row of d coordinates encodes as its zero-padded copy at the padded
+    length (same signs, codebook and packed bytes); u is the dense rotation
+    of the padded row over its norm; decode returns the first d coordinates
+    of the dense inverse."""
+    dp = orc.padded_dim(d)
+    x = _rand_rows(40, d, 13)
+    xp = np.zeros((40, dp), np.float32)
+    xp[:, :d] = x
+    for two in (False, True):
+        p, n, u = orc.encode(x, d, bits, 42, want_u=True, two_sided=two)
+        pp, npad = orc.encode(xp, dp, bits, 42, two_sided=two)
+        assert p.shape == (40, dp * bits // 8)
+        assert np.array_equal(p, pp) and np.array_equal(n, npad)
+        s1, s2 = (v.astype(np.float64) for v in orc.signs2(42, dp))
+        H = scipy.linalg.hadamard(dp) / math.sqrt(dp)
+        R = (np.diag(s2) if two else np.eye(dp)) @ H @ np.diag(s1)
+        np.testing.assert_allclose(u * np.linalg.norm(x.astype(np.float64), axis=1)[:, None],
+                                   xp.astype(np.float64) @ R.T, atol=1e-12)
+        cf, _ = orc.codebook_float(dp, bits)
+        idx = np.stack([orc.unpack(r, dp, bits) for r in p])
+        full = (n[:, None].astype(np.float64) * cf[idx].astype(np.float64)) @ R   # R^T y
+        xh = orc.decode(p, n, d, bits, 42, f64=True, two_sided=two)
+        assert xh.shape == (40, d)
+        np.testing.assert_allclose(xh, full[:, :d], atol=1e-12)
+
+
+@pytest.mark.parametrize("d,bits", [(96, 4), (160, 4), (96, 3), (160, 3)])
+def test_padded_roundtrip_quality(orc, d, bits):
+    # dropping the padded coordinates can only shrink the error of the
+    # padded round trip; the cosine contract of the pages still holds
+    dp = orc.padded_dim(d)
+    x = _rand_rows(1500, d, 22)
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    p, n = orc.encode(x, d, bits, 42)
+    xh = orc.decode(p, n, d, bits, 42, f64=True)
+    xp = np.zeros((x.shape[0], dp))
+    xp[:, :d] = x
+    full = orc.decode(p, n, dp, bits, 42, f64=True)
+    assert np.all(np.linalg.norm(xh - x, axis=1) <= np.linalg.norm(full - xp, axis=1) + 1e-15)
+    cos = (xh * x).sum(1) / np.linalg.norm(xh, axis=1)
+    assert cos.min() >= (0.88 if bits == 4 else 0.85)
+
+
+def test_padded_attention_definition_and_rotated_identity(orc):
+    d, n_kv, G, T = 96, 2, 2, 30
+    rng = np.random.default_rng(19)
+    K = rng.standard_normal((n_kv * T, d)).astype(np.float32)
+    V = rng.standard_normal((n_kv * T, d)).astype(np.float32)
+    kp, kn = orc.encode(K, d, 4, 42)
+    vp, vn = orc.encode(V, d, 2, 42)
+    q = rng.standard_normal((n_kv * G, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    o = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 2, 42, scale)
+    assert o.shape == (n_kv * G, d)
+    orot = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 2, 42, scale, rotated=True)
+    np.testing.assert_allclose(orot, o, atol=1e-12)
+    Kh = orc.decode(kp, kn, d, 4, 42, f64=True).reshape(n_kv, T, d)
+    Vh = orc.decode(vp, vn, d, 2, 42, f64=True).reshape(n_kv, T, d)
+    for h in range(n_kv * G):
+        p = scipy.special.softmax(scale * Kh[h // G] @ q[h].astype(np.float64))
+        np.testing.assert_allclose(o[h], p @ Vh[h // G], atol=1e-12)
