@@ -38,7 +38,13 @@
  *   - Alignment: fp32/bf16 row buffers and packed buffers 16-byte aligned;
  *     norm buffers 4-byte aligned.  Misaligned pointers -> TQ_EINVAL.
  *   - Device kernels accept d in {64, 128, 256} and bits in {2, 3, 4};
- *     other valid values return TQ_EUNSUPPORTED.
+ *     other valid values return TQ_EUNSUPPORTED.  Codec calls (not
+ *     tq_rotate) also accept a d that is a multiple of 32 between 64 and 256
+ *     (96, 160, 192, 224): such rows are zero-padded to the next power of two
+ *     D, rotated, quantised and stored at length D (D*bits/8 packed bytes,
+ *     the signs and codebook of D); decode and attention return the first d
+ *     coordinates ([Foundry] Hadamard Transform Detail: pad a head_dim that is
+ *     not a power of two).  Row buffers of such d hold d values per row.
  *   - n_rows == 0 (or an empty context) succeeds and launches nothing.
  *   - Non-finite inputs are not screened: outputs for such rows are
  *     unspecified, but every access stays inside the buffers described here.
@@ -118,8 +124,9 @@ int tq_codebook_init_density(int d, int bits, int density, tq_codebook *out);
  * d in [1, 2^20]. */
 int tq_signs(int d, uint64_t seed, int8_t *out_pm1);
 
-/* Bytes of one packed row: d * bits / 8 rounded up ([Engine] 2.2).  0 when
- * d <= 0 or bits outside 1..8. */
+/* Bytes of one packed row: D * bits / 8 rounded up ([Engine] 2.2), D = d
+ * for a power of two and the next power of two otherwise (the padded length
+ * rows are stored at).  0 when d <= 0, d > 2^20 or bits outside 1..8. */
 size_t tq_packed_row_bytes(int d, int bits);
 
 /* Rotation only, for checking the transform on the device.

@@ -47,6 +47,7 @@ struct AttnParams {
     float *part;              // [B][Hq][n_chunks][D + 4]: o'[D], max, sum
     float *out;               // [B][Hq][D]
     int Hq, Hkv, window, T, n_chunks, chunk_len;
+    int d_in;                 // head_dim of q and out (<= D; padded to D inside)
     float qscale;             // scale * log2(e) / sqrt(D)
     float gate_log2;          // sparse-V gate: log2(threshold), -inf when off
     float centK[16];
@@ -147,7 +148,13 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
         const int sub2 = lane % P2, r2 = lane / P2;
         float v[kCPL];
         const int h = g * G + (r2 < G ? r2 : 0);
-        load_slice(p.q + ((int64_t)b * p.Hq + h) * D + sub2 * kCPL, v);
+        if (sub2 * kCPL < p.d_in) {
+            load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                v[k] = 0.0f;  // the zero padding of a head_dim below D
+        }
         apply_signs(v, p.signs[sub2]);
         fwht_row<P2>(v, sub2);
         apply_signs(v, p.signs2[sub2]);
@@ -407,8 +414,8 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p)
     for (int k = 0; k < kCPL; k++)
         o[k] *= sc;
     apply_signs(o, p.signs[sub]);
-    if (lane < P)
-        store_slice(p.out + bh * D + sub * kCPL, o);
+    if (lane < P && sub * kCPL < p.d_in)  // padded coordinates are dropped
+        store_slice(p.out + bh * p.d_in + sub * kCPL, o);
 }
 
 int check_cache(const tq_cache_desc *c, int layer, const char *fn)
@@ -500,9 +507,11 @@ extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int
     if (!c || layer < 0 || layer >= c->n_layers || !c->head_dim || n_q_heads < 1 ||
         ctx_len < 1 || c->window < 1 || c->batch < 0 || c->n_kv_heads < 1)
         return 0;
-    const int d = c->head_dim[layer];
+    const int D = tq::padded_dim(c->head_dim[layer]);
+    if (D == 0)
+        return 0;
     Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
-    return (size_t)c->batch * n_q_heads * s.n_chunks * (size_t)(d + 4) * sizeof(float);
+    return (size_t)c->batch * n_q_heads * s.n_chunks * (size_t)(D + 4) * sizeof(float);
 }
 
 extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
@@ -522,10 +531,12 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     const int G = n_q_heads / c->n_kv_heads;
     if (ctx_len < 1)
         return tq::fail(TQ_EINVAL, "tq_attn_decode: ctx_len must be >= 1");
-    const int d = c->head_dim[layer];
-    if (!(d == 64 || d == 128 || d == 256))
-        return tq::fail(tq::is_pow2(d) ? TQ_EUNSUPPORTED : TQ_EINVAL,
-                        "tq_attn_decode: device kernels take head_dim in {64, 128, 256}");
+    const int d = c->head_dim[layer], D = tq::padded_dim(d);
+    if (D == 0)
+        return tq::fail(TQ_EINVAL, "tq_attn_decode: head_dim outside 2..2^20");
+    if (!((D == 64 || D == 128 || D == 256) && (d == D || d % 32 == 0)))
+        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: device kernels take head_dim in "
+                                         "{64, 128, 256} or a multiple of 32 between them");
     const int bits_k = tq::layer_bits(c, layer, 0), bits_v = tq::layer_bits(c, layer, 1);
     for (int bits : {bits_k, bits_v}) {
         if (bits < 1 || bits > 4)
@@ -551,8 +562,8 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     if (tq::take_injected_launch_failure())
         return tq::fail(TQ_EHIP, "tq_attn_decode: injected launch failure (TQ_TEST_FAIL_LAUNCH)");
     tq_codebook ck, cv;
-    if ((rc = tq::get_codebook(d, bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
-        (rc = tq::get_codebook(d, bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
+    if ((rc = tq::get_codebook(D, bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
+        (rc = tq::get_codebook(D, bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
         return rc;
     Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
     AttnParams p;
@@ -569,18 +580,21 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     p.T = s.T;
     p.n_chunks = s.n_chunks;
     p.chunk_len = s.chunk_len;
+    p.d_in = d;
+    // the default scale is 1/sqrt(head_dim); the rotation's 1/sqrt is of the
+    // padded length
     const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)d);
-    p.qscale = sc * kLog2e / sqrtf((float)d);
+    p.qscale = sc * kLog2e / sqrtf((float)D);
     p.gate_log2 = sparse_v_threshold > 0.0f ? log2f(sparse_v_threshold) : -__builtin_huge_valf();
     for (int j = 0; j < 16; j++) {
         p.centK[j] = j < ck.levels ? ck.centroids[j] : 0.0f;
         p.centV[j] = j < cv.levels ? cv.centroids[j] : 0.0f;
     }
-    tq::sign_words(d, c->seed, p.signs);
-    tq::sign_words2(d, c->seed, c->flags, p.signs2);
+    tq::sign_words(D, c->seed, p.signs);
+    tq::sign_words2(D, c->seed, c->flags, p.signs2);
     dim3 grid((unsigned)s.n_chunks, (unsigned)c->n_kv_heads, (unsigned)c->batch);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (d) {
+    switch (D) {
     case 64: launch_attn_d<64>(bits_k, bits_v, G, grid, p, st); break;
     case 128: launch_attn_d<128>(bits_k, bits_v, G, grid, p, st); break;
     default: launch_attn_d<256>(bits_k, bits_v, G, grid, p, st); break;

@@ -110,14 +110,15 @@ struct EncodeSide {
 struct EncodeParams {
     EncodeSide side[2];
     int64_t n_rows;
+    int d_in;            // coordinates per input row (<= D; the rest are zero)
     uint32_t signs[8];
     uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
 
 template <int D, typename T, int BITS>
 __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t n_rows,
-                                                   const SignMasks<T> &sm, uint32_t s2,
-                                                   uint32_t key)
+                                                   int d_in, const SignMasks<T> &sm,
+                                                   uint32_t s2, uint32_t key)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
@@ -125,18 +126,20 @@ __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t 
     const int sub = lane % P, rig = lane / P;
     const T *src = static_cast<const T *>(s.src);
     const int64_t stride = (int64_t)gridDim.x * RPB;
+    // a head_dim below D (padded to D) leaves whole slices of zeros
+    const bool live = sub * kCPL < d_in;
     int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + rig;
     RawSlice<T> cur;
-    if (row < n_rows)
-        load_raw(src + row * D + sub * kCPL, cur);
+    if (row < n_rows && live)
+        load_raw(src + row * d_in + sub * kCPL, cur);
     else
         zero_raw(cur);
     for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows; base += stride) {
         // issue the next pass's loads before transforming this one
         const int64_t nrow = row + stride;
         RawSlice<T> nxt;
-        if (nrow < n_rows)
-            load_raw(src + nrow * D + sub * kCPL, nxt);
+        if (nrow < n_rows && live)
+            load_raw(src + nrow * d_in + sub * kCPL, nxt);
         else
             zero_raw(nxt);
         const bool valid = row < n_rows;
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     const uint32_t s2 = p.signs2[sub];
     const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, sm, s2, key); break;
-    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, sm, s2, key); break;
-    default: encode_contig_loop<D, T, 4>(s, p.n_rows, sm, s2, key); break;
+    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, p.d_in, sm, s2, key); break;
+    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, p.d_in, sm, s2, key); break;
+    default: encode_contig_loop<D, T, 4>(s, p.n_rows, p.d_in, sm, s2, key); break;
     }
 }
 
@@ -595,6 +598,7 @@ struct AppendParams {
     int bh;           // batch * n_kv_heads
     int window;
     int slot;         // pos % window
+    int d_in;         // coordinates per new row (<= D; the rest are zero)
     uint32_t signs[8];
     uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
@@ -614,10 +618,10 @@ __device__ __forceinline__ void append_loop(const AppendSide &s, const AppendPar
         const bool valid = row < n_rows;
         const int64_t r = valid ? row : 0;
         const int li = (int)(r / p.bh), j = (int)(r % p.bh);
-        const T *src = static_cast<const T *>(s.src[li]) + (int64_t)j * D + sub * kCPL;
+        const T *src = static_cast<const T *>(s.src[li]) + (int64_t)j * p.d_in + sub * kCPL;
         const int64_t dst = (int64_t)j * p.window + p.slot;
         RawSlice<T> raw;
-        if (valid)
+        if (valid && sub * kCPL < p.d_in)
             load_raw(src, raw);
         else
             zero_raw(raw);
@@ -660,6 +664,7 @@ struct DecodeParams {
     // exact negation of n c[idx].
     uint32_t flip[32];
     int two_sided;  // flip is nonzero
+    int d_out;      // coordinates kept per output row (PAD kernels; else D)
 };
 
 // One wave per workgroup, one pass of RPW rows per wave, and one launch (or
@@ -669,7 +674,7 @@ struct DecodeParams {
 // both requested before either is used (one memory round trip, not two).
 constexpr int kDecodeBlock = 64;
 
-template <int D, int BITS>
+template <int D, int BITS, bool PAD>
 __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW;
@@ -708,7 +713,14 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
     for (int k = 0; k < kCPL; k++)
         v[k] *= sc;
     apply_signs(v, smask);
-    store_region_coalesced(p.out + row0 * D, v, stage, lane, (p.n_rows - row0) * D);
+    if constexpr (PAD) {
+        // head_dim d_out < D: rows of d_out floats, the padded slices dropped
+        const int64_t rows = min<int64_t>(RPW, p.n_rows - row0);
+        store_region_padded<P>(p.out + row0 * p.d_out, v, stage, lane, rows * p.d_out,
+                               p.d_out / kCPL);
+    } else {
+        store_region_coalesced(p.out + row0 * D, v, stage, lane, (p.n_rows - row0) * D);
+    }
 }
 
 // ----------------------------------------------------------------- rotate
@@ -792,14 +804,20 @@ void launch_all(int64_t n_rows, int rpb, F launch)
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// d supported by the device kernels, else the status to return
-int check_d(int d, const char *fn)
+// d supported by the device kernels, else the status to return: 64, 128,
+// 256, and (allow_pad) the multiples of 32 between them, which run padded to
+// the next power of two
+int check_d(int d, const char *fn, bool allow_pad = true)
 {
-    if (d == 64 || d == 128 || d == 256)
+    const int dp = tq::padded_dim(d);
+    if (dp == 0)
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": d outside 2..2^20");
+    if ((dp == 64 || dp == 128 || dp == 256) && (d == dp || (allow_pad && d % 32 == 0)))
         return TQ_OK;
-    if (tq::is_pow2(d) && d >= 2 && d <= (1 << 20))
-        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device kernels take d in {64, 128, 256}");
-    return tq::fail(TQ_EINVAL, std::string(fn) + ": d must be a power of two");
+    return tq::fail(TQ_EUNSUPPORTED,
+                    std::string(fn) + (allow_pad ? ": device kernels take d in {64, 128, 256} "
+                                                   "or a multiple of 32 between 64 and 256"
+                                                 : ": device kernels take d in {64, 128, 256}"));
 }
 
 int check_bits(int bits, const char *fn)
@@ -948,7 +966,7 @@ void launch_append(int d, const AppendParams &p, int sides, hipStream_t st)
     }
 }
 
-template <int D>
+template <int D, bool PAD>
 void launch_decode_d(int bits, const DecodeParams &p0, hipStream_t st)
 {
     launch_all(p0.n_rows, Shape<D>::RPW, [&](dim3 grid, int64_t first) {
@@ -956,9 +974,9 @@ void launch_decode_d(int bits, const DecodeParams &p0, hipStream_t st)
         p.row_base = first;
         const dim3 block(kDecodeBlock);
         switch (bits) {
-        case 2: hipLaunchKernelGGL((decode_kernel<D, 2>), grid, block, 0, st, p); break;
-        case 3: hipLaunchKernelGGL((decode_kernel<D, 3>), grid, block, 0, st, p); break;
-        default: hipLaunchKernelGGL((decode_kernel<D, 4>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<D, 2, PAD>), grid, block, 0, st, p); break;
+        case 3: hipLaunchKernelGGL((decode_kernel<D, 3, PAD>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((decode_kernel<D, 4, PAD>), grid, block, 0, st, p); break;
         }
     });
 }
@@ -994,7 +1012,7 @@ extern "C" int tq_rotate(const void *in, int dtype, int64_t n_rows, int d, uint6
     int rc = tq::check_flags(flags, fn);
     if (rc != TQ_OK)
         return rc;
-    if ((rc = check_d(d, fn)) != TQ_OK)
+    if ((rc = check_d(d, fn, false)) != TQ_OK)
         return rc;
     if (n_rows == 0)
         return TQ_OK;
@@ -1035,6 +1053,7 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         return rc;
     if ((rc = check_d(d, fn)) != TQ_OK)
         return rc;
+    const int D = tq::padded_dim(d);  // rotated and stored length
     if (n_rows == 0)
         return TQ_OK;  // nothing to do; buffers may be NULL
     if (!k_rows && !v_rows)
@@ -1058,14 +1077,15 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         e.src = src[s];
         e.packed = pk[s];
         e.norms = nm[s];
-        if ((rc = code_table(d, bits[s], tq::density_of(flags), &e.code, fn)) != TQ_OK)
+        if ((rc = code_table(D, bits[s], tq::density_of(flags), &e.code, fn)) != TQ_OK)
             return rc;
     }
     if ((rc = injected(fn)) != TQ_OK)
         return rc;
     p.n_rows = n_rows;
+    p.d_in = d;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dtype == TQ_BF16 && d <= 128) {
+    if (dtype == TQ_BF16 && d <= 128 && d == D) {
         EncodeLaneParams q;
         q.side[0] = p.side[0];
         q.side[1] = p.side[1];
@@ -1090,12 +1110,12 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
                 : launch_encode_lane_d<128, false>(q, b0, b1, st);
         return launch_status(fn);
     }
-    tq::sign_words(d, seed, p.signs);
-    tq::sign_words2(d, seed, flags, p.signs2);
+    tq::sign_words(D, seed, p.signs);
+    tq::sign_words2(D, seed, flags, p.signs2);
     if (dtype == TQ_F32)
-        launch_encode<float>(d, p, sides, st);
+        launch_encode<float>(D, p, sides, st);
     else
-        launch_encode<uint16_t>(d, p, sides, st);
+        launch_encode<uint16_t>(D, p, sides, st);
     return launch_status(fn);
 }
 
@@ -1121,8 +1141,9 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
         return tq::fail(TQ_EINVAL, "tq_decode: misaligned buffer (packed and out need 16 bytes, norms 4)");
     if ((rc = injected(fn)) != TQ_OK)
         return rc;
+    const int D = tq::padded_dim(d);  // rotated and stored length
     tq_codebook cb;
-    if ((rc = tq::get_codebook(d, bits, tq::density_of(flags), &cb)) != TQ_OK)
+    if ((rc = tq::get_codebook(D, bits, tq::density_of(flags), &cb)) != TQ_OK)
         return rc;
     for (int j = 0; j < cb.levels; j++)
         if (cb.centroids[cb.levels - 1 - j] != -cb.centroids[j])
@@ -1132,16 +1153,22 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
     p.norms = norms;
     p.out = out;
     p.n_rows = n_rows;
+    p.d_out = d;
     for (int j = 0; j < 16; j++)
         p.cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
-    tq::sign_words(d, seed, p.signs);
-    flip_words(d, bits, seed, flags, p.flip);
+    tq::sign_words(D, seed, p.signs);
+    flip_words(D, bits, seed, flags, p.flip);
     p.two_sided = (flags & TQ_FLAG_TWO_SIDED) ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    switch (d) {
-    case 64: launch_decode_d<64>(bits, p, st); break;
-    case 128: launch_decode_d<128>(bits, p, st); break;
-    default: launch_decode_d<256>(bits, p, st); break;
+    const bool pad = d != D;
+    switch (D) {
+    case 64: launch_decode_d<64, false>(bits, p, st); break;
+    case 128:
+        pad ? launch_decode_d<128, true>(bits, p, st) : launch_decode_d<128, false>(bits, p, st);
+        break;
+    default:
+        pad ? launch_decode_d<256, true>(bits, p, st) : launch_decode_d<256, false>(bits, p, st);
+        break;
     }
     return launch_status(fn);
 }
@@ -1190,43 +1217,47 @@ extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *cons
         return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int slot = (int)(pos % c->window);
-    // one launch per distinct (head_dim, K width, V width), and per
-    // kMaxAppendLayers layers of it
-    const int dims[3] = {64, 128, 256};
-    for (int key = 0; key < 3 * 9; key++) {
-        const int d = dims[key / 9], bk = 2 + (key % 9) / 3, bv = 2 + key % 3;
-        bool used = false;
-        for (int l = l0; l < l1 && !used; l++)
-            used = c->head_dim[l] == d && tq::layer_bits(c, l, 0) == bk &&
-                   tq::layer_bits(c, l, 1) == bv;
-        if (!used)
+    // one launch per distinct (head_dim, K width, V width), in the order of
+    // their first layers, and per kMaxAppendLayers layers of it
+    auto same = [&](int a, int b) {
+        return c->head_dim[a] == c->head_dim[b] &&
+               tq::layer_bits(c, a, 0) == tq::layer_bits(c, b, 0) &&
+               tq::layer_bits(c, a, 1) == tq::layer_bits(c, b, 1);
+    };
+    for (int first = l0; first < l1; first++) {
+        bool seen = false;
+        for (int l = l0; l < first && !seen; l++)
+            seen = same(l, first);
+        if (seen)
             continue;
+        const int d = c->head_dim[first], D = tq::padded_dim(d);
+        const int bk = tq::layer_bits(c, first, 0), bv = tq::layer_bits(c, first, 1);
         AppendParams p;
         p.bh = bh;
         p.window = c->window;
         p.slot = slot;
-        tq::sign_words(d, c->seed, p.signs);
-        tq::sign_words2(d, c->seed, c->flags, p.signs2);
+        p.d_in = d;
+        tq::sign_words(D, c->seed, p.signs);
+        tq::sign_words2(D, c->seed, c->flags, p.signs2);
         const int dens = tq::density_of(c->flags);
-        if ((rc = code_table(d, bk, dens, &p.side[0].code, fn)) != TQ_OK ||
-            (rc = code_table(d, bv, dens, &p.side[1].code, fn)) != TQ_OK)
+        if ((rc = code_table(D, bk, dens, &p.side[0].code, fn)) != TQ_OK ||
+            (rc = code_table(D, bv, dens, &p.side[1].code, fn)) != TQ_OK)
             return rc;
         p.n_layers = 0;
         for (int l = l0; l <= l1; l++) {
             const bool flush = (l == l1) || (p.n_layers == kMaxAppendLayers);
             if (flush && p.n_layers > 0) {
                 if (dtype == TQ_F32)
-                    launch_append<float>(d, p, 2, st);
+                    launch_append<float>(D, p, 2, st);
                 else
-                    launch_append<uint16_t>(d, p, 2, st);
+                    launch_append<uint16_t>(D, p, 2, st);
                 if ((rc = launch_status(fn)) != TQ_OK)
                     return rc;
                 p.n_layers = 0;
             }
             if (l == l1)
                 break;
-            if (c->head_dim[l] != d || tq::layer_bits(c, l, 0) != bk ||
-                tq::layer_bits(c, l, 1) != bv)
+            if (!same(l, first))
                 continue;
             const int i = l - l0, n = p.n_layers++;
             p.side[0].src[n] = k_new[i];

@@ -219,6 +219,34 @@ __device__ __forceinline__ void store_region_coalesced(float *region, const floa
     wave_lds_fence();
 }
 
+// The same for rows padded to D = P * kCPL of which only the first nv * kCPL
+// coordinates are kept: the region holds RPW rows of nv * kCPL floats, built
+// from the slices sub < nv of each row.
+template <int P>
+__device__ __forceinline__ void store_region_padded(float *region, const float (&v)[kCPL],
+                                                    float *stage, int lane, int64_t valid_floats,
+                                                    int nv)
+{
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        f32x4 t = {v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]};
+        *reinterpret_cast<f32x4 *>(stage + lane * kStageStride + 4 * j) = t;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < kCPL / 4; j++) {
+        const int e = 64 * j + lane;      // float4 index inside the region
+        const int q = e >> 3;             // kept slice: row q / nv, slice q % nv
+        const int r = q / nv;
+        const int src = r * P + (q - r * nv);
+        if ((int64_t)e * 4 < valid_floats && q < (64 / P) * nv) {
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(stage + src * kStageStride + 4 * (e & 7));
+            __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(region) + e);
+        }
+    }
+    wave_lds_fence();
+}
+
 // ------------------------------------------------------------ bit packing
 // Index k of a lane's slice occupies bits [k*BITS, (k+1)*BITS) of the lane's
 // BITS 32-bit words (little-endian), which is the row's bitstream restricted

@@ -308,11 +308,24 @@ extern "C" int tq_signs(int d, uint64_t seed, int8_t *out_pm1)
     return TQ_OK;
 }
 
+namespace tq {
+int padded_dim(int d)
+{
+    if (d < 2 || d > (1 << 20))
+        return 0;
+    int p = 1;
+    while (p < d)
+        p *= 2;
+    return p;
+}
+}  // namespace tq
+
 extern "C" size_t tq_packed_row_bytes(int d, int bits)
 {
-    if (d <= 0 || bits < 1 || bits > 8)
+    const int dp = d == 1 ? 1 : tq::padded_dim(d);
+    if (dp == 0 || bits < 1 || bits > 8)
         return 0;
-    return ((size_t)d * (size_t)bits + 7) / 8;
+    return ((size_t)dp * (size_t)bits + 7) / 8;
 }
 
 extern "C" int tq_layer_bits_boundary(int n_layers, int n_boundary, int bits_inner,

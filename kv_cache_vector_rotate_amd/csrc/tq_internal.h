@@ -44,6 +44,10 @@ inline int layer_bits(const tq_cache_desc *c, int l, int side)
 
 bool is_pow2(int64_t v);
 
+// Length a row of d coordinates is rotated and stored at: d when it is a
+// power of two, else the next power of two; 0 when d is outside 2..2^20.
+int padded_dim(int d);
+
 // Test-only fault injection: when the environment variable TQ_TEST_FAIL_LAUNCH
 // is "1" at the first query, the next device launch reports TQ_EHIP without
 // launching anything (one shot), so host tests can reach the HIP error path.

@@ -41,7 +41,9 @@ def test_version_and_row_bytes(tq):
     for d in (64, 128, 256):
         for b in (2, 3, 4):
             assert tq.tq_packed_row_bytes(d, b) == d * b // 8
-    assert tq.tq_packed_row_bytes(96, 3) == 36
+    # a head_dim that is not a power of two is stored at the next one
+    assert tq.tq_packed_row_bytes(96, 3) == 48 and tq.tq_packed_row_bytes(160, 4) == 128
+    assert tq.tq_packed_row_bytes(100, 2) == 32 and tq.tq_packed_row_bytes((1 << 20) + 1, 4) == 0
     assert tq.tq_packed_row_bytes(0, 4) == 0 and tq.tq_packed_row_bytes(64, 9) == 0
 
 
@@ -112,7 +114,10 @@ def test_encode_decode_validation_without_launch(tq):
     assert L.tq_encode(None, None, 0, 10, 128, 4, 2, 42, 0, A, N, A, N, None) == tq.TQ_EINVAL
     assert "both" in tq.tq_last_error()
     assert L.tq_encode(A, None, 7, 10, 128, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
-    assert L.tq_encode(A, None, 0, 10, 96, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 1, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_encode(A, None, 0, 10, 100, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 32, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_encode(A, None, 0, 10, 288, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_encode(A, None, 0, 10, 512, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_encode(A, None, 0, 10, 128, 1, 2, 42, 0, A, N, None, None, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_encode(A, None, 0, 10, 128, 5, 2, 42, 0, A, N, None, None, None) == tq.TQ_EINVAL
@@ -127,7 +132,12 @@ def test_encode_decode_validation_without_launch(tq):
     assert L.tq_decode(A, N, 5, 128, 1, 42, 0, A, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_decode(None, N, 5, 128, 4, 42, 0, A, None) == tq.TQ_EINVAL
     assert L.tq_rotate(A, 0, 0, 128, 42, 0, 0, A, None) == tq.TQ_OK
-    assert L.tq_rotate(A, 0, 3, 100, 42, 0, 0, A, None) == tq.TQ_EINVAL
+    assert L.tq_rotate(A, 0, 3, 1, 42, 0, 0, A, None) == tq.TQ_EINVAL
+    assert L.tq_rotate(A, 0, 3, 96, 42, 0, 0, A, None) == tq.TQ_EUNSUPPORTED   # codec calls only
+    # padded head_dims pass validation (n_rows = 0: nothing launched)
+    for d in (96, 160, 192, 224):
+        assert L.tq_encode(A, None, 0, 0, d, 4, 2, 42, 0, A, N, None, None, None) == tq.TQ_OK
+        assert L.tq_decode(A, N, 0, d, 3, 42, 0, A, None) == tq.TQ_OK
     # option bits: the two known ones pass validation, any other is rejected
     for fn, args in (("tq_encode", lambda f: (A, None, 0, 0, 128, 4, 2, 42, f, A, N, None, None,
                                               None)),
@@ -175,8 +185,14 @@ def test_cache_and_attention_validation(tq):
     for bad in (-0.1, 1.0, float("nan")):
         assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, bad, A, A, 1 << 20, None) == tq.TQ_EINVAL
     assert "sparse_v" in tq.tq_last_error()
-    d2 = _desc(tq, head_dim=96)
+    d2 = _desc(tq, head_dim=100)
+    assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
+    d2 = _desc(tq, head_dim=1)
     assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
+    d2 = _desc(tq, head_dim=96, batch=0)
+    assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_OK
+    # the workspace holds the padded length: 2 x 4 x 1 x (128 + 4) floats
+    assert L.tq_attn_workspace_bytes(ctypes.byref(_desc(tq, head_dim=96)), 0, 4, 5) == 2 * 4 * 132 * 4
     d3 = _desc(tq, bk=1)
     assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
     d4 = _desc(tq, flags=4)

@@ -213,3 +213,21 @@ def test_attention_per_layer_bits(tq, orc):
         ref = _oracle(orc, cache, layer, q, 1, range(Hkv * G), T, 1 / math.sqrt(hd[layer]))
         for h in range(Hkv * G):
             check_attention(o[1, h], ref[h])
+
+
+@pytest.mark.parametrize("flags", [0, 3])
+@pytest.mark.parametrize("d,G", [(96, 4), (160, 2), (224, 8)])
+def test_attention_padded_head_dim(tq, orc, d, G, flags):
+    """head_dim that is not a power of two: q and out hold d values; the
+    cache rows are stored at the padded length."""
+    B, Hkv, T = 2, 2, 700
+    cache = tq.TQCache(1, B, Hkv, T, d, 4, 2, SEED, flags=flags)
+    _fill(tq, cache, 0, 90 + d)
+    q = kvgen.normal((B, Hkv * G, d), 91 + d, "cuda", torch.bfloat16)
+    o = tq.tq_attn_decode(cache, 0, q, T)
+    assert o.shape == (B, Hkv * G, d)
+    o = o.cpu().numpy()
+    for b in range(B):
+        ref = _oracle(orc, cache, 0, q, b, range(Hkv * G), T, 1 / math.sqrt(d))
+        for h in range(Hkv * G):
+            check_attention(o[b, h], ref[h])

@@ -24,9 +24,10 @@ def _check_slot(orc, rows, packed, norms, d, bits, flags=0, tally=None):
     density = orc.GAUSS if flags & 1 else orc.BETA
     op, on, u = orc.encode(rows.astype(np.float32), d, bits, SEED, want_u=True,
                            density=density, two_sided=bool(flags & 2))
-    _, bnd = orc.codebook_float(d, bits, density)
+    dp = orc.padded_dim(d)          # rows are stored at the padded length
+    _, bnd = orc.codebook_float(dp, bits, density)
     check_norms(norms, on)
-    check_indices(packed, op, u, d, bits, bnd, tally=tally)
+    check_indices(packed, op, u, dp, bits, bnd, tally=tally)
 
 
 @pytest.mark.parametrize("flags", [0, 3])
@@ -145,3 +146,25 @@ def test_append_per_layer_bits(tq, orc, dtype):
     for l in range(6):
         assert torch.count_nonzero(cache.k_norms[l][:, :, [0, 3]]).item() == 0
         assert torch.count_nonzero(cache.v_packed[l][:, :, [0, 3]]).item() == 0
+
+
+def test_append_padded_head_dims(tq, orc):
+    """Layers of head_dim 96, 160 and 128 in one cache: rows of d values are
+    appended at the padded length of their layer."""
+    hd = [96, 160, 128, 96]
+    B, H, W = 2, 2, 3
+    cache = tq.TQCache(4, B, H, W, hd, 4, 3, SEED, flags=2)
+    tally = BandTally()
+    ks = [kvgen.normal((B, H, d), 1200 + l, "cuda") for l, d in enumerate(hd)]
+    vs = [kvgen.normal((B, H, d), 1300 + l, "cuda").to(torch.bfloat16) for l, d in enumerate(hd)]
+    tq.tq_append_row(cache, -1, ks, [v.float() for v in vs], 4)
+    torch.cuda.synchronize()
+    for l, d in enumerate(hd):
+        dp = orc.padded_dim(d)
+        assert cache.k_packed[l].shape[-1] == dp * 4 // 8
+        for x, bits, pk, nm in ((ks[l], 4, cache.k_packed[l], cache.k_norms[l]),
+                                (vs[l].float(), 3, cache.v_packed[l], cache.v_norms[l])):
+            _check_slot(orc, x.cpu().numpy().reshape(-1, d),
+                        pk[:, :, 1].cpu().numpy().reshape(B * H, -1),
+                        nm[:, :, 1].cpu().numpy().reshape(-1), d, bits, flags=2, tally=tally)
+    tally.check()

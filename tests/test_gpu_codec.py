@@ -280,3 +280,35 @@ def test_edge_rows_two_sided(tq, orc, dtype, bits):
         assert np.all(xd[0] == 0)
         check_decoded(xd[1:], orc.decode(gp[1:], gn[1:], d, bits, SEED, density=density,
                                          two_sided=True))
+
+
+@pytest.mark.parametrize("flags", [0, 3])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [96, 160, 192, 224])
+def test_padded_head_dim(tq, orc, d, dtype, flags):
+    """head_dim that is not a power of two: rows of d values, packed at the
+    next power of two, decoded back to d values."""
+    dp = orc.padded_dim(d)
+    density = orc.GAUSS if flags & 1 else orc.BETA
+    two = bool(flags & 2)
+    n = 1000 + 37
+    tally = BandTally()
+    k = kvgen.normal((n, d), 61 + d, "cuda", dtype)
+    v = kvgen.normal((n, d), 62 + d, "cuda", dtype) * 0.5
+    for bk, bv in ((4, 2), (3, 3), (2, 4)):
+        kp, kn, vp, vn = tq.tq_encode(k, v, bk, bv, SEED, flags=flags)
+        torch.cuda.synchronize()
+        for x, bits, p, nm in ((k, bk, kp, kn), (v, bv, vp, vn)):
+            assert p.shape == (n, dp * bits // 8)
+            xh = _np(x).astype(np.float32)
+            op, on, u = orc.encode(xh, d, bits, SEED, density=density, want_u=True,
+                                   two_sided=two)
+            _, bnd = orc.codebook_float(dp, bits, density)
+            gp, gn = p.cpu().numpy(), nm.cpu().numpy()
+            check_norms(gn, on)
+            check_indices(gp, op, u, dp, bits, bnd, tally=tally)
+            xd = tq.tq_decode(p, nm, d, bits, SEED, flags=flags)
+            assert xd.shape == (n, d)
+            check_decoded(xd.cpu().numpy(), orc.decode(gp, gn, d, bits, SEED, density=density,
+                                                       two_sided=two))
+    tally.check()
