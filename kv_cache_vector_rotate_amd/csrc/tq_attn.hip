@@ -377,6 +377,247 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     }
 }
 
+// The same partial results without the sparse-V gate, with an online softmax
+// per wave instead of per tile: the weights of a row are only ever needed by
+// the wave that scored it, so each wave keeps its scores in registers, runs
+// its own running maximum (wave-uniform) and sum, and accumulates V right
+// after each step of CH row passes.  No LDS traffic for scores and no
+// barrier inside the scan; the four waves' (o', max, sum) are merged once at
+// the end.  Rows of wave w: t_begin + it * RPB + w * RPW + (lane / P).
+template <int D, int BK, int BV, int G>
+__global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
+{
+    constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
+    constexpr int P = D / CPL;            // lanes per row
+    constexpr int RPW = 64 / P;
+    constexpr int RPB = RPW * (kBlock / 64);
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int NPK = 1 << (2 * BK), NPV = 1 << (2 * BV);
+    constexpr int RS = D + 4;
+    constexpr int CH = G >= 8 ? 4 : 8;    // row passes per step
+
+    __shared__ float2 tabK[NPK];
+    __shared__ float2 tabV[NPV];
+    __shared__ float qs[G][D];
+    __shared__ float red_m[kBlock / 64][G];
+    __shared__ float red_l[kBlock / 64][G];
+    __shared__ float accs[kBlock / 64][G][D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+
+    for (int i = tid; i < NPK; i += kBlock)
+        tabK[i] = make_float2(p.centK[i & ((1 << BK) - 1)], p.centK[i >> BK]);
+    for (int i = tid; i < NPV; i += kBlock)
+        tabV[i] = make_float2(p.centV[i & ((1 << BV) - 1)], p.centV[i >> BV]);
+
+    // q' = S2 H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV
+    // head (S2 = identity for the one-sided rotation)
+    if (wave == 0) {
+        constexpr int P2 = D / kCPL;
+        const int sub2 = lane % P2, r2 = lane / P2;
+        float v[kCPL];
+        const int h = g * G + (r2 < G ? r2 : 0);
+        if (sub2 * kCPL < p.d_in) {
+            load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                v[k] = 0.0f;  // the zero padding of a head_dim below D
+        }
+        apply_signs(v, p.signs[sub2]);
+        fwht_row<P2>(v, sub2);
+        apply_signs(v, p.signs2[sub2]);
+        if (r2 < G) {
+#pragma unroll
+            for (int k = 0; k < kCPL; k++)
+                qs[r2][sub2 * kCPL + k] = v[k] * p.qscale;
+        }
+    }
+    __syncthreads();
+
+    const int sub = lane % P, rig = lane / P;
+    float qr[G][CPL];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            qr[h][k] = qs[h][sub * CPL + k];
+
+    float acc[G][CPL];
+    float m_run[G], l_part[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        m_run[h] = -__builtin_huge_valf();
+        l_part[h] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            acc[h][k] = 0.0f;
+    }
+
+    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.T, t_begin + p.chunk_len);
+    const int t_lane = t_begin + wave * RPW + rig;  // this lane's row in pass 0
+
+#pragma unroll 1
+    for (int t0 = t_lane; t0 - rig - wave * RPW < t_end; t0 += CH * RPB) {
+        // every K and V load of the step in flight before any arithmetic;
+        // rows past the context read a valid row and are masked below
+        uint64_t kb[CH], vb[CH];
+        float kn[CH], vn[CH];
+#pragma unroll
+        for (int c = 0; c < CH; c++) {
+            const int t = t0 + c * RPB;
+            const int64_t row = rowbase + (t < t_end ? t : t_begin);
+            kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
+            kn[c] = p.kn[row];
+            vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+            vn[c] = p.vn[row];
+        }
+        // scores (log2 units), every lane of a row holding its row's value
+        float sc[CH][G];
+#pragma unroll
+        for (int c = 0; c < CH; c++) {
+            float s[G];
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                s[h] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CPL / 2; m++) {
+                const float2 cc = tabK[(kb[c] >> (2 * BK * m)) & (NPK - 1)];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    s[h] = fmaf(qr[h][2 * m], cc.x, s[h]);
+                    s[h] = fmaf(qr[h][2 * m + 1], cc.y, s[h]);
+                }
+            }
+            // the row's sum is taken whether or not the row is valid: a
+            // select afterwards, not a branch around the cross-lane sum
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                s[h] = sum_across<P>(s[h]) * kn[c];
+            const bool valid = t0 + c * RPB < t_end;
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                sc[c][h] = valid ? s[h] : -__builtin_huge_valf();
+        }
+        // running maximum of the wave; rescale only when it grows
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float mx = sc[0][h];
+#pragma unroll
+            for (int c = 1; c < CH; c++)
+                mx = fmaxf(mx, sc[c][h]);
+            mx = wave_max(mx);
+            if (mx > m_run[h]) {
+                const float fac = exp2f(m_run[h] - mx);  // 0 on the first valid step
+                l_part[h] *= fac;
+#pragma unroll
+                for (int k = 0; k < CPL; k++)
+                    acc[h][k] *= fac;
+                m_run[h] = mx;
+            }
+        }
+        // weights and the V sum of the step (rotated domain)
+#pragma unroll
+        for (int c = 0; c < CH; c++) {
+            float w[G];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                // m_run is -inf only while the wave has seen no valid row;
+                // weights below 2^-126 flush to 0 (v_exp_f32)
+                const float pr = m_run[h] == -__builtin_huge_valf()
+                                     ? 0.0f
+                                     : __builtin_amdgcn_exp2f(sc[c][h] - m_run[h]);
+                l_part[h] += pr;
+                w[h] = pr * vn[c];
+            }
+#pragma unroll
+            for (int m = 0; m < CPL / 2; m++) {
+                const float2 cc = tabV[(vb[c] >> (2 * BV * m)) & (NPV - 1)];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    acc[h][2 * m] = fmaf(w[h], cc.x, acc[h][2 * m]);
+                    acc[h][2 * m + 1] = fmaf(w[h], cc.y, acc[h][2 * m + 1]);
+                }
+            }
+        }
+    }
+
+    // ---- reduce over the rows of the wave (lanes with equal `sub`); every
+    // lane of a row group holds the same sum, so the sums reduce across
+    // row groups only
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float l = l_part[h];
+        if constexpr (P <= 1) l += lane_xor_any<1>(l);
+        if constexpr (P <= 2) l += lane_xor_any<2>(l);
+        if constexpr (P <= 4) l += lane_xor_any<4>(l);
+        if constexpr (P <= 8) l += lane_xor_any<8>(l);
+        if constexpr (P <= 16) l += lane_xor_any<16>(l);
+        if constexpr (P <= 32) l += lane_xor_any<32>(l);
+        l_part[h] = l;
+#pragma unroll
+        for (int k = 0; k < CPL; k++) {
+            float a = acc[h][k];
+            if constexpr (P <= 1) a += lane_xor_any<1>(a);
+            if constexpr (P <= 2) a += lane_xor_any<2>(a);
+            if constexpr (P <= 4) a += lane_xor_any<4>(a);
+            if constexpr (P <= 8) a += lane_xor_any<8>(a);
+            if constexpr (P <= 16) a += lane_xor_any<16>(a);
+            if constexpr (P <= 32) a += lane_xor_any<32>(a);
+            acc[h][k] = a;
+        }
+    }
+    if (rig == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                accs[wave][h][sub * CPL + k] = acc[h][k];
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            red_m[wave][h] = m_run[h];
+            red_l[wave][h] = l_part[h];
+        }
+    }
+    __syncthreads();
+    // ---- merge the waves (log-sum-exp) and write this chunk's record
+    float *rec0 = p.part + (((int64_t)b * p.Hq + g * G) * p.n_chunks + chunk) * RS;
+    const int64_t hstride = (int64_t)p.n_chunks * RS;
+    for (int i = tid; i < G * D; i += kBlock) {
+        const int h = i / D, j = i % D;
+        float M = red_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            M = fmaxf(M, red_m[w][h]);
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; w++) {
+            const float mw = red_m[w][h];
+            o += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * accs[w][h][j];
+        }
+        rec0[h * hstride + j] = o;
+    }
+    if (tid < G) {
+        float M = red_m[0][tid];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            M = fmaxf(M, red_m[w][tid]);
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; w++) {
+            const float mw = red_m[w][tid];
+            l += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * red_l[w][tid];
+        }
+        rec0[tid * hstride + D] = M;
+        rec0[tid * hstride + D + 1] = l;
+    }
+}
+
 // Merge the chunks of one (sequence, query head) and rotate back.  One wave
 // per (sequence, query head); the first D/32 lanes hold the row.
 template <int D>
@@ -467,15 +708,27 @@ void launch_attn_gate(int G, dim3 grid, const AttnParams &p, hipStream_t st)
     }
 }
 
-// the sparse-V gate is a separate instantiation: the kernel without it is
-// the one that runs when the threshold is 0
+template <int D, int BK, int BV>
+void launch_attn_wave(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+{
+    dim3 block(kBlock);
+    switch (G) {
+    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8>), grid, block, 0, st, p); break;
+    }
+}
+
+// with the sparse-V gate the per-tile kernel (the gate's reference maximum is
+// that of a 256-row tile); without it the per-wave kernel
 template <int D, int BK, int BV>
 void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
 {
     if (p.gate_log2 > -__builtin_huge_valf())
         launch_attn_gate<D, BK, BV, true>(G, grid, p, st);
     else
-        launch_attn_gate<D, BK, BV, false>(G, grid, p, st);
+        launch_attn_wave<D, BK, BV>(G, grid, p, st);
 }
 
 template <int D, int BK>
