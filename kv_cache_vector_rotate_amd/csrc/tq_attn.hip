@@ -377,6 +377,40 @@ __global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
     }
 }
 
+// Centroid lookup width of the per-wave kernel: four neighbouring 2-bit
+// indices (one byte) address a 256-entry table of centroid quadruples; wider
+// indices go in pairs.  Either way one LDS read per lookup.
+template <int BITS>
+struct Lookup {
+    static constexpr int W = BITS == 2 ? 4 : 2;  // coordinates per lookup
+    static constexpr int N = 1 << (W * BITS);    // table entries
+};
+
+template <int BITS>
+__device__ __forceinline__ void fill_lookup(float *tab, const float *cent)
+{
+    constexpr int W = Lookup<BITS>::W, N = Lookup<BITS>::N;
+    for (int e = threadIdx.x; e < N; e += kBlock)
+#pragma unroll
+        for (int j = 0; j < W; j++)
+            tab[W * e + j] = cent[(e >> (BITS * j)) & ((1 << BITS) - 1)];
+}
+
+// the W centroids of lookup m of a lane's slice bits
+template <int BITS>
+__device__ __forceinline__ void lookup(const float *tab, uint64_t bits, int m, float *cc)
+{
+    constexpr int W = Lookup<BITS>::W, N = Lookup<BITS>::N;
+    const int e = (int)((bits >> (W * BITS * m)) & (N - 1));
+    if constexpr (W == 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(tab + 4 * e);
+        cc[0] = v.x; cc[1] = v.y; cc[2] = v.z; cc[3] = v.w;
+    } else {
+        const float2 v = *reinterpret_cast<const float2 *>(tab + 2 * e);
+        cc[0] = v.x; cc[1] = v.y;
+    }
+}
+
 // The same partial results without the sparse-V gate, with an online softmax
 // per wave instead of per tile: the weights of a row are only ever needed by
 // the wave that scored it, so each wave keeps its scores in registers, runs
@@ -392,12 +426,12 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     constexpr int RPW = 64 / P;
     constexpr int RPB = RPW * (kBlock / 64);
     constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
-    constexpr int NPK = 1 << (2 * BK), NPV = 1 << (2 * BV);
     constexpr int RS = D + 4;
     constexpr int CH = G >= 8 ? 4 : 8;    // row passes per step
+    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
 
-    __shared__ float2 tabK[NPK];
-    __shared__ float2 tabV[NPV];
+    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK>::N * WK];
+    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV>::N * WV];
     __shared__ float qs[G][D];
     __shared__ float red_m[kBlock / 64][G];
     __shared__ float red_l[kBlock / 64][G];
@@ -406,10 +440,8 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
 
-    for (int i = tid; i < NPK; i += kBlock)
-        tabK[i] = make_float2(p.centK[i & ((1 << BK) - 1)], p.centK[i >> BK]);
-    for (int i = tid; i < NPV; i += kBlock)
-        tabV[i] = make_float2(p.centV[i & ((1 << BV) - 1)], p.centV[i >> BV]);
+    fill_lookup<BK>(tabK, p.centK);
+    fill_lookup<BV>(tabV, p.centV);
 
     // q' = S2 H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV
     // head (S2 = identity for the one-sided rotation)
@@ -484,13 +516,14 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
             for (int h = 0; h < G; h++)
                 s[h] = 0.0f;
 #pragma unroll
-            for (int m = 0; m < CPL / 2; m++) {
-                const float2 cc = tabK[(kb[c] >> (2 * BK * m)) & (NPK - 1)];
+            for (int m = 0; m < CPL / WK; m++) {
+                float cc[WK];
+                lookup<BK>(tabK, kb[c], m, cc);
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    s[h] = fmaf(qr[h][2 * m], cc.x, s[h]);
-                    s[h] = fmaf(qr[h][2 * m + 1], cc.y, s[h]);
-                }
+                for (int j = 0; j < WK; j++)
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
             }
             // the row's sum is taken whether or not the row is valid: a
             // select afterwards, not a branch around the cross-lane sum
@@ -534,13 +567,14 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
                 w[h] = pr * vn[c];
             }
 #pragma unroll
-            for (int m = 0; m < CPL / 2; m++) {
-                const float2 cc = tabV[(vb[c] >> (2 * BV * m)) & (NPV - 1)];
+            for (int m = 0; m < CPL / WV; m++) {
+                float cc[WV];
+                lookup<BV>(tabV, vb[c], m, cc);
 #pragma unroll
-                for (int h = 0; h < G; h++) {
-                    acc[h][2 * m] = fmaf(w[h], cc.x, acc[h][2 * m]);
-                    acc[h][2 * m + 1] = fmaf(w[h], cc.y, acc[h][2 * m + 1]);
-                }
+                for (int j = 0; j < WV; j++)
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
             }
         }
     }
