@@ -67,24 +67,14 @@ __device__ __forceinline__ float lane_xor_any(float v)
 
 __device__ __forceinline__ float wave_max(float x)
 {
-    x = fmaxf(x, lane_xor<1>(x));
-    x = fmaxf(x, lane_xor<2>(x));
-    x = fmaxf(x, lane_xor<4>(x));
-    x = fmaxf(x, lane_xor<8>(x));
-    x = fmaxf(x, lane_xor<16>(x));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    x = max_across<32>(x);
+    return fmaxf(x, __shfl_xor(x, 32));
 }
 
 __device__ __forceinline__ float wave_sum(float x)
 {
-    x += lane_xor<1>(x);
-    x += lane_xor<2>(x);
-    x += lane_xor<4>(x);
-    x += lane_xor<8>(x);
-    x += lane_xor<16>(x);
-    x += __shfl_xor(x, 32);
-    return x;
+    x = sum_across<32>(x);
+    return x + __shfl_xor(x, 32);
 }
 
 // Bits of one lane's slice of a packed row: CPL indices of BITS bits starting

@@ -74,25 +74,43 @@ __device__ __forceinline__ float lane_xor(float v)
     return __int_as_float(x);
 }
 
+// Partner of step M of a butterfly reduction: once steps 1 .. M/2 are done,
+// every lane of an aligned group of M lanes holds the same partial, so any
+// lane of the neighbouring group will do.  Steps 4 and 8 take the mirrored
+// lane of the 8- or 16-lane row (DPP row_half_mirror / row_mirror, a vector
+// instruction) instead of lane ^ M (a swizzle through the LDS unit); the
+// values, and so the results, are the same.  Not for exchanges that need
+// lane ^ M itself (the Hadamard stages).
+template <int M>
+__device__ __forceinline__ float reduce_partner(float v)
+{
+    if constexpr (M == 4)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    else if constexpr (M == 8)
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+    else
+        return lane_xor<M>(v);
+}
+
 template <int P>
 __device__ __forceinline__ float sum_across(float x)
 {
-    if constexpr (P > 1) x += lane_xor<1>(x);
-    if constexpr (P > 2) x += lane_xor<2>(x);
-    if constexpr (P > 4) x += lane_xor<4>(x);
-    if constexpr (P > 8) x += lane_xor<8>(x);
-    if constexpr (P > 16) x += lane_xor<16>(x);
+    if constexpr (P > 1) x += reduce_partner<1>(x);
+    if constexpr (P > 2) x += reduce_partner<2>(x);
+    if constexpr (P > 4) x += reduce_partner<4>(x);
+    if constexpr (P > 8) x += reduce_partner<8>(x);
+    if constexpr (P > 16) x += reduce_partner<16>(x);
     return x;
 }
 
 template <int P>
 __device__ __forceinline__ float max_across(float x)
 {
-    if constexpr (P > 1) x = fmaxf(x, lane_xor<1>(x));
-    if constexpr (P > 2) x = fmaxf(x, lane_xor<2>(x));
-    if constexpr (P > 4) x = fmaxf(x, lane_xor<4>(x));
-    if constexpr (P > 8) x = fmaxf(x, lane_xor<8>(x));
-    if constexpr (P > 16) x = fmaxf(x, lane_xor<16>(x));
+    if constexpr (P > 1) x = fmaxf(x, reduce_partner<1>(x));
+    if constexpr (P > 2) x = fmaxf(x, reduce_partner<2>(x));
+    if constexpr (P > 4) x = fmaxf(x, reduce_partner<4>(x));
+    if constexpr (P > 8) x = fmaxf(x, reduce_partner<8>(x));
+    if constexpr (P > 16) x = fmaxf(x, reduce_partner<16>(x));
     return x;
 }
 
