@@ -13,14 +13,17 @@
 // and sum_t p_t v_t = D H (sum_t p_t n^V_t c_V[idx^V_t]) / sqrt(d).
 //
 // Split over the context: workgroup (chunk, kv head, sequence) handles the G
-// query heads of one KV head over one chunk of rows, in tiles of 256 rows with
-// an online softmax (scores in log2 units), and writes (o', max, sum) for its
-// chunk.  A second kernel merges the chunks of each (sequence, query head) in
-// chunk order (log-sum-exp) and applies the single inverse rotation.  No
-// atomics; the order of every sum is fixed.
+// query heads of one KV head over one chunk of rows with an online softmax
+// (scores in log2 units) and writes (o', max, sum) for its chunk: per wave
+// without the sparse-V gate, per 256-row tile with it (the gate compares each
+// row with its tile's maximum).  A second kernel merges the chunks of each
+// (sequence, query head) in chunk order (log-sum-exp) and applies the single
+// inverse rotation.  No atomics; the order of every sum is fixed.  With the
+// two-sided rotation S2 H S1, q' takes S2 after H and o' takes S2 before it.
 //
-// Centroid lookup: pairs of neighbouring indices (2*bits bits) address a
-// table of centroid pairs in LDS, one 8-byte read per two coordinates.
+// Centroid lookup: neighbouring indices address a table of centroid tuples in
+// LDS, one read per lookup: pairs (2*bits bits) in the per-tile kernel and for
+// 3/4-bit sides of the per-wave kernel, quadruples for its 2-bit sides.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>

@@ -8,11 +8,16 @@
 //   "TurboQuantEngine — Specification" -- 2.2 Memory contract (fp32 norm and
 //     packed indices per head row); 6 P1 follow-ups, W3 (encode only the new
 //     row each step).
+//   "CITATIONS" -- Two-sided Rademacher signs in WHT (a second sign vector
+//     after the butterfly); N(0, 1/d) codebook replacement.
 //
-// Work decomposition: each row is owned by P = d/32 lanes (32 coordinates per
-// lane, see tq_device.h); workgroups of 256 threads walk the rows with a grid
-// stride.  Nothing is shared between rows, so there are no atomics and the
-// result does not depend on the launch shape.
+// Work decomposition: the lane-slice kernels give each row P = d/32 lanes (32
+// coordinates per lane, see tq_device.h); the bf16 encode for d in {64, 128}
+// gives each row one lane (below).  Nothing is shared between rows, so there
+// are no atomics and the result does not depend on the launch shape.  A
+// head_dim that is not a power of two runs at the next one, its rows
+// zero-padded ("TurboQuant KV Cache Compression — Spec", Hadamard Transform
+// Detail).
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
