@@ -103,273 +103,6 @@ __device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *row, int off)
     }
 }
 
-template <int D, int BK, int BV, int G, bool GATE>
-__global__ __launch_bounds__(kBlock) void attn_partial_kernel(AttnParams p)
-{
-    constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
-    constexpr int P = D / CPL;            // lanes per row
-    constexpr int RPW = 64 / P;
-    constexpr int RPB = RPW * (kBlock / 64);
-    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
-    constexpr int NPK = 1 << (2 * BK), NPV = 1 << (2 * BV);
-    constexpr int RS = D + 4;
-    static_assert(kTile == kBlock, "one tile row per thread in the softmax step");
-    static_assert(kTile % RPB == 0, "tile covered by whole passes");
-    constexpr int NIT = kTile / RPB;            // row passes per tile
-    constexpr int CH = NIT < 8 ? NIT : 8;       // passes loaded together
-
-    __shared__ float2 tabK[NPK];
-    __shared__ float2 tabV[NPV];
-    __shared__ float qs[G][D];
-    __shared__ float sc[kTile][G];
-    __shared__ uint32_t keep[GATE ? kTile : 1];  // sparse V: row has a weight
-    __shared__ float red[kBlock / 64][G];
-    __shared__ float accs[kBlock / 64][G][D];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-
-    for (int i = tid; i < NPK; i += kBlock)
-        tabK[i] = make_float2(p.centK[i & ((1 << BK) - 1)], p.centK[i >> BK]);
-    for (int i = tid; i < NPV; i += kBlock)
-        tabV[i] = make_float2(p.centV[i & ((1 << BV) - 1)], p.centV[i >> BV]);
-
-    // q' = S2 H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV
-    // head (S2 = identity for the one-sided rotation)
-    if (wave == 0) {
-        constexpr int P2 = D / kCPL;
-        const int sub2 = lane % P2, r2 = lane / P2;
-        float v[kCPL];
-        const int h = g * G + (r2 < G ? r2 : 0);
-        if (sub2 * kCPL < p.d_in) {
-            load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kCPL; k++)
-                v[k] = 0.0f;  // the zero padding of a head_dim below D
-        }
-        apply_signs(v, p.signs[sub2]);
-        fwht_row<P2>(v, sub2);
-        apply_signs(v, p.signs2[sub2]);
-        if (r2 < G) {
-#pragma unroll
-            for (int k = 0; k < kCPL; k++)
-                qs[r2][sub2 * kCPL + k] = v[k] * p.qscale;
-        }
-    }
-    __syncthreads();
-
-    const int sub = lane % P, rig = lane / P;
-    float qr[G][CPL];
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int k = 0; k < CPL; k++)
-            qr[h][k] = qs[h][sub * CPL + k];
-
-    float acc[G][CPL];
-    float m_run[G], l_part[G];
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-        m_run[h] = -__builtin_huge_valf();
-        l_part[h] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < CPL; k++)
-            acc[h][k] = 0.0f;
-    }
-
-    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
-    const int t_begin = chunk * p.chunk_len;
-    const int t_end = min(p.T, t_begin + p.chunk_len);
-
-    for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        // ---- scores of the tile; each chunk's loads are all issued before
-        // its arithmetic so that several rows per lane are in flight
-#pragma unroll 1
-        for (int it0 = 0; it0 < NIT; it0 += CH) {
-            uint64_t kb[CH];
-            float kn[CH];
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
-                const int64_t row = rowbase + (t < t_end ? t : t_begin);
-                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
-                kn[c] = p.kn[row];
-            }
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int tl = (it0 + c) * RPB + wave * RPW + rig;
-                float s[G];
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    s[h] = 0.0f;
-#pragma unroll
-                for (int m = 0; m < CPL / 2; m++) {
-                    const float2 cc = tabK[(kb[c] >> (2 * BK * m)) & (NPK - 1)];
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        s[h] = fmaf(qr[h][2 * m], cc.x, s[h]);
-                        s[h] = fmaf(qr[h][2 * m + 1], cc.y, s[h]);
-                    }
-                }
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    s[h] = sum_across<P>(s[h]);
-                if (sub == 0) {
-                    const bool valid = t0 + tl < t_end;
-#pragma unroll
-                    for (int h = 0; h < G; h++)
-                        sc[tl][h] = valid ? s[h] * kn[c] : -__builtin_huge_valf();
-                }
-            }
-        }
-        __syncthreads();
-        // ---- running max, weights of the tile
-        float mx[G];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            mx[h] = wave_max(sc[tid][h]);
-        if (lane == 0) {
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                red[wave][h] = mx[h];
-        }
-        __syncthreads();
-        float fac[G];
-        bool any = false;
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            float mt = red[0][h];
-#pragma unroll
-            for (int w = 1; w < kBlock / 64; w++)
-                mt = fmaxf(mt, red[w][h]);
-            const float mnew = fmaxf(m_run[h], mt);
-            fac[h] = exp2f(m_run[h] - mnew);
-            m_run[h] = mnew;
-            const float s_t = sc[tid][h];
-            const float pr = exp2f(s_t - mnew);
-            l_part[h] = l_part[h] * fac[h] + pr;
-            if constexpr (GATE) {
-                // sparse V: the row's V counts only if exp(s - tile max) >
-                // threshold (tiles are aligned 256-slot blocks); it stays in
-                // the denominator
-                const float wv = s_t - mt > p.gate_log2 ? pr : 0.0f;
-                sc[tid][h] = wv;
-                any |= wv != 0.0f;
-            } else {
-                sc[tid][h] = pr;
-            }
-        }
-        if constexpr (GATE)
-            keep[tid] = any ? 1u : 0u;
-        __syncthreads();
-        // ---- V sum of the tile (rotated domain)
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int k = 0; k < CPL; k++)
-                acc[h][k] *= fac[h];
-#pragma unroll 1
-        for (int it0 = 0; it0 < NIT; it0 += CH) {
-            uint64_t vb[CH];
-            float vn[CH];
-            if constexpr (GATE) {
-#pragma unroll
-                for (int c = 0; c < CH; c++) {
-                    const int tl = (it0 + c) * RPB + wave * RPW + rig;
-                    // rows with no weight (gated by sparse V, or past the
-                    // context) are neither loaded nor decoded
-                    vb[c] = 0;
-                    vn[c] = 0.0f;
-                    if (keep[tl]) {
-                        const int64_t row = rowbase + t0 + tl;
-                        vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-                        vn[c] = p.vn[row];
-                    }
-                }
-            } else {
-                // every load issued at once, before any weight is read (rows
-                // past the context read a valid row and get weight 0)
-#pragma unroll
-                for (int c = 0; c < CH; c++) {
-                    const int t = t0 + (it0 + c) * RPB + wave * RPW + rig;
-                    const int64_t row = rowbase + (t < t_end ? t : t_begin);
-                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-                    vn[c] = t < t_end ? p.vn[row] : 0.0f;
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int tl = (it0 + c) * RPB + wave * RPW + rig;
-                float w[G];
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    w[h] = sc[tl][h] * vn[c];
-#pragma unroll
-                for (int m = 0; m < CPL / 2; m++) {
-                    const float2 cc = tabV[(vb[c] >> (2 * BV * m)) & (NPV - 1)];
-#pragma unroll
-                    for (int h = 0; h < G; h++) {
-                        acc[h][2 * m] = fmaf(w[h], cc.x, acc[h][2 * m]);
-                        acc[h][2 * m + 1] = fmaf(w[h], cc.y, acc[h][2 * m + 1]);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    }
-
-    // ---- reduce over the rows of the wave (lanes with equal `sub`)
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int k = 0; k < CPL; k++) {
-            float a = acc[h][k];
-            if constexpr (P <= 1) a += lane_xor_any<1>(a);
-            if constexpr (P <= 2) a += lane_xor_any<2>(a);
-            if constexpr (P <= 4) a += lane_xor_any<4>(a);
-            if constexpr (P <= 8) a += lane_xor_any<8>(a);
-            if constexpr (P <= 16) a += lane_xor_any<16>(a);
-            if constexpr (P <= 32) a += lane_xor_any<32>(a);
-            acc[h][k] = a;
-        }
-    if (rig == 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int k = 0; k < CPL; k++)
-                accs[wave][h][sub * CPL + k] = acc[h][k];
-    }
-    // sum of weights over the block
-#pragma unroll
-    for (int h = 0; h < G; h++)
-        l_part[h] = wave_sum(l_part[h]);
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            red[wave][h] = l_part[h];
-    }
-    __syncthreads();
-    float *rec0 = p.part + (((int64_t)b * p.Hq + g * G) * p.n_chunks + chunk) * RS;
-    const int64_t hstride = (int64_t)p.n_chunks * RS;
-    for (int i = tid; i < G * D; i += kBlock) {
-        const int h = i / D, j = i % D;
-        float o = accs[0][h][j];
-#pragma unroll
-        for (int w = 1; w < kBlock / 64; w++)
-            o += accs[w][h][j];
-        rec0[h * hstride + j] = o;
-    }
-    if (tid < G) {
-        float l = red[0][tid];
-#pragma unroll
-        for (int w = 1; w < kBlock / 64; w++)
-            l += red[w][tid];
-        rec0[tid * hstride + D] = m_run[tid];
-        rec0[tid * hstride + D + 1] = l;
-    }
-}
-
 // Centroid lookup width of the per-wave kernel: four neighbouring 2-bit
 // indices (one byte) address a 256-entry table of centroid quadruples; wider
 // indices go in pairs.  Either way one LDS read per lookup.
@@ -404,6 +137,147 @@ __device__ __forceinline__ void lookup(const float *tab, uint64_t bits, int m, f
     }
 }
 
+// The per-wave scan with the sparse-V gate.  Wave w takes the aligned
+// 256-row blocks w, w + 4, ... of the chunk (chunks start on block
+// boundaries), so the gate's reference, the block's largest score, is known
+// to the wave alone.  Per block: pass A scores every row into the wave's LDS
+// scores and takes the block maximum; pass B turns scores into weights, adds
+// every row's weight to the denominator, loads and decodes V only for rows
+// some head keeps (exp(score - block max) > threshold), and skips the
+// arithmetic of a row pass that no lane keeps.
+template <int D, int BK, int BV, int G, int CPL>
+__device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tabK,
+                                           const float *tabV, float (*scr)[G],
+                                           const float (&qr)[G][CPL], float (&acc)[G][CPL],
+                                           float (&m_run)[G], float (&l_part)[G],
+                                           int64_t rowbase, int t_begin, int t_end, int wave,
+                                           int sub, int rig)
+{
+    constexpr int P = D / CPL, RPW = 64 / P;
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
+    constexpr int NPASS = kTile / RPW;     // row passes per block
+    constexpr int CH = G >= 8 ? 4 : 8;     // row passes per step
+    static_assert(NPASS % CH == 0, "steps cover a block");
+    const int nblk = (t_end - t_begin + kTile - 1) / kTile;
+#pragma unroll 1
+    for (int blk = wave; blk < nblk; blk += kBlock / 64) {
+        const int bs = t_begin + blk * kTile;
+        // ---- pass A: scores of the block, and its maximum
+        float bm[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            bm[h] = -__builtin_huge_valf();
+#pragma unroll 1
+        for (int it0 = 0; it0 < NPASS; it0 += CH) {
+            uint64_t kb[CH];
+            float kn[CH];
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                const int t = bs + (it0 + c) * RPW + rig;
+                const int64_t row = rowbase + (t < t_end ? t : t_begin);
+                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
+                kn[c] = p.kn[row];
+            }
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                float s[G];
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    s[h] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < CPL / WK; m++) {
+                    float cc[WK];
+                    lookup<BK>(tabK, kb[c], m, cc);
+#pragma unroll
+                    for (int j = 0; j < WK; j++)
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+                            s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
+                }
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    s[h] = sum_across<P>(s[h]) * kn[c];
+                const bool valid = bs + (it0 + c) * RPW + rig < t_end;
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    s[h] = valid ? s[h] : -__builtin_huge_valf();
+                    bm[h] = fmaxf(bm[h], s[h]);
+                }
+                if (sub == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        scr[(it0 + c) * RPW + rig][h] = s[h];
+                }
+            }
+        }
+        float bmax[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            bmax[h] = wave_max(bm[h]);
+            if (bmax[h] > m_run[h]) {
+                const float fac = exp2f(m_run[h] - bmax[h]);  // 0 on the first block
+                l_part[h] *= fac;
+#pragma unroll
+                for (int k = 0; k < CPL; k++)
+                    acc[h][k] *= fac;
+                m_run[h] = bmax[h];
+            }
+        }
+        wave_lds_fence();  // the block's scores are in LDS
+        // ---- pass B: weights, the denominator, V of the kept rows
+#pragma unroll 1
+        for (int it0 = 0; it0 < NPASS; it0 += CH) {
+            float sc[CH][G];
+            bool kept[CH];
+            uint64_t vb[CH];
+            float vn[CH];
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                const int tl = (it0 + c) * RPW + rig;
+                kept[c] = false;
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    sc[c][h] = scr[tl][h];
+                    kept[c] |= sc[c][h] - bmax[h] > p.gate_log2;
+                }
+                vb[c] = 0;
+                vn[c] = 0.0f;
+                if (kept[c]) {
+                    const int64_t row = rowbase + bs + tl;
+                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+                    vn[c] = p.vn[row];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                float w[G];
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    const float pr = m_run[h] == -__builtin_huge_valf()
+                                         ? 0.0f
+                                         : __builtin_amdgcn_exp2f(sc[c][h] - m_run[h]);
+                    l_part[h] += pr;  // gated rows stay in the denominator
+                    w[h] = sc[c][h] - bmax[h] > p.gate_log2 ? pr * vn[c] : 0.0f;
+                }
+                if (__ballot(kept[c]) == 0)
+                    continue;  // no lane keeps its row of this pass
+#pragma unroll
+                for (int m = 0; m < CPL / WV; m++) {
+                    float cc[WV];
+                    lookup<BV>(tabV, vb[c], m, cc);
+#pragma unroll
+                    for (int j = 0; j < WV; j++)
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+                            acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
+                }
+            }
+        }
+        wave_lds_fence();  // every lane is done with the block's scores
+    }
+}
+
 // The same partial results without the sparse-V gate, with an online softmax
 // per wave instead of per tile: the weights of a row are only ever needed by
 // the wave that scored it, so each wave keeps its scores in registers, runs
@@ -411,7 +285,7 @@ __device__ __forceinline__ void lookup(const float *tab, uint64_t bits, int m, f
 // after each step of CH row passes.  No LDS traffic for scores and no
 // barrier inside the scan; the four waves' (o', max, sum) are merged once at
 // the end.  Rows of wave w: t_begin + it * RPB + w * RPW + (lane / P).
-template <int D, int BK, int BV, int G>
+template <int D, int BK, int BV, int G, bool GATE>
 __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 {
     constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
@@ -429,6 +303,8 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     __shared__ float red_m[kBlock / 64][G];
     __shared__ float red_l[kBlock / 64][G];
     __shared__ float accs[kBlock / 64][G][D];
+    // sparse V: the scores of the 256-row block a wave is working on
+    __shared__ float scw[GATE ? kBlock / 64 : 1][GATE ? kTile : 1][G];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -485,6 +361,10 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     const int t_end = min(p.T, t_begin + p.chunk_len);
     const int t_lane = t_begin + wave * RPW + rig;  // this lane's row in pass 0
 
+    if constexpr (GATE) {
+        gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
+                                 t_begin, t_end, wave, sub, rig);
+    } else {
 #pragma unroll 1
     for (int t0 = t_lane; t0 - rig - wave * RPW < t_end; t0 += CH * RPB) {
         // every K and V load of the step in flight before any arithmetic;
@@ -570,6 +450,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
                         acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
             }
         }
+    }
     }
 
     // ---- reduce over the rows of the wave (lanes with equal `sub`); every
@@ -724,38 +605,26 @@ Split split_for(int batch, int n_kv, int64_t ctx_len, int window)
 }
 
 template <int D, int BK, int BV, bool GATE>
-void launch_attn_gate(int G, dim3 grid, const AttnParams &p, hipStream_t st)
-{
-    dim3 block(kBlock);
-    switch (G) {
-    case 1: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 1, GATE>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_partial_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p); break;
-    }
-}
-
-template <int D, int BK, int BV>
 void launch_attn_wave(int G, dim3 grid, const AttnParams &p, hipStream_t st)
 {
     dim3 block(kBlock);
     switch (G) {
-    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1, GATE>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p); break;
     }
 }
 
-// with the sparse-V gate the per-tile kernel (the gate's reference maximum is
-// that of a 256-row tile); without it the per-wave kernel
+// the sparse-V gate is a separate instantiation: the kernel without it is the
+// one that runs when the threshold is 0
 template <int D, int BK, int BV>
 void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
 {
     if (p.gate_log2 > -__builtin_huge_valf())
-        launch_attn_gate<D, BK, BV, true>(G, grid, p, st);
+        launch_attn_wave<D, BK, BV, true>(G, grid, p, st);
     else
-        launch_attn_wave<D, BK, BV>(G, grid, p, st);
+        launch_attn_wave<D, BK, BV, false>(G, grid, p, st);
 }
 
 template <int D, int BK>
