@@ -312,3 +312,32 @@ def test_padded_head_dim(tq, orc, d, dtype, flags):
             check_decoded(xd.cpu().numpy(), orc.decode(gp, gn, d, bits, SEED, density=density,
                                                        two_sided=two))
     tally.check()
+
+
+@pytest.mark.parametrize("flags", [2, 3])
+def test_flags_persistent_loop_sampled(tq, orc, flags):
+    """K4/V2 bf16 d = 128 with the flags at 600k rows (several groups per wave
+    of the persistent encode, and a ragged last group), compared on sampled
+    rows."""
+    d, n = 128, 600_000 + 37
+    density = orc.GAUSS if flags & 1 else orc.BETA
+    k = kvgen.ar1_outliers((1, 1, n, d), 70 + flags, "cuda").reshape(n, d)
+    v = kvgen.ar1_outliers((1, 1, n, d), 80 + flags, "cuda").reshape(n, d)
+    kp, kn, vp, vn = tq.tq_encode(k, v, 4, 2, SEED, flags=flags)
+    torch.cuda.synchronize()
+    rows = np.sort(np.concatenate([np.random.default_rng(flags).choice(n - 64, 3000, replace=False),
+                                   np.arange(n - 64, n)]))
+    ridx = torch.from_numpy(rows).cuda()
+    tally = BandTally()
+    for x, bits, p, nm in ((k, 4, kp, kn), (v, 2, vp, vn)):
+        xs = x[ridx].float().cpu().numpy()
+        op, on, u = orc.encode(xs, d, bits, SEED, density=density, want_u=True,
+                               two_sided=bool(flags & 2))
+        _, bnd = orc.codebook_float(d, bits, density)
+        gp, gn = p[ridx].cpu().numpy(), nm[ridx].cpu().numpy()
+        check_norms(gn, on)
+        check_indices(gp, op, u, d, bits, bnd, tally=tally)
+        xd = tq.tq_decode(p, nm, d, bits, SEED, flags=flags)[ridx].cpu().numpy()
+        check_decoded(xd, orc.decode(gp, gn, d, bits, SEED, density=density,
+                                     two_sided=bool(flags & 2)))
+    tally.check()
