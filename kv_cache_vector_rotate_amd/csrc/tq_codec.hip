@@ -120,17 +120,97 @@ struct EncodeParams {
     uint32_t signs2[8];  // second diagonal (two-sided rotation), else zero
 };
 
-template <int D, typename T, int BITS>
+// Coalesced input for the lane-slice encode (rows of exactly D values): the
+// RPW rows of a wave's pass are contiguous, lane l loads 16-byte pieces
+// l + 64 q of them (whole cache lines per instruction), and the pass goes
+// through LDS into the lane-slice layout (slices of SB bytes at a skewed
+// stride SS, against bank conflicts on the slice reads).
+template <int D, typename T>
+struct PassIO {
+    static constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW;
+    static constexpr int SB = kCPL * (int)sizeof(T);  // bytes of one lane's slice
+    static constexpr int SS = SB + 16;                // LDS slice stride
+    static constexpr int RS = P * SS;                 // LDS row stride
+    static constexpr int RB = D * (int)sizeof(T);     // input bytes per row
+    static constexpr int NQ = RPW * RB / 1024;        // 16-byte pieces per lane
+    static constexpr int LDS = RPW * RS;              // LDS bytes per wave
+};
+
+template <int D, typename T>
+__device__ __forceinline__ void load_pass(const uint8_t *src, int64_t row0, int64_t n_rows,
+                                          int lane, u32x4 (&ch)[PassIO<D, T>::NQ])
+{
+    using IO = PassIO<D, T>;
+    const int64_t avail = (n_rows - row0) * IO::RB;  // bytes of real rows from row0 on
+    const u32x4 *g = reinterpret_cast<const u32x4 *>(src + row0 * IO::RB) + lane;
+    if (avail >= (int64_t)IO::RPW * IO::RB) {  // a whole pass (uniform branch)
+#pragma unroll
+        for (int q = 0; q < IO::NQ; q++)
+            ch[q] = __builtin_nontemporal_load(g + 64 * q);
+    } else {
+#pragma unroll
+        for (int q = 0; q < IO::NQ; q++)
+            ch[q] = 16 * (int64_t)(lane + 64 * q) < avail ? __builtin_nontemporal_load(g + 64 * q)
+                                                          : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// The pass from registers into this wave's LDS, then this lane's slice back.
+template <int D, typename T>
+__device__ __forceinline__ void stage_pass(const u32x4 (&ch)[PassIO<D, T>::NQ], uint8_t *stg,
+                                           int lane, int rig, int sub, RawSlice<T> &raw)
+{
+    using IO = PassIO<D, T>;
+    wave_lds_fence();  // every lane is done with the previous pass
+#pragma unroll
+    for (int q = 0; q < IO::NQ; q++) {
+        const int o = 16 * (lane + 64 * q);
+        const int row = o / IO::RB, w = o % IO::RB;
+        *reinterpret_cast<u32x4 *>(stg + row * IO::RS + (w / IO::SB) * IO::SS + w % IO::SB) = ch[q];
+    }
+    wave_lds_fence();
+    using V = typename std::remove_reference<decltype(raw.q[0])>::type;
+    const uint8_t *mine = stg + rig * IO::RS + sub * IO::SS;
+#pragma unroll
+    for (int j = 0; j < (int)(sizeof(raw.q) / sizeof(raw.q[0])); j++)
+        raw.q[j] = *reinterpret_cast<const V *>(mine + 16 * j);
+}
+
+template <int D, typename T, int BITS, bool PAD>
 __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t n_rows,
                                                    int d_in, const SignMasks<T> &sm,
-                                                   uint32_t s2, uint32_t key)
+                                                   uint32_t s2, uint32_t key, uint8_t *stg)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW, RPB = Shape<D>::RPB;
     constexpr int RB = D * BITS / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int sub = lane % P, rig = lane / P;
-    const T *src = static_cast<const T *>(s.src);
     const int64_t stride = (int64_t)gridDim.x * RPB;
+    if constexpr (!PAD) {
+        using IO = PassIO<D, T>;
+        const uint8_t *src = static_cast<const uint8_t *>(s.src);
+        int64_t row0 = (int64_t)blockIdx.x * RPB + wave * RPW;  // this wave's pass
+        u32x4 ch[IO::NQ];
+        load_pass<D, T>(src, row0, n_rows, lane, ch);
+        for (int64_t base = (int64_t)blockIdx.x * RPB; base < n_rows; base += stride) {
+            // the next pass's loads are issued before this one is transformed
+            u32x4 nx[IO::NQ];
+            load_pass<D, T>(src, row0 + stride, n_rows, lane, nx);
+            RawSlice<T> raw;
+            stage_pass<D, T>(ch, stg, lane, rig, sub, raw);
+            const int64_t row = row0 + rig;
+            const bool valid = row < n_rows;
+            const int64_t r = valid ? row : 0;
+            encode_row<D, BITS, T>(raw, valid, sub, sm, s2, key, s.packed + r * RB, s.norms + r);
+#pragma unroll
+            for (int q = 0; q < IO::NQ; q++)
+                ch[q] = nx[q];
+            row0 += stride;
+        }
+        return;
+    }
+    // rows of d_in < D values (padded): each lane loads its own slice
+    const T *src = static_cast<const T *>(s.src);
     // a head_dim below D (padded to D) leaves whole slices of zeros
     const bool live = sub * kCPL < d_in;
     int64_t row = (int64_t)blockIdx.x * RPB + wave * RPW + rig;
@@ -156,10 +236,12 @@ __device__ __forceinline__ void encode_contig_loop(const EncodeSide &s, int64_t 
 }
 
 // blockIdx.y selects the side (0 = first non-NULL side, 1 = second)
-template <int D, typename T>
+template <int D, typename T, bool PAD>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
 {
     __shared__ float2 lut[kLutBins];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[PAD ? 16 : (kBlock / 64) * PassIO<D, T>::LDS];
+    uint8_t *stg = stage + (PAD ? 0 : (threadIdx.x >> 6) * PassIO<D, T>::LDS);
     const EncodeSide &s = p.side[blockIdx.y];
     build_lut(lut, s.code.bnd, (1 << s.code.bits) - 1);
     __syncthreads();
@@ -168,9 +250,9 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     const uint32_t s2 = p.signs2[sub];
     const uint32_t key = lut_key(lut);
     switch (s.code.bits) {
-    case 2: encode_contig_loop<D, T, 2>(s, p.n_rows, p.d_in, sm, s2, key); break;
-    case 3: encode_contig_loop<D, T, 3>(s, p.n_rows, p.d_in, sm, s2, key); break;
-    default: encode_contig_loop<D, T, 4>(s, p.n_rows, p.d_in, sm, s2, key); break;
+    case 2: encode_contig_loop<D, T, 2, PAD>(s, p.n_rows, p.d_in, sm, s2, key, stg); break;
+    case 3: encode_contig_loop<D, T, 3, PAD>(s, p.n_rows, p.d_in, sm, s2, key, stg); break;
+    default: encode_contig_loop<D, T, 4, PAD>(s, p.n_rows, p.d_in, sm, s2, key, stg); break;
     }
 }
 
@@ -948,15 +1030,25 @@ void launch_encode_lane_d(const EncodeLaneParams &q, int b0, int b1, hipStream_t
     }
 }
 
-template <typename T>
-void launch_encode(int d, const EncodeParams &p, int sides, hipStream_t st)
+template <typename T, bool PAD>
+void launch_encode_pad(int d, const EncodeParams &p, int sides, hipStream_t st)
 {
     dim3 block(kBlock);
     switch (d) {
-    case 64: hipLaunchKernelGGL((encode_kernel<64, T>), dim3(grid_for(p.n_rows, Shape<64>::RPB), sides), block, 0, st, p); break;
-    case 128: hipLaunchKernelGGL((encode_kernel<128, T>), dim3(grid_for(p.n_rows, Shape<128>::RPB), sides), block, 0, st, p); break;
-    default: hipLaunchKernelGGL((encode_kernel<256, T>), dim3(grid_for(p.n_rows, Shape<256>::RPB), sides), block, 0, st, p); break;
+    case 64: hipLaunchKernelGGL((encode_kernel<64, T, PAD>), dim3(grid_for(p.n_rows, Shape<64>::RPB), sides), block, 0, st, p); break;
+    case 128: hipLaunchKernelGGL((encode_kernel<128, T, PAD>), dim3(grid_for(p.n_rows, Shape<128>::RPB), sides), block, 0, st, p); break;
+    default: hipLaunchKernelGGL((encode_kernel<256, T, PAD>), dim3(grid_for(p.n_rows, Shape<256>::RPB), sides), block, 0, st, p); break;
     }
+}
+
+// rows of exactly d values take coalesced loads; padded ones per-lane loads
+template <typename T>
+void launch_encode(int d, const EncodeParams &p, int sides, hipStream_t st)
+{
+    if (p.d_in == d)
+        launch_encode_pad<T, false>(d, p, sides, st);
+    else
+        launch_encode_pad<T, true>(d, p, sides, st);
 }
 
 template <typename T>
