@@ -526,45 +526,79 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     }
 }
 
-// Merge the chunks of one (sequence, query head) and rotate back.  One wave
-// per (sequence, query head); the first D/32 lanes hold the row.
+// Merge the chunks of one (sequence, query head) and rotate back.  One
+// workgroup per (sequence, query head): thread t takes coordinates
+// 4 (t % (D/4)) .. +3 of the chunks c = t / (D/4), + NG, + 2 NG, ... (NG
+// groups of chunks in parallel, every record read whole-line), the groups'
+// sums meet in LDS in a fixed order, and the first wave applies the single
+// inverse rotation (its first D/32 lanes hold the row).
+constexpr int kCombineThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnParams p)
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p)
 {
-    constexpr int P = D / kCPL, RS = D + 4;
-    const int lane = threadIdx.x, sub = lane % P;
+    constexpr int P = D / kCPL, RS = D + 4, Q = D / 4, NG = kCombineThreads / Q;
+    __shared__ __attribute__((aligned(16))) float part[NG][D];
+    __shared__ float lsum[NG];
+    __shared__ float wmax[kCombineThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j4 = tid % Q, grp = tid / Q;
     const int64_t bh = blockIdx.x;
     const float *rec = p.part + bh * p.n_chunks * RS;
+    // the largest chunk maximum
     float M = -__builtin_huge_valf();
-    for (int c = 0; c < p.n_chunks; c++)
+    for (int c = tid; c < p.n_chunks; c += kCombineThreads)
         M = fmaxf(M, rec[c * RS + D]);
-    float o[kCPL];
+    M = max_across<32>(M);
+    M = fmaxf(M, __shfl_xor(M, 32));
+    if (lane == 0)
+        wmax[wave] = M;
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kCPL; k++)
-        o[k] = 0.0f;
+    for (int w = 0; w < kCombineThreads / 64; w++)
+        M = fmaxf(M, wmax[w]);
+    // this thread's group of chunks
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float L = 0.0f;
-    for (int c = 0; c < p.n_chunks; c++) {
+    for (int c = grp; c < p.n_chunks; c += NG) {
         const float w = exp2f(rec[c * RS + D] - M);
-        L = fmaf(w, rec[c * RS + D + 1], L);
-        const float4 *src = reinterpret_cast<const float4 *>(rec + c * RS + sub * kCPL);
-#pragma unroll
-        for (int j = 0; j < kCPL / 4; j++) {
-            const float4 t = src[j];
-            o[4 * j] = fmaf(w, t.x, o[4 * j]);
-            o[4 * j + 1] = fmaf(w, t.y, o[4 * j + 1]);
-            o[4 * j + 2] = fmaf(w, t.z, o[4 * j + 2]);
-            o[4 * j + 3] = fmaf(w, t.w, o[4 * j + 3]);
-        }
+        const float4 t = reinterpret_cast<const float4 *>(rec + c * RS)[j4];
+        o.x = fmaf(w, t.x, o.x);
+        o.y = fmaf(w, t.y, o.y);
+        o.z = fmaf(w, t.z, o.z);
+        o.w = fmaf(w, t.w, o.w);
+        if (j4 == 0)
+            L = fmaf(w, rec[c * RS + D + 1], L);
     }
-    apply_signs(o, p.signs2[sub]);
-    fwht_row<P>(o, sub);
-    const float sc = 1.0f / (L * sqrtf((float)D));
+    reinterpret_cast<float4 *>(part[grp])[j4] = o;
+    if (j4 == 0)
+        lsum[grp] = L;
+    __syncthreads();
+    if (wave == 0) {
+        const int sub = lane % P;
+        float v[kCPL];
 #pragma unroll
-    for (int k = 0; k < kCPL; k++)
-        o[k] *= sc;
-    apply_signs(o, p.signs[sub]);
-    if (lane < P && sub * kCPL < p.d_in)  // padded coordinates are dropped
-        store_slice(p.out + bh * p.d_in + sub * kCPL, o);
+        for (int k = 0; k < kCPL; k++) {
+            float a = 0.0f;
+#pragma unroll
+            for (int g2 = 0; g2 < NG; g2++)
+                a += part[g2][sub * kCPL + k];
+            v[k] = a;
+        }
+        float Lt = 0.0f;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; g2++)
+            Lt += lsum[g2];
+        apply_signs(v, p.signs2[sub]);
+        fwht_row<P>(v, sub);
+        const float sc = 1.0f / (Lt * sqrtf((float)D));
+#pragma unroll
+        for (int k = 0; k < kCPL; k++)
+            v[k] *= sc;
+        apply_signs(v, p.signs[sub]);
+        if (lane < P && sub * kCPL < p.d_in)  // padded coordinates are dropped
+            store_slice(p.out + bh * p.d_in + sub * kCPL, v);
+    }
 }
 
 int check_cache(const tq_cache_desc *c, int layer, const char *fn)
@@ -645,7 +679,8 @@ void launch_attn_d(int BK, int BV, int G, dim3 grid, const AttnParams &p, hipStr
     case 3: launch_attn_bv<D, 3>(BV, G, grid, p, st); break;
     default: launch_attn_bv<D, 4>(BV, G, grid, p, st); break;
     }
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(grid.z * p.Hq)), dim3(64), 0, st, p);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(grid.z * p.Hq)),
+                       dim3(kCombineThreads), 0, st, p);
 }
 
 }  // namespace
