@@ -278,6 +278,176 @@ __device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tab
     }
 }
 
+// Layout of the exchange scan: P lanes share a row (CPL coordinates each), a
+// step covers one 256-row tile in P row passes, and lane `sub` of a row group
+// owns the softmax of the group's row in pass `sub`.  It takes this path when
+// the partial scores of a step (P x G per row) fit a small LDS block.
+template <int D, int G>
+struct Xch {
+    static constexpr int CPL = G >= 8 ? 8 : 16;
+    static constexpr int P = D / CPL;
+    static constexpr int RPW = 64 / P;
+    static constexpr int RPB = RPW * (kBlock / 64);
+    static constexpr bool ON = P * G <= 32;
+    static constexpr int XS = P * G + 4;  // floats per (row group, pass): P partials x G heads, padded
+    static constexpr int XW = P * G + 4;  // floats per row group of weights, padded
+    static constexpr int FLOATS = RPW * P * XS + RPW * XW;  // per wave
+};
+
+// One tile of the exchange scan.  The lanes of a row group first score their
+// coordinate slices of the group's P rows and write the partial sums to LDS;
+// lane `sub` then adds the P partials of row `sub` (in lane order), takes the
+// row's G scores and the group's running maximum, and forms the row's weights,
+// which go back through LDS so that every lane of the group can accumulate
+// the P rows' V slices.  The exponentials are taken once per (row, head)
+// rather than on each of the P lanes holding the row.  The running maximum is
+// per row group (the groups are merged after the scan).  TAIL: the tile runs
+// past the context; those rows read a valid row and are masked.
+template <int D, int BK, int BV, int G, bool TAIL>
+__device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, float *xs,
+                                         float *xw, const float (&qr)[G][Xch<D, G>::CPL],
+                                         float (&acc)[G][Xch<D, G>::CPL], float (&m_run)[G],
+                                         float (&l_part)[G], const uint8_t *kbase,
+                                         const uint8_t *vbase, const float *knb,
+                                         const float *vnb, int tw, int t_begin, int t_end,
+                                         int sub, int rig)
+{
+    using X = Xch<D, G>;
+    constexpr int CPL = X::CPL, P = X::P, RPB = X::RPB;
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int SBK = CPL * BK / 8, SBV = CPL * BV / 8;
+    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
+    uint64_t kb[P], vb[P];
+#pragma unroll
+    for (int c = 0; c < P; c++) {
+        int t = tw + c * RPB;
+        if constexpr (TAIL)
+            t = t < t_end ? t : t_begin;
+        kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * SBK);
+        vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)t * RBV, sub * SBV);
+    }
+    int to = tw + sub * RPB;  // the row this lane takes the softmax of
+    const bool valid = to < t_end;
+    if constexpr (TAIL)
+        to = valid ? to : t_begin;
+    const float kn = knb[to], vn = vnb[to];
+
+    // partial scores of the P rows over this lane's slice
+    float *xrow = xs + rig * P * X::XS;
+#pragma unroll
+    for (int c = 0; c < P; c++) {
+        float s[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            s[h] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < CPL / WK; m++) {
+            float cc[WK];
+            lookup<BK>(tabK, kb[c], m, cc);
+#pragma unroll
+            for (int j = 0; j < WK; j++)
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
+        }
+        float *dst = xrow + c * X::XS + sub * G;
+        if constexpr (G == 4) {
+            *reinterpret_cast<float4 *>(dst) = make_float4(s[0], s[1], s[2], s[3]);
+        } else if constexpr (G == 2) {
+            *reinterpret_cast<float2 *>(dst) = make_float2(s[0], s[1]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                dst[h] = s[h];
+        }
+    }
+    wave_lds_fence();
+    // this lane's row: the P partials in lane order
+    float sc[G];
+    {
+        const float *src = xrow + sub * X::XS;
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            sc[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < P; j++) {
+            if constexpr (G == 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(src + j * G);
+                sc[0] += v.x; sc[1] += v.y; sc[2] += v.z; sc[3] += v.w;
+            } else if constexpr (G == 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(src + j * G);
+                sc[0] += v.x; sc[1] += v.y;
+            } else {
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    sc[h] += src[j * G + h];
+            }
+        }
+    }
+    float w[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        sc[h] *= kn;
+        if constexpr (TAIL)
+            sc[h] = valid ? sc[h] : -__builtin_huge_valf();
+        const float mx = max_across<P>(sc[h]);  // the row group's maximum
+        if (mx > m_run[h]) {
+            const float fac = exp2f(m_run[h] - mx);  // 0 on the group's first valid tile
+            l_part[h] *= fac;
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                acc[h][k] *= fac;
+            m_run[h] = mx;
+        }
+        float pr = __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
+        if constexpr (TAIL)
+            pr = m_run[h] == -__builtin_huge_valf() ? 0.0f : pr;  // no valid row yet
+        l_part[h] += pr;
+        w[h] = pr * vn;
+    }
+    float *wrow = xw + rig * X::XW;
+    {
+        float *dst = wrow + sub * G;
+        if constexpr (G == 4) {
+            *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
+        } else if constexpr (G == 2) {
+            *reinterpret_cast<float2 *>(dst) = make_float2(w[0], w[1]);
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                dst[h] = w[h];
+        }
+    }
+    wave_lds_fence();
+    // V slices of the P rows, weighted (rotated domain)
+#pragma unroll
+    for (int c = 0; c < P; c++) {
+        float wc[G];
+        if constexpr (G == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(wrow + c * G);
+            wc[0] = v.x; wc[1] = v.y; wc[2] = v.z; wc[3] = v.w;
+        } else if constexpr (G == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(wrow + c * G);
+            wc[0] = v.x; wc[1] = v.y;
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                wc[h] = wrow[c * G + h];
+        }
+#pragma unroll
+        for (int m = 0; m < CPL / WV; m++) {
+            float cc[WV];
+            lookup<BV>(tabV, vb[c], m, cc);
+#pragma unroll
+            for (int j = 0; j < WV; j++)
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    acc[h][WV * m + j] = fmaf(wc[h], cc[j], acc[h][WV * m + j]);
+        }
+    }
+    wave_lds_fence();  // every lane is done with this tile's LDS blocks
+}
+
 // The same partial results without the sparse-V gate, with an online softmax
 // per wave instead of per tile: the weights of a row are only ever needed by
 // the wave that scored it, so each wave keeps its scores in registers, runs
@@ -302,7 +472,11 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     __shared__ float qs[G][D];
     __shared__ float red_m[kBlock / 64][G];
     __shared__ float red_l[kBlock / 64][G];
-    __shared__ float accs[kBlock / 64][G][D];
+    // exchange scan: each wave's LDS blocks of partial scores and weights;
+    // after the scan the same wave-owned region holds the wave's o' (accs)
+    constexpr bool XON = !GATE && Xch<D, G>::ON;
+    constexpr int AST = XON && Xch<D, G>::FLOATS > G * D ? Xch<D, G>::FLOATS : G * D;
+    __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
     // sparse V: the scores of the 256-row block a wave is working on
     __shared__ float scw[GATE ? kBlock / 64 : 1][GATE ? kTile : 1][G];
 
@@ -364,6 +538,37 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     if constexpr (GATE) {
         gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
                                  t_begin, t_end, wave, sub, rig);
+    } else if constexpr (XON) {
+        using X = Xch<D, G>;
+        float *xs = accs + wave * AST;
+        float *xw = xs + X::RPW * X::P * X::XS;
+        const uint8_t *kbase = p.kp + rowbase * RBK;
+        const uint8_t *vbase = p.vp + rowbase * RBV;
+        const float *knb = p.kn + rowbase, *vnb = p.vn + rowbase;
+        // tiles of 256 rows (chunks start on tile boundaries); the last one
+        // may run past the context
+        int t0 = t_begin;
+#pragma unroll 1
+        for (; t0 + kTile <= t_end; t0 += kTile)
+            xch_step<D, BK, BV, G, false>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
+                                          vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
+                                          t_end, sub, rig);
+        if (t0 < t_end)
+            xch_step<D, BK, BV, G, true>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
+                                         vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
+                                         t_end, sub, rig);
+        // bring the row groups to the wave's maximum; each lane's sum covers
+        // its own rows, so the sums add within the group first
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float M = wave_max(m_run[h]);
+            const float f = m_run[h] == -__builtin_huge_valf() ? 0.0f : exp2f(m_run[h] - M);
+            l_part[h] = sum_across<P>(l_part[h] * f);
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                acc[h][k] *= f;
+            m_run[h] = M;
+        }
     } else {
 #pragma unroll 1
     for (int t0 = t_lane; t0 - rig - wave * RPW < t_end; t0 += CH * RPB) {
@@ -483,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
         for (int h = 0; h < G; h++)
 #pragma unroll
             for (int k = 0; k < CPL; k++)
-                accs[wave][h][sub * CPL + k] = acc[h][k];
+                accs[wave * AST + h * D + sub * CPL + k] = acc[h][k];
     }
     if (lane == 0) {
 #pragma unroll
@@ -506,7 +711,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 #pragma unroll
         for (int w = 0; w < kBlock / 64; w++) {
             const float mw = red_m[w][h];
-            o += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * accs[w][h][j];
+            o += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * accs[w * AST + h * D + j];
         }
         rec0[h * hstride + j] = o;
     }

@@ -57,8 +57,10 @@ def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
 
 
 @pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 2, 1), (256, 4, 4, 2),
-                                       (128, 2, 3, 8), (256, 3, 2, 8), (64, 4, 4, 2)])
-@pytest.mark.parametrize("T", [1, 7, 300, 1100])
+                                       (128, 2, 3, 8), (256, 3, 2, 8), (64, 4, 4, 2),
+                                       (128, 3, 4, 1), (128, 4, 2, 2), (64, 2, 2, 4),
+                                       (256, 2, 3, 1), (256, 4, 2, 4)])
+@pytest.mark.parametrize("T", [1, 7, 256, 300, 1100])
 def test_attention_small(tq, orc, d, bk, bv, G, T):
     B, Hkv = 2, 2
     Hq = Hkv * G
@@ -86,6 +88,21 @@ def test_attention_ring_window_and_scale(tq, orc):
         check_attention(o[0, h], ref[h])
     # the softmax is peaked: outputs are O(1), the bound is still met
     assert max(np.abs(ref[h]).max() for h in ref) > 0.5
+
+
+@pytest.mark.parametrize("d,G", [(64, 4), (128, 1), (128, 4), (256, 2)])
+def test_attention_peaked_row_groups(tq, orc, d, G):
+    """Keys x 8 and queries x 2 (a peaked softmax whose largest scores sit in
+    different rows of each tile), a context with a ragged last tile."""
+    B, Hkv, T = 2, 2, 1100
+    cache = tq.TQCache(1, B, Hkv, T, d, 4, 2, SEED)
+    _fill(tq, cache, 0, 61 + d + G, kscale=8.0)
+    q = (kvgen.normal((B, Hkv * G, d), 62 + G, "cuda") * 2.0).to(torch.bfloat16)
+    o = tq.tq_attn_decode(cache, 0, q, T).cpu().numpy()
+    for b in range(B):
+        ref = _oracle(orc, cache, 0, q, b, range(Hkv * G), T, 1 / math.sqrt(d))
+        for h in range(Hkv * G):
+            check_attention(o[b, h], ref[h])
 
 
 def test_attention_determinism(tq):
