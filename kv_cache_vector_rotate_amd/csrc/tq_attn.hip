@@ -281,14 +281,17 @@ __device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tab
 // Layout of the exchange scan: P lanes share a row (CPL coordinates each), a
 // step covers one 256-row tile in P row passes, and lane `sub` of a row group
 // owns the softmax of the group's row in pass `sub`.  It takes this path when
-// the partial scores of a step (P x G per row) fit a small LDS block.
+// the partial scores of a step (P x G per row) fit a small LDS block and there
+// are at least two query heads per KV head: with one, the per-lane softmax it
+// removes is too small to pay for the two LDS round trips per tile (measured
+// slower at head_dim 64, 128 and 256 with long contexts).
 template <int D, int G>
 struct Xch {
     static constexpr int CPL = G >= 8 ? 8 : 16;
     static constexpr int P = D / CPL;
     static constexpr int RPW = 64 / P;
     static constexpr int RPB = RPW * (kBlock / 64);
-    static constexpr bool ON = P * G <= 32;
+    static constexpr bool ON = P * G <= 32 && G >= 2;
     static constexpr int XS = P * G + 4;  // floats per (row group, pass): P partials x G heads, padded
     static constexpr int XW = P * G + 4;  // floats per row group of weights, padded
     static constexpr int FLOATS = RPW * P * XS + RPW * XW;  // per wave
