@@ -50,6 +50,7 @@ struct AttnParams {
     float *part;              // [B][Hq][n_chunks][D + 4]: o'[D], max, sum
     float *out;               // [B][Hq][D]
     int Hq, Hkv, window, T, n_chunks, chunk_len;
+    int gsplit;               // workgroups per KV head, each taking G of its query heads
     int d_in;                 // head_dim of q and out (<= D; padded to D inside)
     float qscale;             // scale * log2(e) / sqrt(D)
     float gate_log2;          // sparse-V gate: log2(threshold), -inf when off
@@ -484,7 +485,9 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     __shared__ float scw[GATE ? kBlock / 64 : 1][GATE ? kTile : 1][G];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    const int g = blockIdx.y / p.gsplit;  // KV head
+    const int h0 = blockIdx.y * G;        // first of this workgroup's G query heads
 
     fill_lookup<BK>(tabK, p.centK);
     fill_lookup<BV>(tabV, p.centV);
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
         constexpr int P2 = D / kCPL;
         const int sub2 = lane % P2, r2 = lane / P2;
         float v[kCPL];
-        const int h = g * G + (r2 < G ? r2 : 0);
+        const int h = h0 + (r2 < G ? r2 : 0);
         if (sub2 * kCPL < p.d_in) {
             load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
         } else {
@@ -702,7 +705,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     }
     __syncthreads();
     // ---- merge the waves (log-sum-exp) and write this chunk's record
-    float *rec0 = p.part + (((int64_t)b * p.Hq + g * G) * p.n_chunks + chunk) * RS;
+    float *rec0 = p.part + (((int64_t)b * p.Hq + h0) * p.n_chunks + chunk) * RS;
     const int64_t hstride = (int64_t)p.n_chunks * RS;
     for (int i = tid; i < G * D; i += kBlock) {
         const int h = i / D, j = i % D;
@@ -847,14 +850,26 @@ Split split_for(int batch, int n_kv, int64_t ctx_len, int window)
 }
 
 template <int D, int BK, int BV, bool GATE>
-void launch_attn_wave(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+void launch_attn_wave(int G, dim3 grid, AttnParams p, hipStream_t st)
 {
     dim3 block(kBlock);
+    p.gsplit = 1;
     switch (G) {
     case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1, GATE>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
     case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p); break;
+    default:
+        if constexpr (!GATE && Xch<D, 4>::ON && !Xch<D, 8>::ON) {
+            // eight query heads per KV head: two workgroups of four each (the
+            // exchange scan, which needs more LDS than a workgroup of eight
+            // could have); each reads the KV head's rows
+            p.gsplit = 2;
+            grid.y *= 2;
+            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p);
+        } else {
+            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p);
+        }
+        break;
     }
 }
 
@@ -972,6 +987,7 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     p.T = s.T;
     p.n_chunks = s.n_chunks;
     p.chunk_len = s.chunk_len;
+    p.gsplit = 1;
     p.d_in = d;
     // the default scale is 1/sqrt(head_dim); the rotation's 1/sqrt is of the
     // padded length
