@@ -296,7 +296,104 @@ struct Xch {
     static constexpr int XS = P * G + 4;  // floats per (row group, pass): P partials x G heads, padded
     static constexpr int XW = P * G + 4;  // floats per row group of weights, padded
     static constexpr int FLOATS = RPW * P * XS + RPW * XW;  // per wave
+    // + a second weight slot and a 256-row block's scores
+    static constexpr int GATED_FLOATS = FLOATS + RPW * XW + 4 * 64 * (G + 1);
 };
+
+// G consecutive floats of LDS, as one access where the width allows
+template <int G>
+__device__ __forceinline__ void lds_put(float *dst, const float (&v)[G])
+{
+    if constexpr (G == 4) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (G == 2) {
+        *reinterpret_cast<float2 *>(dst) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            dst[h] = v[h];
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void lds_get(const float *src, float (&v)[G])
+{
+    if constexpr (G == 4) {
+        const float4 t = *reinterpret_cast<const float4 *>(src);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else if constexpr (G == 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(src);
+        v[0] = t.x; v[1] = t.y;
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            v[h] = src[h];
+    }
+}
+
+// Exchange scan, first half: the partial scores of the P rows of this lane's
+// row group over its coordinate slice, into the group's LDS block (`xrow`,
+// pass-major), then this lane's row's G scores as the P partials added in
+// lane order.
+template <int D, int BK, int G>
+__device__ __forceinline__ void xch_scores(const float *tabK, float *xrow,
+                                           const float (&qr)[G][Xch<D, G>::CPL],
+                                           const uint64_t (&kb)[Xch<D, G>::P], int sub,
+                                           float (&sc)[G])
+{
+    using X = Xch<D, G>;
+    constexpr int CPL = X::CPL, P = X::P, WK = Lookup<BK>::W;
+#pragma unroll
+    for (int c = 0; c < P; c++) {
+        float s[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            s[h] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < CPL / WK; m++) {
+            float cc[WK];
+            lookup<BK>(tabK, kb[c], m, cc);
+#pragma unroll
+            for (int j = 0; j < WK; j++)
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
+        }
+        lds_put<G>(xrow + c * X::XS + sub * G, s);
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int h = 0; h < G; h++)
+        sc[h] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        float v[G];
+        lds_get<G>(xrow + sub * X::XS + j * G, v);
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            sc[h] += v[h];
+    }
+}
+
+// Exchange scan, second half: the weighted V slice of one row pass (rotated
+// domain) added to this lane's accumulators
+template <int D, int BV, int G>
+__device__ __forceinline__ void xch_accumulate(const float *tabV, uint64_t vbits,
+                                               const float (&wc)[G],
+                                               float (&acc)[G][Xch<D, G>::CPL])
+{
+    constexpr int CPL = Xch<D, G>::CPL, WV = Lookup<BV>::W;
+#pragma unroll
+    for (int m = 0; m < CPL / WV; m++) {
+        float cc[WV];
+        lookup<BV>(tabV, vbits, m, cc);
+#pragma unroll
+        for (int j = 0; j < WV; j++)
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                acc[h][WV * m + j] = fmaf(wc[h], cc[j], acc[h][WV * m + j]);
+    }
+}
 
 // One tile of the exchange scan.  The lanes of a row group first score their
 // coordinate slices of the group's P rows and write the partial sums to LDS;
@@ -320,7 +417,6 @@ __device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, f
     constexpr int CPL = X::CPL, P = X::P, RPB = X::RPB;
     constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
     constexpr int SBK = CPL * BK / 8, SBV = CPL * BV / 8;
-    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
     uint64_t kb[P], vb[P];
 #pragma unroll
     for (int c = 0; c < P; c++) {
@@ -336,58 +432,9 @@ __device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, f
         to = valid ? to : t_begin;
     const float kn = knb[to], vn = vnb[to];
 
-    // partial scores of the P rows over this lane's slice
     float *xrow = xs + rig * P * X::XS;
-#pragma unroll
-    for (int c = 0; c < P; c++) {
-        float s[G];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            s[h] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < CPL / WK; m++) {
-            float cc[WK];
-            lookup<BK>(tabK, kb[c], m, cc);
-#pragma unroll
-            for (int j = 0; j < WK; j++)
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
-        }
-        float *dst = xrow + c * X::XS + sub * G;
-        if constexpr (G == 4) {
-            *reinterpret_cast<float4 *>(dst) = make_float4(s[0], s[1], s[2], s[3]);
-        } else if constexpr (G == 2) {
-            *reinterpret_cast<float2 *>(dst) = make_float2(s[0], s[1]);
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                dst[h] = s[h];
-        }
-    }
-    wave_lds_fence();
-    // this lane's row: the P partials in lane order
     float sc[G];
-    {
-        const float *src = xrow + sub * X::XS;
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            sc[h] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < P; j++) {
-            if constexpr (G == 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(src + j * G);
-                sc[0] += v.x; sc[1] += v.y; sc[2] += v.z; sc[3] += v.w;
-            } else if constexpr (G == 2) {
-                const float2 v = *reinterpret_cast<const float2 *>(src + j * G);
-                sc[0] += v.x; sc[1] += v.y;
-            } else {
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    sc[h] += src[j * G + h];
-            }
-        }
-    }
+    xch_scores<D, BK, G>(tabK, xrow, qr, kb, sub, sc);
     float w[G];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -410,46 +457,169 @@ __device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, f
         w[h] = pr * vn;
     }
     float *wrow = xw + rig * X::XW;
-    {
-        float *dst = wrow + sub * G;
-        if constexpr (G == 4) {
-            *reinterpret_cast<float4 *>(dst) = make_float4(w[0], w[1], w[2], w[3]);
-        } else if constexpr (G == 2) {
-            *reinterpret_cast<float2 *>(dst) = make_float2(w[0], w[1]);
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                dst[h] = w[h];
-        }
-    }
+    lds_put<G>(wrow + sub * G, w);
     wave_lds_fence();
-    // V slices of the P rows, weighted (rotated domain)
 #pragma unroll
     for (int c = 0; c < P; c++) {
         float wc[G];
-        if constexpr (G == 4) {
-            const float4 v = *reinterpret_cast<const float4 *>(wrow + c * G);
-            wc[0] = v.x; wc[1] = v.y; wc[2] = v.z; wc[3] = v.w;
-        } else if constexpr (G == 2) {
-            const float2 v = *reinterpret_cast<const float2 *>(wrow + c * G);
-            wc[0] = v.x; wc[1] = v.y;
-        } else {
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                wc[h] = wrow[c * G + h];
-        }
-#pragma unroll
-        for (int m = 0; m < CPL / WV; m++) {
-            float cc[WV];
-            lookup<BV>(tabV, vb[c], m, cc);
-#pragma unroll
-            for (int j = 0; j < WV; j++)
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    acc[h][WV * m + j] = fmaf(wc[h], cc[j], acc[h][WV * m + j]);
-        }
+        lds_get<G>(wrow + c * G, wc);
+        xch_accumulate<D, BV, G>(tabV, vb[c], wc, acc);
     }
     wave_lds_fence();  // every lane is done with this tile's LDS blocks
+}
+
+// The exchange scan with the sparse-V gate.  The gate compares each row with
+// the largest score of its aligned 256-row block, so each wave takes whole
+// blocks (w, w + 4, ... of the chunk; chunks start on block boundaries) in
+// four 64-row parts: the wave scores the four parts, takes the block maximum,
+// then per part forms the weights (every row in the denominator; zero for
+// the heads that gate the row), passes them through LDS and loads and
+// decodes V only for rows with a nonzero weight.  The running maximum is per
+// wave.  The block's scores wait in LDS (`scs`, [part][lane][G], then the
+// rows' V norms [part][lane]) between the two passes; the V norms are read in
+// the score pass with the K norms, so that the second pass has no load whose
+// wait would also drain the V slices in flight.  Part j + 1's V slices are
+// issued (its weights in the other of two LDS slots) before part j is
+// accumulated.  Rows past the context read the last row (masked, or not
+// used).
+template <int D, int BK, int BV, int G>
+__device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float *tabK,
+                                               const float *tabV, float *xs, float *xw,
+                                               const float (&qr)[G][Xch<D, G>::CPL],
+                                               float (&acc)[G][Xch<D, G>::CPL],
+                                               float (&m_run)[G], float (&l_part)[G],
+                                               const uint8_t *kbase, const uint8_t *vbase,
+                                               const float *knb, const float *vnb, float *scs,
+                                               int t_begin, int t_end, int wave, int sub,
+                                               int rig)
+{
+    using X = Xch<D, G>;
+    constexpr int CPL = X::CPL, P = X::P, RPW = X::RPW;
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int SBK = CPL * BK / 8, SBV = CPL * BV / 8;
+    constexpr int NPART = kTile / 64;
+    const int lane = threadIdx.x & 63;
+    float *xrow = xs + rig * P * X::XS;
+    const int nblk = (t_end - t_begin + kTile - 1) / kTile;
+    float *vns = scs + 4 * 64 * G;
+    // K slices and this lane's row's K and V norms of the part whose first
+    // row (of this lane's row group) is tp
+    auto load_k = [&](int tp, uint64_t (&kb)[P], float &kn, float &vn) {
+#pragma unroll
+        for (int c = 0; c < P; c++) {
+            const int t = min(tp + c * RPW, t_end - 1);
+            kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * SBK);
+        }
+        const int to = min(tp + sub * RPW, t_end - 1);
+        kn = knb[to];
+        vn = vnb[to];
+    };
+    // part j's weights into LDS slot j & 1, then its kept rows' V slices
+    auto weights_and_v = [&](int bs, int j, const float (&bmax)[G], uint64_t (&vb)[P],
+                             uint32_t &kept) {
+        const int tp = bs + 64 * j + rig;
+        float *wrow = xw + ((j & 1) * RPW + rig) * X::XW;
+        float sc[G], w[G];
+        lds_get<G>(scs + (64 * j + lane) * G, sc);
+        const float vnr = vns[64 * j + lane];
+        bool keep = false;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            const float pr = m_run[h] == -__builtin_huge_valf()
+                                 ? 0.0f
+                                 : __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
+            l_part[h] += pr;  // gated rows stay in the denominator
+            const bool kh = sc[h] - bmax[h] > p.gate_log2;
+            w[h] = kh ? pr : 0.0f;
+            keep |= kh;
+        }
+        const float vn = keep ? vnr : 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            w[h] *= vn;
+        lds_put<G>(wrow + sub * G, w);
+        wave_lds_fence();
+        kept = 0;  // bit c: this row group keeps its row of pass c
+#pragma unroll
+        for (int c = 0; c < P; c++) {
+            float wc[G];
+            lds_get<G>(wrow + c * G, wc);
+            bool kc = false;
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                kc |= wc[h] != 0.0f;
+            // the same for every lane of the row group; no branch around the
+            // load (where paths join the compiler would wait for every load in
+            // flight): rows no head keeps read the block's first row (a cache
+            // hit), unused
+            vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)(kc ? tp + c * RPW : bs) * RBV,
+                                             sub * SBV);
+            kept |= (uint32_t)kc << c;
+        }
+    };
+#pragma unroll 1
+    for (int blk = wave; blk < nblk; blk += kBlock / 64) {
+        const int bs = t_begin + blk * kTile;
+        // ---- the block's scores (this lane's row of each part) and maximum
+        float bm[G];
+#pragma unroll
+        for (int h = 0; h < G; h++)
+            bm[h] = -__builtin_huge_valf();
+#pragma unroll
+        for (int j = 0; j < NPART; j++) {
+            uint64_t kb[P];
+            float kn, vnp;
+            load_k(bs + 64 * j + rig, kb, kn, vnp);
+            const int to = bs + 64 * j + rig + sub * RPW;
+            float sc[G];
+            xch_scores<D, BK, G>(tabK, xrow, qr, kb, sub, sc);
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                sc[h] = to < t_end ? sc[h] * kn : -__builtin_huge_valf();
+                bm[h] = fmaxf(bm[h], sc[h]);
+            }
+            lds_put<G>(scs + (64 * j + lane) * G, sc);
+            vns[64 * j + lane] = vnp;
+            wave_lds_fence();  // the part's partials are read before the next part's
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float bmax[G];
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            bmax[h] = wave_max(bm[h]);
+            if (bmax[h] > m_run[h]) {
+                const float fac = exp2f(m_run[h] - bmax[h]);  // 0 on the first block
+                l_part[h] *= fac;
+#pragma unroll
+                for (int k = 0; k < CPL; k++)
+                    acc[h][k] *= fac;
+                m_run[h] = bmax[h];
+            }
+        }
+        // ---- weights and the V of the kept rows, one part ahead
+        uint64_t vb[2][P];
+        uint32_t kept[2];
+        weights_and_v(bs, 0, bmax, vb[0], kept[0]);
+#pragma unroll
+        for (int j = 0; j < NPART; j++) {
+            const int cur = j & 1, nxt = cur ^ 1;
+            if (j + 1 < NPART)
+                weights_and_v(bs, j + 1, bmax, vb[nxt], kept[nxt]);
+            __builtin_amdgcn_sched_barrier(0);
+            const float *wrow = xw + (cur * RPW + rig) * X::XW;
+#pragma unroll
+            for (int c = 0; c < P; c++) {
+                if (__ballot((kept[cur] >> c) & 1u) == 0)
+                    continue;  // no row group keeps its row of this pass
+                float wc[G];
+                lds_get<G>(wrow + c * G, wc);
+                xch_accumulate<D, BV, G>(tabV, vb[cur][c], wc, acc);
+            }
+            // slot `cur` is read before part j + 2 writes it
+            wave_lds_fence();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
 }
 
 // The same partial results without the sparse-V gate, with an online softmax
@@ -478,11 +648,12 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     __shared__ float red_l[kBlock / 64][G];
     // exchange scan: each wave's LDS blocks of partial scores and weights;
     // after the scan the same wave-owned region holds the wave's o' (accs)
-    constexpr bool XON = !GATE && Xch<D, G>::ON;
-    constexpr int AST = XON && Xch<D, G>::FLOATS > G * D ? Xch<D, G>::FLOATS : G * D;
+    constexpr bool XON = Xch<D, G>::ON;
+    constexpr int XFL = GATE ? Xch<D, G>::GATED_FLOATS : Xch<D, G>::FLOATS;
+    constexpr int AST = XON && XFL > G * D ? XFL : G * D;
     __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
-    // sparse V: the scores of the 256-row block a wave is working on
-    __shared__ float scw[GATE ? kBlock / 64 : 1][GATE ? kTile : 1][G];
+    // sparse V on the per-lane scan: the scores of a wave's 256-row block
+    __shared__ float scw[GATE && !XON ? kBlock / 64 : 1][GATE && !XON ? kTile : 1][G];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x, b = blockIdx.z;
@@ -541,28 +712,31 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     const int t_end = min(p.T, t_begin + p.chunk_len);
     const int t_lane = t_begin + wave * RPW + rig;  // this lane's row in pass 0
 
-    if constexpr (GATE) {
-        gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
-                                 t_begin, t_end, wave, sub, rig);
-    } else if constexpr (XON) {
+    if constexpr (XON) {
         using X = Xch<D, G>;
         float *xs = accs + wave * AST;
         float *xw = xs + X::RPW * X::P * X::XS;
         const uint8_t *kbase = p.kp + rowbase * RBK;
         const uint8_t *vbase = p.vp + rowbase * RBV;
         const float *knb = p.kn + rowbase, *vnb = p.vn + rowbase;
-        // tiles of 256 rows (chunks start on tile boundaries); the last one
-        // may run past the context
-        int t0 = t_begin;
+        if constexpr (GATE) {
+            xch_gated_scan<D, BK, BV, G>(p, tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
+                                         vbase, knb, vnb, xw + 2 * X::RPW * X::XW, t_begin, t_end,
+                                         wave, sub, rig);
+        } else {
+            // tiles of 256 rows (chunks start on tile boundaries); the last
+            // one may run past the context
+            int t0 = t_begin;
 #pragma unroll 1
-        for (; t0 + kTile <= t_end; t0 += kTile)
-            xch_step<D, BK, BV, G, false>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
-                                          vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
-                                          t_end, sub, rig);
-        if (t0 < t_end)
-            xch_step<D, BK, BV, G, true>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
-                                         vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
-                                         t_end, sub, rig);
+            for (; t0 + kTile <= t_end; t0 += kTile)
+                xch_step<D, BK, BV, G, false>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
+                                              vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
+                                              t_end, sub, rig);
+            if (t0 < t_end)
+                xch_step<D, BK, BV, G, true>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
+                                             vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
+                                             t_end, sub, rig);
+        }
         // bring the row groups to the wave's maximum; each lane's sum covers
         // its own rows, so the sums add within the group first
 #pragma unroll
@@ -575,6 +749,9 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
                 acc[h][k] *= f;
             m_run[h] = M;
         }
+    } else if constexpr (GATE) {
+        gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
+                                 t_begin, t_end, wave, sub, rig);
     } else {
 #pragma unroll 1
     for (int t0 = t_lane; t0 - rig - wave * RPW < t_end; t0 += CH * RPB) {
@@ -859,7 +1036,7 @@ void launch_attn_wave(int G, dim3 grid, AttnParams p, hipStream_t st)
     case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
     case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
     default:
-        if constexpr (!GATE && Xch<D, 4>::ON && !Xch<D, 8>::ON) {
+        if constexpr (Xch<D, 4>::ON && !Xch<D, 8>::ON) {
             // eight query heads per KV head: two workgroups of four each (the
             // exchange scan, which needs more LDS than a workgroup of eight
             // could have); each reads the KV head's rows

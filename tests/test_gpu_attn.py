@@ -153,7 +153,9 @@ def test_config5_long_context_attention_sampled(tq, orc):
             check_attention(o[0, h], ref[h])
 
 
-@pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 3, 2), (256, 2, 4, 1)])
+@pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 3, 2), (256, 2, 4, 1),
+                                       (128, 3, 2, 2), (128, 4, 4, 8), (256, 4, 2, 2),
+                                       (64, 2, 3, 4), (256, 3, 3, 8)])
 def test_attention_sparse_v(tq, orc, d, bk, bv, G):
     """Sparse-V gate (threshold 1e-3) against the oracle's rule, on a peaked
     softmax over several 256-slot blocks and a ragged last block; a large
@@ -173,6 +175,23 @@ def test_attention_sparse_v(tq, orc, d, bk, bv, G):
     # the gate changes the result (rows were dropped) but only slightly
     assert np.abs(o - o0).max() > 0
     assert np.abs(o - o0).max() < 0.05
+
+
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 2)])
+@pytest.mark.parametrize("T", [1, 7, 256, 300])
+def test_attention_sparse_v_short(tq, orc, d, G, T):
+    """The gate on contexts of one row, a few rows, one whole block and one
+    block plus a ragged part (keys x 6: many rows gated)."""
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    cache = tq.TQCache(1, B, Hkv, max(T, 16), d, 4, 2, SEED)
+    _fill(tq, cache, 0, 90 + T + d, kscale=6.0)
+    q = (kvgen.normal((B, Hq, d), 91 + T, "cuda") * 2.0).to(torch.bfloat16)
+    o = tq.tq_attn_decode(cache, 0, q, T, scale=0.5, sparse_v=1e-3).cpu().numpy()
+    for b in range(B):
+        ref = _oracle(orc, cache, 0, q, b, range(Hq), T, 0.5, sparse_v=1e-3)
+        for h in range(Hq):
+            check_attention(o[b, h], ref[h])
 
 
 def test_config4_attention_sparse_v_sampled(tq, orc):
