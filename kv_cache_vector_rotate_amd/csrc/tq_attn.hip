@@ -945,18 +945,38 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
 #pragma unroll
     for (int w = 0; w < kCombineThreads / 64; w++)
         M = fmaxf(M, wmax[w]);
-    // this thread's group of chunks
+    // this thread's group of chunks, in chunk order; the records of UN chunks
+    // are loaded together (one latency per batch: with few (sequence, head)
+    // pairs this kernel is latency-bound)
+    constexpr int UN = 8;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float L = 0.0f;
-    for (int c = grp; c < p.n_chunks; c += NG) {
-        const float w = exp2f(rec[c * RS + D] - M);
-        const float4 t = reinterpret_cast<const float4 *>(rec + c * RS)[j4];
+    auto add = [&](float mx, const float4 &t, float lv) {
+        const float w = exp2f(mx - M);
         o.x = fmaf(w, t.x, o.x);
         o.y = fmaf(w, t.y, o.y);
         o.z = fmaf(w, t.z, o.z);
         o.w = fmaf(w, t.w, o.w);
-        if (j4 == 0)
-            L = fmaf(w, rec[c * RS + D + 1], L);
+        L = fmaf(w, lv, L);  // lv = 0 except on the thread holding coordinates 0..3
+    };
+    int c = grp;
+    for (; c + (UN - 1) * NG < p.n_chunks; c += UN * NG) {
+        float mx[UN], lv[UN];
+        float4 t[UN];
+#pragma unroll
+        for (int u = 0; u < UN; u++) {
+            const float *r = rec + (c + u * NG) * RS;
+            mx[u] = r[D];
+            lv[u] = j4 == 0 ? r[D + 1] : 0.0f;
+            t[u] = reinterpret_cast<const float4 *>(r)[j4];
+        }
+#pragma unroll
+        for (int u = 0; u < UN; u++)
+            add(mx[u], t[u], lv[u]);
+    }
+    for (; c < p.n_chunks; c += NG) {
+        const float *r = rec + c * RS;
+        add(r[D], reinterpret_cast<const float4 *>(r)[j4], j4 == 0 ? r[D + 1] : 0.0f);
     }
     reinterpret_cast<float4 *>(part[grp])[j4] = o;
     if (j4 == 0)
