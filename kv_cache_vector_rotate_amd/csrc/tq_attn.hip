@@ -29,6 +29,7 @@
 #include <cfloat>
 #include <cmath>
 #include <string>
+#include <type_traits>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -73,12 +74,6 @@ __device__ __forceinline__ float wave_max(float x)
 {
     x = max_across<32>(x);
     return fmaxf(x, __shfl_xor(x, 32));
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-    x = sum_across<32>(x);
-    return x + __shfl_xor(x, 32);
 }
 
 // Bits of one lane's slice of a packed row: CPL indices of BITS bits starting
@@ -710,7 +705,6 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
     const int t_begin = chunk * p.chunk_len;
     const int t_end = min(p.T, t_begin + p.chunk_len);
-    const int t_lane = t_begin + wave * RPW + rig;  // this lane's row in pass 0
 
     if constexpr (XON) {
         using X = Xch<D, G>;
@@ -753,20 +747,27 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
         gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
                                  t_begin, t_end, wave, sub, rig);
     } else {
-#pragma unroll 1
-    for (int t0 = t_lane; t0 - rig - wave * RPW < t_end; t0 += CH * RPB) {
+    // steps of CH row passes (CH * RPB rows); 32-bit row offsets from uniform
+    // bases; only a step that runs past the context (the last) masks rows
+    const uint8_t *kbase = p.kp + rowbase * RBK;
+    const uint8_t *vbase = p.vp + rowbase * RBV;
+    const float *knb = p.kn + rowbase, *vnb = p.vn + rowbase;
+    auto step = [&](const int s0, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int t0 = s0 + wave * RPW + rig;  // this lane's row in pass 0
         // every K and V load of the step in flight before any arithmetic;
-        // rows past the context read a valid row and are masked below
+        // rows past the context read the last row and are masked below
         uint64_t kb[CH], vb[CH];
         float kn[CH], vn[CH];
 #pragma unroll
         for (int c = 0; c < CH; c++) {
-            const int t = t0 + c * RPB;
-            const int64_t row = rowbase + (t < t_end ? t : t_begin);
-            kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
-            kn[c] = p.kn[row];
-            vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
-            vn[c] = p.vn[row];
+            int t = t0 + c * RPB;
+            if constexpr (TAIL)
+                t = min(t, t_end - 1);
+            kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * (CPL * BK / 8));
+            kn[c] = knb[t];
+            vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)t * RBV, sub * (CPL * BV / 8));
+            vn[c] = vnb[t];
         }
         // scores (log2 units), every lane of a row holding its row's value
         float sc[CH][G];
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 #pragma unroll
             for (int h = 0; h < G; h++)
                 s[h] = sum_across<P>(s[h]) * kn[c];
-            const bool valid = t0 + c * RPB < t_end;
+            const bool valid = !TAIL || t0 + c * RPB < t_end;
 #pragma unroll
             for (int h = 0; h < G; h++)
                 sc[c][h] = valid ? s[h] : -__builtin_huge_valf();
@@ -819,11 +820,12 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
             float w[G];
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                // m_run is -inf only while the wave has seen no valid row;
-                // weights below 2^-126 flush to 0 (v_exp_f32)
-                const float pr = m_run[h] == -__builtin_huge_valf()
-                                     ? 0.0f
-                                     : __builtin_amdgcn_exp2f(sc[c][h] - m_run[h]);
+                // weights below 2^-126 flush to 0 (v_exp_f32); m_run is -inf
+                // only while the wave has seen no valid row, which a step
+                // inside the context cannot leave behind
+                float pr = __builtin_amdgcn_exp2f(sc[c][h] - m_run[h]);
+                if constexpr (TAIL)
+                    pr = m_run[h] == -__builtin_huge_valf() ? 0.0f : pr;
                 l_part[h] += pr;
                 w[h] = pr * vn[c];
             }
@@ -838,7 +840,14 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
                         acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
             }
         }
-    }
+    };
+    constexpr int SR = CH * RPB;  // rows per step of the workgroup
+    int s0 = t_begin;
+#pragma unroll 1
+    for (; s0 + SR <= t_end; s0 += SR)
+        step(s0, std::integral_constant<bool, false>{});
+    if (s0 < t_end)
+        step(s0, std::integral_constant<bool, true>{});
     }
 
     // ---- reduce over the rows of the wave (lanes with equal `sub`); every
