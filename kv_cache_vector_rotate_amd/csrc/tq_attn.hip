@@ -39,7 +39,6 @@ using namespace tqd;
 namespace {
 
 constexpr int kTile = 256;           // rows per online-softmax tile (= threads)
-constexpr int kTargetBlocks = 1024;  // split the context until about this many workgroups
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnParams {
@@ -1035,16 +1034,52 @@ struct Split {
     int T, n_chunks, chunk_len;
 };
 
-// Context split: enough chunks for about kTargetBlocks workgroups, chunks a
-// whole number of tiles.  Depends only on the arguments, so results are the
-// same on every device.
-Split split_for(int batch, int n_kv, int64_t ctx_len, int window)
+// Which scan a launch runs (the host's mirror of the kernels' choice): the
+// exchange scan for two or four query heads per KV head where its LDS blocks
+// fit, and for eight as two workgroups of four; the per-lane scan otherwise.
+template <int D>
+bool exchange_scan(int G)
+{
+    switch (G) {
+    case 2: return Xch<D, 2>::ON;
+    case 4: return Xch<D, 4>::ON;
+    case 8: return Xch<D, 8>::ON || Xch<D, 4>::ON;
+    default: return false;
+    }
+}
+
+bool exchange_scan_for(int D, int G)
+{
+    return D == 64 ? exchange_scan<64>(G) : D == 128 ? exchange_scan<128>(G) : exchange_scan<256>(G);
+}
+
+// Workgroups per KV head (eight query heads on the exchange scan: two of four)
+int groups_per_kv_head(int D, int G)
+{
+    if (G == 8) {
+        const bool split = D == 64    ? Xch<64, 4>::ON && !Xch<64, 8>::ON
+                           : D == 128 ? Xch<128, 4>::ON && !Xch<128, 8>::ON
+                                      : Xch<256, 4>::ON && !Xch<256, 8>::ON;
+        return split ? 2 : 1;
+    }
+    return 1;
+}
+
+// Context split: enough chunks for about `target` workgroups, chunks a whole
+// number of tiles.  The target is one round of resident workgroups over the
+// 256 CUs: two per CU for the exchange scan (its registers and LDS), four for
+// the per-lane scan; measured, 512 and 1024 beat the other choice and 2048 for
+// each.  Depends only on the arguments, so results are the same on every
+// device.
+Split split_for(int batch, int n_kv, int64_t ctx_len, int window, int D, int G)
 {
     Split s;
     s.T = (int)(ctx_len < window ? ctx_len : window);
-    const int units = batch * n_kv > 0 ? batch * n_kv : 1;
+    const int target = exchange_scan_for(D, G) ? 512 : 1024;
+    const int units =
+        batch * n_kv * groups_per_kv_head(D, G) > 0 ? batch * n_kv * groups_per_kv_head(D, G) : 1;
     const int tiles = (s.T + kTile - 1) / kTile;
-    int want = (kTargetBlocks + units - 1) / units;
+    int want = (target + units - 1) / units;
     if (want > tiles)
         want = tiles;
     if (want < 1)
@@ -1123,7 +1158,7 @@ extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int
     const int D = tq::padded_dim(c->head_dim[layer]);
     if (D == 0)
         return 0;
-    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
+    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window, D, n_q_heads / c->n_kv_heads);
     return (size_t)c->batch * n_q_heads * s.n_chunks * (size_t)(D + 4) * sizeof(float);
 }
 
@@ -1178,7 +1213,7 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     if ((rc = tq::get_codebook(D, bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
         (rc = tq::get_codebook(D, bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
         return rc;
-    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window);
+    Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window, D, G);
     AttnParams p;
     p.q = q_bf16;
     p.kp = c->k_packed[layer];
