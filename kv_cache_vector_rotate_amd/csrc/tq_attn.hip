@@ -13,17 +13,22 @@
 // and sum_t p_t v_t = D H (sum_t p_t n^V_t c_V[idx^V_t]) / sqrt(d).
 //
 // Split over the context: workgroup (chunk, kv head, sequence) handles the G
-// query heads of one KV head over one chunk of rows with an online softmax
-// (scores in log2 units) and writes (o', max, sum) for its chunk: per wave
-// without the sparse-V gate, per 256-row tile with it (the gate compares each
-// row with its tile's maximum).  A second kernel merges the chunks of each
-// (sequence, query head) in chunk order (log-sum-exp) and applies the single
-// inverse rotation.  No atomics; the order of every sum is fixed.  With the
-// two-sided rotation S2 H S1, q' takes S2 after H and o' takes S2 before it.
+// query heads of one KV head (or four of eight) over one chunk of rows with
+// an online softmax (scores in log2 units) and writes (o', max, sum) for its
+// chunk.  Two scans: the exchange scan (two or more query heads per KV head)
+// passes each tile's partial scores through LDS so that one lane per row
+// takes the row's softmax; the per-lane scan (one query head per KV head)
+// keeps every row's scores on all the lanes that hold the row.  With the
+// sparse-V gate each wave takes whole 256-row blocks (the gate compares each
+// row with its block's maximum) and loads V only for kept rows.  A second
+// kernel merges the chunks of each (sequence, query head) in chunk order
+// (log-sum-exp) and applies the single inverse rotation.  No atomics; the
+// order of every sum is fixed.  With the two-sided rotation S2 H S1, q' takes
+// S2 after H and o' takes S2 before it.
 //
 // Centroid lookup: neighbouring indices address a table of centroid tuples in
-// LDS, one read per lookup: pairs (2*bits bits) in the per-tile kernel and for
-// 3/4-bit sides of the per-wave kernel, quadruples for its 2-bit sides.
+// LDS, one read per lookup: pairs (2*bits bits) for 3/4-bit sides,
+// quadruples for 2-bit sides.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -616,13 +621,14 @@ __device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float 
     }
 }
 
-// The same partial results without the sparse-V gate, with an online softmax
-// per wave instead of per tile: the weights of a row are only ever needed by
-// the wave that scored it, so each wave keeps its scores in registers, runs
-// its own running maximum (wave-uniform) and sum, and accumulates V right
-// after each step of CH row passes.  No LDS traffic for scores and no
-// barrier inside the scan; the four waves' (o', max, sum) are merged once at
-// the end.  Rows of wave w: t_begin + it * RPB + w * RPW + (lane / P).
+// Partial results of one chunk.  The exchange scan (above) runs where its LDS
+// blocks fit and there are at least two query heads per KV head; otherwise
+// the per-lane scan: each wave keeps its rows' scores in registers (every lane
+// of a row holds the row's sums), runs its own running maximum (wave-uniform)
+// and sum, and accumulates V right after each step of CH row passes, with no
+// LDS traffic for scores and no barrier inside the scan.  Either way the four
+// waves' (o', max, sum) are merged once at the end.  Per-lane rows of wave w:
+// t_begin + it * RPB + w * RPW + (lane / P).
 template <int D, int BK, int BV, int G, bool GATE>
 __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 {
