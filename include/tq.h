@@ -236,7 +236,9 @@ size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
  * to the running maximum is neither loaded nor decoded); gated rows stay in
  * the softmax denominator.  Invalid (negative, >= 1 or NaN) -> TQ_EINVAL.
  * workspace: device buffer of at least tq_attn_workspace_bytes(...) bytes,
- * 16-byte aligned; its contents need no initialisation.  ctx_len >= 1. */
+ * 16-byte aligned; its contents need no initialisation.  ctx_len >= 1.
+ * window * head_dim / 2 (one KV head's packed rows at 4 bits, padded
+ * head_dim) must stay below 2^31, else TQ_EUNSUPPORTED. */
 int tq_attn_decode(const tq_cache_desc *cache, int layer, const uint16_t *q_bf16,
                    int n_q_heads, int64_t ctx_len, float scale, float sparse_v_threshold,
                    float *out, void *workspace, size_t ws_bytes, void *stream);

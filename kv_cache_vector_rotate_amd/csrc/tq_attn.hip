@@ -81,21 +81,24 @@ __device__ __forceinline__ float wave_max(float x)
 }
 
 // Bits of one lane's slice of a packed row: CPL indices of BITS bits starting
-// at byte `off` of the row (the slice never crosses the row end).  Reads the
-// 4-byte words that cover it and shifts the slice down to bit 0.
+// at byte `off` from `base` (the slice never crosses the row end; rows are a
+// multiple of 4 bytes, of 8 where the slice is 8 bytes).  Reads the 4-byte
+// words that cover it and shifts the slice down to bit 0.  One unsigned
+// 32-bit offset from a uniform base: a scalar base and a vector offset per
+// load, no 64-bit address arithmetic.
 template <int BITS, int CPL>
-__device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *row, int off)
+__device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *base, uint32_t off)
 {
     constexpr int NB = CPL * BITS / 8;  // bytes in the slice
     if constexpr (NB == 8) {
-        return *reinterpret_cast<const uint64_t *>(row + off);  // off % 8 == 0
+        return *reinterpret_cast<const uint64_t *>(base + off);  // off % 8 == 0
     } else if constexpr (NB == 4) {
-        return *reinterpret_cast<const uint32_t *>(row + off);  // off % 4 == 0
+        return *reinterpret_cast<const uint32_t *>(base + off);  // off % 4 == 0
     } else if constexpr (NB == 2) {
-        return *reinterpret_cast<const uint16_t *>(row + off);  // off % 2 == 0
+        return *reinterpret_cast<const uint16_t *>(base + off);  // off % 2 == 0
     } else {
-        const int a = off & ~3, sh = off & 3;
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(row + a);
+        const uint32_t a = off & ~3u, sh = off & 3u;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(base + a);
         uint64_t v = w[0];
         if (sh + NB > 4)
             v |= (uint64_t)w[1] << 32;
@@ -176,7 +179,7 @@ __device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tab
             for (int c = 0; c < CH; c++) {
                 const int t = bs + (it0 + c) * RPW + rig;
                 const int64_t row = rowbase + (t < t_end ? t : t_begin);
-                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, sub * (CPL * BK / 8));
+                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, (uint32_t)(sub * (CPL * BK / 8)));
                 kn[c] = p.kn[row];
             }
 #pragma unroll
@@ -245,7 +248,7 @@ __device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tab
                 vn[c] = 0.0f;
                 if (kept[c]) {
                     const int64_t row = rowbase + bs + tl;
-                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, sub * (CPL * BV / 8));
+                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, (uint32_t)(sub * (CPL * BV / 8)));
                     vn[c] = p.vn[row];
                 }
             }
@@ -422,8 +425,8 @@ __device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, f
         int t = tw + c * RPB;
         if constexpr (TAIL)
             t = t < t_end ? t : t_begin;
-        kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * SBK);
-        vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)t * RBV, sub * SBV);
+        kb[c] = load_slice_bits<BK, CPL>(kbase, (uint32_t)t * RBK + (uint32_t)(sub * SBK));
+        vb[c] = load_slice_bits<BV, CPL>(vbase, (uint32_t)t * RBV + (uint32_t)(sub * SBV));
     }
     int to = tw + sub * RPB;  // the row this lane takes the softmax of
     const bool valid = to < t_end;
@@ -507,7 +510,7 @@ __device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float 
 #pragma unroll
         for (int c = 0; c < P; c++) {
             const int t = min(tp + c * RPW, t_end - 1);
-            kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * SBK);
+            kb[c] = load_slice_bits<BK, CPL>(kbase, (uint32_t)t * RBK + (uint32_t)(sub * SBK));
         }
         const int to = min(tp + sub * RPW, t_end - 1);
         kn = knb[to];
@@ -551,8 +554,8 @@ __device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float 
             // load (where paths join the compiler would wait for every load in
             // flight): rows no head keeps read the block's first row (a cache
             // hit), unused
-            vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)(kc ? tp + c * RPW : bs) * RBV,
-                                             sub * SBV);
+            vb[c] = load_slice_bits<BV, CPL>(
+                vbase, (uint32_t)(kc ? tp + c * RPW : bs) * RBV + (uint32_t)(sub * SBV));
             kept |= (uint32_t)kc << c;
         }
     };
@@ -769,9 +772,11 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
             int t = t0 + c * RPB;
             if constexpr (TAIL)
                 t = min(t, t_end - 1);
-            kb[c] = load_slice_bits<BK, CPL>(kbase + (uint32_t)t * RBK, sub * (CPL * BK / 8));
+            kb[c] = load_slice_bits<BK, CPL>(kbase,
+                                             (uint32_t)t * RBK + (uint32_t)(sub * (CPL * BK / 8)));
             kn[c] = knb[t];
-            vb[c] = load_slice_bits<BV, CPL>(vbase + (uint32_t)t * RBV, sub * (CPL * BV / 8));
+            vb[c] = load_slice_bits<BV, CPL>(vbase,
+                                             (uint32_t)t * RBV + (uint32_t)(sub * (CPL * BV / 8)));
             vn[c] = vnb[t];
         }
         // scores (log2 units), every lane of a row holding its row's value
@@ -1200,6 +1205,10 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     }
     if (!(G == 1 || G == 2 || G == 4 || G == 8))
         return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: query/KV head ratio must be 1, 2, 4 or 8");
+    // the kernels address one KV head's packed rows with 32-bit byte offsets
+    if ((uint64_t)c->window * (uint64_t)(D / 2) >= (1ull << 31))
+        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: window too large (one KV head's packed "
+                                         "rows must span less than 2 GiB)");
     if (c->batch == 0)
         return TQ_OK;
     if (!q_bf16 || !out || !workspace || !c->k_packed[layer] || !c->k_norms[layer] ||

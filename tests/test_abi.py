@@ -198,6 +198,10 @@ def test_cache_and_attention_validation(tq):
     d4 = _desc(tq, flags=4)
     assert L.tq_attn_decode(ctypes.byref(d4), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
     assert "flag" in tq.tq_last_error()
+    # one KV head's packed rows (window x head_dim / 2 bytes) must stay below 2 GiB
+    d5 = _desc(tq, head_dim=256, window=1 << 24)
+    assert L.tq_attn_decode(ctypes.byref(d5), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 30, None) == tq.TQ_EUNSUPPORTED
+    assert "window" in tq.tq_last_error()
     assert L.tq_append_row(ctypes.byref(d4), -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
     assert "flag" in tq.tq_last_error()
 
