@@ -66,7 +66,7 @@ __device__ __forceinline__ void encode_row(const RawSlice<T> &raw, bool valid, i
         for (int k = 0; k < kCPL; k++)
             m = fmaxf(m, fabsf(v[k]));
         m = max_across<P>(m);
-        if (m > 0.0f && m <= FLT_MAX) {
+        if (m > 0.0f && m <= FLT_MAX && ss == ss) {
             (void)frexpf(m, &nexp);
 #pragma unroll
             for (int k = 0; k < kCPL; k++)
@@ -76,7 +76,7 @@ __device__ __forceinline__ void encode_row(const RawSlice<T> &raw, bool valid, i
             for (int k = 0; k < kCPL; k++)
                 ss = fmaf(v[k], v[k], ss);
             ss = sum_across<P>(ss);
-        } else if (!(m <= FLT_MAX)) {
+        } else if (!(m <= FLT_MAX) || ss != ss) {  // an Inf or a NaN (the max skips NaN)
             nbad = ss + m;  // inf or NaN
 #pragma unroll
             for (int k = 0; k < kCPL; k++)
@@ -461,7 +461,8 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
                 for (int c = 0; c < 4; c++)
                     mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
             }
-            bad = !(mx <= FLT_MAX);
+            const float ss0 = ss;  // the fast path's sum
+            bad = !(mx <= FLT_MAX) || ss0 != ss0;  // an Inf or a NaN (the max skips NaN)
             if (!bad && mx > 0.0f)
                 (void)frexpf(mx, &nexp);
             ss = 0.0f;
@@ -482,7 +483,7 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
                 *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
             }
             if (bad)
-                ss = mx;  // stored as the norm: not finite
+                ss = ss0 + mx;  // stored as the norm: not finite
         }
         t = (ss > 0.0f && !bad) ? 128.0f / sqrtf((float)D * ss) : 0.0f;
         nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);

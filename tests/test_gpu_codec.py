@@ -128,6 +128,58 @@ def test_edge_rows(tq, orc):
         assert np.array_equal(sn.cpu().numpy(), gn[8:] * np.float32(2.0 ** k))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_edge_rows_d128_d256(tq, orc, bits, d, dtype):
+    """Zero, constant, spike, exact-tie, tiny and huge rows against the
+    oracle; rows holding an Inf or a NaN encode as the zero row with a
+    non-finite norm; power-of-two scale invariance (indices identical, norms
+    scaled exactly, except that the one-lane-per-row bf16 kernel (d <= 128)
+    sums a rescaled row's squares in another order: there within 1e-6)."""
+    rng = np.random.default_rng(5)
+    e = np.eye(d, dtype=np.float32)
+    base = rng.standard_normal((6, d)).astype(np.float32)
+    rows = [np.zeros(d, np.float32), np.ones(d, np.float32), e[d - 56] * 3.0, e[0] + e[1],
+            e[3] - e[d // 2 + 2], base[0] * np.float32(1e-30), base[1] * np.float32(1e30)]
+    x = torch.from_numpy(np.stack(rows + list(base))).cuda().to(dtype)
+    kp, kn, _, _ = tq.tq_encode(x, None, bits, 2, SEED)
+    torch.cuda.synchronize()
+    op, on, u = orc.encode(_np(x).astype(np.float32), d, bits, SEED, want_u=True)
+    gp, gn = kp.cpu().numpy(), kn.cpu().numpy()
+    check_norms(gn, on)
+    # rows with exactly zero rotated coordinates sit on the middle boundary
+    # (either neighbouring cell is as near); every other index is bit-exact
+    ig, io = unpack_rows(gp, d, bits), unpack_rows(op, d, bits)
+    _, bnd = orc.codebook_float(d, bits)
+    away = np.abs(u[..., None] - bnd.astype(np.float64)).min(-1) > 1e-6
+    assert np.array_equal(ig[away], io[away])
+    assert np.all(np.abs(ig[~away].astype(int) - io[~away].astype(int)) <= 1)
+    L = 1 << bits
+    assert gn[0] == 0 and np.all(ig[0] == L // 2 - 1)
+    xd = tq.tq_decode(kp, kn, d, bits, SEED).cpu().numpy()
+    assert np.all(xd[0] == 0)
+    check_decoded(xd[1:], orc.decode(gp[1:], gn[1:], d, bits, SEED))
+    # exact power-of-two scaling leaves the indices unchanged
+    for k in (-60, -20, 20, 60):  # +-60 take the rescaled path
+        xs = x[7:] * float(2.0 ** k)
+        sp, sn, _, _ = tq.tq_encode(xs, None, bits, 2, SEED)
+        assert np.array_equal(sp.cpu().numpy(), gp[7:])
+        want = gn[7:] * np.float32(2.0 ** k)
+        if abs(k) > 20 and dtype == torch.bfloat16 and d <= 128:
+            np.testing.assert_allclose(sn.cpu().numpy(), want, rtol=1e-6)
+        else:
+            assert np.array_equal(sn.cpu().numpy(), want)
+    # Inf and NaN rows
+    bad = x[7:9].clone()
+    bad[0, 17] = float("inf")
+    bad[1, d - 6] = float("nan")
+    bp, bn, _, _ = tq.tq_encode(bad, None, bits, 2, SEED)
+    bn = bn.cpu().numpy()
+    assert not np.isfinite(bn).any()
+    assert np.all(unpack_rows(bp.cpu().numpy(), d, bits) == L // 2 - 1)
+
+
 def test_empty_and_single_row(tq, orc):
     d = 128
     x = torch.empty(0, d, device="cuda")
