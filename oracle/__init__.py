@@ -50,7 +50,6 @@ def lib():
         L.orc_unpack.argtypes = [P, i32, i32, P]
         L.orc_codebook.argtypes = [i32, i32, i32, P, P, P]
         L.orc_codebook.restype = i32
-        L.orc_codebook_residual.argtypes = [i32, i32, i32, P, P, P, P]
         L.orc_sphere_mse.argtypes = [i32, i32, P, P]
         L.orc_sphere_mse.restype = f64
         L.orc_codebook_float.argtypes = [i32, i32, i32, P, P]
@@ -159,15 +158,6 @@ def codebook(d: int, bits: int, density: int = BETA):
     if rc != 0:
         raise RuntimeError(f"orc_codebook({d},{bits},{density}) -> {rc}")
     return c, b[: L - 1], it.value
-
-
-def codebook_residual(d, bits, c, b, density=BETA):
-    rm, rb = ctypes.c_double(0), ctypes.c_double(0)
-    c = _c(c, np.float64)
-    b = _c(b, np.float64)
-    lib().orc_codebook_residual(d, bits, density, _p(c), _p(b), ctypes.byref(rm),
-                                ctypes.byref(rb))
-    return rm.value, rb.value
 
 
 def sphere_mse(d, bits, c, b) -> float:

@@ -392,56 +392,6 @@ int orc_codebook(int d, int bits, int density, double *c, double *b, int *iters)
     return 0;
 }
 
-/* Conditional-mean and midpoint residuals of a codebook under its density
- * (for the fixed-point check): max over cells of |c_j - E[X | cell j]| and
- * of |b_j - (c_j + c_{j+1})/2|, both in x units. */
-int orc_codebook_residual(int d, int bits, int density, const double *c,
-                          const double *b, double *res_mean, double *res_mid)
-{
-    gl_init();
-    int L = 1 << bits;
-    orc_beta_z bp = beta_z_codebook_density(d);
-    double scale = density == ORC_BETA ? bp.sigma : 1.0 / sqrt((double)d);
-    double zend = density == ORC_BETA ? bp.zmax : 40.0;
-    double rm = 0.0, rb = 0.0;
-    for (int j = 0; j < L; j++) {
-        double lo = j == 0 ? -zend : b[j - 1] / scale;
-        double hi = j == L - 1 ? zend : b[j] / scale;
-        double m0, m1, m2;
-        if (density == ORC_BETA) {
-            beta_z_moments(&bp, lo, hi, &m0, &m1, &m2);
-        } else {
-            /* split at zero so that both halves use the positive closed form */
-            double a0, a1;
-            m0 = 0.0;
-            m1 = 0.0;
-            if (lo < 0.0) {
-                double h2 = hi < 0.0 ? -hi : 0.0;
-                gauss_moments(h2, -lo, &a0, &a1);
-                m0 += a0;
-                m1 -= a1;
-            }
-            if (hi > 0.0) {
-                double l2 = lo > 0.0 ? lo : 0.0;
-                gauss_moments(l2, hi, &a0, &a1);
-                m0 += a0;
-                m1 += a1;
-            }
-        }
-        double e = fabs(c[j] - m1 / m0 * scale);
-        if (e > rm)
-            rm = e;
-        if (j + 1 < L) {
-            double e2 = fabs(b[j] - 0.5 * (c[j] + c[j + 1]));
-            if (e2 > rb)
-                rb = e2;
-        }
-    }
-    *res_mean = rm;
-    *res_mid = rb;
-    return 0;
-}
-
 /* Expected squared reconstruction error of a unit vector drawn uniformly
  * from the sphere: d * integral (x - Q(x))^2 f_true(x) dx, where f_true is
  * the exact marginal of one coordinate, ~ (1 - x^2)^((d-3)/2).  Rotation is
@@ -675,11 +625,6 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
 /* Attention                                                           */
 /* ------------------------------------------------------------------ */
 
-/* Positions per block of the sparse-V reference maximum (a reading: the
- * pages gate on the running maximum of an online softmax and leave its
- * blocking open). */
-#define ORC_SPARSE_V_BLOCK 256
-
 /* Softmax attention of n_q query heads over T cached rows, plain definition:
  *   khat_t, vhat_t = decode of the stored K, V rows (fp64, not rounded)
  *   score_t = scale * <q, khat_t>,  p = softmax(score) (max subtracted)
@@ -689,12 +634,15 @@ int orc_decode_f64(const uint8_t *packed, const float *norms, int64_t n_rows,
  * exactly).  Cache rows are [n_kv][T] with row strides of one packed row
  * (dp*bits/8 bytes, dp = orc_padded_dim(d)); khat, vhat are the d decoded
  * coordinates.
- * sparse_v_threshold > 0 gates the V sum ([Atlas] "Sparse V dequant"): a
- * row's V contributes only if its exponent relative to the running maximum
- * exceeds the threshold, here taken against a fixed reference, the largest
- * score of the row's aligned block of ORC_SPARSE_V_BLOCK positions:
- *   keep_t = exp(score_t - max_{t' in block(t)} score_t') > threshold;
- * gated rows still count in the softmax denominator (their V is zero, the
+ * sparse_v_threshold > 0 gates the V sum ([Atlas] "Sparse V dequant"): the
+ * V row of a position contributes only when its softmax exponent, taken
+ * against the softmax's maximum, exceeds the threshold.  Reading: the
+ * maximum is that of the whole context (of this query head), so
+ *   keep_t = exp(score_t - max_t' score_t') > threshold,
+ * i.e. the row's attention weight relative to the largest weight; the
+ * running maximum of an online softmax only ever approaches it from below,
+ * and this is the one choice that does not depend on the loop order.  Gated
+ * rows still count in the softmax denominator (their V is left at zero; the
  * kept weights are not renormalised).  0 disables the gate. */
 int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
                   const float *k_norms, const uint8_t *v_packed,
@@ -742,21 +690,11 @@ int orc_attention(const float *q, int n_q, const uint8_t *k_packed,
             double *oh = out + (size_t)h * d;
             for (int i = 0; i < d; i++)
                 oh[i] = 0.0;
-            double eb = 0.0;  /* largest exp(score - m) of the current block */
             for (int t = 0; t < T; t++) {
                 double p = sc[t] / denom;
-                if (sparse_v_threshold > 0.0) {
-                    /* sc holds exp(score - m); the block's largest is exp(mb - m) */
-                    if (t % ORC_SPARSE_V_BLOCK == 0) {
-                        int b1 = t + ORC_SPARSE_V_BLOCK < T ? t + ORC_SPARSE_V_BLOCK : T;
-                        eb = 0.0;
-                        for (int u = t; u < b1; u++)
-                            if (sc[u] > eb)
-                                eb = sc[u];
-                    }
-                    if (!(sc[t] / eb > sparse_v_threshold))
-                        continue;
-                }
+                /* sc holds exp(score - m), m the context's largest score */
+                if (sparse_v_threshold > 0.0 && !(sc[t] > sparse_v_threshold))
+                    continue;
                 for (int i = 0; i < d; i++)
                     oh[i] += p * V[(size_t)t * d + i];
             }

@@ -360,8 +360,9 @@ def test_attention_quality_matches_pages_table(orc, bk, bv, want):
 
 
 def test_attention_sparse_v_gate(orc):
-    """One block (T <= 256): the gate reduces to p_t / max_t p_t > threshold,
-    checked against scipy's softmax; gated rows stay in the denominator."""
+    """One short context: keep_t = p_t / max_t' p_t' > threshold (the weight
+    relative to the largest one), checked against scipy's softmax; gated rows
+    stay in the denominator; threshold 0 is the plain definition."""
     d, n_kv, T = 64, 1, 40
     K, V, kp, kn, vp, vn = _cache(orc, n_kv, T, d, 4, 4, 8, kscale=3.0)
     q = (np.random.default_rng(9).standard_normal((1, d)) * 3).astype(np.float32)
@@ -373,36 +374,74 @@ def test_attention_sparse_v_gate(orc):
     keep = p / p.max() > thr
     assert 0 < keep.sum() < T
     np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-13)
-    # threshold 0 is the plain definition
     o0 = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 4, 42, 0.2, sparse_v_threshold=0.0)
     np.testing.assert_allclose(o0[0], p @ Vh, atol=1e-13)
 
 
-def test_attention_sparse_v_gate_per_block(orc):
-    """Rows are gated against the largest score of their own aligned block of
-    256 positions, not the global one: with one dominant row in block 0, every
-    row of block 1 (each with global weight far below the threshold) still
-    contributes, while block 0 keeps only its dominant row."""
-    d, n_kv, T = 64, 1, 512
-    K, V, kp, kn, vp, vn = _cache(orc, n_kv, T, d, 4, 4, 10)
+def _dominant_row_case(orc, T, t_dom, seed):
+    """A context of T rows where row t_dom dominates: q is a unit vector along
+    its key, the other rows' scores lie in [-1, 1] and the dominant row's
+    score is 10.5 (its key norm raised to that end), so every other row's
+    weight relative to it lies in [e^-11.5, e^-9.5], below 1e-4."""
+    d = 64
+    K, V, kp, kn, vp, vn = _cache(orc, 1, T, d, 4, 4, seed)
+    Kh = orc.decode(kp, kn, d, 4, 42, f64=True)
+    q = np.zeros((1, d), np.float32)
+    q[0] = Kh[t_dom] / np.linalg.norm(Kh[t_dom])
+    qd = q[0].astype(np.float64)
+    scale = 1.0 / float(np.abs(np.delete(Kh, t_dom, axis=0) @ qd).max())
     kn = kn.copy()
-    kn[3] *= 60.0  # row 3 dominates everything by far
+    kn[t_dom] *= np.float32(10.5 / (scale * float(Kh[t_dom] @ qd)))
     Kh = orc.decode(kp, kn, d, 4, 42, f64=True)
     Vh = orc.decode(vp, vn, d, 4, 42, f64=True)
-    q = np.zeros((1, d), np.float32)
-    q[0, :] = Kh[3] / np.linalg.norm(Kh[3])
-    scale = 1.0 / float(np.abs(Kh[256:] @ q[0].astype(np.float64)).max())  # block 1 spread <= 2
-    s = scale * Kh @ q[0].astype(np.float64)
-    p = scipy.special.softmax(s)
-    assert p[256:].max() < 1e-6
+    return d, kp, kn, vp, vn, Kh, Vh, q, scale
+
+
+@pytest.mark.parametrize("t_dom", [3, 700])
+def test_attention_sparse_v_gate_whole_context_maximum(orc, t_dom):
+    """The gate's reference is the largest score of the whole context,
+    wherever it sits: with one dominant row early (3) or late (700) in a
+    context of 1000 rows, every other row's weight relative to it is below
+    the threshold, so every other row is gated -- also the rows before the
+    dominant one and those in other 256-row blocks -- and the output is the
+    dominant row's weighted V alone, while the ungated output still carries
+    the other rows' (together visible) weights.  Checked against scipy's
+    softmax."""
+    T = 1000
+    d, kp, kn, vp, vn, Kh, Vh, q, scale = _dominant_row_case(orc, T, t_dom, 10 + t_dom)
+    p = scipy.special.softmax(scale * Kh @ q[0].astype(np.float64))
+    rest = np.delete(p, t_dom)
+    assert rest.max() / p.max() < 1e-4 and rest.sum() / p.max() > 1e-2
     thr = 1e-3
-    o = orc.attention(q, kp, kn, vp, vn, n_kv, T, d, 4, 4, 42, scale, sparse_v_threshold=thr)
-    keep = np.zeros(T, bool)
-    for b0 in (0, 256):
-        e = np.exp(s[b0:b0 + 256] - s[b0:b0 + 256].max())
-        keep[b0:b0 + 256] = e > thr
-    assert keep[256:].sum() > 10 and keep[:256].sum() < 256
-    np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-15, rtol=1e-10)
+    o = orc.attention(q, kp, kn, vp, vn, 1, T, d, 4, 4, 42, scale, sparse_v_threshold=thr)
+    np.testing.assert_allclose(o[0], p[t_dom] * Vh[t_dom], atol=1e-13)
+    o0 = orc.attention(q, kp, kn, vp, vn, 1, T, d, 4, 4, 42, scale, sparse_v_threshold=0.0)
+    np.testing.assert_allclose(o0[0], p @ Vh, atol=1e-13)
+    assert np.abs(o0[0] - o[0]).max() > 1e-3
+    # a threshold below every relative weight keeps every row
+    o1 = orc.attention(q, kp, kn, vp, vn, 1, T, d, 4, 4, 42, scale, sparse_v_threshold=1e-6)
+    np.testing.assert_allclose(o1[0], p @ Vh, atol=1e-13)
+
+
+def test_attention_sparse_v_gate_long_context_scipy(orc):
+    """A 1300-row context of ordinary scores (keys x 3, several 256-row
+    blocks and a ragged end) at thresholds 1e-3 and 1e-2: keep exactly the
+    rows whose scipy softmax weight is above threshold x the largest weight;
+    the kept set shrinks as the threshold grows."""
+    d, T = 64, 1300
+    K, V, kp, kn, vp, vn = _cache(orc, 1, T, d, 3, 2, 12, kscale=3.0)
+    q = (np.random.default_rng(13).standard_normal((1, d)) * 2).astype(np.float32)
+    Kh = orc.decode(kp, kn, d, 3, 42, f64=True)
+    Vh = orc.decode(vp, vn, d, 2, 42, f64=True)
+    scale = 0.25
+    p = scipy.special.softmax(scale * Kh @ q[0].astype(np.float64))
+    kept = []
+    for thr in (1e-3, 1e-2):
+        keep = p / p.max() > thr
+        kept.append(int(keep.sum()))
+        o = orc.attention(q, kp, kn, vp, vn, 1, T, d, 3, 2, 42, scale, sparse_v_threshold=thr)
+        np.testing.assert_allclose(o[0], (p * keep) @ Vh, atol=1e-13)
+    assert T > kept[0] > kept[1] > 0
 
 
 # --------------------------------------------------------------------------
