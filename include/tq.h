@@ -46,8 +46,10 @@
  *     coordinates ([Foundry] Hadamard Transform Detail: pad a head_dim that is
  *     not a power of two).  Row buffers of such d hold d values per row.
  *   - n_rows == 0 (or an empty context) succeeds and launches nothing.
- *   - Non-finite inputs are not screened: outputs for such rows are
- *     unspecified, but every access stays inside the buffers described here.
+ *   - Non-finite inputs: a row holding an Inf or a NaN encodes as the zero
+ *     row (every index L/2 - 1) with a non-finite stored norm (tq_encode,
+ *     tq_append_row); decode and attention pass such norms on as IEEE
+ *     arithmetic does.  Every access stays inside the buffers described here.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -213,9 +215,13 @@ int tq_append_row(const tq_cache_desc *cache, int layer, const void *const *k_ne
                   const void *const *v_new, int dtype, int64_t pos, void *stream);
 
 /* Workspace bytes tq_attn_decode needs for this (cache, layer, n_q_heads,
- * ctx_len); 0 on invalid arguments. */
+ * ctx_len, sparse_v_threshold): the chunk records of the split over the
+ * context and, with the sparse-V gate on (threshold > 0), also every context
+ * row's scores (4 bytes per row and query head) and the chunk maxima.  0 on
+ * invalid arguments. */
 size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
-                               int n_q_heads, int64_t ctx_len);
+                               int n_q_heads, int64_t ctx_len,
+                               float sparse_v_threshold);
 
 /* Decode-step attention over the compressed cache of one layer, in the
  * rotated domain ([Foundry] Optimization: Fused dequant-dot; [Engine] 6
@@ -231,10 +237,13 @@ size_t tq_attn_workspace_bytes(const tq_cache_desc *cache, int layer,
  * scale <= 0 selects 1/sqrt(d).  out: [batch][n_q_heads][d] fp32 (device).
  * sparse_v_threshold in [0, 1): 0 disables the gate; otherwise the V row of
  * slot t contributes only where exp(score_t - m) > sparse_v_threshold, m the
- * largest score among slots [256 floor(t/256), +256) of the same query head
- * ([Atlas] "Sparse V dequant": V of rows with a negligible weight relative
- * to the running maximum is neither loaded nor decoded); gated rows stay in
- * the softmax denominator.  Invalid (negative, >= 1 or NaN) -> TQ_EINVAL.
+ * largest score of the whole context of the same query head, i.e. where the
+ * row's weight relative to the largest weight exceeds the threshold ([Atlas]
+ * "Sparse V dequant": V of rows whose softmax exponent against the maximum
+ * is below the threshold is neither loaded nor decoded).  Gated rows stay in
+ * the softmax denominator.  The gated path first scores the whole context
+ * (K only), then reads V for the kept rows.  Invalid (negative, >= 1 or NaN)
+ * -> TQ_EINVAL.
  * workspace: device buffer of at least tq_attn_workspace_bytes(...) bytes,
  * 16-byte aligned; its contents need no initialisation.  ctx_len >= 1.
  * window * head_dim / 2 (one KV head's packed rows at 4 bits, padded

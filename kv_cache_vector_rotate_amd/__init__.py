@@ -104,6 +104,7 @@ def tq_rotate(x: torch.Tensor, seed: int, inverse: bool = False, out=None, strea
     n = x.numel() // d if d else 0
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _check_shape(out, x.shape, "out", "tq_rotate")
     _check(lib().tq_rotate(_dev(x, "x"), _DTYPES[x.dtype], n, d, ctypes.c_uint64(seed), flags,
                            1 if inverse else 0, _dev(out, "out", torch.float32), _stream(stream)),
            "tq_rotate")
@@ -216,40 +217,72 @@ class TQCache:
         return self.layer_bits_k[layer], self.layer_bits_v[layer]
 
 
+def _check_shape(t, shape, name, fn):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def tq_append_row(cache: TQCache, layer: int, k_new, v_new, pos: int, stream=None):
     """k_new / v_new: a list of per-layer tensors [batch, n_kv, d_l] (layer = -1)
     or one tensor (a single layer)."""
-    ks = list(k_new) if layer < 0 else [k_new]
-    vs = list(v_new) if layer < 0 else [v_new]
-    if not ks or len(ks) != len(vs):
-        raise ValueError("tq_append_row: k_new / v_new lengths differ")
+    fn = "tq_append_row"
+    if layer < 0:
+        if layer != -1:
+            raise ValueError(f"{fn}: layer must be -1 (every layer) or a layer index")
+        ks, vs = list(k_new), list(v_new)
+        layers = range(cache.n_layers)
+        if len(ks) != cache.n_layers or len(vs) != cache.n_layers:
+            raise ValueError(f"{fn}: layer = -1 needs {cache.n_layers} K and V tensors "
+                             f"(got {len(ks)} and {len(vs)})")
+    else:
+        if layer >= cache.n_layers:
+            raise ValueError(f"{fn}: layer {layer} out of range (n_layers {cache.n_layers})")
+        ks, vs = [k_new], [v_new]
+        layers = [layer]
+    for l, kt, vt in zip(layers, ks, vs):
+        want = (cache.batch, cache.n_kv_heads, cache.head_dim[l])
+        _check_shape(kt, want, f"k_new[{l}]", fn)
+        _check_shape(vt, want, f"v_new[{l}]", fn)
+    if ks[0].dtype not in _DTYPES:
+        raise ValueError(f"{fn}: rows must be float32 or bfloat16")
     dt = _DTYPES[ks[0].dtype]
     for t in ks + vs:
         if t.dtype != ks[0].dtype:
-            raise ValueError("tq_append_row: mixed dtypes")
+            raise ValueError(f"{fn}: mixed dtypes")
     kp = (ctypes.c_void_p * len(ks))(*[_dev(t, "k_new").value for t in ks])
     vp = (ctypes.c_void_p * len(vs))(*[_dev(t, "v_new").value for t in vs])
     _check(lib().tq_append_row(ctypes.byref(cache.desc), layer, kp, vp, dt, pos, _stream(stream)),
-           "tq_append_row")
+           fn)
 
 
-def tq_attn_workspace_bytes(cache: TQCache, layer: int, n_q_heads: int, ctx_len: int) -> int:
-    return int(lib().tq_attn_workspace_bytes(ctypes.byref(cache.desc), layer, n_q_heads, ctx_len))
+def tq_attn_workspace_bytes(cache: TQCache, layer: int, n_q_heads: int, ctx_len: int,
+                            sparse_v: float = 0.0) -> int:
+    return int(lib().tq_attn_workspace_bytes(ctypes.byref(cache.desc), layer, n_q_heads, ctx_len,
+                                             ctypes.c_float(sparse_v)))
 
 
 def tq_attn_decode(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int, scale: float = 0.0,
                    out=None, workspace=None, stream=None, sparse_v: float = 0.0):
     """q: bf16 [batch, n_q_heads, d]; returns fp32 [batch, n_q_heads, d].
     sparse_v: the sparse-V gate threshold (0 = off)."""
-    n_q = q.shape[-2]
+    fn = "tq_attn_decode"
+    if not 0 <= layer < cache.n_layers:
+        raise ValueError(f"{fn}: layer {layer} out of range (n_layers {cache.n_layers})")
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError(f"{fn}: q must be a 3-D tensor [batch, n_q_heads, head_dim]")
+    n_q = q.shape[1]
+    _check_shape(q, (cache.batch, n_q, cache.head_dim[layer]), "q", fn)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    ws = tq_attn_workspace_bytes(cache, layer, n_q, ctx_len)
+    _check_shape(out, q.shape, "out", fn)
+    ws = tq_attn_workspace_bytes(cache, layer, n_q, ctx_len, sparse_v)
     if workspace is None:
         workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
     _check(lib().tq_attn_decode(ctypes.byref(cache.desc), layer, _dev(q, "q", torch.bfloat16), n_q,
                                 ctx_len, ctypes.c_float(scale), ctypes.c_float(sparse_v),
                                 _dev(out, "out", torch.float32),
                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                                _stream(stream)), "tq_attn_decode")
+                                _stream(stream)), fn)
     return out

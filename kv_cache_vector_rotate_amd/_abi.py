@@ -74,7 +74,7 @@ def lib():
         L.tq_encode.argtypes = [P, P, i32, i64, i32, i32, i32, u64, u32, P, P, P, P, P]
         L.tq_decode.argtypes = [P, P, i64, i32, i32, u64, u32, P, P]
         L.tq_append_row.argtypes = [P, i32, P, P, i32, i64, P]
-        L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64]
+        L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64, ctypes.c_float]
         L.tq_attn_workspace_bytes.restype = sz
         L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P, sz, P]
         L.tq_layer_bits_boundary.argtypes = [i32, i32, i32, i32, P]

@@ -53,6 +53,8 @@ struct AttnParams {
     const uint8_t *vp;
     const float *vn;
     float *part;              // [B][Hq][n_chunks][D + 4]: o'[D], max, sum
+    float *cmax;              // sparse-V gate: [B][Hq][n_chunks] chunk maxima of the scores
+    float *scores;            // sparse-V gate: [B][Hkv * gsplit][T][G / gsplit] scores
     float *out;               // [B][Hq][D]
     int Hq, Hkv, window, T, n_chunks, chunk_len;
     int gsplit;               // workgroups per KV head, each taking G of its query heads
@@ -140,147 +142,6 @@ __device__ __forceinline__ void lookup(const float *tab, uint64_t bits, int m, f
     }
 }
 
-// The per-wave scan with the sparse-V gate.  Wave w takes the aligned
-// 256-row blocks w, w + 4, ... of the chunk (chunks start on block
-// boundaries), so the gate's reference, the block's largest score, is known
-// to the wave alone.  Per block: pass A scores every row into the wave's LDS
-// scores and takes the block maximum; pass B turns scores into weights, adds
-// every row's weight to the denominator, loads and decodes V only for rows
-// some head keeps (exp(score - block max) > threshold), and skips the
-// arithmetic of a row pass that no lane keeps.
-template <int D, int BK, int BV, int G, int CPL>
-__device__ __forceinline__ void gated_scan(const AttnParams &p, const float *tabK,
-                                           const float *tabV, float (*scr)[G],
-                                           const float (&qr)[G][CPL], float (&acc)[G][CPL],
-                                           float (&m_run)[G], float (&l_part)[G],
-                                           int64_t rowbase, int t_begin, int t_end, int wave,
-                                           int sub, int rig)
-{
-    constexpr int P = D / CPL, RPW = 64 / P;
-    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
-    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
-    constexpr int NPASS = kTile / RPW;     // row passes per block
-    constexpr int CH = G >= 8 ? 4 : 8;     // row passes per step
-    static_assert(NPASS % CH == 0, "steps cover a block");
-    const int nblk = (t_end - t_begin + kTile - 1) / kTile;
-#pragma unroll 1
-    for (int blk = wave; blk < nblk; blk += kBlock / 64) {
-        const int bs = t_begin + blk * kTile;
-        // ---- pass A: scores of the block, and its maximum
-        float bm[G];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            bm[h] = -__builtin_huge_valf();
-#pragma unroll 1
-        for (int it0 = 0; it0 < NPASS; it0 += CH) {
-            uint64_t kb[CH];
-            float kn[CH];
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int t = bs + (it0 + c) * RPW + rig;
-                const int64_t row = rowbase + (t < t_end ? t : t_begin);
-                kb[c] = load_slice_bits<BK, CPL>(p.kp + row * RBK, (uint32_t)(sub * (CPL * BK / 8)));
-                kn[c] = p.kn[row];
-            }
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                float s[G];
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    s[h] = 0.0f;
-#pragma unroll
-                for (int m = 0; m < CPL / WK; m++) {
-                    float cc[WK];
-                    lookup<BK>(tabK, kb[c], m, cc);
-#pragma unroll
-                    for (int j = 0; j < WK; j++)
-#pragma unroll
-                        for (int h = 0; h < G; h++)
-                            s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
-                }
-#pragma unroll
-                for (int h = 0; h < G; h++)
-                    s[h] = sum_across<P>(s[h]) * kn[c];
-                const bool valid = bs + (it0 + c) * RPW + rig < t_end;
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    s[h] = valid ? s[h] : -__builtin_huge_valf();
-                    bm[h] = fmaxf(bm[h], s[h]);
-                }
-                if (sub == 0) {
-#pragma unroll
-                    for (int h = 0; h < G; h++)
-                        scr[(it0 + c) * RPW + rig][h] = s[h];
-                }
-            }
-        }
-        float bmax[G];
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            bmax[h] = wave_max(bm[h]);
-            if (bmax[h] > m_run[h]) {
-                const float fac = exp2f(m_run[h] - bmax[h]);  // 0 on the first block
-                l_part[h] *= fac;
-#pragma unroll
-                for (int k = 0; k < CPL; k++)
-                    acc[h][k] *= fac;
-                m_run[h] = bmax[h];
-            }
-        }
-        wave_lds_fence();  // the block's scores are in LDS
-        // ---- pass B: weights, the denominator, V of the kept rows
-#pragma unroll 1
-        for (int it0 = 0; it0 < NPASS; it0 += CH) {
-            float sc[CH][G];
-            bool kept[CH];
-            uint64_t vb[CH];
-            float vn[CH];
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                const int tl = (it0 + c) * RPW + rig;
-                kept[c] = false;
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    sc[c][h] = scr[tl][h];
-                    kept[c] |= sc[c][h] - bmax[h] > p.gate_log2;
-                }
-                vb[c] = 0;
-                vn[c] = 0.0f;
-                if (kept[c]) {
-                    const int64_t row = rowbase + bs + tl;
-                    vb[c] = load_slice_bits<BV, CPL>(p.vp + row * RBV, (uint32_t)(sub * (CPL * BV / 8)));
-                    vn[c] = p.vn[row];
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < CH; c++) {
-                float w[G];
-#pragma unroll
-                for (int h = 0; h < G; h++) {
-                    const float pr = m_run[h] == -__builtin_huge_valf()
-                                         ? 0.0f
-                                         : __builtin_amdgcn_exp2f(sc[c][h] - m_run[h]);
-                    l_part[h] += pr;  // gated rows stay in the denominator
-                    w[h] = sc[c][h] - bmax[h] > p.gate_log2 ? pr * vn[c] : 0.0f;
-                }
-                if (__ballot(kept[c]) == 0)
-                    continue;  // no lane keeps its row of this pass
-#pragma unroll
-                for (int m = 0; m < CPL / WV; m++) {
-                    float cc[WV];
-                    lookup<BV>(tabV, vb[c], m, cc);
-#pragma unroll
-                    for (int j = 0; j < WV; j++)
-#pragma unroll
-                        for (int h = 0; h < G; h++)
-                            acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
-                }
-            }
-        }
-        wave_lds_fence();  // every lane is done with the block's scores
-    }
-}
-
 // Layout of the exchange scan: P lanes share a row (CPL coordinates each), a
 // step covers one 256-row tile in P row passes, and lane `sub` of a row group
 // owns the softmax of the group's row in pass `sub`.  It takes this path when
@@ -298,13 +159,12 @@ struct Xch {
     static constexpr int XS = P * G + 4;  // floats per (row group, pass): P partials x G heads, padded
     static constexpr int XW = P * G + 4;  // floats per row group of weights, padded
     static constexpr int FLOATS = RPW * P * XS + RPW * XW;  // per wave
-    // + a second weight slot and a 256-row block's scores
-    static constexpr int GATED_FLOATS = FLOATS + RPW * XW + 4 * 64 * (G + 1);
 };
 
-// G consecutive floats of LDS, as one access where the width allows
+// G consecutive floats (LDS or global memory), as one access where the
+// width allows
 template <int G>
-__device__ __forceinline__ void lds_put(float *dst, const float (&v)[G])
+__device__ __forceinline__ void put_vec(float *dst, const float (&v)[G])
 {
     if constexpr (G == 4) {
         *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
@@ -318,7 +178,7 @@ __device__ __forceinline__ void lds_put(float *dst, const float (&v)[G])
 }
 
 template <int G>
-__device__ __forceinline__ void lds_get(const float *src, float (&v)[G])
+__device__ __forceinline__ void get_vec(const float *src, float (&v)[G])
 {
     if constexpr (G == 4) {
         const float4 t = *reinterpret_cast<const float4 *>(src);
@@ -361,7 +221,7 @@ __device__ __forceinline__ void xch_scores(const float *tabK, float *xrow,
                 for (int h = 0; h < G; h++)
                     s[h] = fmaf(qr[h][WK * m + j], cc[j], s[h]);
         }
-        lds_put<G>(xrow + c * X::XS + sub * G, s);
+        put_vec<G>(xrow + c * X::XS + sub * G, s);
     }
     wave_lds_fence();
 #pragma unroll
@@ -370,7 +230,7 @@ __device__ __forceinline__ void xch_scores(const float *tabK, float *xrow,
 #pragma unroll
     for (int j = 0; j < P; j++) {
         float v[G];
-        lds_get<G>(xrow + sub * X::XS + j * G, v);
+        get_vec<G>(xrow + sub * X::XS + j * G, v);
 #pragma unroll
         for (int h = 0; h < G; h++)
             sc[h] += v[h];
@@ -459,168 +319,138 @@ __device__ __forceinline__ void xch_step(const float *tabK, const float *tabV, f
         w[h] = pr * vn;
     }
     float *wrow = xw + rig * X::XW;
-    lds_put<G>(wrow + sub * G, w);
+    put_vec<G>(wrow + sub * G, w);
     wave_lds_fence();
 #pragma unroll
     for (int c = 0; c < P; c++) {
         float wc[G];
-        lds_get<G>(wrow + c * G, wc);
+        get_vec<G>(wrow + c * G, wc);
         xch_accumulate<D, BV, G>(tabV, vb[c], wc, acc);
     }
     wave_lds_fence();  // every lane is done with this tile's LDS blocks
 }
 
-// The exchange scan with the sparse-V gate.  The gate compares each row with
-// the largest score of its aligned 256-row block, so each wave takes whole
-// blocks (w, w + 4, ... of the chunk; chunks start on block boundaries) in
-// four 64-row parts: the wave scores the four parts, takes the block maximum,
-// then per part forms the weights (every row in the denominator; zero for
-// the heads that gate the row), passes them through LDS and loads and
-// decodes V only for rows with a nonzero weight.  The running maximum is per
-// wave.  The block's scores wait in LDS (`scs`, [part][lane][G], then the
-// rows' V norms [part][lane]) between the two passes; the V norms are read in
-// the score pass with the K norms, so that the second pass has no load whose
-// wait would also drain the V slices in flight.  Part j + 1's V slices are
-// issued (its weights in the other of two LDS slots) before part j is
-// accumulated.  Rows past the context read the last row (masked, or not
-// used).
-template <int D, int BK, int BV, int G>
-__device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float *tabK,
-                                               const float *tabV, float *xs, float *xw,
-                                               const float (&qr)[G][Xch<D, G>::CPL],
-                                               float (&acc)[G][Xch<D, G>::CPL],
-                                               float (&m_run)[G], float (&l_part)[G],
-                                               const uint8_t *kbase, const uint8_t *vbase,
-                                               const float *knb, const float *vnb, float *scs,
-                                               int t_begin, int t_end, int wave, int sub,
-                                               int rig)
+// q' = S2 H (D q) * scale * log2(e) / sqrt(d) for query heads h0 .. h0 + G - 1
+// of sequence b (S2 = identity for the one-sided rotation), into qs[G][D].
+// Wave 0 rotates; the caller synchronises the workgroup before reading qs.
+template <int D, int G>
+__device__ __forceinline__ void rotate_queries(const AttnParams &p, float (*qs)[D], int b, int h0,
+                                               int wave, int lane)
 {
-    using X = Xch<D, G>;
-    constexpr int CPL = X::CPL, P = X::P, RPW = X::RPW;
-    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
-    constexpr int SBK = CPL * BK / 8, SBV = CPL * BV / 8;
-    constexpr int NPART = kTile / 64;
-    const int lane = threadIdx.x & 63;
-    float *xrow = xs + rig * P * X::XS;
-    const int nblk = (t_end - t_begin + kTile - 1) / kTile;
-    float *vns = scs + 4 * 64 * G;
-    // K slices and this lane's row's K and V norms of the part whose first
-    // row (of this lane's row group) is tp
-    auto load_k = [&](int tp, uint64_t (&kb)[P], float &kn, float &vn) {
+    if (wave != 0)
+        return;
+    constexpr int P2 = D / kCPL;
+    const int sub2 = lane % P2, r2 = lane / P2;
+    float v[kCPL];
+    const int h = h0 + (r2 < G ? r2 : 0);
+    if (sub2 * kCPL < p.d_in) {
+        load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
+    } else {
 #pragma unroll
-        for (int c = 0; c < P; c++) {
-            const int t = min(tp + c * RPW, t_end - 1);
-            kb[c] = load_slice_bits<BK, CPL>(kbase, (uint32_t)t * RBK + (uint32_t)(sub * SBK));
-        }
-        const int to = min(tp + sub * RPW, t_end - 1);
-        kn = knb[to];
-        vn = vnb[to];
-    };
-    // part j's weights into LDS slot j & 1, then its kept rows' V slices
-    auto weights_and_v = [&](int bs, int j, const float (&bmax)[G], uint64_t (&vb)[P],
-                             uint32_t &kept) {
-        const int tp = bs + 64 * j + rig;
-        float *wrow = xw + ((j & 1) * RPW + rig) * X::XW;
-        float sc[G], w[G];
-        lds_get<G>(scs + (64 * j + lane) * G, sc);
-        const float vnr = vns[64 * j + lane];
-        bool keep = false;
+        for (int k = 0; k < kCPL; k++)
+            v[k] = 0.0f;  // the zero padding of a head_dim below D
+    }
+    apply_signs(v, p.signs[sub2]);
+    fwht_row<P2>(v, sub2);
+    apply_signs(v, p.signs2[sub2]);
+    if (r2 < G) {
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float pr = m_run[h] == -__builtin_huge_valf()
-                                 ? 0.0f
-                                 : __builtin_amdgcn_exp2f(sc[h] - m_run[h]);
-            l_part[h] += pr;  // gated rows stay in the denominator
-            const bool kh = sc[h] - bmax[h] > p.gate_log2;
-            w[h] = kh ? pr : 0.0f;
-            keep |= kh;
+        for (int k = 0; k < kCPL; k++)
+            qs[r2][sub2 * kCPL + k] = v[k] * p.qscale;
+    }
+}
+
+// This lane's coordinate slice of the G rotated queries
+template <int D, int G, int CPL>
+__device__ __forceinline__ void query_slices(const float (*qs)[D], int sub, float (&qr)[G][CPL])
+{
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            qr[h][k] = qs[h][sub * CPL + k];
+}
+
+// The end of a chunk: each wave's (o', max, sum) reduced over its row groups
+// (every lane of a row group holds the same sum, so the sums reduce across
+// row groups only), the waves merged by log-sum-exp through LDS (accs holds
+// wave w's o' at w * AST), and the chunk's record (o'[D], max, sum) of each
+// of the G query heads written to the workspace.
+template <int D, int G, int CPL, int AST>
+__device__ __forceinline__ void write_chunk_record(const AttnParams &p, float (&acc)[G][CPL],
+                                                   const float (&m_run)[G], float (&l_part)[G],
+                                                   float *accs, float (*red_m)[G],
+                                                   float (*red_l)[G], int b, int h0, int chunk)
+{
+    constexpr int P = D / CPL, RS = D + 4;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sub = lane % P, rig = lane / P;
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        float l = l_part[h];
+        if constexpr (P <= 1) l += lane_xor_any<1>(l);
+        if constexpr (P <= 2) l += lane_xor_any<2>(l);
+        if constexpr (P <= 4) l += lane_xor_any<4>(l);
+        if constexpr (P <= 8) l += lane_xor_any<8>(l);
+        if constexpr (P <= 16) l += lane_xor_any<16>(l);
+        if constexpr (P <= 32) l += lane_xor_any<32>(l);
+        l_part[h] = l;
+#pragma unroll
+        for (int k = 0; k < CPL; k++) {
+            float a = acc[h][k];
+            if constexpr (P <= 1) a += lane_xor_any<1>(a);
+            if constexpr (P <= 2) a += lane_xor_any<2>(a);
+            if constexpr (P <= 4) a += lane_xor_any<4>(a);
+            if constexpr (P <= 8) a += lane_xor_any<8>(a);
+            if constexpr (P <= 16) a += lane_xor_any<16>(a);
+            if constexpr (P <= 32) a += lane_xor_any<32>(a);
+            acc[h][k] = a;
         }
-        const float vn = keep ? vnr : 0.0f;
+    }
+    if (rig == 0) {
 #pragma unroll
         for (int h = 0; h < G; h++)
-            w[h] *= vn;
-        lds_put<G>(wrow + sub * G, w);
-        wave_lds_fence();
-        kept = 0;  // bit c: this row group keeps its row of pass c
 #pragma unroll
-        for (int c = 0; c < P; c++) {
-            float wc[G];
-            lds_get<G>(wrow + c * G, wc);
-            bool kc = false;
-#pragma unroll
-            for (int h = 0; h < G; h++)
-                kc |= wc[h] != 0.0f;
-            // the same for every lane of the row group; no branch around the
-            // load (where paths join the compiler would wait for every load in
-            // flight): rows no head keeps read the block's first row (a cache
-            // hit), unused
-            vb[c] = load_slice_bits<BV, CPL>(
-                vbase, (uint32_t)(kc ? tp + c * RPW : bs) * RBV + (uint32_t)(sub * SBV));
-            kept |= (uint32_t)kc << c;
-        }
-    };
-#pragma unroll 1
-    for (int blk = wave; blk < nblk; blk += kBlock / 64) {
-        const int bs = t_begin + blk * kTile;
-        // ---- the block's scores (this lane's row of each part) and maximum
-        float bm[G];
-#pragma unroll
-        for (int h = 0; h < G; h++)
-            bm[h] = -__builtin_huge_valf();
-#pragma unroll
-        for (int j = 0; j < NPART; j++) {
-            uint64_t kb[P];
-            float kn, vnp;
-            load_k(bs + 64 * j + rig, kb, kn, vnp);
-            const int to = bs + 64 * j + rig + sub * RPW;
-            float sc[G];
-            xch_scores<D, BK, G>(tabK, xrow, qr, kb, sub, sc);
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                sc[h] = to < t_end ? sc[h] * kn : -__builtin_huge_valf();
-                bm[h] = fmaxf(bm[h], sc[h]);
-            }
-            lds_put<G>(scs + (64 * j + lane) * G, sc);
-            vns[64 * j + lane] = vnp;
-            wave_lds_fence();  // the part's partials are read before the next part's
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        float bmax[G];
+            for (int k = 0; k < CPL; k++)
+                accs[wave * AST + h * D + sub * CPL + k] = acc[h][k];
+    }
+    if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            bmax[h] = wave_max(bm[h]);
-            if (bmax[h] > m_run[h]) {
-                const float fac = exp2f(m_run[h] - bmax[h]);  // 0 on the first block
-                l_part[h] *= fac;
-#pragma unroll
-                for (int k = 0; k < CPL; k++)
-                    acc[h][k] *= fac;
-                m_run[h] = bmax[h];
-            }
+            red_m[wave][h] = m_run[h];
+            red_l[wave][h] = l_part[h];
         }
-        // ---- weights and the V of the kept rows, one part ahead
-        uint64_t vb[2][P];
-        uint32_t kept[2];
-        weights_and_v(bs, 0, bmax, vb[0], kept[0]);
+    }
+    __syncthreads();
+    float *rec0 = p.part + (((int64_t)b * p.Hq + h0) * p.n_chunks + chunk) * RS;
+    const int64_t hstride = (int64_t)p.n_chunks * RS;
+    for (int i = tid; i < G * D; i += kBlock) {
+        const int h = i / D, j = i % D;
+        float M = red_m[0][h];
 #pragma unroll
-        for (int j = 0; j < NPART; j++) {
-            const int cur = j & 1, nxt = cur ^ 1;
-            if (j + 1 < NPART)
-                weights_and_v(bs, j + 1, bmax, vb[nxt], kept[nxt]);
-            __builtin_amdgcn_sched_barrier(0);
-            const float *wrow = xw + (cur * RPW + rig) * X::XW;
+        for (int w = 1; w < kBlock / 64; w++)
+            M = fmaxf(M, red_m[w][h]);
+        float o = 0.0f;
 #pragma unroll
-            for (int c = 0; c < P; c++) {
-                if (__ballot((kept[cur] >> c) & 1u) == 0)
-                    continue;  // no row group keeps its row of this pass
-                float wc[G];
-                lds_get<G>(wrow + c * G, wc);
-                xch_accumulate<D, BV, G>(tabV, vb[cur][c], wc, acc);
-            }
-            // slot `cur` is read before part j + 2 writes it
-            wave_lds_fence();
-            __builtin_amdgcn_sched_barrier(0);
+        for (int w = 0; w < kBlock / 64; w++) {
+            const float mw = red_m[w][h];
+            o += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * accs[w * AST + h * D + j];
         }
+        rec0[h * hstride + j] = o;
+    }
+    if (tid < G) {
+        float M = red_m[0][tid];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            M = fmaxf(M, red_m[w][tid]);
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kBlock / 64; w++) {
+            const float mw = red_m[w][tid];
+            l += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * red_l[w][tid];
+        }
+        rec0[tid * hstride + D] = M;
+        rec0[tid * hstride + D + 1] = l;
     }
 }
 
@@ -632,7 +462,7 @@ __device__ __forceinline__ void xch_gated_scan(const AttnParams &p, const float 
 // LDS traffic for scores and no barrier inside the scan.  Either way the four
 // waves' (o', max, sum) are merged once at the end.  Per-lane rows of wave w:
 // t_begin + it * RPB + w * RPW + (lane / P).
-template <int D, int BK, int BV, int G, bool GATE>
+template <int D, int BK, int BV, int G>
 __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 {
     constexpr int CPL = G >= 8 ? 8 : 16;  // coordinates per lane in the scan
@@ -640,7 +470,6 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     constexpr int RPW = 64 / P;
     constexpr int RPB = RPW * (kBlock / 64);
     constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
-    constexpr int RS = D + 4;
     constexpr int CH = G >= 8 ? 4 : 8;    // row passes per step
     constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
 
@@ -652,11 +481,9 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     // exchange scan: each wave's LDS blocks of partial scores and weights;
     // after the scan the same wave-owned region holds the wave's o' (accs)
     constexpr bool XON = Xch<D, G>::ON;
-    constexpr int XFL = GATE ? Xch<D, G>::GATED_FLOATS : Xch<D, G>::FLOATS;
+    constexpr int XFL = Xch<D, G>::FLOATS;
     constexpr int AST = XON && XFL > G * D ? XFL : G * D;
     __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
-    // sparse V on the per-lane scan: the scores of a wave's 256-row block
-    __shared__ float scw[GATE && !XON ? kBlock / 64 : 1][GATE && !XON ? kTile : 1][G];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int chunk = blockIdx.x, b = blockIdx.z;
@@ -665,39 +492,12 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 
     fill_lookup<BK>(tabK, p.centK);
     fill_lookup<BV>(tabV, p.centV);
-
-    // q' = S2 H (D q) * scale * log2(e) / sqrt(d) for the G heads of this KV
-    // head (S2 = identity for the one-sided rotation)
-    if (wave == 0) {
-        constexpr int P2 = D / kCPL;
-        const int sub2 = lane % P2, r2 = lane / P2;
-        float v[kCPL];
-        const int h = h0 + (r2 < G ? r2 : 0);
-        if (sub2 * kCPL < p.d_in) {
-            load_slice(p.q + ((int64_t)b * p.Hq + h) * p.d_in + sub2 * kCPL, v);
-        } else {
-#pragma unroll
-            for (int k = 0; k < kCPL; k++)
-                v[k] = 0.0f;  // the zero padding of a head_dim below D
-        }
-        apply_signs(v, p.signs[sub2]);
-        fwht_row<P2>(v, sub2);
-        apply_signs(v, p.signs2[sub2]);
-        if (r2 < G) {
-#pragma unroll
-            for (int k = 0; k < kCPL; k++)
-                qs[r2][sub2 * kCPL + k] = v[k] * p.qscale;
-        }
-    }
+    rotate_queries<D, G>(p, qs, b, h0, wave, lane);
     __syncthreads();
 
     const int sub = lane % P, rig = lane / P;
     float qr[G][CPL];
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int k = 0; k < CPL; k++)
-            qr[h][k] = qs[h][sub * CPL + k];
+    query_slices<D, G, CPL>(qs, sub, qr);
 
     float acc[G][CPL];
     float m_run[G], l_part[G];
@@ -721,24 +521,18 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
         const uint8_t *kbase = p.kp + rowbase * RBK;
         const uint8_t *vbase = p.vp + rowbase * RBV;
         const float *knb = p.kn + rowbase, *vnb = p.vn + rowbase;
-        if constexpr (GATE) {
-            xch_gated_scan<D, BK, BV, G>(p, tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
-                                         vbase, knb, vnb, xw + 2 * X::RPW * X::XW, t_begin, t_end,
-                                         wave, sub, rig);
-        } else {
-            // tiles of 256 rows (chunks start on tile boundaries); the last
-            // one may run past the context
-            int t0 = t_begin;
+        // tiles of 256 rows (chunks start on tile boundaries); the last one
+        // may run past the context
+        int t0 = t_begin;
 #pragma unroll 1
-            for (; t0 + kTile <= t_end; t0 += kTile)
-                xch_step<D, BK, BV, G, false>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
-                                              vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
-                                              t_end, sub, rig);
-            if (t0 < t_end)
-                xch_step<D, BK, BV, G, true>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase,
-                                             vbase, knb, vnb, t0 + wave * RPW + rig, t_begin,
-                                             t_end, sub, rig);
-        }
+        for (; t0 + kTile <= t_end; t0 += kTile)
+            xch_step<D, BK, BV, G, false>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase, vbase,
+                                          knb, vnb, t0 + wave * RPW + rig, t_begin, t_end, sub,
+                                          rig);
+        if (t0 < t_end)
+            xch_step<D, BK, BV, G, true>(tabK, tabV, xs, xw, qr, acc, m_run, l_part, kbase, vbase,
+                                         knb, vnb, t0 + wave * RPW + rig, t_begin, t_end, sub,
+                                         rig);
         // bring the row groups to the wave's maximum; each lane's sum covers
         // its own rows, so the sums add within the group first
 #pragma unroll
@@ -751,9 +545,6 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
                 acc[h][k] *= f;
             m_run[h] = M;
         }
-    } else if constexpr (GATE) {
-        gated_scan<D, BK, BV, G>(p, tabK, tabV, scw[wave], qr, acc, m_run, l_part, rowbase,
-                                 t_begin, t_end, wave, sub, rig);
     } else {
     // steps of CH row passes (CH * RPB rows); 32-bit row offsets from uniform
     // bases; only a step that runs past the context (the last) masks rows
@@ -860,77 +651,253 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
         step(s0, std::integral_constant<bool, true>{});
     }
 
-    // ---- reduce over the rows of the wave (lanes with equal `sub`); every
-    // lane of a row group holds the same sum, so the sums reduce across
-    // row groups only
+    write_chunk_record<D, G, CPL, AST>(p, acc, m_run, l_part, accs, red_m, red_l, b, h0, chunk);
+}
+
+// ---- The sparse-V gate ([Atlas] "Sparse V dequant"): the V row of a slot is
+// loaded and decoded only where the row's weight relative to the largest
+// weight of the context, exp(score - max score), exceeds the threshold;
+// every row stays in the softmax denominator.  The maximum needs every score
+// of the context, so the gated path runs two passes over the chunks.
+// attn_scores_kernel reads K only: each row's scores (log2 units) go to the
+// workspace, [B][n_grp][T][G] (the G query heads of a workgroup together;
+// n_grp = Hkv * gsplit), and each chunk's largest score per head to cmax.
+// attn_gated_v_kernel takes the context maximum from all chunk maxima, adds
+// every row's weight to the denominator and loads V only for the rows some
+// head keeps.  Its chunk records carry the context maximum, and the combine
+// kernel merges them like the ungated ones.
+template <int D, int BK, int G>
+__global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
+{
+    constexpr int CPL = G >= 8 ? 8 : 16;
+    constexpr int P = D / CPL, RPW = 64 / P, RPB = RPW * (kBlock / 64);
+    constexpr int RBK = D * BK / 8, SBK = CPL * BK / 8;
+    constexpr int WK = Lookup<BK>::W;
+    constexpr int CH = G >= 8 ? 4 : 8;  // row passes per step of the per-lane form
+    using X = Xch<D, G>;
+    constexpr bool XON = X::ON;
+
+    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK>::N * WK];
+    __shared__ float qs[G][D];
+    __shared__ float red_m[kBlock / 64][G];
+    __shared__ __attribute__((aligned(16))) float xbuf[XON ? kBlock / 64 * X::FLOATS : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    const int g = blockIdx.y / p.gsplit;
+    const int h0 = blockIdx.y * G;
+    fill_lookup<BK>(tabK, p.centK);
+    rotate_queries<D, G>(p, qs, b, h0, wave, lane);
+    __syncthreads();
+    const int sub = lane % P, rig = lane / P;
+    float qr[G][CPL];
+    query_slices<D, G, CPL>(qs, sub, qr);
+
+    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
+    const uint8_t *kbase = p.kp + rowbase * RBK;
+    const float *knb = p.kn + rowbase;
+    float *srow = p.scores + ((int64_t)b * gridDim.y + blockIdx.y) * p.T * G;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.T, t_begin + p.chunk_len);
+    float mx[G];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+        mx[h] = -__builtin_huge_valf();
+
+    if constexpr (XON) {
+        // tiles of 256 rows: P row passes per wave, lane `sub` of a row group
+        // sums the partials of the group's row of pass `sub` (exchange scan)
+        float *xrow = xbuf + wave * X::FLOATS + rig * P * X::XS;
+#pragma unroll 1
+        for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
+            const int tw = t0 + wave * RPW + rig;
+            uint64_t kb[P];
+#pragma unroll
+            for (int c = 0; c < P; c++) {
+                const int t = min(tw + c * RPB, t_end - 1);
+                kb[c] = load_slice_bits<BK, CPL>(kbase, (uint32_t)t * RBK + (uint32_t)(sub * SBK));
+            }
+            const int to = tw + sub * RPB;
+            const float kn = knb[min(to, t_end - 1)];
+            float sc[G];
+            xch_scores<D, BK, G>(tabK, xrow, qr, kb, sub, sc);
+            if (to < t_end) {
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    sc[h] *= kn;
+                    mx[h] = fmaxf(mx[h], sc[h]);
+                }
+                put_vec<G>(srow + (int64_t)to * G, sc);
+            }
+            wave_lds_fence();  // the tile's partials are read before the next tile's
+        }
+    } else {
+        // steps of CH row passes; every lane of a row holds the row's sums
+#pragma unroll 1
+        for (int s0 = t_begin; s0 < t_end; s0 += CH * RPB) {
+            const int t0 = s0 + wave * RPW + rig;
+            uint64_t kb[CH];
+            float kn[CH];
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                const int t = min(t0 + c * RPB, t_end - 1);
+                kb[c] = load_slice_bits<BK, CPL>(kbase, (uint32_t)t * RBK + (uint32_t)(sub * SBK));
+                kn[c] = knb[t];
+            }
+#pragma unroll
+            for (int c = 0; c < CH; c++) {
+                float sc[G];
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    sc[h] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < CPL / WK; m++) {
+                    float cc[WK];
+                    lookup<BK>(tabK, kb[c], m, cc);
+#pragma unroll
+                    for (int j = 0; j < WK; j++)
+#pragma unroll
+                        for (int h = 0; h < G; h++)
+                            sc[h] = fmaf(qr[h][WK * m + j], cc[j], sc[h]);
+                }
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    sc[h] = sum_across<P>(sc[h]) * kn[c];
+                const int t = t0 + c * RPB;
+                if (t < t_end) {
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        mx[h] = fmaxf(mx[h], sc[h]);
+                    if (sub == 0)
+                        put_vec<G>(srow + (int64_t)t * G, sc);
+                }
+            }
+        }
+    }
+    // the chunk's largest score per head
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        float l = l_part[h];
-        if constexpr (P <= 1) l += lane_xor_any<1>(l);
-        if constexpr (P <= 2) l += lane_xor_any<2>(l);
-        if constexpr (P <= 4) l += lane_xor_any<4>(l);
-        if constexpr (P <= 8) l += lane_xor_any<8>(l);
-        if constexpr (P <= 16) l += lane_xor_any<16>(l);
-        if constexpr (P <= 32) l += lane_xor_any<32>(l);
-        l_part[h] = l;
-#pragma unroll
-        for (int k = 0; k < CPL; k++) {
-            float a = acc[h][k];
-            if constexpr (P <= 1) a += lane_xor_any<1>(a);
-            if constexpr (P <= 2) a += lane_xor_any<2>(a);
-            if constexpr (P <= 4) a += lane_xor_any<4>(a);
-            if constexpr (P <= 8) a += lane_xor_any<8>(a);
-            if constexpr (P <= 16) a += lane_xor_any<16>(a);
-            if constexpr (P <= 32) a += lane_xor_any<32>(a);
-            acc[h][k] = a;
-        }
-    }
-    if (rig == 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++)
-#pragma unroll
-            for (int k = 0; k < CPL; k++)
-                accs[wave * AST + h * D + sub * CPL + k] = acc[h][k];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; h++) {
-            red_m[wave][h] = m_run[h];
-            red_l[wave][h] = l_part[h];
-        }
+        const float m = wave_max(mx[h]);
+        if (lane == 0)
+            red_m[wave][h] = m;
     }
     __syncthreads();
-    // ---- merge the waves (log-sum-exp) and write this chunk's record
-    float *rec0 = p.part + (((int64_t)b * p.Hq + h0) * p.n_chunks + chunk) * RS;
-    const int64_t hstride = (int64_t)p.n_chunks * RS;
-    for (int i = tid; i < G * D; i += kBlock) {
-        const int h = i / D, j = i % D;
-        float M = red_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kBlock / 64; w++)
-            M = fmaxf(M, red_m[w][h]);
-        float o = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kBlock / 64; w++) {
-            const float mw = red_m[w][h];
-            o += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * accs[w * AST + h * D + j];
-        }
-        rec0[h * hstride + j] = o;
-    }
     if (tid < G) {
-        float M = red_m[0][tid];
+        float m = red_m[0][tid];
 #pragma unroll
         for (int w = 1; w < kBlock / 64; w++)
-            M = fmaxf(M, red_m[w][tid]);
-        float l = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kBlock / 64; w++) {
-            const float mw = red_m[w][tid];
-            l += mw == -__builtin_huge_valf() ? 0.0f : exp2f(mw - M) * red_l[w][tid];
-        }
-        rec0[tid * hstride + D] = M;
-        rec0[tid * hstride + D + 1] = l;
+            m = fmaxf(m, red_m[w][tid]);
+        p.cmax[((int64_t)b * p.Hq + h0 + tid) * p.n_chunks + chunk] = m;
     }
+}
+
+template <int D, int BV, int G>
+__global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
+{
+    constexpr int CPL = G >= 8 ? 8 : 16;
+    constexpr int P = D / CPL, RPW = 64 / P, RPB = RPW * (kBlock / 64);
+    constexpr int RBV = D * BV / 8, SBV = CPL * BV / 8;
+    constexpr int WV = Lookup<BV>::W;
+    constexpr int CH = G >= 8 ? 4 : 8;  // row passes per step
+    constexpr int AST = G * D;
+
+    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV>::N * WV];
+    __shared__ float red_m[kBlock / 64][G];
+    __shared__ float red_l[kBlock / 64][G];
+    __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, b = blockIdx.z;
+    const int g = blockIdx.y / p.gsplit;
+    const int h0 = blockIdx.y * G;
+    fill_lookup<BV>(tabV, p.centV);
+    // the context's largest score of each head: the largest chunk maximum
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const float *cm = p.cmax + ((int64_t)b * p.Hq + h0 + h) * p.n_chunks;
+        float m = -__builtin_huge_valf();
+        for (int c = tid; c < p.n_chunks; c += kBlock)
+            m = fmaxf(m, cm[c]);
+        m = wave_max(m);
+        if (lane == 0)
+            red_m[wave][h] = m;
+    }
+    __syncthreads();
+    float M[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        M[h] = red_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kBlock / 64; w++)
+            M[h] = fmaxf(M[h], red_m[w][h]);
+    }
+    __syncthreads();  // red_m is reused by the record
+
+    const int sub = lane % P, rig = lane / P;
+    float acc[G][CPL], l_part[G];
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        l_part[h] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CPL; k++)
+            acc[h][k] = 0.0f;
+    }
+    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
+    const uint8_t *vbase = p.vp + rowbase * RBV;
+    const float *vnb = p.vn + rowbase;
+    const float *srow = p.scores + ((int64_t)b * gridDim.y + blockIdx.y) * p.T * G;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.T, t_begin + p.chunk_len);
+#pragma unroll 1
+    for (int s0 = t_begin; s0 < t_end; s0 += CH * RPB) {
+        const int t0 = s0 + wave * RPW + rig;
+        float sc[CH][G];
+#pragma unroll
+        for (int c = 0; c < CH; c++)
+            get_vec<G>(srow + (int64_t)min(t0 + c * RPB, t_end - 1) * G, sc[c]);
+        // V of the rows some head keeps (the same decision on every lane of a
+        // row); no branch around the load: rows nobody keeps read the chunk's
+        // first row, which is not used
+        uint64_t vb[CH];
+        float vn[CH];
+        bool kept[CH];
+#pragma unroll
+        for (int c = 0; c < CH; c++) {
+            const int t = t0 + c * RPB;
+            bool k = false;
+#pragma unroll
+            for (int h = 0; h < G; h++)
+                k |= sc[c][h] - M[h] > p.gate_log2;
+            kept[c] = k && t < t_end;
+            const int tv = kept[c] ? t : t_begin;
+            vb[c] = load_slice_bits<BV, CPL>(vbase, (uint32_t)tv * RBV + (uint32_t)(sub * SBV));
+            vn[c] = vnb[tv];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; c++) {
+            const bool valid = t0 + c * RPB < t_end;
+            float w[G];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float pr = valid ? __builtin_amdgcn_exp2f(sc[c][h] - M[h]) : 0.0f;
+                l_part[h] += pr;
+                w[h] = kept[c] && sc[c][h] - M[h] > p.gate_log2 ? pr * vn[c] : 0.0f;
+            }
+            if (__ballot(kept[c]) == 0)
+                continue;  // no lane keeps its row of this pass
+#pragma unroll
+            for (int m = 0; m < CPL / WV; m++) {
+                float cc[WV];
+                lookup<BV>(tabV, vb[c], m, cc);
+#pragma unroll
+                for (int j = 0; j < WV; j++)
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        acc[h][WV * m + j] = fmaf(w[h], cc[j], acc[h][WV * m + j]);
+            }
+        }
+    }
+    write_chunk_record<D, G, CPL, AST>(p, acc, M, l_part, accs, red_m, red_l, b, h0, chunk);
 }
 
 // Merge the chunks of one (sequence, query head) and rotate back.  One
@@ -1101,15 +1068,15 @@ Split split_for(int batch, int n_kv, int64_t ctx_len, int window, int D, int G)
     return s;
 }
 
-template <int D, int BK, int BV, bool GATE>
+template <int D, int BK, int BV>
 void launch_attn_wave(int G, dim3 grid, AttnParams p, hipStream_t st)
 {
     dim3 block(kBlock);
     p.gsplit = 1;
     switch (G) {
-    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1, GATE>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2, GATE>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
     default:
         if constexpr (Xch<D, 4>::ON && !Xch<D, 8>::ON) {
             // eight query heads per KV head: two workgroups of four each (the
@@ -1117,23 +1084,46 @@ void launch_attn_wave(int G, dim3 grid, AttnParams p, hipStream_t st)
             // could have); each reads the KV head's rows
             p.gsplit = 2;
             grid.y *= 2;
-            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4, GATE>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4>), grid, block, 0, st, p);
         } else {
-            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8, GATE>), grid, block, 0, st, p);
+            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 8>), grid, block, 0, st, p);
         }
         break;
     }
 }
 
-// the sparse-V gate is a separate instantiation: the kernel without it is the
-// one that runs when the threshold is 0
-template <int D, int BK, int BV>
-void launch_attn_g(int G, dim3 grid, const AttnParams &p, hipStream_t st)
+// the sparse-V gate's two passes for workgroups of GW query heads
+template <int D, int BK, int BV, int GW>
+void launch_gated(dim3 grid, const AttnParams &p, hipStream_t st)
 {
-    if (p.gate_log2 > -__builtin_huge_valf())
-        launch_attn_wave<D, BK, BV, true>(G, grid, p, st);
-    else
-        launch_attn_wave<D, BK, BV, false>(G, grid, p, st);
+    hipLaunchKernelGGL((attn_scores_kernel<D, BK, GW>), grid, dim3(kBlock), 0, st, p);
+    hipLaunchKernelGGL((attn_gated_v_kernel<D, BV, GW>), grid, dim3(kBlock), 0, st, p);
+}
+
+// Query heads per workgroup of the sparse-V passes: as on the ungated path
+// (eight query heads as two workgroups of four where the exchange scan runs)
+template <int D, int BK, int BV>
+void launch_attn_g(int G, dim3 grid, AttnParams p, hipStream_t st)
+{
+    if (!(p.gate_log2 > -__builtin_huge_valf())) {
+        launch_attn_wave<D, BK, BV>(G, grid, p, st);
+        return;
+    }
+    switch (G) {
+    case 1: p.gsplit = 1; launch_gated<D, BK, BV, 1>(grid, p, st); break;
+    case 2: p.gsplit = 1; launch_gated<D, BK, BV, 2>(grid, p, st); break;
+    case 4: p.gsplit = 1; launch_gated<D, BK, BV, 4>(grid, p, st); break;
+    default:
+        if constexpr (Xch<D, 4>::ON && !Xch<D, 8>::ON) {
+            p.gsplit = 2;
+            grid.y *= 2;
+            launch_gated<D, BK, BV, 4>(grid, p, st);
+        } else {
+            p.gsplit = 1;
+            launch_gated<D, BK, BV, 8>(grid, p, st);
+        }
+        break;
+    }
 }
 
 template <int D, int BK>
@@ -1158,19 +1148,38 @@ void launch_attn_d(int BK, int BV, int G, dim3 grid, const AttnParams &p, hipStr
                        dim3(kCombineThreads), 0, st, p);
 }
 
+// Workspace layout: the chunk records [B][Hq][n_chunks][D + 4] floats; with
+// the sparse-V gate also the chunk maxima [B][Hq][n_chunks] (padded to 16
+// bytes) and every row's scores [B][Hq][T] floats.
+struct WsLayout {
+    size_t part, cmax, scores, total;  // byte offsets and the size
+};
+
+WsLayout ws_layout(int batch, int n_q_heads, const Split &s, int D, bool gated)
+{
+    WsLayout w;
+    const size_t bh = (size_t)batch * (size_t)n_q_heads;
+    w.part = 0;
+    w.cmax = bh * s.n_chunks * (size_t)(D + 4) * sizeof(float);
+    w.scores = w.cmax + (gated ? (bh * s.n_chunks * sizeof(float) + 15) / 16 * 16 : 0);
+    w.total = w.scores + (gated ? bh * (size_t)s.T * sizeof(float) : 0);
+    return w;
+}
+
 }  // namespace
 
 extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int n_q_heads,
-                                          int64_t ctx_len)
+                                          int64_t ctx_len, float sparse_v_threshold)
 {
     if (!c || layer < 0 || layer >= c->n_layers || !c->head_dim || n_q_heads < 1 ||
-        ctx_len < 1 || c->window < 1 || c->batch < 0 || c->n_kv_heads < 1)
+        ctx_len < 1 || c->window < 1 || c->batch < 0 || c->n_kv_heads < 1 ||
+        !(sparse_v_threshold >= 0.0f && sparse_v_threshold < 1.0f))
         return 0;
     const int D = tq::padded_dim(c->head_dim[layer]);
     if (D == 0)
         return 0;
     Split s = split_for(c->batch, c->n_kv_heads, ctx_len, c->window, D, n_q_heads / c->n_kv_heads);
-    return (size_t)c->batch * n_q_heads * s.n_chunks * (size_t)(D + 4) * sizeof(float);
+    return ws_layout(c->batch, n_q_heads, s, D, sparse_v_threshold > 0.0f).total;
 }
 
 extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
@@ -1218,7 +1227,7 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
          (uintptr_t)c->k_packed[layer] | (uintptr_t)c->v_packed[layer]) % 16 != 0 ||
         ((uintptr_t)c->k_norms[layer] | (uintptr_t)c->v_norms[layer]) % 4 != 0)
         return tq::fail(TQ_EINVAL, "tq_attn_decode: misaligned buffer");
-    const size_t need = tq_attn_workspace_bytes(c, layer, n_q_heads, ctx_len);
+    const size_t need = tq_attn_workspace_bytes(c, layer, n_q_heads, ctx_len, sparse_v_threshold);
     if (ws_bytes < need)
         return tq::fail(TQ_EINVAL, "tq_attn_decode: workspace too small (need " +
                                        std::to_string(need) + " bytes)");
@@ -1235,7 +1244,10 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     p.kn = c->k_norms[layer];
     p.vp = c->v_packed[layer];
     p.vn = c->v_norms[layer];
-    p.part = static_cast<float *>(workspace);
+    const WsLayout wl = ws_layout(c->batch, n_q_heads, s, D, sparse_v_threshold > 0.0f);
+    p.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + wl.part);
+    p.cmax = reinterpret_cast<float *>(static_cast<char *>(workspace) + wl.cmax);
+    p.scores = reinterpret_cast<float *>(static_cast<char *>(workspace) + wl.scores);
     p.out = out;
     p.Hq = n_q_heads;
     p.Hkv = c->n_kv_heads;

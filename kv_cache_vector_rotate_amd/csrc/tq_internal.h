@@ -1,5 +1,5 @@
 // Internal declarations shared by the host half (tq_host.cpp) and the device
-// half (tq_kernels.hip) of libtq.so.  Not installed; not part of the ABI.
+// half (tq_codec.hip, tq_attn.hip) of libtq.so.  Not installed; not part of the ABI.
 #pragma once
 
 #include <cstdint>

@@ -10,7 +10,14 @@ Tolerances (the task's contract for this codec, restated):
   * norms: |n_gpu - n_oracle| <= 1e-5 * n_oracle;
   * decoded rows (compared on identical packed input, so index flips cannot
     leak in): max_i |x_gpu - x_oracle| <= 1e-5 * ||x_oracle||_2 per row;
-  * attention outputs: within 2e-3 absolute (fp32 accumulation).
+  * attention outputs: within 2e-3 absolute (fp32 accumulation) and, since
+    outputs of long contexts are small (RMS ~ sqrt(e/T) for N(0,1) scores),
+    a relative L2 error of at most 1e-4 per output row (fp32 against the
+    fp64 definition sits near 1e-6).
+
+Where several results are correct -- a coordinate exactly on a decision
+boundary, whose two neighbouring cells are equally near -- the index must
+be one of those two (check_indices_with_ties).
 """
 from __future__ import annotations
 
@@ -21,6 +28,7 @@ BAND_FRACTION = 1e-5
 NORM_RTOL = 1e-5
 DECODE_RTOL = 1e-5
 ATTN_ATOL = 2e-3
+ATTN_REL_L2 = 1e-4
 
 
 def unpack_rows(packed: np.ndarray, d: int, bits: int) -> np.ndarray:
@@ -67,6 +75,27 @@ def check_indices(gpu_packed, orc_packed, u, d, bits, boundaries, total_coords=N
     return n_mism
 
 
+def check_indices_with_ties(gpu_packed, orc_packed, u, d, bits, boundaries, tally):
+    """check_indices for hand-made rows with exact ties: where the oracle's u
+    lies exactly on a boundary either neighbouring cell is correct (|diff| <=
+    1, not counted); every other coordinate follows check_indices (exact
+    outside the 1e-6 band, in-band mismatches counted in the tally)."""
+    ig = unpack_rows(gpu_packed, d, bits).astype(np.int64)
+    io = unpack_rows(orc_packed, d, bits).astype(np.int64)
+    b = np.asarray(boundaries, np.float64)
+    dist = np.abs(np.asarray(u, np.float64)[..., None] - b).min(-1)
+    tie = dist == 0.0
+    assert np.all(np.abs(ig[tie] - io[tie]) <= 1), "a tie took a cell that is not next to it"
+    mism = (ig != io) & ~tie
+    outside = mism & (dist > BAND)
+    assert not outside.any(), (
+        f"{int(outside.sum())} index mismatches outside the 1e-6 band; first at "
+        f"{np.argwhere(outside)[:3].tolist()}")
+    tally.mismatches += int(mism.sum())
+    tally.coords += int((~tie).sum())
+    return int(tie.sum())
+
+
 def check_norms(gpu, orc):
     gpu = np.asarray(gpu, np.float64)
     orc = np.asarray(orc, np.float64)
@@ -91,9 +120,13 @@ def check_decoded(gpu, orc):
 
 
 def check_attention(gpu, orc):
+    """One output row (or a stack of rows compared row by row)."""
     gpu = np.asarray(gpu, np.float64)
     orc = np.asarray(orc, np.float64)
     err = np.abs(gpu - orc).max()
     assert err <= ATTN_ATOL, f"attention max abs error {err}"
-    rel = np.linalg.norm(gpu - orc) / max(np.linalg.norm(orc), 1e-30)
+    g2 = gpu.reshape(-1, gpu.shape[-1])
+    o2 = orc.reshape(-1, orc.shape[-1])
+    rel = (np.linalg.norm(g2 - o2, axis=1) / np.maximum(np.linalg.norm(o2, axis=1), 1e-30)).max()
+    assert rel <= ATTN_REL_L2, f"attention relative L2 error {rel}"
     return float(err), float(rel)

@@ -9,6 +9,7 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -178,10 +179,15 @@ def test_cache_and_attention_validation(tq):
     assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 0, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EINVAL
     assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, 0.0, A, A, 16, None) == tq.TQ_EINVAL
     assert "workspace" in tq.tq_last_error()
-    ws = L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5)
+    ws = L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5, 0.0)
     # 2 sequences x 4 query heads x 1 chunk x (128 + 4) floats
     assert ws == 2 * 4 * 1 * 132 * 4
-    assert L.tq_attn_workspace_bytes(ctypes.byref(d), 5, 4, 5) == 0
+    # with the sparse-V gate: + the chunk maxima (2 x 4 x 1 floats, padded to
+    # 16 bytes) + every context row's scores (2 x 4 x 5 floats)
+    assert L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5, 1e-3) == ws + 32 + 2 * 4 * 5 * 4
+    assert L.tq_attn_workspace_bytes(ctypes.byref(d), 5, 4, 5, 0.0) == 0
+    for bad in (-0.1, 1.0, float("nan")):
+        assert L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 5, bad) == 0
     for bad in (-0.1, 1.0, float("nan")):
         assert L.tq_attn_decode(ctypes.byref(d), 0, A, 4, 5, 0.0, bad, A, A, 1 << 20, None) == tq.TQ_EINVAL
     assert "sparse_v" in tq.tq_last_error()
@@ -192,7 +198,7 @@ def test_cache_and_attention_validation(tq):
     d2 = _desc(tq, head_dim=96, batch=0)
     assert L.tq_attn_decode(ctypes.byref(d2), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_OK
     # the workspace holds the padded length: 2 x 4 x 1 x (128 + 4) floats
-    assert L.tq_attn_workspace_bytes(ctypes.byref(_desc(tq, head_dim=96)), 0, 4, 5) == 2 * 4 * 132 * 4
+    assert L.tq_attn_workspace_bytes(ctypes.byref(_desc(tq, head_dim=96)), 0, 4, 5, 0.0) == 2 * 4 * 132 * 4
     d3 = _desc(tq, bk=1)
     assert L.tq_attn_decode(ctypes.byref(d3), 0, A, 4, 5, 0.0, 0.0, A, A, 1 << 20, None) == tq.TQ_EUNSUPPORTED
     d4 = _desc(tq, flags=4)
@@ -204,6 +210,40 @@ def test_cache_and_attention_validation(tq):
     assert "window" in tq.tq_last_error()
     assert L.tq_append_row(ctypes.byref(d4), -1, arr, arr, 0, 0, None) == tq.TQ_EINVAL
     assert "flag" in tq.tq_last_error()
+
+
+def test_binding_rejects_mismatched_shapes(tq):
+    """The Python binding checks every tensor against the cache before any
+    pointer reaches the library (host-only: CPU tensors, so a shape that
+    passed would fail the device check instead, with another message)."""
+    cache = tq.TQCache(3, 2, 2, 16, [128, 64, 128], 4, 2, device="cpu")
+    bf = torch.bfloat16
+    for q in (torch.zeros(1, 4, 128, dtype=bf),       # batch 1, cache batch 2
+              torch.zeros(2, 4, 64, dtype=bf),        # head_dim of another layer
+              torch.zeros(2, 4, 128, 1, dtype=bf),    # not 3-D
+              torch.zeros(8, 128, dtype=bf)):
+        with pytest.raises(ValueError, match="q"):
+            tq.tq_attn_decode(cache, 0, q, 16)
+    with pytest.raises(ValueError, match="out"):
+        tq.tq_attn_decode(cache, 0, torch.zeros(2, 4, 128, dtype=bf), 16,
+                          out=torch.zeros(2, 4, 64))
+    with pytest.raises(ValueError, match="layer"):
+        tq.tq_attn_decode(cache, 3, torch.zeros(2, 4, 128, dtype=bf), 16)
+    rows = [torch.zeros(2, 2, d) for d in (128, 64, 128)]
+    with pytest.raises(ValueError, match="3 K and V"):
+        tq.tq_append_row(cache, -1, rows[:2], rows[:2], 0)
+    with pytest.raises(ValueError, match="3 K and V"):
+        tq.tq_append_row(cache, -1, rows, rows[:2], 0)
+    with pytest.raises(ValueError, match=r"k_new\[1\]"):
+        tq.tq_append_row(cache, -1, [rows[0], rows[0], rows[2]], rows, 0)
+    with pytest.raises(ValueError, match=r"v_new\[0\]"):
+        tq.tq_append_row(cache, 0, rows[0], torch.zeros(2, 3, 128), 0)
+    with pytest.raises(ValueError, match="out of range"):
+        tq.tq_append_row(cache, 3, rows[0], rows[0], 0)
+    with pytest.raises(ValueError, match="device"):   # shapes pass, then the device check
+        tq.tq_append_row(cache, 1, rows[1], rows[1], 0)
+    with pytest.raises(ValueError, match="out"):
+        tq.tq_rotate(torch.zeros(4, 128), 42, out=torch.zeros(4, 64))
 
 
 def test_layer_bits_boundary_policy(tq):

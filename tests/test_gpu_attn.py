@@ -194,6 +194,42 @@ def test_attention_sparse_v_short(tq, orc, d, G, T):
             check_attention(o[b, h], ref[h])
 
 
+@pytest.mark.parametrize("t_dom", [5, 2900])
+def test_attention_sparse_v_dominant_row_across_chunks(tq, orc, t_dom):
+    """One dominant row, early or late, in a 3000-slot context that the
+    kernels split over many chunks: against the context's largest score
+    every other row of the four query heads that share it is gated, in every
+    chunk (a reference maximum per chunk or per 256-row block would keep
+    hundreds of them).  The other KV head's heads see ordinary scores."""
+    d, B, Hkv, G, T = 128, 1, 2, 4, 3000
+    cache = tq.TQCache(1, B, Hkv, T, d, 4, 2, SEED)
+    _fill(tq, cache, 0, 95 + t_dom)
+    kp = cache.k_packed[0][0, 0].cpu().numpy()
+    kn = cache.k_norms[0][0, 0].cpu().numpy()
+    Kh = orc.decode(kp, kn, d, 4, SEED, f64=True)
+    qd = Kh[t_dom] / np.linalg.norm(Kh[t_dom]) * 3.0
+    q = kvgen.normal((B, Hkv * G, d), 96, "cuda", torch.bfloat16)
+    q[0, :G] = torch.from_numpy(qd).to(torch.bfloat16).cuda()
+    qf = q[0, 0].float().cpu().numpy().astype(np.float64)
+    scale = 1 / math.sqrt(d)
+    s = scale * Kh @ qf
+    # raise the row's key norm until its score leads every other by 10
+    f = (np.delete(s, t_dom).max() + 10.0) / s[t_dom]
+    assert f > 1
+    cache.k_norms[0][0, 0, t_dom] *= float(f)
+    kn = cache.k_norms[0][0, 0].cpu().numpy()
+    s = scale * orc.decode(kp, kn, d, 4, SEED, f64=True) @ qf
+    rel = np.exp(s - s.max())
+    assert (rel > 1e-3).sum() == 1
+    per_block = sum(int((np.exp(s[b0:b0 + 256] - s[b0:b0 + 256].max()) > 1e-3).sum())
+                    for b0 in range(0, T, 256))
+    assert per_block > 100
+    o = tq.tq_attn_decode(cache, 0, q, T, sparse_v=1e-3).cpu().numpy()
+    ref = _oracle(orc, cache, 0, q, 0, range(Hkv * G), T, scale, sparse_v=1e-3)
+    for h in range(Hkv * G):
+        check_attention(o[0, h], ref[h])
+
+
 def test_config4_attention_sparse_v_sampled(tq, orc):
     """The bench's attention launch with the sparse-V gate at 1e-3, sampled."""
     B, Hq, Hkv, d, T = 32, 32, 8, 128, 16384
