@@ -252,6 +252,30 @@ int tq_attn_decode(const tq_cache_desc *cache, int layer, const uint16_t *q_bf16
                    int n_q_heads, int64_t ctx_len, float scale, float sparse_v_threshold,
                    float *out, void *workspace, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * attention as tq_attn_decode -- same kernels, same results -- with the
+ * library's own static device scratch in place of the caller's workspace.
+ * The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); the caller still passes q, out and the cache.
+ * Scratch: one file-scope device array of TQ_ATTN_NOALLOC_MAX_BYTES per GPU,
+ * held from the library's load on that GPU until the process ends.  A call
+ * whose tq_attn_workspace_bytes(...) exceeds it returns TQ_EINVAL (the
+ * ungated path needs B * n_q_heads * n_chunks * (D + 4) * 4 bytes, about
+ * 1 MiB at batch 32 x 32 query heads; the sparse-V gate adds 4 bytes per
+ * context row and query head).  Every call on a GPU shares that GPU's
+ * scratch, which keeps the last call's contents (the kernels need no
+ * initialisation): calls that overlap on one GPU (several streams or host
+ * threads without ordering between them) race.  Arguments and errors
+ * otherwise as tq_attn_decode; the first call on a device also looks up the
+ * scratch's address there (TQ_EHIP if the runtime fails). */
+#define TQ_ATTN_NOALLOC_MAX_BYTES (16u << 20)
+
+int tq_attn_decode_noalloc(const tq_cache_desc *cache, int layer, const uint16_t *q_bf16,
+                           int n_q_heads, int64_t ctx_len, float scale,
+                           float sparse_v_threshold, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

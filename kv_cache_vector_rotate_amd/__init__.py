@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 from . import _abi
-from ._abi import (TQ_BETA_HALF_D, TQ_BF16, TQ_EHIP, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_F32,
+from ._abi import (TQ_ATTN_NOALLOC_MAX_BYTES, TQ_BETA_HALF_D, TQ_BF16, TQ_EHIP, TQ_EINVAL,
+                   TQ_EUNSUPPORTED, TQ_F32,
                    TQ_FLAG_GAUSS_1_OVER_D, TQ_FLAG_TWO_SIDED, TQ_GAUSS_1_OVER_D, TQ_MAX_LAYERS,
                    TQ_OK, TqCodebook, TqError, lib, library_path)
 
@@ -23,7 +24,7 @@ __all__ = [
     "TqError", "TQCache", "lib", "library_path", "tq_codebook_init", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
     "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
-    "tq_layer_bits_boundary",
+    "tq_layer_bits_boundary", "tq_attn_decode_noalloc", "TQ_ATTN_NOALLOC_MAX_BYTES",
     "TQ_F32", "TQ_BF16", "TQ_BETA_HALF_D", "TQ_GAUSS_1_OVER_D", "TQ_OK", "TQ_EINVAL",
     "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS", "TQ_FLAG_GAUSS_1_OVER_D", "TQ_FLAG_TWO_SIDED",
 ]
@@ -285,4 +286,26 @@ def tq_attn_decode(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int, sc
                                 _dev(out, "out", torch.float32),
                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                 _stream(stream)), fn)
+    return out
+
+
+def tq_attn_decode_noalloc(cache: TQCache, layer: int, q: torch.Tensor, ctx_len: int,
+                           out: torch.Tensor, scale: float = 0.0, stream=None,
+                           sparse_v: float = 0.0):
+    """tq_attn_decode without a workspace: the library's static device scratch
+    (TQ_ATTN_NOALLOC_MAX_BYTES per GPU) takes its place, and nothing is
+    allocated -- `out` (fp32 [batch, n_q_heads, d]) must be given.  Calls that
+    overlap on one GPU share the scratch and race."""
+    fn = "tq_attn_decode_noalloc"
+    if not 0 <= layer < cache.n_layers:
+        raise ValueError(f"{fn}: layer {layer} out of range (n_layers {cache.n_layers})")
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError(f"{fn}: q must be a 3-D tensor [batch, n_q_heads, head_dim]")
+    n_q = q.shape[1]
+    _check_shape(q, (cache.batch, n_q, cache.head_dim[layer]), "q", fn)
+    _check_shape(out, q.shape, "out", fn)
+    _check(lib().tq_attn_decode_noalloc(ctypes.byref(cache.desc), layer,
+                                        _dev(q, "q", torch.bfloat16), n_q, ctx_len,
+                                        ctypes.c_float(scale), ctypes.c_float(sparse_v),
+                                        _dev(out, "out", torch.float32), _stream(stream)), fn)
     return out

@@ -18,7 +18,9 @@ EXPORTS = [
     "tq_last_error", "tq_version", "tq_codebook_init", "tq_codebook_init_density", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
     "tq_attn_workspace_bytes", "tq_attn_decode", "tq_layer_bits_boundary",
+    "tq_attn_decode_noalloc",
 ]
+TQ_ATTN_NOALLOC_MAX_BYTES = 16 << 20
 
 
 class TqError(RuntimeError):
@@ -78,9 +80,11 @@ def lib():
         L.tq_attn_workspace_bytes.restype = sz
         L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P, sz, P]
         L.tq_layer_bits_boundary.argtypes = [i32, i32, i32, i32, P]
+        L.tq_attn_decode_noalloc.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float,
+                                             P, P]
         for name in ("tq_codebook_init", "tq_codebook_init_density", "tq_signs", "tq_rotate",
                      "tq_encode", "tq_decode", "tq_append_row", "tq_attn_decode",
-                     "tq_layer_bits_boundary"):
+                     "tq_layer_bits_boundary", "tq_attn_decode_noalloc"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

@@ -33,6 +33,7 @@
 
 #include <cfloat>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1182,57 +1183,104 @@ extern "C" size_t tq_attn_workspace_bytes(const tq_cache_desc *c, int layer, int
     return ws_layout(c->batch, n_q_heads, s, D, sparse_v_threshold > 0.0f).total;
 }
 
-extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
-                              int n_q_heads, int64_t ctx_len, float scale,
-                              float sparse_v_threshold, float *out, void *workspace,
-                              size_t ws_bytes, void *stream)
+// ---- Scratch of the allocation-free entry point: one file-scope device
+// array per GPU (each device that loads the library holds its own copy until
+// the process ends).  Host code never names `scratch` in a kernel argument or
+// a copy: in host code the name is a host-side stand-in, not a device
+// address.  Its device address is taken once per device with that device
+// current and kept in scratch_ptr.
+constexpr size_t kScratchBytes = TQ_ATTN_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];
+
+// The current device's scratch address (looked up on its first use)
+static int scratch_for_current_device(void **ptr, const char *fn)
 {
-    static const char *fn = "tq_attn_decode";
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return tq::fail(TQ_EHIP, std::string(fn) + ": hipGetDevice: " + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device index above " +
+                                             std::to_string(kMaxDevices - 1));
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return tq::fail(TQ_EHIP, std::string(fn) + ": hipGetSymbolAddress(scratch): " +
+                                         hipGetErrorString(e));
+        scratch_ptr[dev] = p;
+    }
+    *ptr = scratch_ptr[dev];
+    return TQ_OK;
+}
+
+// tq_attn_decode, and (noalloc) the same with the static scratch in place of
+// the caller's workspace
+static int attn_decode_impl(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
+                            int n_q_heads, int64_t ctx_len, float scale, float sparse_v_threshold,
+                            float *out, void *workspace, size_t ws_bytes, void *stream,
+                            bool noalloc, const char *fn)
+{
     tq::clear_error();
     int rc = check_cache(c, layer, fn);
     if (rc != TQ_OK)
         return rc;
     if (!(sparse_v_threshold >= 0.0f && sparse_v_threshold < 1.0f))
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: sparse_v_threshold must be in [0, 1)");
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": sparse_v_threshold must be in [0, 1)");
     if (n_q_heads < 1 || n_q_heads % c->n_kv_heads != 0)
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: n_q_heads must be a positive multiple of n_kv_heads");
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": n_q_heads must be a positive multiple of n_kv_heads");
     const int G = n_q_heads / c->n_kv_heads;
     if (ctx_len < 1)
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: ctx_len must be >= 1");
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": ctx_len must be >= 1");
     const int d = c->head_dim[layer], D = tq::padded_dim(d);
     if (D == 0)
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: head_dim outside 2..2^20");
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": head_dim outside 2..2^20");
     if (!((D == 64 || D == 128 || D == 256) && (d == D || d % 32 == 0)))
-        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: device kernels take head_dim in "
-                                         "{64, 128, 256} or a multiple of 32 between them");
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device kernels take head_dim in "
+                                         + "{64, 128, 256} or a multiple of 32 between them");
     const int bits_k = tq::layer_bits(c, layer, 0), bits_v = tq::layer_bits(c, layer, 1);
     for (int bits : {bits_k, bits_v}) {
         if (bits < 1 || bits > 4)
-            return tq::fail(TQ_EINVAL, "tq_attn_decode: bits must be in 1..4");
+            return tq::fail(TQ_EINVAL, std::string(fn) + ": bits must be in 1..4");
         if (bits == 1)
-            return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: device kernels take bits in {2, 3, 4}");
+            return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": device kernels take bits in {2, 3, 4}");
     }
     if (!(G == 1 || G == 2 || G == 4 || G == 8))
-        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: query/KV head ratio must be 1, 2, 4 or 8");
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": query/KV head ratio must be 1, 2, 4 or 8");
     // the kernels address one KV head's packed rows with 32-bit byte offsets
     if ((uint64_t)c->window * (uint64_t)(D / 2) >= (1ull << 31))
-        return tq::fail(TQ_EUNSUPPORTED, "tq_attn_decode: window too large (one KV head's packed "
-                                         "rows must span less than 2 GiB)");
+        return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": window too large (one KV head's packed "
+                                         + "rows must span less than 2 GiB)");
     if (c->batch == 0)
         return TQ_OK;
-    if (!q_bf16 || !out || !workspace || !c->k_packed[layer] || !c->k_norms[layer] ||
-        !c->v_packed[layer] || !c->v_norms[layer])
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: NULL buffer");
+    if (!q_bf16 || !out || (!noalloc && !workspace) || !c->k_packed[layer] ||
+        !c->k_norms[layer] || !c->v_packed[layer] || !c->v_norms[layer])
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": NULL buffer");
     if (((uintptr_t)q_bf16 | (uintptr_t)out | (uintptr_t)workspace |
          (uintptr_t)c->k_packed[layer] | (uintptr_t)c->v_packed[layer]) % 16 != 0 ||
         ((uintptr_t)c->k_norms[layer] | (uintptr_t)c->v_norms[layer]) % 4 != 0)
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: misaligned buffer");
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": misaligned buffer");
     const size_t need = tq_attn_workspace_bytes(c, layer, n_q_heads, ctx_len, sparse_v_threshold);
-    if (ws_bytes < need)
-        return tq::fail(TQ_EINVAL, "tq_attn_decode: workspace too small (need " +
+    if (noalloc) {
+        if (need > kScratchBytes)
+            return tq::fail(TQ_EINVAL, std::string(fn) + ": this call needs " + std::to_string(need) +
+                                           " bytes of scratch; the library's static scratch holds " +
+                                           std::to_string(kScratchBytes) +
+                                           " (use tq_attn_decode with a workspace)");
+        if ((rc = scratch_for_current_device(&workspace, fn)) != TQ_OK)
+            return rc;
+        ws_bytes = kScratchBytes;
+    } else if (ws_bytes < need) {
+        return tq::fail(TQ_EINVAL, std::string(fn) + ": workspace too small (need " +
                                        std::to_string(need) + " bytes)");
+    }
     if (tq::take_injected_launch_failure())
-        return tq::fail(TQ_EHIP, "tq_attn_decode: injected launch failure (TQ_TEST_FAIL_LAUNCH)");
+        return tq::fail(TQ_EHIP, std::string(fn) + ": injected launch failure (TQ_TEST_FAIL_LAUNCH)");
     tq_codebook ck, cv;
     if ((rc = tq::get_codebook(D, bits_k, tq::density_of(c->flags), &ck)) != TQ_OK ||
         (rc = tq::get_codebook(D, bits_v, tq::density_of(c->flags), &cv)) != TQ_OK)
@@ -1277,6 +1325,23 @@ extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t 
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
-        return tq::fail(TQ_EHIP, std::string("tq_attn_decode: ") + hipGetErrorString(e));
+        return tq::fail(TQ_EHIP, std::string(std::string(fn) + ": ") + hipGetErrorString(e));
     return TQ_OK;
+}
+
+extern "C" int tq_attn_decode(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
+                              int n_q_heads, int64_t ctx_len, float scale,
+                              float sparse_v_threshold, float *out, void *workspace,
+                              size_t ws_bytes, void *stream)
+{
+    return attn_decode_impl(c, layer, q_bf16, n_q_heads, ctx_len, scale, sparse_v_threshold, out,
+                            workspace, ws_bytes, stream, false, "tq_attn_decode");
+}
+
+extern "C" int tq_attn_decode_noalloc(const tq_cache_desc *c, int layer, const uint16_t *q_bf16,
+                                      int n_q_heads, int64_t ctx_len, float scale,
+                                      float sparse_v_threshold, float *out, void *stream)
+{
+    return attn_decode_impl(c, layer, q_bf16, n_q_heads, ctx_len, scale, sparse_v_threshold, out,
+                            nullptr, 0, stream, true, "tq_attn_decode_noalloc");
 }

@@ -246,6 +246,24 @@ def test_binding_rejects_mismatched_shapes(tq):
         tq.tq_rotate(torch.zeros(4, 128), 42, out=torch.zeros(4, 64))
 
 
+def test_noalloc_validation_without_launch(tq):
+    """tq_attn_decode_noalloc checks its arguments like tq_attn_decode and
+    rejects a call whose workspace would exceed its static scratch before
+    touching the device."""
+    L = tq.lib()
+    A = _c(4096)
+    d = _desc(tq, window=1 << 20)
+    assert L.tq_attn_workspace_bytes(ctypes.byref(d), 0, 4, 1 << 20, 1e-3) > tq.TQ_ATTN_NOALLOC_MAX_BYTES
+    assert L.tq_attn_decode_noalloc(ctypes.byref(d), 0, A, 4, 1 << 20, 0.0, 1e-3, A, None) == tq.TQ_EINVAL
+    assert "scratch" in tq.tq_last_error()
+    assert L.tq_attn_decode_noalloc(ctypes.byref(d), 0, A, 4, 5, 0.0, 0.0, None, None) == tq.TQ_EINVAL
+    assert "NULL" in tq.tq_last_error()
+    assert L.tq_attn_decode_noalloc(ctypes.byref(d), 0, A, 3, 5, 0.0, 0.0, A, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode_noalloc(ctypes.byref(d), 0, A, 4, 5, 0.0, 2.0, A, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode_noalloc(ctypes.byref(_desc(tq, batch=0)), 0, A, 4, 5, 0.0, 0.0, A,
+                                    None) == tq.TQ_OK
+
+
 def test_layer_bits_boundary_policy(tq):
     assert tq.tq_layer_bits_boundary(10, 2, 4) == [4, 4, 2, 2, 2, 2, 2, 2, 4, 4]
     assert tq.tq_layer_bits_boundary(10, 3, 4, n_boundary=1) == [4] + [3] * 8 + [4]
