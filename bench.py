@@ -5,10 +5,22 @@ One step = the codec hot path over the bulk-prefill workload: encode K (4-bit)
 and V (2-bit) of 32 layers x 8 KV heads x 32768 tokens x head_dim 128 (bf16
 AR(1)-correlated rows with outlier channels) in one launch, then decode both
 back to fp32 (two launches).  `value` is the whole step's algorithmic bytes
-per second (inputs already resident in HBM).  The same run also times the
-fused decode-step attention (batch 32, 32 query / 8 KV heads, head_dim 128,
-context 16384, K4/V2) and reports its microseconds per step, and times the
-oracle on a bounded sample of the same codec workload on the host CPU.
+per second (inputs already resident in HBM).
+
+The same run measures the other workloads (each with its own algorithmic
+bytes, GB/s and % of the 8 TB/s HBM peak):
+  * round trip: 4096 x 128 fp32 N(0,1) rows, K 4-bit (launch-bound);
+  * Gemma-3-4B-shaped cache: 34 layers, 4 KV heads, head_dim 256, window 512,
+    batch 64, fp32 K4/V4; a step appends one row per layer and decodes every
+    layer's full window;
+  * fused decode attention: batch 32, 32 query / 8 KV heads, head_dim 128,
+    context 16384, K4/V2 (also with the sparse-V gate);
+  * long context K3/V2: 1 sequence x 8 heads x 131072 tokens, 32 layers of
+    head_dim 64 and 256, bf16 Student-t(3): encode, decode and attention over
+    every layer;
+plus storage (bits per element, compression against fp16), reconstruction and
+attention quality (cosines against the unquantised rows), and the oracle timed
+on the host CPU on bounded samples (all threads and one thread).
 
 Prints one JSON line.  Only --gpus 1 is supported (this build targets a
 single GPU).
@@ -29,12 +41,22 @@ sys.path.insert(0, ROOT)
 
 METRIC = "codec GB/s & rows/s (K4/V2, d=128) as % HBM peak; tq_attn_decode µs/step"
 HBM_PEAK_GBS = 8000.0
+# vector-ALU issue ceiling: 256 CUs x 4 SIMDs, one wave64 instruction per SIMD
+# per 4 clocks, at the 2.4 GHz peak engine clock
+VALU_PEAK_GINST_S = 256 * 4 * 2.4 / 4
 SEED = 42
 
-# bulk prefill workload
+# round trip
+N1, D1, B1 = 4096, 128, 4
+# Gemma-3-4B-shaped append-only cache
+L2, B2, H2, W2, D2, BK2, BV2 = 34, 64, 4, 512, 256, 4, 4
+# bulk prefill (the headline step)
 L3, H3, T3, D3, BK3, BV3 = 32, 8, 32768, 128, 4, 2
-# fused decode attention workload
+# fused decode attention
 B4, HQ4, HKV4, D4, T4, BK4, BV4 = 32, 32, 8, 128, 16384, 4, 2
+# long context
+L5, H5, T5, BK5, BV5 = 32, 8, 131072, 3, 2
+HD5 = [64 if l % 2 == 0 else 256 for l in range(L5)]
 
 
 def enc_bytes(n, d, bits, in_bytes):
@@ -52,6 +74,11 @@ def attn_bytes(B, Hq, Hkv, d, T, bk, bv):
     return B * Hkv * T * (d * bk // 8 + 4 + d * bv // 8 + 4) + B * Hq * d * (2 + 4)
 
 
+def bits_per_elem(d, bits):
+    """stored bits per coordinate: the packed indices plus the fp32 norm"""
+    return (d * bits + 32) / d
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_vector_rotate_amd", "csrc")
@@ -61,18 +88,31 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(name):
+    """A committed counter summary (profiles/<name>.json) if it was taken on
+    the current kernel sources, else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    if rec.get("source_hash") != source_hash():
-        return None
-    k = rec.get("kernels", {}).get(kernel)
+    return rec if rec.get("source_hash") == source_hash() else None
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs, if they were taken on the current kernel sources; else None."""
+    rec = _profile_record("traffic.json")
+    k = None if rec is None else rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def valu_insts_for(kernel: str):
+    """Vector-ALU wave instructions per launch (SQ_INSTS_VALU) from a committed
+    counter run on the current sources; else None."""
+    rec = _profile_record("valu.json")
+    k = None if rec is None else rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("valu_insts_per_launch")
 
 
 def copy_calibration():
@@ -87,62 +127,173 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
-def cpu_baseline(sample_rows: int, threads: int):
-    """Oracle (plain fp64 C) encode + decode of a sample of the bulk-prefill
-    rows, rows split statically over `threads` host threads."""
-    import numpy as np
-    import kvgen
-    import oracle
-    tokens = max(sample_rows // (H3 * 2), 1)
-    k = kvgen.ar1_outliers((2, H3, tokens, D3), 3).float().numpy().reshape(-1, D3)
-    v = kvgen.ar1_outliers((2, H3, tokens, D3), 103).float().numpy().reshape(-1, D3)
-    oracle.codebook_float(D3, BK3)
-    oracle.codebook_float(D3, BV3)
-
-    def job(args):
-        x, bits = args
-        p, n = oracle.encode(x, D3, bits, SEED)
-        oracle.decode(p, n, D3, bits, SEED)
-
-    parts = [(c, BK3) for c in np.array_split(k, threads)] + \
-            [(c, BV3) for c in np.array_split(v, threads)]
-    t0, c0 = time.perf_counter(), time.process_time()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        list(ex.map(job, parts))
-    dt, cpu_s = time.perf_counter() - t0, time.process_time() - c0
-    n = k.shape[0]
-    nbytes = (enc_bytes(n, D3, BK3, 2) + enc_bytes(n, D3, BV3, 2)
-              + dec_bytes(n, D3, BK3) + dec_bytes(n, D3, BV3))
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} K rows + {n} V rows of the bulk-prefill workload (2 layers x 8 heads x "
-                      f"{tokens} tokens), encode + decode, {dt:.2f} s wall, {cpu_s:.1f} s of CPU time",
-            "rows_per_s": 2 * n / dt}
+def log(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--attn-reps", type=int, default=30)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1 << 22)
-    ap.add_argument("--copy-calibration", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1", file=sys.stderr)
-        sys.exit(2)
+# --------------------------------------------------------------------------
+# timing helpers (every launch goes to torch's current stream, the stream the
+# binding passes to the library, so torch's events bracket the kernels)
+
+def timed_reps(fn, reps, warm=2):
+    """GPU time of each of `reps` back-to-back calls of fn (µs)."""
     import torch
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    import kvgen
-    import kv_cache_vector_rotate_amd as tq
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
 
-    # ---------------- codec step: encode K4/V2 + decode both
+
+def settle(fn, seconds):
+    """Untimed: a freshly started GPU runs its first ~0.1 s of work at a lower
+    clock; repeat the work until the clock has settled."""
+    import torch
+    t = time.perf_counter()
+    while time.perf_counter() - t < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
+def summary(ts, nbytes=None, rows=None):
+    avg = sum(ts) / len(ts)
+    out = {"avg_us": round(avg, 3), "median_us": round(sorted(ts)[len(ts) // 2], 3),
+           "min_us": round(min(ts), 3), "max_us": round(max(ts), 3)}
+    if nbytes is not None:
+        out["alg_bytes"] = nbytes
+        out["GB_s"] = round(nbytes / avg / 1e3, 2)
+        out["pct_hbm_peak"] = round(100 * nbytes / avg / 1e3 / HBM_PEAK_GBS, 2)
+    if rows is not None:
+        out["rows_per_s"] = round(rows / avg * 1e6, 1)
+    return out
+
+
+def row_cosines(x, xhat):
+    """per-row cosine of the decoded rows against the originals (fp32)"""
+    import torch
+    x = x.float().reshape(-1, x.shape[-1])
+    xhat = xhat.float().reshape(-1, xhat.shape[-1])
+    c = (x * xhat).sum(-1) / (torch.linalg.vector_norm(x, dim=-1) *
+                              torch.linalg.vector_norm(xhat, dim=-1)).clamp_min(1e-30)
+    return {"mean": round(float(c.mean()), 5), "min": round(float(c.min()), 5)}
+
+
+def attention_fp32(q, K, V, scale):
+    """Full-precision reference: softmax attention of q [Hq, d] over the
+    unquantised rows K, V [Hkv, T, d] (fp32, GQA groups contiguous)."""
+    import torch
+    Hq, Hkv = q.shape[0], K.shape[0]
+    G = Hq // Hkv
+    out = []
+    for h in range(Hq):
+        k = K[h // G].float().contiguous()
+        s = torch.matmul(k, q[h].float()) * scale
+        p = torch.softmax(s, dim=0)
+        out.append(torch.matmul(p, V[h // G].float().contiguous()))
+    return torch.stack(out)
+
+
+# --------------------------------------------------------------------------
+# workloads
+
+def bench_roundtrip(tq, kvgen):
+    import torch
+    x = kvgen.normal((N1, D1), 1, "cuda")
+    kp, kn, _, _ = tq.tq_encode(x, None, B1, 0, SEED)
+    out = torch.empty(N1, D1, dtype=torch.float32, device="cuda")
+    te = timed_reps(lambda: tq.tq_encode(x, None, B1, 0, SEED, kp, kn), 100, 5)
+    td = timed_reps(lambda: tq.tq_decode(kp, kn, D1, B1, SEED, out=out), 100, 5)
+    # one call made and waited for alone (host side of the binding included)
+    lat = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        tq.tq_encode(x, None, B1, 0, SEED, kp, kn)
+        tq.tq_decode(kp, kn, D1, B1, SEED, out=out)
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - t) * 1e6)
+    cos = row_cosines(x, out)
+    nb = enc_bytes(N1, D1, B1, 4)
+    return {
+        "workload": "round trip: 4096 rows x head_dim 128 fp32 iid N(0,1), K 4-bit, 1 head, sign "
+                    "seed 42 (launch-bound: not an HBM measurement)",
+        "encode": summary(te, nb, N1), "decode": summary(td, dec_bytes(N1, D1, B1), N1),
+        "encode_plus_decode_call_latency_us": round(sorted(lat)[len(lat) // 2], 2),
+        "roundtrip_cosine": cos, "cosine_contract_4bit": 0.88,
+    }
+
+
+def bench_gemma_cache(tq, kvgen, reps):
+    import torch
+    cache = tq.TQCache(L2, B2, H2, W2, D2, BK2, BV2, SEED)
+    k0 = None
+    for l in range(L2):  # prefill every slot (untimed)
+        k = kvgen.unit_dirs_lognormal((B2, H2, W2, D2), 200 + l, "cuda")
+        v = kvgen.unit_dirs_lognormal((B2, H2, W2, D2), 300 + l, "cuda")
+        tq.tq_encode(k, v, BK2, BV2, SEED, cache.k_packed[l], cache.k_norms[l],
+                     cache.v_packed[l], cache.v_norms[l])
+        if l == 0:
+            k0 = k
+    del k, v
+    knew = [kvgen.unit_dirs_lognormal((B2, H2, D2), 400 + l, "cuda") for l in range(L2)]
+    vnew = [kvgen.unit_dirs_lognormal((B2, H2, D2), 500 + l, "cuda") for l in range(L2)]
+    dk = torch.empty(B2, H2, W2, D2, dtype=torch.float32, device="cuda")
+    dv = torch.empty(B2, H2, W2, D2, dtype=torch.float32, device="cuda")
+    # quality on layer 0 before any append overwrites a slot
+    tq.tq_decode(cache.k_packed[0], cache.k_norms[0], D2, BK2, SEED, out=dk)
+    cos = row_cosines(k0, dk)
+    del k0
+    pos = [W2]
+
+    def decode_all():
+        for l in range(L2):
+            tq.tq_decode(cache.k_packed[l], cache.k_norms[l], D2, BK2, SEED, out=dk)
+            tq.tq_decode(cache.v_packed[l], cache.v_norms[l], D2, BV2, SEED, out=dv)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        tq.tq_append_row(cache, -1, knew, vnew, pos[0])
+        pos[0] += 1
+        if ev: ev[1].record()
+        decode_all()
+        if ev: ev[2].record()
+
+    settle(step, 0.2)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    ta = [ev[0].elapsed_time(ev[1]) * 1e3 for ev in evs]
+    td = [ev[1].elapsed_time(ev[2]) * 1e3 for ev in evs]
+    ts = [ev[0].elapsed_time(ev[2]) * 1e3 for ev in evs]
+    app_b = enc_bytes(L2 * B2 * H2, D2, BK2, 4) + enc_bytes(L2 * B2 * H2, D2, BV2, 4)
+    dec_b = dec_bytes(L2 * B2 * H2 * W2, D2, BK2) + dec_bytes(L2 * B2 * H2 * W2, D2, BV2)
+    return {
+        "workload": "Gemma-3-4B-shaped append-only cache: 34 layers, 4 KV heads, head_dim 256, "
+                    "window 512, batch 64, fp32 rows z/|z| x lognormal(0, 0.5), K4/V4; step = append "
+                    "one K and V row per layer (one launch) + decode every layer's full K and V "
+                    "window (68 launches)",
+        "step": summary(ts, app_b + dec_b, 2 * L2 * B2 * H2 * (W2 + 1)),
+        "append": summary(ta, app_b, 2 * L2 * B2 * H2),
+        "decode_window": summary(td, dec_b, 2 * L2 * B2 * H2 * W2),
+        "roundtrip_cosine_k_layer0": cos,
+    }
+
+
+def bench_prefill(tq, kvgen, args):
+    """The headline step; returns (result dict, tensors kept for quality)."""
+    import torch
     n = L3 * H3 * T3
-    print(f"bench: generating {n} K and V rows (bf16)", file=sys.stderr, flush=True)
+    log(f"generating {n} K and V rows (bf16)")
     k = kvgen.ar1_outliers((L3, H3, T3, D3), 3, "cuda")
     v = kvgen.ar1_outliers((L3, H3, T3, D3), 103, "cuda")
     kp = torch.empty(n, D3 * BK3 // 8, dtype=torch.uint8, device="cuda")
@@ -156,14 +307,6 @@ def main():
               "decode_k4": dec_bytes(n, D3, BK3), "decode_v2": dec_bytes(n, D3, BV3)}
     step_bytes = sum(nbytes.values())
 
-    def settle(fn=None, seconds=0.3):
-        # untimed: a freshly started GPU runs its first ~0.1 s of work at a
-        # lower clock; repeat the work until the clock has settled
-        t = time.perf_counter()
-        while time.perf_counter() - t < seconds:
-            (fn or step)()
-            torch.cuda.synchronize()
-
     def step(ev=None):
         if ev: ev[0].record()
         tq.tq_encode(k, v, BK3, BV3, SEED, kp, kn, vp, vn)
@@ -173,7 +316,7 @@ def main():
         tq.tq_decode(vp, vn, D3, BV3, SEED, out=vo)
         if ev: ev[3].record()
 
-    settle()
+    settle(step, 0.3)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -184,62 +327,248 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {nm: [] for nm in names}
-    for ev in evs:
-        for j, nm in enumerate(names):
-            per[nm].append(ev[j].elapsed_time(ev[j + 1]) * 1e-3)
     kern = {}
-    for nm in names:
-        avg = sum(per[nm]) / len(per[nm])
-        kern[nm] = {"avg_us": avg * 1e6, "min_us": min(per[nm]) * 1e6,
-                    "alg_bytes": nbytes[nm], "GB_s": nbytes[nm] / avg / 1e9,
-                    "pct_hbm_peak": 100 * nbytes[nm] / avg / 1e9 / HBM_PEAK_GBS}
-    del ko, vo
-    value = step_bytes * args.steps / wall / 1e9
-    dom = max(names, key=lambda nm: kern[nm]["avg_us"])
+    for j, nm in enumerate(names):
+        ts = [ev[j].elapsed_time(ev[j + 1]) * 1e3 for ev in evs]
+        kern[nm] = summary(ts, nbytes[nm], 2 * n if nm.startswith("encode") else n)
+    # reconstruction quality on the first layer (decoded in the last step)
+    m = H3 * T3
+    quality = {"roundtrip_cosine_k4": row_cosines(k.reshape(-1, D3)[:m], ko[:m]),
+               "roundtrip_cosine_v2": row_cosines(v.reshape(-1, D3)[:m], vo[:m]),
+               "rows": f"layer 0 ({m} K and {m} V rows)"}
+    return {"n": n, "wall": wall, "step_bytes": step_bytes, "kernels": kern,
+            "quality": quality}
 
-    # ---------------- fused decode attention, two caches alternated (> MALL)
-    print("bench: attention cache", file=sys.stderr, flush=True)
+
+def bench_attention(tq, kvgen, reps):
+    import torch
     caches = []
+    ref = None
     for c in range(2):
         cache = tq.TQCache(1, B4, HKV4, T4, D4, BK4, BV4, SEED)
         kk = kvgen.normal((B4, HKV4, T4, D4), 4 + 10 * c, "cuda")
         vv = kvgen.normal((B4, HKV4, T4, D4), 5 + 10 * c, "cuda")
         tq.tq_encode(kk, vv, BK4, BV4, SEED, cache.k_packed[0], cache.k_norms[0],
                      cache.v_packed[0], cache.v_norms[0])
+        if c == 0:
+            ref = (kk[:2].clone(), vv[:2].clone())
         del kk, vv
         caches.append(cache)
     q = kvgen.normal((B4, HQ4, D4), 44, "cuda", torch.bfloat16)
     out = torch.empty(B4, HQ4, D4, dtype=torch.float32, device="cuda")
     ws = torch.empty(tq.tq_attn_workspace_bytes(caches[0], 0, HQ4, T4), dtype=torch.uint8,
                      device="cuda")
-    settle(lambda: [tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws)
-                    for i in range(4)], 0.2)
-    for i in range(3):
-        tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws)
-    torch.cuda.synchronize()
-    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.attn_reps)]
-    for i, (a, b) in enumerate(aev):
-        a.record()
-        tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws)
-        b.record()
-    torch.cuda.synchronize()
-    at = sorted(a.elapsed_time(b) * 1e3 for a, b in aev)
-    attn_us = sum(at) / len(at)
-    ab = attn_bytes(B4, HQ4, HKV4, D4, T4, BK4, BV4)
-    # the same launch with the sparse-V gate at 1e-3 (N(0,1) keys: few rows gated)
     ws_g = torch.empty(tq.tq_attn_workspace_bytes(caches[0], 0, HQ4, T4, 1e-3),
                        dtype=torch.uint8, device="cuda")
-    for i in range(3):
-        tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws_g, sparse_v=1e-3)
-    for i, (a, b) in enumerate(aev):
-        a.record()
-        tq.tq_attn_decode(caches[i % 2], 0, q, T4, out=out, workspace=ws_g, sparse_v=1e-3)
-        b.record()
-    torch.cuda.synchronize()
-    ats = [a.elapsed_time(b) * 1e3 for a, b in aev]
-    attn_sparse_us = sum(ats) / len(ats)
+    # quality: compressed attention against fp32 attention over the
+    # unquantised rows (sequences 0 and 1 of the first cache)
+    o = tq.tq_attn_decode(caches[0], 0, q, T4, out=out, workspace=ws)
+    scale = 1.0 / math.sqrt(D4)
+    cos = row_cosines(o[:2], torch.stack([attention_fp32(q[b], ref[0][b], ref[1][b], scale)
+                                          for b in range(2)]))
+    og = tq.tq_attn_decode(caches[0], 0, q, T4, out=torch.empty_like(out), workspace=ws_g,
+                           sparse_v=1e-3)
+    cos_g = row_cosines(og[:2], o[:2])
+    del ref
+    it = [0]
+
+    def call(w, thr):
+        def f():
+            tq.tq_attn_decode(caches[it[0] % 2], 0, q, T4, out=out, workspace=w, sparse_v=thr)
+            it[0] += 1
+        return f
+
+    settle(call(ws, 0.0), 0.2)
+    ab = attn_bytes(B4, HQ4, HKV4, D4, T4, BK4, BV4)
+    at = timed_reps(call(ws, 0.0), reps, 3)
+    ats = timed_reps(call(ws_g, 1e-3), reps, 3)
+    res = {
+        "workload": "tq_attn_decode batch 32, 32 query heads on 8 KV heads, head_dim 128, context "
+                    "16384, K4/V2 cache of N(0,1) rows, bf16 q, scale 1/sqrt(128), two caches "
+                    "alternated (872 MB > the 256 MB Infinity Cache)",
+        **summary(at, ab),
+        "sparse_v_1e-3": summary(ats),
+        "attention_cosine_vs_fp32": cos,
+        "sparse_v_1e-3_cosine_vs_ungated": cos_g,
+    }
+    return res, caches, q
+
+
+def bench_long_context(tq, kvgen, reps_codec, reps_attn):
+    import torch
+    c5 = tq.TQCache(L5, 1, H5, T5, HD5, BK5, BV5, SEED)
+    log("long context: generating 32 layers of bf16 Student-t rows")
+    xin = [(kvgen.student_t((1, H5, T5, d), 600 + l, device="cuda"),
+            kvgen.student_t((1, H5, T5, d), 700 + l, device="cuda")) for l, d in enumerate(HD5)]
+    qs = [kvgen.student_t((1, H5, d), 800 + l, device="cuda") for l, d in enumerate(HD5)]
+    dbuf = {d: torch.empty(1, H5, T5, d, dtype=torch.float32, device="cuda") for d in (64, 256)}
+    outs = {d: torch.empty(1, H5, d, dtype=torch.float32, device="cuda") for d in (64, 256)}
+    ws = torch.empty(max(tq.tq_attn_workspace_bytes(c5, l, H5, T5) for l in range(2)),
+                     dtype=torch.uint8, device="cuda")
+
+    def enc():
+        for l in range(L5):
+            k, v = xin[l]
+            tq.tq_encode(k, v, BK5, BV5, SEED, c5.k_packed[l], c5.k_norms[l], c5.v_packed[l],
+                         c5.v_norms[l])
+
+    def dec():
+        for l in range(L5):
+            d = HD5[l]
+            tq.tq_decode(c5.k_packed[l], c5.k_norms[l], d, BK5, SEED, out=dbuf[d])
+            tq.tq_decode(c5.v_packed[l], c5.v_norms[l], d, BV5, SEED, out=dbuf[d])
+
+    def att():
+        for l in range(L5):
+            tq.tq_attn_decode(c5, l, qs[l], T5, out=outs[HD5[l]], workspace=ws)
+
+    enc()
+    quality = {}
+    for l in (0, 1):
+        d = HD5[l]
+        tq.tq_decode(c5.k_packed[l], c5.k_norms[l], d, BK5, SEED, out=dbuf[d])
+        quality[f"roundtrip_cosine_k3_d{d}"] = row_cosines(xin[l][0], dbuf[d])
+        tq.tq_decode(c5.v_packed[l], c5.v_norms[l], d, BV5, SEED, out=dbuf[d])
+        quality[f"roundtrip_cosine_v2_d{d}"] = row_cosines(xin[l][1], dbuf[d])
+        o = tq.tq_attn_decode(c5, l, qs[l], T5)
+        ref = attention_fp32(qs[l][0], xin[l][0][0], xin[l][1][0], 1.0 / math.sqrt(d))
+        quality[f"attention_cosine_vs_fp32_d{d}"] = row_cosines(o[0], ref)
+    settle(enc, 0.2)
+    te = timed_reps(enc, reps_codec, 1)
+    td = timed_reps(dec, reps_codec, 1)
+    ta = timed_reps(att, reps_attn, 2)
+    enc_b = sum(enc_bytes(H5 * T5, d, BK5, 2) + enc_bytes(H5 * T5, d, BV5, 2) for d in HD5)
+    dec_b = sum(dec_bytes(H5 * T5, d, BK5) + dec_bytes(H5 * T5, d, BV5) for d in HD5)
+    att_b = sum(attn_bytes(1, H5, H5, d, T5, BK5, BV5) for d in HD5)
+    rows = 2 * L5 * H5 * T5
+    return {
+        "workload": "long context K3/V2: 1 sequence x 8 KV heads (8 query heads) x 131072 tokens, "
+                    "32 layers (head_dim 64 and 256 alternating), bf16 Student-t(3) rows; encode "
+                    "all layers (32 launches), decode all layers (64 launches), attention over all "
+                    "layers (32 calls)",
+        "encode_all_layers": summary(te, enc_b, rows),
+        "decode_all_layers": summary(td, dec_b, rows),
+        "attention_all_layers": summary(ta, att_b),
+        "quality": quality,
+    }
+
+
+# --------------------------------------------------------------------------
+# the oracle on the host CPU
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(sample_rows: int, threads: int, att_sample):
+    """Oracle (plain fp64 C, never tuned) on bounded samples of the bulk-
+    prefill codec workload -- all `threads` threads, and one thread -- and of
+    the fused-attention workload; rows split statically over the threads
+    (ctypes releases the GIL)."""
+    import numpy as np
+    import kvgen
+    import oracle
+    tokens = max(sample_rows // (H3 * 2), 1)
+    k = kvgen.ar1_outliers((2, H3, tokens, D3), 3).float().numpy().reshape(-1, D3)
+    v = kvgen.ar1_outliers((2, H3, tokens, D3), 103).float().numpy().reshape(-1, D3)
+    oracle.codebook_float(D3, BK3)
+    oracle.codebook_float(D3, BV3)
+
+    def job(a):
+        x, bits = a
+        p, nrm = oracle.encode(x, D3, bits, SEED)
+        oracle.decode(p, nrm, D3, bits, SEED)
+
+    def run(kx, vx, nthreads):
+        parts = [(c, BK3) for c in np.array_split(kx, nthreads)] + \
+                [(c, BV3) for c in np.array_split(vx, nthreads)]
+        t0, c0 = time.perf_counter(), time.process_time()
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(job, parts))
+        dt, cpu_s = time.perf_counter() - t0, time.process_time() - c0
+        n = kx.shape[0]
+        nb = (enc_bytes(n, D3, BK3, 2) + enc_bytes(n, D3, BV3, 2)
+              + dec_bytes(n, D3, BK3) + dec_bytes(n, D3, BV3))
+        return nb / dt / 1e9, 2 * n / dt, dt, cpu_s
+
+    gbs, rps, dt, cpu_s = run(k, v, threads)
+    n1 = max(k.shape[0] // 16, 1)
+    gbs1, rps1, dt1, _ = run(k[:n1], v[:n1], 1)
+    res = {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{k.shape[0]} K rows + {v.shape[0]} V rows of the bulk-prefill workload "
+                     f"(2 layers x 8 heads x {tokens} tokens), encode + decode, {dt:.2f} s wall "
+                     f"on {threads} threads, {cpu_s:.1f} s of CPU time",
+           "rows_per_s": round(rps, 1),
+           "single_thread": {"GB_s": round(gbs1, 4), "rows_per_s": round(rps1, 1),
+                             "sample": f"{n1} K rows + {n1} V rows, {dt1:.2f} s"},
+           "host": {"cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+                    "cpus_available": len(os.sched_getaffinity(0))}}
+    if att_sample is not None:
+        caches, q, groups = att_sample
+        cache = caches[0]
+        jobs = []
+        for i in range(groups):
+            b, g = (i * 7) % B4, (i * 3) % HKV4
+            G = HQ4 // HKV4
+            jobs.append((q[b, g * G:(g + 1) * G].float().cpu().numpy(),
+                         cache.k_packed[0][b, g].cpu().numpy(), cache.k_norms[0][b, g].cpu().numpy(),
+                         cache.v_packed[0][b, g].cpu().numpy(), cache.v_norms[0][b, g].cpu().numpy()))
+
+        def ajob(a):
+            qq, kp, kn, vp, vn = a
+            oracle.attention(qq, kp, kn, vp, vn, 1, T4, D4, BK4, BV4, SEED, 1.0 / math.sqrt(D4))
+
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(ajob, jobs))
+        dt = time.perf_counter() - t0
+        res["attention"] = {
+            "us_per_step": round(dt / groups * (B4 * HKV4) * 1e6, 1), "threads": threads,
+            "sample": f"{groups} of the {B4 * HKV4} (sequence, KV head) groups of the fused-"
+                      f"attention workload (4 query heads each, context {T4}), {dt:.2f} s wall; "
+                      f"scaled to the whole step"}
+    return res
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--attn-reps", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1 << 22)
+    ap.add_argument("--cpu-attn-groups", type=int, default=32)
+    ap.add_argument("--workloads", default="1,2,4,5",
+                    help="workloads measured beside the headline step (comma list of 1, 2, 4, 5)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import kvgen
+    import kv_cache_vector_rotate_amd as tq
+    wl = {int(x) for x in args.workloads.split(",") if x.strip()}
+
+    pre = bench_prefill(tq, kvgen, args)
+    n, wall, step_bytes, kern = pre["n"], pre["wall"], pre["step_bytes"], pre["kernels"]
+    value = step_bytes * args.steps / wall / 1e9
+    dom = max(kern, key=lambda nm: kern[nm]["avg_us"])
+    torch.cuda.empty_cache()
 
     res = {
         "metric": METRIC,
@@ -263,29 +592,63 @@ def main():
         },
         "rows_per_s": round(2 * n * args.steps / wall, 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "kernels": {nm: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
-                         for kk, vv in kern[nm].items()} for nm in names},
-        "attn_us_per_step": round(attn_us, 2),
-        "attn": {
-            "workload": "tq_attn_decode batch 32, 32 query heads on 8 KV heads, head_dim 128, "
-                        "context 16384, K4/V2, bf16 q, two caches alternated",
-            "median_us": round(at[len(at) // 2], 2), "min_us": round(at[0], 2),
-            "alg_bytes": ab, "GB_s": round(ab / attn_us / 1e3, 1),
-            "pct_hbm_peak": round(100 * ab / attn_us / 1e3 / HBM_PEAK_GBS, 2),
-            "sparse_v_1e-3_us": round(attn_sparse_us, 2),
-        },
-        "roofline": {
-            "bound": "hbm", "kernel": dom,
-            "achieved": round(kern[dom]["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for(dom),
-        },
+        "kernels": kern,
+        "quality": pre["quality"],
     }
+    del pre
+    for nm in kern:
+        insts = valu_insts_for(nm)
+        if insts is not None:
+            kern[nm]["valu_issue_frac_at_2.4GHz"] = round(
+                insts / (kern[nm]["avg_us"] * 1e-6) / 1e9 / VALU_PEAK_GINST_S, 4)
+
+    att_sample = None
+    if 4 in wl:
+        log("fused decode attention")
+        attn, caches, q = bench_attention(tq, kvgen, args.attn_reps)
+        insts = valu_insts_for("attn_decode")
+        if insts is not None:
+            attn["valu_issue_frac_at_2.4GHz"] = round(
+                insts / (attn["avg_us"] * 1e-6) / 1e9 / VALU_PEAK_GINST_S, 4)
+        res["attn_us_per_step"] = attn["avg_us"]
+        res["attn"] = attn
+        att_sample = (caches, q, args.cpu_attn_groups)
+    workloads = {}
+    if 1 in wl:
+        log("round trip")
+        workloads["roundtrip_4096x128_k4"] = bench_roundtrip(tq, kvgen)
+    if 2 in wl:
+        log("Gemma-3-4B-shaped cache")
+        workloads["gemma3_4b_cache_k4v4_d256"] = bench_gemma_cache(tq, kvgen, 10)
+        torch.cuda.empty_cache()
+    if 5 in wl:
+        workloads["long_context_k3v2_131072"] = bench_long_context(tq, kvgen, 5, 20)
+        torch.cuda.empty_cache()
+    if workloads:
+        res["workloads"] = workloads
+    res["storage"] = {
+        "bits_per_elem": {f"d{d}_b{b}": round(bits_per_elem(d, b), 4)
+                          for d in (64, 128, 256) for b in (2, 3, 4)},
+        "compression_vs_fp16": {
+            "bulk_prefill_k4v2_d128": round(32 / (bits_per_elem(128, 4) + bits_per_elem(128, 2)), 3),
+            "gemma_cache_k4v4_d256": round(16 / bits_per_elem(256, 4), 3),
+            "long_context_k3v2_d64": round(32 / (bits_per_elem(64, 3) + bits_per_elem(64, 2)), 3),
+            "long_context_k3v2_d256": round(32 / (bits_per_elem(256, 3) + bits_per_elem(256, 2)), 3),
+        },
+        "note": "a stored row is its packed b-bit indices plus a 4-byte fp32 norm",
+    }
+    res["roofline"] = {
+        "bound": "hbm", "kernel": dom,
+        "achieved": kern[dom]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(kern[dom]["GB_s"] / HBM_PEAK_GBS, 4),
+        "traffic": traffic_for(dom),
+    }
+    if "valu_issue_frac_at_2.4GHz" in kern[dom]:
+        res["roofline"]["valu_issue_frac_at_2.4GHz"] = kern[dom]["valu_issue_frac_at_2.4GHz"]
     if not args.no_cpu_baseline:
-        print("bench: oracle CPU baseline", file=sys.stderr, flush=True)
-        threads = min(16, os.cpu_count() or 1)
-        res["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows, threads)
-        res["cpu_baseline"]["value"] = round(res["cpu_baseline"]["value"], 4)
+        log("oracle CPU baseline")
+        threads = min(16, len(os.sched_getaffinity(0)))
+        res["cpu_baseline"] = cpu_baseline(args.cpu_sample_rows, threads, att_sample)
     print(json.dumps(res), flush=True)
 
 
