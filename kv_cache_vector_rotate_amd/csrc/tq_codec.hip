@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
 // permute and Q = (s_k, +-s_{k+d/2}) the bf16 sign pair, the bf16 dot product
 // instruction gives s_k x_k +- s_{k+d/2} x_{k+d/2} exactly rounded to fp32:
 // sign, conversion and the first stage in one instruction.  The Q words are
-// the same for every row and are read from LDS.  The remaining stages are
+// the same for every row and are held in scalar registers.  The remaining stages are
 // plain fp32 add/sub; the last one is fused with the scaling to
 // T = 128 u = 128 y / ||x||, which feeds the bucketize table directly.  With
 // d = 128 a lane makes two passes of 64 outputs (coordinates 0..63, then
@@ -285,7 +285,7 @@ struct SignBits {
 struct EncodeLaneParams {
     EncodeSide side[2];
     int64_t n_rows;
-    uint32_t sbits[4];  // sign bits of the diagonal (bit k set: s_k = -1)
+    uint32_t qw[64];    // bf16 sign pairs: [j] (s_2j, s_2j+1), [32 + j] (s_2j+d/2, s_2j+1+d/2)
     SignBits s2;        // second diagonal of the two-sided rotation
 };
 
@@ -315,29 +315,24 @@ __device__ __forceinline__ f32x2 lut_entry(float t, uint32_t key)
     return *reinterpret_cast<const __attribute__((address_space(3))) f32x2 *>((uintptr_t)a);
 }
 
-__device__ __forceinline__ u32x4 lds_u32x4(uint32_t addr)
-{
-    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)addr);
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// First two stages of pass `pass` for one lane's staged row, from the raw
+// First two stages of pass PASS for one lane's staged row, from the raw
 // bf16 words: A = (x_{2j}, x_{2j+1}) and B = (x_{2j+d/2}, x_{2j+1+d/2}).  The
 // stage across halves (h = d/2) and the stage h = 1 give
 //   y_{2j}   = s_{2j} x_{2j} + s_{2j+1} x_{2j+1} + sigma (s' x' + s'' x'')
 //   y_{2j+1} = s_{2j} x_{2j} - s_{2j+1} x_{2j+1} + sigma (s' x' - s'' x'')
 // (primes: the partners d/2 further on), i.e. two bf16 dot products each
 // against sign pairs.  sigma = +1 gives output coordinates 0..d/2-1, sigma =
-// -1 the rest.  The sign pairs are the same for every row and sit in LDS:
-// word 4 (32 g + j) + {0,1,2,3} of the table is (s_{2j}, s_{2j+1}),
-// (s_{2j}, -s_{2j+1}), sigma (s', s''), sigma (s', -s'') with g = 0 for sigma
-// = +1 and g = 1 for -1; `qaddr` is the table's LDS byte address.
-//   d = 128: pass p gives v[k] = output 64 p + k, k < 64.
+// -1 the rest.  The sign pairs are the same for every row and arrive as
+// kernel arguments, which stay in scalar registers: qw[j] = (s_{2j},
+// s_{2j+1}) and qw[32 + j] = (s', s''); the negated forms are the dot
+// product's source-negation modifiers.
+//   d = 128: pass PASS gives v[k] = output 64 PASS + k, k < 64.
 //   d = 64:  one pass; v[k] = output k for both signs of sigma.
-template <int D>
-__device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, int pass,
+template <int D, int PASS>
+__device__ __forceinline__ void first_stage(const uint8_t *row, const uint32_t (&qw)[64],
                                             float (&v)[64])
 {
     constexpr int HB = D;  // bytes of half a row
@@ -351,19 +346,15 @@ __device__ __forceinline__ void first_stage(const uint8_t *row, uint32_t qaddr, 
 #pragma unroll
             for (int c = 0; c < 4; c++) {
                 const int j = 4 * m + c;
-                const u32x4 q4 = lds_u32x4(qaddr + 16 * j);
-                const u32x4 r4 = lds_u32x4(qaddr + 16 * (32 + j));
-                dot2_quad(a[c], b[c], q4.x, q4.y, q4.z, q4.w, r4.z, r4.w, v[2 * j],
-                          v[2 * j + 1], v[32 + 2 * j], v[33 + 2 * j]);
+                dot2_quad_s(a[c], b[c], qw[j], qw[32 + j], v[2 * j], v[2 * j + 1], v[32 + 2 * j],
+                            v[33 + 2 * j]);
             }
         } else {
 #pragma unroll
             for (int c = 0; c < 4; c += 2) {
                 const int j = 4 * m + c;
-                const u32x4 q4 = lds_u32x4(qaddr + 16 * (32 * pass + j));
-                const u32x4 q5 = lds_u32x4(qaddr + 16 * (32 * pass + j + 1));
-                dot2_pair2(a[c], b[c], q4, a[c + 1], b[c + 1], q5, v[2 * j], v[2 * j + 1],
-                           v[2 * j + 2], v[2 * j + 3]);
+                dot2_pair2_s<PASS>(a[c], b[c], qw[j], qw[32 + j], a[c + 1], b[c + 1], qw[j + 1],
+                                   qw[33 + j], v[2 * j], v[2 * j + 1], v[2 * j + 2], v[2 * j + 3]);
             }
         }
     }
@@ -426,7 +417,7 @@ __device__ __forceinline__ void stage_group(const u32x4 (&pf)[64 * 2 * D / 1024]
 template <int D, int BITS, bool S2>
 __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t g0,
                                              const int64_t n_rows, const uint32_t key,
-                                             uint8_t *stg, const uint32_t qaddr,
+                                             uint8_t *stg, const uint32_t (&qw)[64],
                                              const SignBits &s2)
 {
     constexpr int NP = D / 64;            // passes of 64 outputs
@@ -493,7 +484,10 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
         float v[64];
         // reread the row in every pass rather than keep it in registers
         wave_lds_fence();
-        first_stage<D>(mine, qaddr, pass, v);
+        if (pass == 0)
+            first_stage<D, 0>(mine, qw, v);
+        else
+            first_stage<D, 1>(mine, qw, v);
         // remaining stages but the last (h = 1 is part of the first)
 #pragma unroll
         for (int h = 2; h < HL; h *= 2)
@@ -526,36 +520,47 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
                 }
         } else {
             // last stage, scaled to T = 128 u, bucketized and packed, four
-            // outputs at a time
+            // outputs at a time; the table reads of the next four are issued
+            // before this four's compares (software pipeline)
+            constexpr int NB = 16;  // batches of four outputs per pass
+            auto first_of = [](int q) { return 2 * HL * ((2 * q) / HL) + (2 * q) % HL; };
+            float tt[2][4], bb[2][4];
+            uint32_t base[2][4];
+            auto issue = [&](int q, int slot) {
+                const int i = first_of(q);
 #pragma unroll
-            for (int j = 0; j < 64; j += 2 * HL)
-#pragma unroll
-                for (int i = j; i < j + HL; i += 2) {
-                    float tt[4], bb[4];
-                    uint32_t base[4], idx[4];
+                for (int h = 0; h < 2; h++) {
+                    const float bt = v[i + h + HL] * t;
+                    tt[slot][h] = fmaf(v[i + h], t, bt);
+                    tt[slot][h + 2] = fmaf(v[i + h], t, -bt);
+                }
+                if constexpr (S2) {
                     const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
 #pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const float bt = v[i + h + HL] * t;
-                        tt[h] = fmaf(v[i + h], t, bt);
-                        tt[h + 2] = fmaf(v[i + h], t, -bt);
-                    }
-                    if constexpr (S2) {
-#pragma unroll
-                        for (int q = 0; q < 4; q++)
-                            tt[q] = flip_by(tt[q], s2, 64 * pass + k[q]);
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const f32x2 e = lut_entry(tt[q], key);
-                        bb[q] = e.x;
-                        base[q] = __float_as_uint(e.y);
-                    }
-                    bucket_add4(tt, bb, base, idx);
-#pragma unroll
-                    for (int q = 0; q < 4; q++)
-                        put_bits(w, (64 * pass + k[q]) * BITS, BITS, idx[q]);
+                    for (int r = 0; r < 4; r++)
+                        tt[slot][r] = flip_by(tt[slot][r], s2, 64 * pass + k[r]);
                 }
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const f32x2 e = lut_entry(tt[slot][r], key);
+                    bb[slot][r] = e.x;
+                    base[slot][r] = __float_as_uint(e.y);
+                }
+            };
+            issue(0, 0);
+#pragma unroll
+            for (int q = 0; q < NB; q++) {
+                if (q + 1 < NB)
+                    issue(q + 1, (q + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t idx[4];
+                bucket_add4(tt[q & 1], bb[q & 1], base[q & 1], idx);
+                const int i = first_of(q);
+                const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    put_bits(w, (64 * pass + k[r]) * BITS, BITS, idx[r]);
+            }
         }
         // keep the passes in order: this pass's words are complete here
         // (otherwise the whole pass can be sunk below the next pass's loads)
@@ -609,17 +614,13 @@ template <int D, int B0, int B1, bool S2>
 __device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const EncodeSide &s1,
                                                  const int64_t n_rows, const uint32_t key0,
                                                  const uint32_t key1, uint8_t *stg,
-                                                 const uint32_t *qt, const SignBits &s2)
+                                                 const uint32_t (&qw)[64], const SignBits &s2)
 {
     constexpr int NCH = 64 * 2 * D / 1024;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
     const uint8_t *src0 = static_cast<const uint8_t *>(s0.src);
     const uint8_t *src1 = static_cast<const uint8_t *>(s1.src);
-    // the sign-pair table's LDS address as an opaque register value: its reads
-    // then take base + immediate offset instead of one materialised address each
-    uint32_t qaddr = lds_address(qt);
-    asm volatile("" : "+v"(qaddr));
     int64_t g0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 64;
     u32x4 pf[NCH];
     load_group<D>(src0, g0, n_rows, lane, pf);
@@ -629,11 +630,11 @@ __device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const Enc
             load_group<D>(src1, g0, n_rows, lane, pf);
         else
             load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-        encode_group<D, B0, S2>(s0, g0, n_rows, key0, stg, qaddr, s2);
+        encode_group<D, B0, S2>(s0, g0, n_rows, key0, stg, qw, s2);
         if constexpr (B1 > 0) {
             stage_group<D>(pf, stg, lane);
             load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-            encode_group<D, B1, S2>(s1, g0, n_rows, key1, stg, qaddr, s2);
+            encode_group<D, B1, S2>(s1, g0, n_rows, key1, stg, qw, s2);
         }
     }
 }
@@ -644,29 +645,14 @@ void encode_lane_kernel(EncodeLaneParams p)
 {
     __shared__ float2 lut0[kLutBins];
     __shared__ float2 lut1[kLutBins];
-    __shared__ __attribute__((aligned(16))) uint32_t qt[256];
     __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][64 * (2 * D + 16)];
-    static_assert(kBlock == 256, "one sign-pair word per thread");
-    // bf16 sign pairs of the first two stages (layout at first_stage)
-    {
-        const int i = threadIdx.x, sg = i >> 7, j = (i >> 2) & 31, form = i & 3;
-        const uint32_t w0 = p.sbits[0], w1 = p.sbits[1], w2 = p.sbits[2], w3 = p.sbits[3];
-        auto neg = [&](int k) -> uint32_t {  // 1 if s_k = -1
-            const uint32_t w = k < 32 ? w0 : k < 64 ? w1 : k < 96 ? w2 : w3;
-            return (w >> (k & 31)) & 1u;
-        };
-        const int k = (form < 2 ? 0 : D / 2) + 2 * j;
-        const uint32_t lo = neg(k) ^ (form < 2 ? 0u : (uint32_t)sg);
-        const uint32_t hi = neg(k + 1) ^ (form & 1u) ^ (form < 2 ? 0u : (uint32_t)sg);
-        qt[i] = (0x3F80u | (lo << 15)) | ((0x3F80u | (hi << 15)) << 16);
-    }
     if constexpr (B0 != 2)
         build_lut(lut0, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
     if constexpr (B1 > 2)
         build_lut(lut1, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
     __syncthreads();
     encode_lane_loop<D, B0, B1, S2>(p.side[0], p.side[1], p.n_rows, lut_key(lut0),
-                                    lut_key(lut1), stage[threadIdx.x >> 6], qt, p.s2);
+                                    lut_key(lut1), stage[threadIdx.x >> 6], p.qw, p.s2);
 }
 
 // ----------------------------------------------------------------- append
@@ -1195,10 +1181,20 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         if (sides == 1)
             q.side[1] = q.side[0];  // unused
         q.n_rows = n_rows;
+        // the sign diagonal as bf16 (+-1, +-1) pairs of the first two stages
+        uint32_t sb[4] = {0u, 0u, 0u, 0u};
         for (int w = 0; w < 4; w++)
-            q.sbits[w] = q.s2.w[w] = 0u;
-        tq::sign_words(d, seed, q.sbits);
+            q.s2.w[w] = 0u;
+        tq::sign_words(d, seed, sb);
         tq::sign_words2(d, seed, flags, q.s2.w);
+        auto neg = [&](int k) -> uint32_t { return (sb[k >> 5] >> (k & 31)) & 1u; };
+        auto pairw = [&](int k) -> uint32_t {
+            return (0x3F80u | (neg(k) << 15)) | ((0x3F80u | (neg(k + 1) << 15)) << 16);
+        };
+        for (int j = 0; j < 32; j++) {
+            q.qw[j] = 2 * j < d / 2 ? pairw(2 * j) : 0u;
+            q.qw[32 + j] = 2 * j < d / 2 ? pairw(2 * j + d / 2) : 0u;
+        }
         const bool two = (flags & TQ_FLAG_TWO_SIDED) != 0;
         if (d == 64)
             two ? launch_encode_lane_d<64, true>(q, b0, b1, st)
