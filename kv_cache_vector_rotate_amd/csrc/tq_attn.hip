@@ -109,19 +109,24 @@ __device__ __forceinline__ uint64_t load_slice_bits(const uint8_t *base, uint32_
     }
 }
 
-// Centroid lookup width of the per-wave kernel: four neighbouring 2-bit
-// indices (one byte) address a 256-entry table of centroid quadruples; wider
-// indices go in pairs.  Either way one LDS read per lookup.
-template <int BITS>
+// Centroid lookups: neighbouring indices address a table of centroid tuples
+// in LDS, one read per lookup.  3- and 4-bit indices go in pairs (64- and
+// 256-entry tables of float2).  2-bit indices go in quadruples (one byte, a
+// 256-entry table of float4: one address instruction per four coordinates)
+// where four or more query heads share a KV head, which makes the scan
+// vector-ALU bound; with one or two the scan is bound by the LDS, and pairs
+// (a 16-entry, 128-byte table whose reads hit distinct banks) measured faster
+// than the 4 KB quadruple table's bank conflicts.
+template <int BITS, int G>
 struct Lookup {
-    static constexpr int W = BITS == 2 ? 4 : 2;  // coordinates per lookup
-    static constexpr int N = 1 << (W * BITS);    // table entries
+    static constexpr int W = BITS == 2 && G >= 4 ? 4 : 2;  // coordinates per lookup
+    static constexpr int N = 1 << (W * BITS);              // table entries
 };
 
-template <int BITS>
+template <int BITS, int G>
 __device__ __forceinline__ void fill_lookup(float *tab, const float *cent)
 {
-    constexpr int W = Lookup<BITS>::W, N = Lookup<BITS>::N;
+    constexpr int W = Lookup<BITS, G>::W, N = Lookup<BITS, G>::N;
     for (int e = threadIdx.x; e < N; e += kBlock)
 #pragma unroll
         for (int j = 0; j < W; j++)
@@ -129,10 +134,10 @@ __device__ __forceinline__ void fill_lookup(float *tab, const float *cent)
 }
 
 // the W centroids of lookup m of a lane's slice bits
-template <int BITS>
+template <int BITS, int G>
 __device__ __forceinline__ void lookup(const float *tab, uint64_t bits, int m, float *cc)
 {
-    constexpr int W = Lookup<BITS>::W, N = Lookup<BITS>::N;
+    constexpr int W = Lookup<BITS, G>::W, N = Lookup<BITS, G>::N;
     const int e = (int)((bits >> (W * BITS * m)) & (N - 1));
     if constexpr (W == 4) {
         const float4 v = *reinterpret_cast<const float4 *>(tab + 4 * e);
@@ -205,7 +210,7 @@ __device__ __forceinline__ void xch_scores(const float *tabK, float *xrow,
                                            float (&sc)[G])
 {
     using X = Xch<D, G>;
-    constexpr int CPL = X::CPL, P = X::P, WK = Lookup<BK>::W;
+    constexpr int CPL = X::CPL, P = X::P, WK = Lookup<BK, G>::W;
 #pragma unroll
     for (int c = 0; c < P; c++) {
         float s[G];
@@ -215,7 +220,7 @@ __device__ __forceinline__ void xch_scores(const float *tabK, float *xrow,
 #pragma unroll
         for (int m = 0; m < CPL / WK; m++) {
             float cc[WK];
-            lookup<BK>(tabK, kb[c], m, cc);
+            lookup<BK, G>(tabK, kb[c], m, cc);
 #pragma unroll
             for (int j = 0; j < WK; j++)
 #pragma unroll
@@ -245,11 +250,11 @@ __device__ __forceinline__ void xch_accumulate(const float *tabV, uint64_t vbits
                                                const float (&wc)[G],
                                                float (&acc)[G][Xch<D, G>::CPL])
 {
-    constexpr int CPL = Xch<D, G>::CPL, WV = Lookup<BV>::W;
+    constexpr int CPL = Xch<D, G>::CPL, WV = Lookup<BV, G>::W;
 #pragma unroll
     for (int m = 0; m < CPL / WV; m++) {
         float cc[WV];
-        lookup<BV>(tabV, vbits, m, cc);
+        lookup<BV, G>(tabV, vbits, m, cc);
 #pragma unroll
         for (int j = 0; j < WV; j++)
 #pragma unroll
@@ -472,10 +477,10 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     constexpr int RPB = RPW * (kBlock / 64);
     constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
     constexpr int CH = G >= 8 ? 4 : 8;    // row passes per step
-    constexpr int WK = Lookup<BK>::W, WV = Lookup<BV>::W;
+    constexpr int WK = Lookup<BK, G>::W, WV = Lookup<BV, G>::W;
 
-    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK>::N * WK];
-    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV>::N * WV];
+    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK, G>::N * WK];
+    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV, G>::N * WV];
     __shared__ float qs[G][D];
     __shared__ float red_m[kBlock / 64][G];
     __shared__ float red_l[kBlock / 64][G];
@@ -491,8 +496,8 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     const int g = blockIdx.y / p.gsplit;  // KV head
     const int h0 = blockIdx.y * G;        // first of this workgroup's G query heads
 
-    fill_lookup<BK>(tabK, p.centK);
-    fill_lookup<BV>(tabV, p.centV);
+    fill_lookup<BK, G>(tabK, p.centK);
+    fill_lookup<BV, G>(tabV, p.centV);
     rotate_queries<D, G>(p, qs, b, h0, wave, lane);
     __syncthreads();
 
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 #pragma unroll
             for (int m = 0; m < CPL / WK; m++) {
                 float cc[WK];
-                lookup<BK>(tabK, kb[c], m, cc);
+                lookup<BK, G>(tabK, kb[c], m, cc);
 #pragma unroll
                 for (int j = 0; j < WK; j++)
 #pragma unroll
@@ -634,7 +639,7 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
 #pragma unroll
             for (int m = 0; m < CPL / WV; m++) {
                 float cc[WV];
-                lookup<BV>(tabV, vb[c], m, cc);
+                lookup<BV, G>(tabV, vb[c], m, cc);
 #pragma unroll
                 for (int j = 0; j < WV; j++)
 #pragma unroll
@@ -673,12 +678,12 @@ __global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
     constexpr int CPL = G >= 8 ? 8 : 16;
     constexpr int P = D / CPL, RPW = 64 / P, RPB = RPW * (kBlock / 64);
     constexpr int RBK = D * BK / 8, SBK = CPL * BK / 8;
-    constexpr int WK = Lookup<BK>::W;
+    constexpr int WK = Lookup<BK, G>::W;
     constexpr int CH = G >= 8 ? 4 : 8;  // row passes per step of the per-lane form
     using X = Xch<D, G>;
     constexpr bool XON = X::ON;
 
-    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK>::N * WK];
+    __shared__ __attribute__((aligned(16))) float tabK[Lookup<BK, G>::N * WK];
     __shared__ float qs[G][D];
     __shared__ float red_m[kBlock / 64][G];
     __shared__ __attribute__((aligned(16))) float xbuf[XON ? kBlock / 64 * X::FLOATS : 1];
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
     const int chunk = blockIdx.x, b = blockIdx.z;
     const int g = blockIdx.y / p.gsplit;
     const int h0 = blockIdx.y * G;
-    fill_lookup<BK>(tabK, p.centK);
+    fill_lookup<BK, G>(tabK, p.centK);
     rotate_queries<D, G>(p, qs, b, h0, wave, lane);
     __syncthreads();
     const int sub = lane % P, rig = lane / P;
@@ -754,7 +759,7 @@ __global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
 #pragma unroll
                 for (int m = 0; m < CPL / WK; m++) {
                     float cc[WK];
-                    lookup<BK>(tabK, kb[c], m, cc);
+                    lookup<BK, G>(tabK, kb[c], m, cc);
 #pragma unroll
                     for (int j = 0; j < WK; j++)
 #pragma unroll
@@ -798,11 +803,11 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
     constexpr int CPL = G >= 8 ? 8 : 16;
     constexpr int P = D / CPL, RPW = 64 / P, RPB = RPW * (kBlock / 64);
     constexpr int RBV = D * BV / 8, SBV = CPL * BV / 8;
-    constexpr int WV = Lookup<BV>::W;
+    constexpr int WV = Lookup<BV, G>::W;
     constexpr int CH = G >= 8 ? 4 : 8;  // row passes per step
     constexpr int AST = G * D;
 
-    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV>::N * WV];
+    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV, G>::N * WV];
     __shared__ float red_m[kBlock / 64][G];
     __shared__ float red_l[kBlock / 64][G];
     __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
@@ -811,7 +816,7 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
     const int chunk = blockIdx.x, b = blockIdx.z;
     const int g = blockIdx.y / p.gsplit;
     const int h0 = blockIdx.y * G;
-    fill_lookup<BV>(tabV, p.centV);
+    fill_lookup<BV, G>(tabV, p.centV);
     // the context's largest score of each head: the largest chunk maximum
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
 #pragma unroll
             for (int m = 0; m < CPL / WV; m++) {
                 float cc[WV];
-                lookup<BV>(tabV, vb[c], m, cc);
+                lookup<BV, G>(tabV, vb[c], m, cc);
 #pragma unroll
                 for (int j = 0; j < WV; j++)
 #pragma unroll
