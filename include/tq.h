@@ -214,6 +214,21 @@ int tq_layer_bits_boundary(int n_layers, int n_boundary, int bits_inner,
 int tq_append_row(const tq_cache_desc *cache, int layer, const void *const *k_new,
                   const void *const *v_new, int dtype, int64_t pos, void *stream);
 
+/* Decode ring slots [start, start + count) of every (sequence, KV head) of a
+ * layer back to fp32 ([Foundry] API "Quantize / Dequantize": dequantize a
+ * range of cached positions of a layer; Performance Budget: the full-window
+ * dequantize).  layer = -1 decodes every layer; otherwise only that layer.
+ * k_out / v_out are host arrays of device pointers with n_layers entries
+ * (layer = -1) or 1 entry; entry i receives [batch][n_kv_heads][count]
+ * [head_dim] floats, the rows tq_decode gives for the same packed rows.  A
+ * NULL array skips that side, a NULL entry that (layer, side).  One launch
+ * covers up to 64 (layer, side) buffers of the same (head_dim, bits).
+ * 0 <= start, 0 <= count, start + count <= window, else TQ_EINVAL; count = 0
+ * decodes nothing.  Slots hold whatever was last written there (zero rows
+ * where nothing was). */
+int tq_cache_decode(const tq_cache_desc *cache, int layer, int64_t start, int64_t count,
+                    float *const *k_out, float *const *v_out, void *stream);
+
 /* Workspace bytes tq_attn_decode needs for this (cache, layer, n_q_heads,
  * ctx_len, sparse_v_threshold): the chunk records of the split over the
  * context and, with the sparse-V gate on (threshold > 0), also every context

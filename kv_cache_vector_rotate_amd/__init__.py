@@ -23,7 +23,7 @@ from ._abi import (TQ_ATTN_NOALLOC_MAX_BYTES, TQ_BETA_HALF_D, TQ_BF16, TQ_EHIP, 
 __all__ = [
     "TqError", "TQCache", "lib", "library_path", "tq_codebook_init", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
-    "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
+    "tq_cache_decode", "tq_attn_workspace_bytes", "tq_attn_decode", "tq_last_error", "tq_version",
     "tq_layer_bits_boundary", "tq_attn_decode_noalloc", "TQ_ATTN_NOALLOC_MAX_BYTES",
     "TQ_F32", "TQ_BF16", "TQ_BETA_HALF_D", "TQ_GAUSS_1_OVER_D", "TQ_OK", "TQ_EINVAL",
     "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_MAX_LAYERS", "TQ_FLAG_GAUSS_1_OVER_D", "TQ_FLAG_TWO_SIDED",
@@ -256,6 +256,56 @@ def tq_append_row(cache: TQCache, layer: int, k_new, v_new, pos: int, stream=Non
     vp = (ctypes.c_void_p * len(vs))(*[_dev(t, "v_new").value for t in vs])
     _check(lib().tq_append_row(ctypes.byref(cache.desc), layer, kp, vp, dt, pos, _stream(stream)),
            fn)
+
+
+def tq_cache_decode(cache: TQCache, layer: int, start: int = 0, count: int | None = None,
+                    k_out=None, v_out=None, sides: str = "kv", stream=None):
+    """Decode ring slots [start, start + count) (default: the whole window) of
+    one layer, or of every layer (layer = -1), to fp32.  k_out / v_out: a list
+    of per-layer tensors [batch, n_kv, count, d_l] (layer = -1) or one tensor;
+    allocated when None for the sides named in `sides`.  Returns (k_out, v_out)
+    with None for a side not decoded."""
+    fn = "tq_cache_decode"
+    if count is None:
+        count = cache.window - start
+    if layer < 0:
+        if layer != -1:
+            raise ValueError(f"{fn}: layer must be -1 (every layer) or a layer index")
+        layers = list(range(cache.n_layers))
+    else:
+        if layer >= cache.n_layers:
+            raise ValueError(f"{fn}: layer {layer} out of range (n_layers {cache.n_layers})")
+        layers = [layer]
+    if start < 0 or count < 0 or start + count > cache.window:
+        raise ValueError(f"{fn}: slots [{start}, {start + count}) outside [0, {cache.window})")
+
+    def alloc(outs, want):
+        if outs is not None or not want:
+            return outs
+        outs = [torch.empty(cache.batch, cache.n_kv_heads, count, cache.head_dim[l],
+                            dtype=torch.float32, device=cache.k_packed[l].device) for l in layers]
+        return outs if layer < 0 else outs[0]
+
+    k_out = alloc(k_out, "k" in sides)
+    v_out = alloc(v_out, "v" in sides)
+    lists = []
+    for outs, name in ((k_out, "k_out"), (v_out, "v_out")):
+        if outs is None:
+            lists.append(None)
+            continue
+        lst = list(outs) if layer < 0 else [outs]
+        if len(lst) != len(layers):
+            raise ValueError(f"{fn}: {name} needs {len(layers)} tensors (got {len(lst)})")
+        for l, t in zip(layers, lst):
+            _check_shape(t, (cache.batch, cache.n_kv_heads, count, cache.head_dim[l]),
+                         f"{name}[{l}]", fn)
+        lists.append(lst)
+    arrays = [None if lst is None else (ctypes.c_void_p * len(lst))(
+        *[_dev(t, name, torch.float32).value for t in lst])
+        for lst, name in zip(lists, ("k_out", "v_out"))]
+    _check(lib().tq_cache_decode(ctypes.byref(cache.desc), layer, start, count, arrays[0],
+                                 arrays[1], _stream(stream)), fn)
+    return k_out, v_out
 
 
 def tq_attn_workspace_bytes(cache: TQCache, layer: int, n_q_heads: int, ctx_len: int,

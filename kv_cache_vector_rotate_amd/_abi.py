@@ -18,7 +18,7 @@ EXPORTS = [
     "tq_last_error", "tq_version", "tq_codebook_init", "tq_codebook_init_density", "tq_signs",
     "tq_packed_row_bytes", "tq_rotate", "tq_encode", "tq_decode", "tq_append_row",
     "tq_attn_workspace_bytes", "tq_attn_decode", "tq_layer_bits_boundary",
-    "tq_attn_decode_noalloc",
+    "tq_attn_decode_noalloc", "tq_cache_decode",
 ]
 TQ_ATTN_NOALLOC_MAX_BYTES = 16 << 20
 
@@ -76,6 +76,7 @@ def lib():
         L.tq_encode.argtypes = [P, P, i32, i64, i32, i32, i32, u64, u32, P, P, P, P, P]
         L.tq_decode.argtypes = [P, P, i64, i32, i32, u64, u32, P, P]
         L.tq_append_row.argtypes = [P, i32, P, P, i32, i64, P]
+        L.tq_cache_decode.argtypes = [P, i32, i64, i64, P, P, P]
         L.tq_attn_workspace_bytes.argtypes = [P, i32, i32, i64, ctypes.c_float]
         L.tq_attn_workspace_bytes.restype = sz
         L.tq_attn_decode.argtypes = [P, i32, P, i32, i64, ctypes.c_float, ctypes.c_float, P, P, sz, P]
@@ -84,7 +85,7 @@ def lib():
                                              P, P]
         for name in ("tq_codebook_init", "tq_codebook_init_density", "tq_signs", "tq_rotate",
                      "tq_encode", "tq_decode", "tq_append_row", "tq_attn_decode",
-                     "tq_layer_bits_boundary", "tq_attn_decode_noalloc"):
+                     "tq_layer_bits_boundary", "tq_attn_decode_noalloc", "tq_cache_decode"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib

@@ -20,10 +20,13 @@
 // Detail).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cfloat>
 #include <cmath>
 #include <mutex>
 #include <string>
+
+#include <vector>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -724,12 +727,9 @@ __global__ __launch_bounds__(kBlock) void append_kernel(AppendParams p)
 
 // ----------------------------------------------------------------- decode
 
-struct DecodeParams {
-    const uint8_t *packed;
-    const float *norms;
-    float *out;
-    int64_t n_rows;
-    int64_t row_base;  // first row of this launch
+// Per-call tables of a decode: centroids, the sign words of this lane's
+// slice, and the xor masks of the two-sided rotation
+struct DecodeTables {
     float cent[16];
     uint32_t signs[8];
     // packed-row xor mask: all bits of index i set where the second diagonal
@@ -741,6 +741,15 @@ struct DecodeParams {
     int d_out;      // coordinates kept per output row (PAD kernels; else D)
 };
 
+struct DecodeParams {
+    DecodeTables t;
+    const uint8_t *packed;
+    const float *norms;
+    float *out;
+    int64_t n_rows;
+    int64_t row_base;  // first row of this launch
+};
+
 // One wave per workgroup, one pass of RPW rows per wave, and one launch (or
 // a few, for grids beyond the launch limit) covering all rows: short-lived
 // workgroups keep the write stream in few DRAM pages at a time, which a
@@ -748,34 +757,34 @@ struct DecodeParams {
 // both requested before either is used (one memory round trip, not two).
 constexpr int kDecodeBlock = 64;
 
+// The wave's RPW consecutive rows: packed rows from `in`, norms from `nrm`,
+// `valid` (1..RPW) of them written to `out` (rows of D floats, or of d_out
+// for PAD).  Rows past `valid` read row 0 and are not stored.
 template <int D, int BITS, bool PAD>
-__global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
+__device__ __forceinline__ void decode_wave(const DecodeTables &t, const uint8_t *in,
+                                            const float *nrm, float *out, int valid)
 {
     constexpr int P = Shape<D>::P, RPW = Shape<D>::RPW;
     constexpr int RB = D * BITS / 8;
     __shared__ float cent[16];
     __shared__ __attribute__((aligned(16))) float stage[kStageFloats];
     if (threadIdx.x < 16)
-        cent[threadIdx.x] = p.cent[threadIdx.x];
+        cent[threadIdx.x] = t.cent[threadIdx.x];
     __syncthreads();
     const int lane = threadIdx.x;
     const int sub = lane % P, rig = lane / P;
-    const int64_t row0 = p.row_base + (int64_t)blockIdx.x * RPW;
-    if (row0 >= p.n_rows)
-        return;
-    const uint32_t smask = p.signs[sub];
+    const uint32_t smask = t.signs[sub];
     uint32_t w[BITS];
     float n;
     {
-        const int64_t row = row0 + rig;
-        const int64_t r = row < p.n_rows ? row : row0;
-        load_words<BITS>(p.packed + r * RB + sub * 4 * BITS, w);
-        n = p.norms[r];
+        const int r = rig < valid ? rig : 0;
+        load_words<BITS>(in + (int64_t)r * RB + sub * 4 * BITS, w);
+        n = nrm[r];
     }
-    if (p.two_sided) {
+    if (t.two_sided) {
 #pragma unroll
         for (int j = 0; j < BITS; j++)
-            w[j] ^= p.flip[sub * BITS + j];
+            w[j] ^= t.flip[sub * BITS + j];
     }
     float v[kCPL];
 #pragma unroll
@@ -789,12 +798,53 @@ __global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
     apply_signs(v, smask);
     if constexpr (PAD) {
         // head_dim d_out < D: rows of d_out floats, the padded slices dropped
-        const int64_t rows = min<int64_t>(RPW, p.n_rows - row0);
-        store_region_padded<P>(p.out + row0 * p.d_out, v, stage, lane, rows * p.d_out,
-                               p.d_out / kCPL);
+        store_region_padded<P>(out, v, stage, lane, (int64_t)valid * t.d_out, t.d_out / kCPL);
     } else {
-        store_region_coalesced(p.out + row0 * D, v, stage, lane, (p.n_rows - row0) * D);
+        (void)RPW;
+        store_region_coalesced(out, v, stage, lane, (int64_t)valid * D);
     }
+}
+
+template <int D, int BITS, bool PAD>
+__global__ __launch_bounds__(kDecodeBlock) void decode_kernel(DecodeParams p)
+{
+    constexpr int RPW = Shape<D>::RPW, RB = D * BITS / 8;
+    const int64_t row0 = p.row_base + (int64_t)blockIdx.x * RPW;
+    if (row0 >= p.n_rows)
+        return;
+    const int valid = (int)min<int64_t>(RPW, p.n_rows - row0);
+    decode_wave<D, BITS, PAD>(p.t, p.packed + row0 * RB, p.norms + row0,
+                              p.out + row0 * (PAD ? p.t.d_out : D), valid);
+}
+
+// ---- Decode of a range of ring slots of cache layers ([Foundry] API
+// "Quantize / Dequantize": dequantize a range of cached positions of a
+// layer).  One launch covers up to kMaxDecodeSegs (layer, K or V) buffers of
+// one (D, bits, padding): blockIdx.z picks the buffer, blockIdx.y the
+// (sequence, head) (plus bh_base), blockIdx.x a run of RPW slots.  Slots
+// [start, start + count) of every (sequence, head) go to out rows
+// [bh][count][d_out].
+constexpr int kMaxDecodeSegs = 64;
+
+struct CacheDecodeParams {
+    DecodeTables t;
+    const uint8_t *packed[kMaxDecodeSegs];
+    const float *norms[kMaxDecodeSegs];
+    float *out[kMaxDecodeSegs];
+    int window, start, count, bh_base;
+};
+
+template <int D, int BITS, bool PAD>
+__global__ __launch_bounds__(kDecodeBlock) void cache_decode_kernel(CacheDecodeParams p)
+{
+    constexpr int RPW = Shape<D>::RPW, RB = D * BITS / 8;
+    const int seg = blockIdx.z;
+    const int64_t bh = (int64_t)p.bh_base + blockIdx.y;
+    const int slot0 = blockIdx.x * RPW;
+    const int valid = min(RPW, p.count - slot0);
+    const int64_t row = bh * p.window + p.start + slot0;  // first packed row
+    decode_wave<D, BITS, PAD>(p.t, p.packed[seg] + row * RB, p.norms[seg] + row,
+                              p.out[seg] + (bh * p.count + slot0) * (PAD ? p.t.d_out : D), valid);
 }
 
 // ----------------------------------------------------------------- rotate
@@ -946,6 +996,30 @@ void flip_words(int d, int bits, uint64_t seed, uint32_t flags, uint32_t *flip)
     }
 }
 
+void fill_decode_tables(const tq_codebook &cb, int d, int D, int bits, uint64_t seed,
+                        uint32_t flags, DecodeTables *t)
+{
+    for (int j = 0; j < 16; j++)
+        t->cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
+    tq::sign_words(D, seed, t->signs);
+    flip_words(D, bits, seed, flags, t->flip);
+    t->two_sided = (flags & TQ_FLAG_TWO_SIDED) ? 1 : 0;
+    t->d_out = d;
+}
+
+// The decode kernels negate through the index bits: the codebook must be
+// exactly symmetric
+int decode_codebook(int D, int bits, uint32_t flags, tq_codebook *cb, const char *fn)
+{
+    int rc = tq::get_codebook(D, bits, tq::density_of(flags), cb);
+    if (rc != TQ_OK)
+        return rc;
+    for (int j = 0; j < cb->levels; j++)
+        if (cb->centroids[cb->levels - 1 - j] != -cb->centroids[j])
+            return tq::fail(TQ_EUNSUPPORTED, std::string(fn) + ": codebook is not symmetric");
+    return TQ_OK;
+}
+
 int launch_status(const char *fn)
 {
     hipError_t e = hipGetLastError();
@@ -1063,6 +1137,27 @@ void launch_decode_d(int bits, const DecodeParams &p0, hipStream_t st)
         default: hipLaunchKernelGGL((decode_kernel<D, 4, PAD>), grid, block, 0, st, p); break;
         }
     });
+}
+
+// grid.y holds at most 65535 (sequence, head) pairs per launch
+constexpr int64_t kMaxGridY = 65535;
+
+template <int D, bool PAD>
+void launch_cache_decode_d(int bits, int nseg, int64_t n_bh, const CacheDecodeParams &p0,
+                           hipStream_t st)
+{
+    const unsigned gx = (unsigned)((p0.count + Shape<D>::RPW - 1) / Shape<D>::RPW);
+    for (int64_t b0 = 0; b0 < n_bh; b0 += kMaxGridY) {
+        CacheDecodeParams p = p0;
+        p.bh_base = (int)b0;
+        const dim3 grid(gx, (unsigned)std::min<int64_t>(kMaxGridY, n_bh - b0), (unsigned)nseg);
+        const dim3 block(kDecodeBlock);
+        switch (bits) {
+        case 2: hipLaunchKernelGGL((cache_decode_kernel<D, 2, PAD>), grid, block, 0, st, p); break;
+        case 3: hipLaunchKernelGGL((cache_decode_kernel<D, 3, PAD>), grid, block, 0, st, p); break;
+        default: hipLaunchKernelGGL((cache_decode_kernel<D, 4, PAD>), grid, block, 0, st, p); break;
+        }
+    }
 }
 
 template <typename T>
@@ -1237,22 +1332,14 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
         return rc;
     const int D = tq::padded_dim(d);  // rotated and stored length
     tq_codebook cb;
-    if ((rc = tq::get_codebook(D, bits, tq::density_of(flags), &cb)) != TQ_OK)
+    if ((rc = decode_codebook(D, bits, flags, &cb, fn)) != TQ_OK)
         return rc;
-    for (int j = 0; j < cb.levels; j++)
-        if (cb.centroids[cb.levels - 1 - j] != -cb.centroids[j])
-            return tq::fail(TQ_EUNSUPPORTED, "tq_decode: codebook is not symmetric");
     DecodeParams p;
     p.packed = packed;
     p.norms = norms;
     p.out = out;
     p.n_rows = n_rows;
-    p.d_out = d;
-    for (int j = 0; j < 16; j++)
-        p.cent[j] = j < cb.levels ? cb.centroids[j] : 0.0f;
-    tq::sign_words(D, seed, p.signs);
-    flip_words(D, bits, seed, flags, p.flip);
-    p.two_sided = (flags & TQ_FLAG_TWO_SIDED) ? 1 : 0;
+    fill_decode_tables(cb, d, D, bits, seed, flags, &p.t);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool pad = d != D;
     switch (D) {
@@ -1265,6 +1352,113 @@ extern "C" int tq_decode(const uint8_t *packed, const float *norms, int64_t n_ro
         break;
     }
     return launch_status(fn);
+}
+
+extern "C" int tq_cache_decode(const tq_cache_desc *c, int layer, int64_t start,
+                               int64_t count, float *const *k_out, float *const *v_out,
+                               void *stream)
+{
+    static const char *fn = "tq_cache_decode";
+    tq::clear_error();
+    if (!c)
+        return tq::fail(TQ_EINVAL, "tq_cache_decode: cache is NULL");
+    if (c->n_layers < 1 || c->n_layers > TQ_MAX_LAYERS || c->batch < 0 || c->n_kv_heads < 0 ||
+        c->window < 1 || !c->head_dim || !c->k_packed || !c->k_norms || !c->v_packed ||
+        !c->v_norms)
+        return tq::fail(TQ_EINVAL, "tq_cache_decode: invalid cache descriptor");
+    if (layer < -1 || layer >= c->n_layers)
+        return tq::fail(TQ_EINVAL, "tq_cache_decode: layer out of range");
+    if (start < 0 || count < 0 || start + count > c->window)
+        return tq::fail(TQ_EINVAL, "tq_cache_decode: slots [start, start + count) must lie in "
+                                   "[0, window)");
+    if (tq::check_flags(c->flags, fn) != TQ_OK)
+        return TQ_EINVAL;
+    int rc;
+    const int l0 = layer < 0 ? 0 : layer, l1 = layer < 0 ? c->n_layers : layer + 1;
+    // the (layer, side) buffers to decode: side 0 = K, 1 = V
+    struct Seg {
+        int layer, side, d, D, bits;
+        const uint8_t *packed;
+        const float *norms;
+        float *out;
+    };
+    std::vector<Seg> segs;
+    for (int l = l0; l < l1; l++) {
+        if ((rc = check_d(c->head_dim[l], fn)) != TQ_OK)
+            return rc;
+        for (int side = 0; side < 2; side++) {
+            float *const *outs = side == 0 ? k_out : v_out;
+            float *o = outs ? outs[l - l0] : nullptr;
+            if (!o)
+                continue;  // side or layer not requested
+            const int bits = tq::layer_bits(c, l, side);
+            if ((rc = check_bits(bits, fn)) != TQ_OK)
+                return rc;
+            const uint8_t *pk = side == 0 ? c->k_packed[l] : c->v_packed[l];
+            const float *nm = side == 0 ? c->k_norms[l] : c->v_norms[l];
+            if (!pk || !nm)
+                return tq::fail(TQ_EINVAL, "tq_cache_decode: NULL layer buffer");
+            if (!aligned(pk, 16) || !aligned(o, 16) || !aligned(nm, 4))
+                return tq::fail(TQ_EINVAL, "tq_cache_decode: misaligned buffer (packed and out "
+                                           "need 16 bytes, norms 4)");
+            const int d = c->head_dim[l];
+            segs.push_back({l, side, d, tq::padded_dim(d), bits, pk, nm, o});
+        }
+    }
+    const int64_t n_bh = (int64_t)c->batch * c->n_kv_heads;
+    if (n_bh == 0 || count == 0 || segs.empty())
+        return TQ_OK;
+    if ((rc = injected(fn)) != TQ_OK)
+        return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // one launch per distinct (head_dim, bits) and per kMaxDecodeSegs buffers
+    // of it, in the order of their first buffers
+    std::vector<bool> done(segs.size(), false);
+    for (size_t first = 0; first < segs.size(); first++) {
+        if (done[first])
+            continue;
+        const Seg &f = segs[first];
+        tq_codebook cb;
+        if ((rc = decode_codebook(f.D, f.bits, c->flags, &cb, fn)) != TQ_OK)
+            return rc;
+        CacheDecodeParams p;
+        fill_decode_tables(cb, f.d, f.D, f.bits, c->seed, c->flags, &p.t);
+        p.window = c->window;
+        p.start = (int)start;
+        p.count = (int)count;
+        p.bh_base = 0;
+        int n = 0;
+        for (size_t i = first; i <= segs.size(); i++) {
+            const bool flush = i == segs.size() || n == kMaxDecodeSegs;
+            if (flush && n > 0) {
+                const bool pad = f.d != f.D;
+                switch (f.D) {
+                case 64: launch_cache_decode_d<64, false>(f.bits, n, n_bh, p, st); break;
+                case 128:
+                    pad ? launch_cache_decode_d<128, true>(f.bits, n, n_bh, p, st)
+                        : launch_cache_decode_d<128, false>(f.bits, n, n_bh, p, st);
+                    break;
+                default:
+                    pad ? launch_cache_decode_d<256, true>(f.bits, n, n_bh, p, st)
+                        : launch_cache_decode_d<256, false>(f.bits, n, n_bh, p, st);
+                    break;
+                }
+                if ((rc = launch_status(fn)) != TQ_OK)
+                    return rc;
+                n = 0;
+            }
+            if (i == segs.size())
+                break;
+            if (done[i] || segs[i].d != f.d || segs[i].bits != f.bits)
+                continue;
+            done[i] = true;
+            p.packed[n] = segs[i].packed;
+            p.norms[n] = segs[i].norms;
+            p.out[n] = segs[i].out;
+            n++;
+        }
+    }
+    return TQ_OK;
 }
 
 extern "C" int tq_append_row(const tq_cache_desc *c, int layer, const void *const *k_new,

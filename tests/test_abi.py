@@ -212,6 +212,49 @@ def test_cache_and_attention_validation(tq):
     assert "flag" in tq.tq_last_error()
 
 
+def test_cache_decode_validation_without_launch(tq):
+    """tq_cache_decode rejects bad descriptors, layers, slot ranges, widths and
+    buffers before launching anything; empty requests succeed and launch
+    nothing."""
+    L = tq.lib()
+    d = _desc(tq)                                   # 2 layers, window 8, K4/V2, d 128
+    outs = (ctypes.c_void_p * 2)(8192, 8192)
+    assert L.tq_cache_decode(None, -1, 0, 8, outs, outs, None) == tq.TQ_EINVAL
+    for layer in (-2, 2):
+        assert L.tq_cache_decode(ctypes.byref(d), layer, 0, 8, outs, outs, None) == tq.TQ_EINVAL
+        assert "layer" in tq.tq_last_error()
+    for start, count in ((-1, 4), (0, -1), (4, 5), (9, 0)):
+        assert L.tq_cache_decode(ctypes.byref(d), -1, start, count, outs, outs, None) == tq.TQ_EINVAL
+        assert "slots" in tq.tq_last_error()
+    mis = (ctypes.c_void_p * 2)(8192 + 4, 8192)
+    assert L.tq_cache_decode(ctypes.byref(d), -1, 0, 8, mis, None, None) == tq.TQ_EINVAL
+    assert "misaligned" in tq.tq_last_error()
+    assert L.tq_cache_decode(ctypes.byref(_desc(tq, bv=1)), -1, 0, 8, None, outs,
+                             None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_cache_decode(ctypes.byref(_desc(tq, head_dim=100)), 0, 0, 8, outs, None,
+                             None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_cache_decode(ctypes.byref(_desc(tq, flags=4)), 0, 0, 8, outs, None,
+                             None) == tq.TQ_EINVAL
+    # nothing to decode: no launch
+    assert L.tq_cache_decode(ctypes.byref(d), -1, 3, 0, outs, outs, None) == tq.TQ_OK
+    assert L.tq_cache_decode(ctypes.byref(d), -1, 0, 8, None, None, None) == tq.TQ_OK
+    nulls = (ctypes.c_void_p * 2)(None, None)
+    assert L.tq_cache_decode(ctypes.byref(d), -1, 0, 8, nulls, None, None) == tq.TQ_OK
+    assert L.tq_cache_decode(ctypes.byref(_desc(tq, batch=0)), -1, 0, 8, outs, outs,
+                             None) == tq.TQ_OK
+    # the binding checks counts and shapes first
+    cache = tq.TQCache(2, 2, 2, 8, [128, 64], 4, 2, device="cpu")
+    with pytest.raises(ValueError, match="slots"):
+        tq.tq_cache_decode(cache, -1, 4, 5)
+    with pytest.raises(ValueError, match="2 tensors"):
+        tq.tq_cache_decode(cache, -1, 0, 8, k_out=[torch.zeros(2, 2, 8, 128)])
+    with pytest.raises(ValueError, match=r"k_out\[1\]"):
+        tq.tq_cache_decode(cache, -1, 0, 8, k_out=[torch.zeros(2, 2, 8, 128)] * 2)
+    with pytest.raises(ValueError, match=r"v_out\[0\]"):
+        tq.tq_cache_decode(cache, 0, 2, 4, k_out=torch.zeros(2, 2, 4, 128),
+                           v_out=torch.zeros(2, 2, 8, 128))
+
+
 def test_binding_rejects_mismatched_shapes(tq):
     """The Python binding checks every tensor against the cache before any
     pointer reaches the library (host-only: CPU tensors, so a shape that
