@@ -129,22 +129,34 @@ def test_edge_rows(tq, orc):
         assert np.array_equal(sn.cpu().numpy(), gn[8:] * np.float32(2.0 ** k))
 
 
+@pytest.mark.parametrize("sides", [1, 2])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_edge_rows_d128_d256(tq, orc, bits, d, dtype):
+def test_edge_rows_d128_d256(tq, orc, bits, d, dtype, sides):
     """Zero, constant, spike, exact-tie, tiny and huge rows against the
     oracle; rows holding an Inf or a NaN encode as the zero row with a
     non-finite norm; power-of-two scale invariance (indices identical, norms
-    scaled exactly, except that the one-lane-per-row bf16 kernel (d <= 128)
-    sums a rescaled row's squares in another order: there within 1e-6)."""
+    scaled exactly, except that the one-lane-per-row bf16 kernels sum a
+    rescaled row's squares in another order: there within 1e-6).  sides = 2
+    encodes the rows as K and as V in one call (the two results must be
+    identical)."""
+    def tq_encode(rows, bits_k, bits_v, seed):
+        if sides == 1:
+            return tq.tq_encode(rows, None, bits_k, bits_v, seed)
+        kp_, kn_, vp_, vn_ = tq.tq_encode(rows, rows, bits_k, bits_k, seed)
+        assert torch.equal(kp_, vp_)
+        assert torch.equal(kn_.nan_to_num(), vn_.nan_to_num())
+        return kp_, kn_, None, None
+
+    lane_per_row = dtype == torch.bfloat16
     rng = np.random.default_rng(5)
     e = np.eye(d, dtype=np.float32)
     base = rng.standard_normal((6, d)).astype(np.float32)
     rows = [np.zeros(d, np.float32), np.ones(d, np.float32), e[d - 56] * 3.0, e[0] + e[1],
             e[3] - e[d // 2 + 2], base[0] * np.float32(1e-30), base[1] * np.float32(1e30)]
     x = torch.from_numpy(np.stack(rows + list(base))).cuda().to(dtype)
-    kp, kn, _, _ = tq.tq_encode(x, None, bits, 2, SEED)
+    kp, kn, _, _ = tq_encode(x, bits, 2, SEED)
     torch.cuda.synchronize()
     op, on, u = orc.encode(_np(x).astype(np.float32), d, bits, SEED, want_u=True)
     gp, gn = kp.cpu().numpy(), kn.cpu().numpy()
@@ -165,10 +177,10 @@ def test_edge_rows_d128_d256(tq, orc, bits, d, dtype):
     # exact power-of-two scaling leaves the indices unchanged
     for k in (-60, -20, 20, 60):  # +-60 take the rescaled path
         xs = x[7:] * float(2.0 ** k)
-        sp, sn, _, _ = tq.tq_encode(xs, None, bits, 2, SEED)
+        sp, sn, _, _ = tq_encode(xs, bits, 2, SEED)
         assert np.array_equal(sp.cpu().numpy(), gp[7:])
         want = gn[7:] * np.float32(2.0 ** k)
-        if abs(k) > 20 and dtype == torch.bfloat16 and d <= 128:
+        if abs(k) > 20 and lane_per_row:
             np.testing.assert_allclose(sn.cpu().numpy(), want, rtol=1e-6)
         else:
             assert np.array_equal(sn.cpu().numpy(), want)
@@ -176,7 +188,7 @@ def test_edge_rows_d128_d256(tq, orc, bits, d, dtype):
     bad = x[7:9].clone()
     bad[0, 17] = float("inf")
     bad[1, d - 6] = float("nan")
-    bp, bn, _, _ = tq.tq_encode(bad, None, bits, 2, SEED)
+    bp, bn, _, _ = tq_encode(bad, bits, 2, SEED)
     bn = bn.cpu().numpy()
     assert not np.isfinite(bn).any()
     assert np.all(unpack_rows(bp.cpu().numpy(), d, bits) == L // 2 - 1)
