@@ -127,6 +127,136 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
 
 
+# -- rocprofv3 output -> profiles/ ------------------------------------------
+# The kernels whose algorithmic bytes per launch the bench knows, by the
+# name rocprofv3 reports (template arguments included) and a short key.
+def _known_kernels():
+    n3 = L3 * H3 * T3
+    n5 = H5 * T5
+    return {
+        "encode_lane_kernel<128, 4, 2, false>":
+            ("encode_k4v2", enc_bytes(n3, D3, BK3, 2) + enc_bytes(n3, D3, BV3, 2)),
+        "decode_kernel<128, 4, false>": ("decode_k4", dec_bytes(n3, D3, BK3)),
+        "decode_kernel<128, 2, false>": ("decode_v2", dec_bytes(n3, D3, BV3)),
+        "attn_partial_wave_kernel<128, 4, 2, 4>":
+            ("attn_decode", attn_bytes(B4, HQ4, HKV4, D4, T4, BK4, BV4)),
+        "encode_lane_kernel<64, 3, 2, false>":
+            ("long_encode_d64", enc_bytes(n5, 64, BK5, 2) + enc_bytes(n5, 64, BV5, 2)),
+        "encode256_kernel<3, 2, false>":
+            ("long_encode_d256", enc_bytes(n5, 256, BK5, 2) + enc_bytes(n5, 256, BV5, 2)),
+        "decode_kernel<64, 3, false>": ("long_decode_k3_d64", dec_bytes(n5, 64, BK5)),
+        "decode_kernel<64, 2, false>": ("long_decode_v2_d64", dec_bytes(n5, 64, BV5)),
+        "decode_kernel<256, 3, false>": ("long_decode_k3_d256", dec_bytes(n5, 256, BK5)),
+        "decode_kernel<256, 2, false>": ("long_decode_v2_d256", dec_bytes(n5, 256, BV5)),
+        "append_kernel<256, float>":
+            ("gemma_append", enc_bytes(L2 * B2 * H2, D2, BK2, 4) + enc_bytes(L2 * B2 * H2, D2, BV2, 4)),
+    }
+
+
+def _short_name(name):
+    import re
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("(anonymous namespace)::", "")
+    return re.sub(r"\((\w+)\)$", "", name).strip()
+
+
+def _pmc(path):
+    """{kernel: {counter: [values per dispatch]}} from a counter_collection.csv"""
+    import csv
+    out = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            k = _short_name(r["Kernel_Name"])
+            out.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def summarize_profiles(root):
+    """Markdown tables and profiles/{traffic,valu}.json from the rocprofv3
+    runs under `root`: trace/ (kernel trace), fetch/, write/ (FETCH_SIZE,
+    WRITE_SIZE), copy_fetch/, copy_write/ (the copy calibration), valu/
+    (SQ_INSTS_VALU, SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT, GRBM_COUNT).  A
+    kernel launched at several sizes (decode_kernel<128, 4> by the bulk
+    step and by the small round trip; cache_decode_kernel by 64 and then 4
+    buffers) is summarised over its largest launches: those at least half
+    the largest."""
+    import glob
+    import sqlite3
+    import statistics
+
+    def big(vals):
+        top = max(vals)
+        return [v for v in vals if v >= 0.5 * top]
+
+    def med(vals):
+        return statistics.median(big(vals))
+    known = _known_kernels()
+    db = glob.glob(os.path.join(root, "trace", "*_results.db"))[0]
+    con = sqlite3.connect(db)
+    cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
+    name_col = "name" if "name" in cols else "kernel_name"
+    dur = {}
+    for name, t0, t1 in con.execute(f"select {name_col}, start, end from kernels"):
+        dur.setdefault(_short_name(name), []).append((t1 - t0) / 1e3)
+    ours = ("encode", "decode", "attn_", "append", "rotate")
+    print("| kernel | launches | avg us | median us | algorithmic bytes / launch | GB/s at avg | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|")
+    for k, v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        if not any(o in k for o in ours):
+            continue
+        a = known.get(k, (None, None))[1]
+        v = big(v)
+        avg = statistics.mean(v)
+        extra = (f"{a} | {a / avg / 1e3:.0f} | {100 * a / avg / 1e3 / HBM_PEAK_GBS:.1f}" if a
+                 else "- | - | -")
+        print(f"| `{k}` | {len(v)} | {avg:.2f} | {statistics.median(v):.2f} | {extra} |")
+    fetch = _pmc(os.path.join(root, "fetch", "run_counter_collection.csv"))
+    write = _pmc(os.path.join(root, "write", "run_counter_collection.csv"))
+    cf = med(next(iter(_pmc(os.path.join(root, "copy_fetch", "run_counter_collection.csv")).values()))["FETCH_SIZE"])
+    cw = med(next(iter(_pmc(os.path.join(root, "copy_write", "run_counter_collection.csv")).values()))["WRITE_SIZE"])
+    nbytes = (1 << 28) * 4  # the copy calibration moves 1 GiB each way
+    fs, ws = nbytes / (cf * 1024), nbytes / (cw * 1024)
+    print(f"\ncopy calibration: FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB per 1 GiB copy: "
+          f"read scale {fs:.4f}, write scale {ws:.4f}\n")
+    print("| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch | algorithmic | ratio |")
+    print("|---|---|---|---|---|---|---|")
+    traffic = {"source_hash": source_hash(), "calibration": {"fetch_scale": fs, "write_scale": ws},
+               "kernels": {}}
+    for k in sorted(fetch):
+        f = med(fetch[k]["FETCH_SIZE"])
+        w = med(write.get(k, {}).get("WRITE_SIZE", [0.0]))
+        rd, wr = f * 1024 * fs, w * 1024 * ws
+        key, a = known.get(k, (None, None))
+        if key:
+            traffic["kernels"][key] = {"kernel": k, "hbm_bytes_per_launch": int(rd + wr),
+                                       "read": int(rd), "written": int(wr), "alg_bytes": a}
+        nl = len(big(fetch[k]["FETCH_SIZE"]))
+        print(f"| `{k}` | {nl} | {f:.0f} | {w:.0f} | {rd + wr:.4g} | "
+              f"{a if a else '-'} | {(rd + wr) / a:.3f} |" if a else
+              f"| `{k}` | {nl} | {f:.0f} | {w:.0f} | {rd + wr:.4g} | - | - |")
+    valu = _pmc(os.path.join(root, "valu", "run_counter_collection.csv"))
+    print("\n| kernel | launches | SQ_INSTS_VALU / launch | clocks (GRBM_COUNT / 8) | VALU issue share | "
+          "SQ_INSTS_LDS | LDS bank-conflict share of CU clocks |")
+    print("|---|---|---|---|---|---|---|")
+    vrec = {"source_hash": source_hash(), "kernels": {}}
+    for k in sorted(valu):
+        c = valu[k]
+        vi = med(c["SQ_INSTS_VALU"])
+        clk = med(c["GRBM_COUNT"]) / 8
+        lds = med(c["SQ_INSTS_LDS"])
+        conf = med(c["SQ_LDS_BANK_CONFLICT"]) / 256
+        key = known.get(k, (None, None))[0]
+        if key:
+            vrec["kernels"][key] = {"kernel": k, "valu_insts_per_launch": int(vi)}
+        # one wave64 vector instruction occupies a SIMD for 4 clocks; 1024 SIMDs
+        print(f"| `{k}` | {len(big(c['SQ_INSTS_VALU']))} | {vi:.4g} | {clk:.4g} | "
+              f"{vi * 4 / 1024 / clk:.3f} | {lds:.4g} | {conf / clk:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(traffic, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", "valu.json"), "w") as fh:
+        json.dump(vrec, fh, indent=1)
+
+
 def log(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
@@ -551,7 +681,13 @@ def main():
     ap.add_argument("--workloads", default="1,2,4,5",
                     help="workloads measured beside the headline step (comma list of 1, 2, 4, 5)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/traffic.json and profiles/valu.json and print the tables "
+                         "from the rocprofv3 runs under DIR (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
