@@ -445,9 +445,11 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
         if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
             // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
             // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
-            // first stage below then runs on it unchanged
+            // first stage below then runs on it unchanged.  The loops stay
+            // rolled: unrolled, their row reads are allocated alongside the
+            // common path's registers
             float mx = 0.0f;
-#pragma unroll
+#pragma unroll 2
             for (int m = 0; m < CB / 16; m++) {
                 const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
                 const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
@@ -460,7 +462,7 @@ __device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t 
             if (!bad && mx > 0.0f)
                 (void)frexpf(mx, &nexp);
             ss = 0.0f;
-#pragma unroll
+#pragma unroll 2
             for (int m = 0; m < CB / 16; m++) {
                 const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
                 uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
