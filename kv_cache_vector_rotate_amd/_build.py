@@ -18,7 +18,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 math
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-ffp-contract=fast"]
+             "-ffp-contract=fast",
+             # matrix-core results in ordinary VGPRs: the encode reads every
+             # one with vector instructions, which accumulation registers would
+             # cost a copy each
+             "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
 

@@ -259,47 +259,8 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeParams p)
     }
 }
 
-// --------------------------------------------- encode, one lane per row
-// For bf16 rows of d in {64, 128} lane l of a wave owns row l of a 64-row
-// group.  The rows of the group are staged in LDS (whole-line global loads,
-// the next group's loads in flight while this one is transformed), and each
-// lane reads its own row from there.
-//
-// The first Hadamard stage (across the halves of the row, h = d/2) takes the
-// raw bf16 words: with P = (x_k, x_{k+d/2}) packed from two words by a byte
-// permute and Q = (s_k, +-s_{k+d/2}) the bf16 sign pair, the bf16 dot product
-// instruction gives s_k x_k +- s_{k+d/2} x_{k+d/2} exactly rounded to fp32:
-// sign, conversion and the first stage in one instruction.  The Q words are
-// the same for every row and are held in scalar registers.  The remaining stages are
-// plain fp32 add/sub; the last one is fused with the scaling to
-// T = 128 u = 128 y / ||x||, which feeds the bucketize table directly.  With
-// d = 128 a lane makes two passes of 64 outputs (coordinates 0..63, then
-// 64..127), each reading the staged row again.
-//
-// The sum of squares uses the same dot product on the raw words.  Rows whose
-// sum of squares leaves [2^-100, 2^100] (tiny, huge, zero or non-finite) take
-// an exact power-of-two rescale of the input instead; rows holding Inf or NaN
-// encode as the zero row and store a non-finite norm.
-
-struct SignBits {
-    uint32_t w[4];  // bit k of w[k / 32] set: coordinate k is negated
-};
-
-struct EncodeLaneParams {
-    EncodeSide side[2];
-    int64_t n_rows;
-    uint32_t qw[64];    // bf16 sign pairs: [j] (s_2j, s_2j+1), [32 + j] (s_2j+d/2, s_2j+1+d/2)
-    SignBits s2;        // second diagonal of the two-sided rotation
-};
-
-// t negated when output coordinate k carries a -1 of the second diagonal (k
-// is a compile-time index once the loops are unrolled, and the words are
-// uniform: the mask is scalar work, the xor one vector instruction)
-__device__ __forceinline__ float flip_by(float t, const SignBits &s2, int k)
-{
-    return __uint_as_float(__float_as_uint(t) ^ ((s2.w[k >> 5] << (31 - (k & 31))) & 0x80000000u));
-}
-
+// ------------------------------------------------- encode, shared helpers
+// idx (nbits wide) into the little-endian bit stream w at bit `bit`
 template <int NWORDS>
 __device__ __forceinline__ void put_bits(uint32_t (&w)[NWORDS], int bit, int nbits, uint32_t idx)
 {
@@ -321,48 +282,6 @@ __device__ __forceinline__ f32x2 lut_entry(float t, uint32_t key)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// First two stages of pass PASS for one lane's staged row, from the raw
-// bf16 words: A = (x_{2j}, x_{2j+1}) and B = (x_{2j+d/2}, x_{2j+1+d/2}).  The
-// stage across halves (h = d/2) and the stage h = 1 give
-//   y_{2j}   = s_{2j} x_{2j} + s_{2j+1} x_{2j+1} + sigma (s' x' + s'' x'')
-//   y_{2j+1} = s_{2j} x_{2j} - s_{2j+1} x_{2j+1} + sigma (s' x' - s'' x'')
-// (primes: the partners d/2 further on), i.e. two bf16 dot products each
-// against sign pairs.  sigma = +1 gives output coordinates 0..d/2-1, sigma =
-// -1 the rest.  The sign pairs are the same for every row and arrive as
-// kernel arguments, which stay in scalar registers: qw[j] = (s_{2j},
-// s_{2j+1}) and qw[32 + j] = (s', s''); the negated forms are the dot
-// product's source-negation modifiers.
-//   d = 128: pass PASS gives v[k] = output 64 PASS + k, k < 64.
-//   d = 64:  one pass; v[k] = output k for both signs of sigma.
-template <int D, int PASS>
-__device__ __forceinline__ void first_stage(const uint8_t *row, const uint32_t (&qw)[64],
-                                            float (&v)[64])
-{
-    constexpr int HB = D;  // bytes of half a row
-#pragma unroll
-    for (int m = 0; m < HB / 16; m++) {
-        const u32x4 wa = *reinterpret_cast<const u32x4 *>(row + 16 * m);
-        const u32x4 wb = *reinterpret_cast<const u32x4 *>(row + HB + 16 * m);
-        const uint32_t a[4] = {wa.x, wa.y, wa.z, wa.w};
-        const uint32_t b[4] = {wb.x, wb.y, wb.z, wb.w};
-        if constexpr (D == 64) {
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                const int j = 4 * m + c;
-                dot2_quad_s(a[c], b[c], qw[j], qw[32 + j], v[2 * j], v[2 * j + 1], v[32 + 2 * j],
-                            v[33 + 2 * j]);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < 4; c += 2) {
-                const int j = 4 * m + c;
-                dot2_pair2_s<PASS>(a[c], b[c], qw[j], qw[32 + j], a[c + 1], b[c + 1], qw[j + 1],
-                                   qw[33 + j], v[2 * j], v[2 * j + 1], v[2 * j + 2], v[2 * j + 3]);
-            }
-        }
-    }
-}
-
 // Sum of squares of NB bytes of a staged bf16 row (products exact, fp32 sums).
 template <int NB>
 __device__ __forceinline__ float row_sumsq(const uint8_t *row)
@@ -379,285 +298,6 @@ __device__ __forceinline__ float row_sumsq(const uint8_t *row)
         }
     }
     return ss0 + ss1;
-}
-
-// The 64 rows of a group starting at row g0 of `src`: chunk c of lane l is
-// bytes [1024 c + 16 l, +16) of the group (rows past n_rows read as zeros).
-template <int D>
-__device__ __forceinline__ void load_group(const uint8_t *src, int64_t g0, int64_t n_rows,
-                                           int lane, u32x4 (&pf)[64 * 2 * D / 1024])
-{
-    constexpr int CB = 2 * D, NCH = 64 * CB / 1024, RPC = 1024 / CB, LPC = 64 / RPC;
-    const u32x4 *gp = reinterpret_cast<const u32x4 *>(src + g0 * CB) + lane;
-    if (g0 + 64 <= n_rows) {  // a whole group (uniform branch): no per-lane checks
-#pragma unroll
-        for (int c = 0; c < NCH; c++)
-            pf[c] = __builtin_nontemporal_load(gp + 64 * c);
-    } else {
-        const int crow = lane / LPC;
-#pragma unroll
-        for (int c = 0; c < NCH; c++)
-            pf[c] = g0 + c * RPC + crow < n_rows ? __builtin_nontemporal_load(gp + 64 * c)
-                                                 : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// The group's rows from registers into this wave's LDS stage (row stride SR).
-template <int D>
-__device__ __forceinline__ void stage_group(const u32x4 (&pf)[64 * 2 * D / 1024], uint8_t *stg,
-                                            int lane)
-{
-    constexpr int CB = 2 * D, SR = CB + 16, NCH = 64 * CB / 1024, RPC = 1024 / CB,
-                  LPC = 64 / RPC;
-    const int crow = lane / LPC, cbyte = (lane % LPC) * 16;
-#pragma unroll
-    for (int c = 0; c < NCH; c++)
-        *reinterpret_cast<u32x4 *>(stg + (c * RPC + crow) * SR + cbyte) = pf[c];
-    wave_lds_fence();
-}
-
-// Encode the staged group of 64 rows starting at row g0 for one side.
-template <int D, int BITS, bool S2>
-__device__ __forceinline__ void encode_group(const EncodeSide &s, const int64_t g0,
-                                             const int64_t n_rows, const uint32_t key,
-                                             uint8_t *stg, const uint32_t (&qw)[64],
-                                             const SignBits &s2)
-{
-    constexpr int NP = D / 64;            // passes of 64 outputs
-    constexpr int CB = 2 * D;             // input bytes per row
-    constexpr int SR = CB + 16;           // LDS stride of a staged row
-    constexpr int RB = D * BITS / 8;      // packed bytes per row
-    constexpr int NW = D * BITS / 32;     // packed words per row
-    constexpr int NWP = 2 * BITS;         // packed words per pass
-    constexpr int HL = D / 4;             // half-width of the last stage
-    const int lane = threadIdx.x & 63;
-    uint8_t *mine = stg + lane * SR;
-    const int nvalid = (int)min<int64_t>(64, n_rows - g0);
-    uint32_t w[NW];
-#pragma unroll
-    for (int q = 0; q < NW; q++)
-        w[q] = 0u;
-    float t = 0.0f, nstore = 0.0f;
-    {
-        float ss = row_sumsq<CB>(mine);
-        int nexp = 0;
-        bool bad = false;
-        if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {
-            // rare: rewrite this lane's staged row as x * 2^-nexp (max |x|
-            // in [1/2, 1)), or zeros if it holds Inf or NaN; the fast
-            // first stage below then runs on it unchanged.  The loops stay
-            // rolled: unrolled, their row reads are allocated alongside the
-            // common path's registers
-            float mx = 0.0f;
-#pragma unroll 2
-            for (int m = 0; m < CB / 16; m++) {
-                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int c = 0; c < 4; c++)
-                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
-            }
-            const float ss0 = ss;  // the fast path's sum
-            bad = !(mx <= FLT_MAX) || ss0 != ss0;  // an Inf or a NaN (the max skips NaN)
-            if (!bad && mx > 0.0f)
-                (void)frexpf(mx, &nexp);
-            ss = 0.0f;
-#pragma unroll 2
-            for (int m = 0; m < CB / 16; m++) {
-                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    // exact for normal results; parts below 2^-126 of the
-                    // largest magnitude may round, far under fp32 precision
-                    const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
-                    const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
-                    ss = fmaf(x0, x0, ss);
-                    ss = fmaf(x1, x1, ss);
-                    xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
-                }
-                *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
-            }
-            if (bad)
-                ss = ss0 + mx;  // stored as the norm: not finite
-        }
-        t = (ss > 0.0f && !bad) ? 128.0f / sqrtf((float)D * ss) : 0.0f;
-        nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);
-    }
-#pragma unroll
-    for (int pass = 0; pass < NP; pass++) {
-        float v[64];
-        // reread the row in every pass rather than keep it in registers
-        wave_lds_fence();
-        if (pass == 0)
-            first_stage<D, 0>(mine, qw, v);
-        else
-            first_stage<D, 1>(mine, qw, v);
-        // remaining stages but the last (h = 1 is part of the first)
-#pragma unroll
-        for (int h = 2; h < HL; h *= 2)
-#pragma unroll
-            for (int j = 0; j < 64; j += 2 * h)
-#pragma unroll
-                for (int i = j; i < j + h; i++) {
-                    const float a = v[i], b = v[i + h];
-                    v[i] = a + b;
-                    v[i + h] = a - b;
-                }
-        if constexpr (BITS == 2) {
-            // boundaries -b, 0, b are equally spaced: with T' = u / b the
-            // index #{boundaries < u} is 1 - clamp(floor(-T'), -2, 1); the
-            // words collect sum c 4^k and take 0x55..55 - that at the end
-            const float t2 = t * s.code.istep;
-#pragma unroll
-            for (int j = 0; j < 64; j += 2 * HL)
-#pragma unroll
-                for (int i = j; i < j + HL; i++) {
-                    const float bt = v[i + HL] * t2;
-                    float ta = fmaf(v[i], t2, bt);
-                    float tb = fmaf(v[i], t2, -bt);
-                    const int ka = 64 * pass + i, kb = ka + HL;
-                    if constexpr (S2) {
-                        ta = flip_by(ta, s2, ka);
-                        tb = flip_by(tb, s2, kb);
-                    }
-                    pack_c2(ta, tb, 2 * (ka & 15), 2 * (kb & 15), w[ka >> 4], w[kb >> 4]);
-                }
-        } else {
-            // last stage, scaled to T = 128 u, bucketized and packed, four
-            // outputs at a time; the table reads of the next four are issued
-            // before this four's compares (software pipeline)
-            constexpr int NB = 16;  // batches of four outputs per pass
-            auto first_of = [](int q) { return 2 * HL * ((2 * q) / HL) + (2 * q) % HL; };
-            float tt[2][4], bb[2][4];
-            uint32_t base[2][4];
-            auto issue = [&](int q, int slot) {
-                const int i = first_of(q);
-#pragma unroll
-                for (int h = 0; h < 2; h++) {
-                    const float bt = v[i + h + HL] * t;
-                    tt[slot][h] = fmaf(v[i + h], t, bt);
-                    tt[slot][h + 2] = fmaf(v[i + h], t, -bt);
-                }
-                if constexpr (S2) {
-                    const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
-#pragma unroll
-                    for (int r = 0; r < 4; r++)
-                        tt[slot][r] = flip_by(tt[slot][r], s2, 64 * pass + k[r]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const f32x2 e = lut_entry(tt[slot][r], key);
-                    bb[slot][r] = e.x;
-                    base[slot][r] = __float_as_uint(e.y);
-                }
-            };
-            issue(0, 0);
-#pragma unroll
-            for (int q = 0; q < NB; q++) {
-                if (q + 1 < NB)
-                    issue(q + 1, (q + 1) & 1);
-                __builtin_amdgcn_sched_barrier(0);
-                uint32_t idx[4];
-                bucket_add4(tt[q & 1], bb[q & 1], base[q & 1], idx);
-                const int i = first_of(q);
-                const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    put_bits(w, (64 * pass + k[r]) * BITS, BITS, idx[r]);
-            }
-        }
-        // keep the passes in order: this pass's words are complete here
-        // (otherwise the whole pass can be sunk below the next pass's loads)
-#pragma unroll
-        for (int q = 0; q < NWP; q++)
-            asm volatile("" ::"v"(w[NWP * pass + q]));
-    }
-    if constexpr (BITS == 2) {
-#pragma unroll
-        for (int q = 0; q < NW; q++)
-            w[q] = 0x55555555u - w[q];
-    }
-    if (lane < nvalid)
-        *as_global(s.norms + g0 + lane) = nstore;
-    wave_lds_fence();  // every lane is done with the staged rows
-    // packed rows, densely (the group's global layout), then whole-line stores
-    if constexpr (RB % 16 == 0) {
-#pragma unroll
-        for (int q = 0; q < NW / 4; q++)
-            *reinterpret_cast<u32x4 *>(stg + lane * RB + 16 * q) =
-                u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
-    } else {
-#pragma unroll
-        for (int q = 0; q < NW / 2; q++)
-            *reinterpret_cast<u32x2 *>(stg + lane * RB + 8 * q) = u32x2{w[2 * q], w[2 * q + 1]};
-    }
-    wave_lds_fence();
-    {
-        const int bytes = nvalid * RB;
-        __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + g0 * RB);
-#pragma unroll
-        for (int q = 0; q < (64 * RB + 1023) / 1024; q++) {
-            const int e = 64 * q + lane;  // 16-byte granule of the group's packed rows
-            if (16 * e + 16 <= bytes) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + 16 * e);
-                __builtin_nontemporal_store(x, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
-            } else if (16 * e < bytes) {  // an 8-byte tail (RB is a multiple of 8)
-                *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(dst + 16 * e) =
-                    *reinterpret_cast<const u32x2 *>(stg + 16 * e);
-            }
-        }
-    }
-    wave_lds_fence();
-}
-
-// Persistent loop over groups; with two sides (B1 > 0) each wave encodes
-// group g of the first side, then group g of the second, so that every wave
-// carries the same work whatever the bit widths.  The next group's loads are
-// issued before the current one is transformed.
-template <int D, int B0, int B1, bool S2>
-__device__ __forceinline__ void encode_lane_loop(const EncodeSide &s0, const EncodeSide &s1,
-                                                 const int64_t n_rows, const uint32_t key0,
-                                                 const uint32_t key1, uint8_t *stg,
-                                                 const uint32_t (&qw)[64], const SignBits &s2)
-{
-    constexpr int NCH = 64 * 2 * D / 1024;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64) * 64;
-    const uint8_t *src0 = static_cast<const uint8_t *>(s0.src);
-    const uint8_t *src1 = static_cast<const uint8_t *>(s1.src);
-    int64_t g0 = ((int64_t)blockIdx.x * (kBlock / 64) + wave) * 64;
-    u32x4 pf[NCH];
-    load_group<D>(src0, g0, n_rows, lane, pf);
-    for (; g0 < n_rows; g0 += stride) {
-        stage_group<D>(pf, stg, lane);
-        if constexpr (B1 > 0)
-            load_group<D>(src1, g0, n_rows, lane, pf);
-        else
-            load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-        encode_group<D, B0, S2>(s0, g0, n_rows, key0, stg, qw, s2);
-        if constexpr (B1 > 0) {
-            stage_group<D>(pf, stg, lane);
-            load_group<D>(src0, g0 + stride, n_rows, lane, pf);
-            encode_group<D, B1, S2>(s1, g0, n_rows, key1, stg, qw, s2);
-        }
-    }
-}
-
-template <int D, int B0, int B1, bool S2>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
-void encode_lane_kernel(EncodeLaneParams p)
-{
-    __shared__ float2 lut0[kLutBins];
-    __shared__ float2 lut1[kLutBins];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][64 * (2 * D + 16)];
-    if constexpr (B0 != 2)
-        build_lut(lut0, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
-    if constexpr (B1 > 2)
-        build_lut(lut1, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
-    __syncthreads();
-    encode_lane_loop<D, B0, B1, S2>(p.side[0], p.side[1], p.n_rows, lut_key(lut0),
-                                    lut_key(lut1), stage[threadIdx.x >> 6], p.qw, p.s2);
 }
 
 // ------------------------------------------- encode, bf16 rows of d = 256
@@ -838,7 +478,9 @@ __device__ __forceinline__ void e256_pass(const EncodeSide &s, const uint32_t ke
                 v[i + h] = a - b;
             }
     if constexpr (BITS == 2) {
-        // boundaries -b, 0, b equally spaced (see encode_group)
+        // boundaries -b, 0, b equally spaced: with T' = u / b the index is
+        // 1 - clamp(floor(-T'), -2, 1); the words collect sum c 4^k and
+        // take 0x55..55 - that at the end
         const float t2 = t * s.code.istep;
 #pragma unroll
         for (int i = 0; i < HL; i++) {
@@ -918,7 +560,7 @@ __device__ __forceinline__ void encode256_group(const EncodeSide &s, const int64
     if (__builtin_amdgcn_ballot_w64(rare) != 0) {
         if (wave == 0 && rare) {
             // rewrite the staged row as x * 2^-nexp (max |x| in [1/2, 1)),
-            // or zeros if it holds Inf or NaN (as encode_group does); the
+            // or zeros if it holds Inf or NaN (as mfma_block does); the
             // loops stay rolled: unrolled, their 32 row reads would all be
             // in registers at once and push the common path into spills
             float mx = 0.0f;
@@ -1067,6 +709,509 @@ void encode256_kernel(Encode256Params p)
             encode256_group<B1, S2>(p.side[1], g0, n_rows, key1, stage, sh, p.s2);
         }
     }
+}
+
+// ------------------------------------- encode, bf16 rows on the matrix cores
+// For d = 32 Q the Hadamard matrix (Sylvester order) factors over coordinate
+// k = 32 a + b (segment a, place b) as H_d = H_Q (x) H_32, so the rotation of
+// a row is
+//   Y_a = H_32 S_a x_a                 (each segment on its own)
+//   y_{32 a' + b'} = sum_a (H_Q)_{a' a} Y_a[b']
+// with S_a the segment's part of the sign diagonal.  Y_a is a product with a
+// fixed +-1 matrix: for 16 rows at a time, two 16 x 16 x 32 bf16 matrix-core
+// products per segment (exact products, fp32 sums), S_a folded into the
+// constant operand.  The Q-point transform across segments, scaled to
+// T = 128 u in its last stage, the table bucketize and the packing then run
+// on the vector ALUs: log2 Q add/sub stages per output instead of the whole
+// butterfly's log2 d.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, kq = l / 16):
+//   A (16 x 32): lane l holds A[l % 16][8 kq + j], j < 8
+//   B (32 x 16): lane l holds B[8 kq + j][l % 16]
+//   C (16 x 16): lane l holds C[4 kq + i][l % 16], i < 4
+// B is the block's rows: column n = l % 16 is row n of the block, and lane
+// l's eight values are coordinates 32 a + 8 kq .. + 7 of it (one 16-byte
+// load).  Row m of the constant operand in M-block mb stands for output
+// b' = 8 (m / 4) + 4 mb + m % 4, so that lane l ends with outputs
+// b' = 8 kq + j (j = 4 mb + i) of row n: eight consecutive coordinates of
+// every segment, a byte-aligned field of 8 BITS bits of the packed row.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+struct EncodeMfmaParams {
+    EncodeSide side[2];
+    int64_t n_rows;
+    SignBits8 s1;  // the sign diagonal: bit k set where s_k = -1
+    SignBits8 s2;  // second diagonal of the two-sided rotation
+};
+
+// The constant operand of segment a, M-block mb for this lane: bf16 pairs
+// (H_32)[b'][k] s_{32 a + k} for its row m = lane % 16 and k = 8 kq + j.
+template <int Q>
+__device__ __forceinline__ void mfma_rotation_operand(const SignBits8 &s1, int lane,
+                                                      u32x4 (&am)[Q][2])
+{
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < Q; a++)
+#pragma unroll
+        for (int mb = 0; mb < 2; mb++) {
+            const int bp = 8 * (m >> 2) + 4 * mb + (m & 3);
+            uint32_t w[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const int k0 = 8 * kq + 2 * jj, k1 = k0 + 1;
+                const uint32_t n0 = ((uint32_t)__popc(bp & k0) ^ (s1.w[a] >> k0)) & 1u;
+                const uint32_t n1 = ((uint32_t)__popc(bp & k1) ^ (s1.w[a] >> k1)) & 1u;
+                w[jj] = (0x3F80u | (n0 << 15)) | ((0x3F80u | (n1 << 15)) << 16);
+            }
+            am[a][mb] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+}
+
+// Ring of block inputs in LDS: the loads of a block go straight from memory
+// to its slot (no registers held while they are in flight).  Instruction i
+// of a block reads the block's rows RPI i .. RPI i + RPI - 1 (RPI =
+// 1024 / (2 D)), 1 KiB of memory in one piece, whole lines, and puts lane
+// l's 16 bytes at byte 16 l of the slot's region i; the regions are kSeg
+// bytes apart (1024 + 16), so that the B operands read back without bank
+// conflicts.  Lane l = 16 kq + Q r + s fetches row RPI i + r, the 16 bytes
+// 8 kq .. 8 kq + 7 of segment s.  The operand of segment a for lane (n, kq)
+// is then granule 16 kq + Q r + a of region i = n / RPI (r = n % RPI), at
+// 16-byte bank group i + Q r + a (mod 16): for each (a, kq) the 16 rows fall
+// in 16 different groups.  Rows past n_rows load row n_rows - 1 instead
+// (every block issues the same loads, so the wait counts below hold) and
+// read as zeros.
+constexpr int kSeg = 1024 + 16;
+
+template <int D>
+__device__ __forceinline__ void issue_block_lds(const uint8_t *src, int64_t r0, int64_t n_rows,
+                                                int lane, uint8_t *slot)
+{
+    constexpr int Q = D / 32, RPI = 512 / D;
+    // a uniform base (the block's first row, or the last row) and a 32-bit
+    // offset per lane
+    const int64_t b0 = r0 < n_rows ? r0 : n_rows - 1;
+    const uint64_t ga = (uint64_t)(uintptr_t)(src + b0 * (2 * D));
+    // uniform (scalar registers); the builtin returns int: both halves are
+    // widened as unsigned, or a low word at or above 2^31 would sign-extend
+    // into the high one
+    const uint32_t ga_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+    const uint32_t ga_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)ga);
+    const uint8_t *gb = (const uint8_t *)(uintptr_t)(((uint64_t)ga_hi << 32) | (uint64_t)ga_lo);
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(LdsBytes *)slot);
+    const int kq = lane >> 4, r = (lane & 15) / Q, sg = lane & (Q - 1);
+    const uint32_t lane_off = (uint32_t)(r * (2 * D) + 64 * sg + 16 * kq);
+    // Written out rather than through the compiler's builtin, whose tracking
+    // of loads into LDS makes every later LDS read wait for all of them: the
+    // waits for these are placed by hand (wait_vmcnt).  No register is
+    // written: the data goes to LDS at M0 + 16 lane (the instruction's offset
+    // field would move the LDS address as well, so it stays 0).
+    auto dma = [](uint32_t voff, const uint8_t *g, uint32_t m0) {
+        asm volatile("s_mov_b32 m0, %2\n\t"
+                     "global_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"(voff), "s"(g), "s"(m0)
+                     : "memory", "m0");
+    };
+    if (b0 + 16 <= n_rows) {  // uniform: a whole block, instruction i lane_off past row RPI i
+#pragma unroll
+        for (int i = 0; i < Q; i++)
+            dma(lane_off, gb + 1024 * i, base + kSeg * i);
+    } else {  // at the end: rows clamped to the last one
+        const int last = (int)(n_rows - 1 - b0);
+#pragma unroll
+        for (int i = 0; i < Q; i++)
+            dma((uint32_t)(min(RPI * i + r, last) * (2 * D) + 64 * sg + 16 * kq), gb,
+                base + kSeg * i);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void read_block_lds(const uint8_t *slot, int64_t r0, int64_t n_rows,
+                                               int lane, u32x4 (&x)[D / 32])
+{
+    constexpr int Q = D / 32, RPI = 512 / D;
+    const int n = lane & 15, kq = lane >> 4;
+    LdsBytes *rp = (LdsBytes *)slot + kSeg * (n / RPI) + 16 * (16 * kq + Q * (n % RPI));
+#pragma unroll
+    for (int a = 0; a < Q; a++)
+        x[a] = *reinterpret_cast<LdsU32x4 *>(rp + 16 * a);
+    if (r0 + 16 > n_rows) {  // uniform: a block at the end
+        const bool ok = r0 + n < n_rows;
+#pragma unroll
+        for (int a = 0; a < Q; a++)
+            x[a] = ok ? x[a] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// op over the four lanes holding parts of one row (lanes n, n + 16, n + 32,
+// n + 48): the swaps of 16-lane rows and of 32-lane halves pair each lane
+// with its partners in registers, and both lanes of a pair combine the same
+// two values in the same order, so the four lanes end with identical bits.
+template <typename F>
+__device__ __forceinline__ float row_across_kq(float v, F op)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const uint32_t w = __float_as_uint(v);
+    const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return op(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Sum of squares of row lane % 16 of a block: each of the four lanes holding
+// a part of it adds its 8 Q values, then the parts are exchanged, so the
+// four lanes end with the same value (products exact, fp32 sums)
+template <int Q>
+__device__ __forceinline__ float mfma_block_sumsq(const u32x4 (&x)[Q])
+{
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int a = 0; a < Q; a++) {
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x[a].x), as_bf16x2(x[a].x), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x[a].y), as_bf16x2(x[a].y), s1, false);
+        s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x[a].z), as_bf16x2(x[a].z), s0, false);
+        s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x[a].w), as_bf16x2(x[a].w), s1, false);
+    }
+    return row_across_kq(s0 + s1, [](float a, float b) { return a + b; });
+}
+
+// the block's 2 Q products, M-block by M-block (the first M-block's results,
+// which the transform takes first, are ready first)
+template <int Q>
+__device__ __forceinline__ void mfma_block_products(const u32x4 (&am)[Q][2], const u32x4 (&x)[Q],
+                                                    f32x4 (&acc)[Q][2])
+{
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int a = 0; a < Q; a++)
+            acc[a][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, am[a][mb]), __builtin_bit_cast(bf16x8_t, x[a]),
+                f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+}
+
+// Where byte o of row n of a block's packed rows sits in the wave's LDS stage
+// (16 rows of RB bytes): its 16-byte granule is exchanged with granule
+// c ^ f(n), so that the lanes of one store (rows n, four lanes each) fall in
+// different banks where RB / 4 words per row divide the 64 banks; the
+// readback undoes the exchange.
+template <int RB>
+constexpr bool stage_swizzled()
+{
+    return RB % 16 == 0 && ((RB / 4) & (RB / 4 - 1)) == 0 && RB / 4 <= 64;
+}
+
+template <int RB>
+__device__ __forceinline__ int stage_offset(int n, int o)
+{
+    if constexpr (stage_swizzled<RB>()) {
+        constexpr int G = RB / 16, P = 256 / RB;  // granules per row; rows per bank cycle
+        const int f = (n / P) % G;
+        return n * RB + (((o >> 4) ^ f) << 4) + (o & 15);
+    } else {
+        return n * RB + o;
+    }
+}
+
+// where granule e of the block's dense packed rows sits in the stage
+template <int RB>
+__device__ __forceinline__ int stage_granule(int e)
+{
+    if constexpr (stage_swizzled<RB>())
+        return stage_offset<RB>(e / (RB / 16), 16 * (e % (RB / 16)));
+    else
+        return 16 * e;
+}
+
+// store instructions of a whole block's packed rows (RB granules of 16 bytes)
+template <int RB>
+constexpr int kMfmaStores = (RB + 63) / 64;
+
+// Encode one block (16 rows starting at r0) of one side: the rows arrive in
+// x in the B layout; packed rows and norms go to memory through the wave's
+// LDS stage.
+template <int D, int BITS, bool S2>
+__device__ __forceinline__ void mfma_block(u32x4 (&x)[D / 32], const u32x4 (&am)[D / 32][2],
+                                           const EncodeSide &s, uint32_t key, const SignBits8 &s2,
+                                           int64_t r0, int64_t n_rows, uint8_t *stg, int lane)
+{
+    constexpr int Q = D / 32, RB = D * BITS / 8, H = Q / 2;
+    const int n = lane & 15, kq = lane >> 4;
+    // the products first: the sum of squares and the scale are worked out
+    // while the matrix cores run
+    f32x4 acc[Q][2];
+    mfma_block_products<Q>(am, x, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    float ss = mfma_block_sumsq<Q>(x);
+    int nexp = 0;
+    bool bad = false;
+    const bool rare = !(ss >= 0x1p-100f && ss <= 0x1p100f);
+    if (__builtin_amdgcn_ballot_w64(rare) != 0) {
+        // rare (a wave-uniform branch): rows out of range are rewritten as
+        // x * 2^-nexp (max |x| in [1/2, 1)), or zeros if they hold an Inf or
+        // a NaN, and the block's products are taken again
+        float mx = 0.0f;
+#pragma unroll
+        for (int a = 0; a < Q; a++) {
+            const uint32_t xw[4] = {x[a].x, x[a].y, x[a].z, x[a].w};
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+                mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
+        }
+        mx = row_across_kq(mx, [](float a, float b) { return fmaxf(a, b); });
+        const float ss0 = ss;  // the fast path's sum
+        bad = rare && (!(mx <= FLT_MAX) || ss0 != ss0);  // an Inf or a NaN (the max skips NaN)
+        if (rare && !bad && mx > 0.0f)
+            (void)frexpf(mx, &nexp);
+        if (rare) {
+#pragma unroll
+            for (int a = 0; a < Q; a++) {
+                uint32_t xw[4] = {x[a].x, x[a].y, x[a].z, x[a].w};
+#pragma unroll
+                for (int c = 0; c < 4; c++) {
+                    // exact for normal results; parts below 2^-126 of the
+                    // largest magnitude may round, far under fp32 precision
+                    const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
+                    const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
+                    xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
+                }
+                x[a] = u32x4{xw[0], xw[1], xw[2], xw[3]};
+            }
+        }
+        ss = mfma_block_sumsq<Q>(x);
+        if (bad)
+            ss = ss0 + mx;  // stored as the norm: not finite
+        mfma_block_products<Q>(am, x, acc);
+    }
+    // the hardware reciprocal square root and square root (about 1 ulp):
+    // every block takes them, four lanes per row, so the correctly rounded
+    // expansions would cost a fifth of the block; their error stays two
+    // orders under the tolerance of u and of the norm
+    const float t = (ss > 0.0f && !bad) ? 128.0f * __builtin_amdgcn_rsqf((float)D * ss) : 0.0f;
+    const float nrm = bad ? ss : ldexpf(__builtin_amdgcn_sqrtf(ss), nexp);
+    // the Q-point transform across segments for each of the lane's eight
+    // places j = 4 mb + i; the last stage carries the scale
+    const float ts = BITS == 2 ? t * s.code.istep : t;
+    float T[Q][8];
+#pragma unroll
+    for (int mb = 0; mb < 2; mb++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float v[Q];
+#pragma unroll
+            for (int a = 0; a < Q; a++)
+                v[a] = acc[a][mb][i];
+#pragma unroll
+            for (int h = 1; h < H; h *= 2)
+#pragma unroll
+                for (int j = 0; j < Q; j += 2 * h)
+#pragma unroll
+                    for (int a = j; a < j + h; a++) {
+                        const float u = v[a], w = v[a + h];
+                        v[a] = u + w;
+                        v[a + h] = u - w;
+                    }
+#pragma unroll
+            for (int a = 0; a < H; a++) {
+                const float bt = v[a + H] * ts;
+                T[a][4 * mb + i] = fmaf(v[a], ts, bt);
+                T[a + H][4 * mb + i] = fmaf(v[a], ts, -bt);
+            }
+        }
+#pragma unroll
+    for (int a = 0; a < Q; a++) {
+        if constexpr (S2) {
+            // the second diagonal's signs of coordinates 32 a + 8 kq + j
+            const uint32_t sb = s2.w[a] >> (8 * kq);
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                T[a][j] = __uint_as_float(__float_as_uint(T[a][j]) ^ ((sb << (31 - j)) & 0x80000000u));
+        }
+        uint32_t w;
+        if constexpr (BITS == 2) {
+            // boundaries -b, 0, b equally spaced (T scaled by 1 / b): the
+            // field collects sum c 4^j with c = clamp(floor(-T), -2, 1) and
+            // takes 0x5555 - that
+            uint32_t we = 0u, wo = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; j += 2)
+                pack_c2(T[a][j], T[a][j + 1], 2 * j, 2 * j + 2, we, wo);
+            w = 0x5555u - (we + wo);
+        } else {
+            uint32_t idx[8];
+#pragma unroll
+            for (int h = 0; h < 8; h += 4) {
+                float tt[4], bb[4];
+                uint32_t base[4], id4[4];
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    tt[r] = T[a][h + r];
+                    const f32x2 e = lut_entry(tt[r], key);
+                    bb[r] = e.x;
+                    base[r] = __float_as_uint(e.y);
+                }
+                bucket_add4(tt, bb, base, id4);
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    idx[h + r] = id4[r];
+            }
+            w = idx[0];
+#pragma unroll
+            for (int j = 1; j < 8; j++)
+                w = lshl_or(idx[j], BITS * j, w);
+        }
+        // the field: 8 BITS bits at byte BITS (4 a + kq) of row n
+        if constexpr (BITS == 4) {
+            *reinterpret_cast<uint32_t *>(stg + stage_offset<RB>(n, 16 * a + 4 * kq)) = w;
+        } else if constexpr (BITS == 2) {
+            *reinterpret_cast<uint16_t *>(stg + stage_offset<RB>(n, 8 * a + 2 * kq)) = (uint16_t)w;
+        } else {
+            // three bytes at 12 a + 3 kq: a halfword and a byte, the
+            // halfword at the even address
+            const bool odd = (kq & 1) != 0;
+            uint8_t *f = stg + stage_offset<RB>(n, 12 * a + 3 * kq);
+            *reinterpret_cast<uint16_t *>(f + (odd ? 1 : 0)) = (uint16_t)(odd ? w >> 8 : w);
+            f[odd ? 0 : 2] = (uint8_t)(odd ? w : w >> 16);
+        }
+    }
+    // the block's packed rows (dense, as in memory: whole lines where the
+    // block is whole) and norms
+    const int nvalid = (int)min<int64_t>(16, n_rows - r0);
+    wave_lds_fence();
+    if (nvalid == 16) {
+        // a whole block: every lane stores, without branches; the four
+        // lanes of a row store the same norm, and lanes past the block's RB
+        // granules repeat granules
+        *as_global(s.norms + r0 + n) = nrm;
+        __attribute__((address_space(1))) u32x4 *dst =
+            reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(as_global(s.packed + r0 * RB));
+#pragma unroll
+        for (int q = 0; q < kMfmaStores<RB>; q++) {
+            const int e = (64 * q + lane) % RB;  // granule (16 rows of RB bytes: RB granules)
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + stage_granule<RB>(e));
+            __builtin_nontemporal_store(v, dst + e);
+        }
+    } else {
+        if (kq == 0 && n < nvalid)
+            *as_global(s.norms + r0 + n) = nrm;
+        const int bytes = nvalid * RB;
+        __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + r0 * RB);
+#pragma unroll
+        for (int q = 0; q < (16 * RB + 1023) / 1024; q++) {
+            const int e = 64 * q + lane;  // 16-byte granule of the block's packed rows
+            if (16 * e + 16 <= bytes) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + stage_granule<RB>(e));
+                __builtin_nontemporal_store(v, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
+            } else if (16 * e < bytes) {  // an 8-byte tail (RB is a multiple of 8, not of 16)
+                *reinterpret_cast<__attribute__((address_space(1))) u32x2 *>(dst + 16 * e) =
+                    *reinterpret_cast<const u32x2 *>(stg + 16 * e);
+            }
+        }
+    }
+    wave_lds_fence();
+}
+
+// Waits on the vector-memory count or the LDS count alone (memory clobbers: no memory access moves across them)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+}
+
+template <int D>
+constexpr int ring_slots()
+{
+    return D == 64 ? 3 : 2;
+}
+
+// One group of 64 rows of one side per wave: its four blocks pass through
+// the wave's ring of R slots, a slot refilled with the group's next block as
+// soon as it has been read into registers.
+template <int D, int BITS, bool S2>
+__device__ __forceinline__ void mfma_group(const EncodeSide &s, int64_t g0, int64_t n_rows,
+                                           uint32_t key, const SignBits8 &s2,
+                                           const u32x4 (&am)[D / 32][2], uint8_t *slots,
+                                           uint8_t *stg, int lane)
+{
+    constexpr int Q = D / 32, R = ring_slots<D>(), SLOT = Q * kSeg;
+    const uint8_t *src = static_cast<const uint8_t *>(s.src);
+#pragma unroll
+    for (int u = 0; u < R; u++)
+        issue_block_lds<D>(src, g0 + 16 * u, n_rows, lane, slots + u * SLOT);
+#pragma unroll 1
+    for (int u = 0; u < 4; u++) {
+        const int64_t r0 = g0 + 16 * u;
+        uint8_t *slot = slots + (u % R) * SLOT;
+        // this block's loads are done once at most those issued after them
+        // are outstanding: the group's next R - 1 blocks (loads complete in
+        // order; stores are not ordered with them and are left out, which
+        // can only wait longer).  Near the group's end fewer follow: all.
+        if (u + R <= 4)
+            wait_vmcnt<(R - 1) * Q>();
+        else
+            wait_vmcnt<0>();
+        u32x4 x[Q];
+        read_block_lds<D>(slot, r0, n_rows, lane, x);
+        if (u + R < 4) {
+            wait_lgkmcnt0();  // the slot is read before it is refilled
+            issue_block_lds<D>(src, g0 + 16 * (u + R), n_rows, lane, slot);
+        }
+        if (r0 < n_rows)
+            mfma_block<D, BITS, S2>(x, am, s, key, s2, r0, n_rows, stg, lane);
+    }
+}
+
+// One launch, one group of 64 rows per wave, every group of the first side
+// before any of the second (workgroups [0, nb) take the first side, [nb, 2 nb)
+// the second): the launch walks memory as one compact window, side by side.
+// Measured on the bulk workload, a streaming kernel of this traffic with no
+// arithmetic reaches 76% of HBM in this order and about 70% when each wave
+// loops over many groups or alternates the sides.
+template <int D, int B0, int B1, bool S2>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(S2 && D == 128 ? 3 : 4)))
+void encode_mfma_kernel(EncodeMfmaParams p)
+{
+    constexpr int Q = D / 32, R = ring_slots<D>();
+    constexpr int RBM = D * B0 / 8;  // B0 >= B1
+    constexpr int SLOT = Q * kSeg;   // Q regions of 1 KiB, padded
+    __shared__ float2 lut[(B0 > 2 || B1 > 2) ? kLutBins : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kBlock / 64][R * SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][16 * RBM];
+    const int64_t n_rows = p.n_rows;
+    const int64_t nb = (n_rows + 255) / 256;  // workgroups per side
+    const bool second = B1 > 0 && (int64_t)blockIdx.x >= nb;
+    if (second) {
+        if constexpr (B1 > 2)
+            build_lut(lut, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
+    } else {
+        if constexpr (B0 > 2)
+            build_lut(lut, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t g0 = (((int64_t)blockIdx.x - (second ? nb : 0)) * (kBlock / 64) + wave) * 64;
+    if (g0 >= n_rows)
+        return;
+    u32x4 am[Q][2];
+    mfma_rotation_operand<Q>(p.s1, lane, am);
+    const uint32_t key = lut_key(lut);
+    if constexpr (B1 > 0) {
+        if (second) {
+            mfma_group<D, (B1 > 0 ? B1 : B0), S2>(p.side[1], g0, n_rows, key, p.s2, am, ring[wave],
+                                                  stage[wave], lane);
+            return;
+        }
+    }
+    mfma_group<D, B0, S2>(p.side[0], g0, n_rows, key, p.s2, am, ring[wave], stage[wave], lane);
 }
 
 // ----------------------------------------------------------------- append
@@ -1472,19 +1617,6 @@ int resident_blocks(K kern, int block = kBlock)
     return n;
 }
 
-template <int D, int B0, int B1, bool S2>
-void launch_encode_lane_k(const EncodeLaneParams &q, hipStream_t st)
-{
-    auto kern = encode_lane_kernel<D, B0, B1, S2>;
-    const int64_t groups = (q.n_rows + 63) / 64;  // 64 rows per wave
-    const int64_t need = (groups + kBlock / 64 - 1) / (kBlock / 64);
-    // the resident workgroups, each looping over groups
-    int64_t cap = (int64_t)device_cus() * resident_blocks(kern);
-    if (cap < 1)
-        cap = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(need < cap ? need : cap)), dim3(kBlock), 0, st, q);
-}
-
 // sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
 template <int B0, int B1, bool S2>
 void launch_encode256_k(const Encode256Params &q, hipStream_t st)
@@ -1515,19 +1647,30 @@ void launch_encode256(const Encode256Params &q, int b0, int b1, hipStream_t st)
     }
 }
 
+template <int D, int B0, int B1, bool S2>
+void launch_encode_mfma_k(const EncodeMfmaParams &q, hipStream_t st)
+{
+    auto kern = encode_mfma_kernel<D, B0, B1, S2>;
+    // 256 rows per workgroup and side, every group of the first side first
+    const int64_t per_side = (q.n_rows + 255) / 256;
+    const int64_t blocks = per_side * (B1 > 0 ? 2 : 1);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), 0, st, q);
+}
+
+// sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
 template <int D, bool S2>
-void launch_encode_lane_d(const EncodeLaneParams &q, int b0, int b1, hipStream_t st)
+void launch_encode_mfma_d(const EncodeMfmaParams &q, int b0, int b1, hipStream_t st)
 {
     switch (b0 * 10 + b1) {
-    case 40: launch_encode_lane_k<D, 4, 0, S2>(q, st); break;
-    case 30: launch_encode_lane_k<D, 3, 0, S2>(q, st); break;
-    case 20: launch_encode_lane_k<D, 2, 0, S2>(q, st); break;
-    case 44: launch_encode_lane_k<D, 4, 4, S2>(q, st); break;
-    case 43: launch_encode_lane_k<D, 4, 3, S2>(q, st); break;
-    case 42: launch_encode_lane_k<D, 4, 2, S2>(q, st); break;
-    case 33: launch_encode_lane_k<D, 3, 3, S2>(q, st); break;
-    case 32: launch_encode_lane_k<D, 3, 2, S2>(q, st); break;
-    default: launch_encode_lane_k<D, 2, 2, S2>(q, st); break;
+    case 40: launch_encode_mfma_k<D, 4, 0, S2>(q, st); break;
+    case 30: launch_encode_mfma_k<D, 3, 0, S2>(q, st); break;
+    case 20: launch_encode_mfma_k<D, 2, 0, S2>(q, st); break;
+    case 44: launch_encode_mfma_k<D, 4, 4, S2>(q, st); break;
+    case 43: launch_encode_mfma_k<D, 4, 3, S2>(q, st); break;
+    case 42: launch_encode_mfma_k<D, 4, 2, S2>(q, st); break;
+    case 33: launch_encode_mfma_k<D, 3, 3, S2>(q, st); break;
+    case 32: launch_encode_mfma_k<D, 3, 2, S2>(q, st); break;
+    default: launch_encode_mfma_k<D, 2, 2, S2>(q, st); break;
     }
 }
 
@@ -1705,7 +1848,7 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
     p.d_in = d;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (dtype == TQ_BF16 && d <= 128 && d == D) {
-        EncodeLaneParams q;
+        EncodeMfmaParams q;
         q.side[0] = p.side[0];
         q.side[1] = p.side[1];
         if (sides == 2 && q.side[1].code.bits > q.side[0].code.bits) {
@@ -1716,27 +1859,17 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         if (sides == 1)
             q.side[1] = q.side[0];  // unused
         q.n_rows = n_rows;
-        // the sign diagonal as bf16 (+-1, +-1) pairs of the first two stages
-        uint32_t sb[4] = {0u, 0u, 0u, 0u};
-        for (int w = 0; w < 4; w++)
-            q.s2.w[w] = 0u;
-        tq::sign_words(d, seed, sb);
+        for (int w = 0; w < 8; w++)
+            q.s1.w[w] = q.s2.w[w] = 0u;
+        tq::sign_words(d, seed, q.s1.w);
         tq::sign_words2(d, seed, flags, q.s2.w);
-        auto neg = [&](int k) -> uint32_t { return (sb[k >> 5] >> (k & 31)) & 1u; };
-        auto pairw = [&](int k) -> uint32_t {
-            return (0x3F80u | (neg(k) << 15)) | ((0x3F80u | (neg(k + 1) << 15)) << 16);
-        };
-        for (int j = 0; j < 32; j++) {
-            q.qw[j] = 2 * j < d / 2 ? pairw(2 * j) : 0u;
-            q.qw[32 + j] = 2 * j < d / 2 ? pairw(2 * j + d / 2) : 0u;
-        }
         const bool two = (flags & TQ_FLAG_TWO_SIDED) != 0;
         if (d == 64)
-            two ? launch_encode_lane_d<64, true>(q, b0, b1, st)
-                : launch_encode_lane_d<64, false>(q, b0, b1, st);
+            two ? launch_encode_mfma_d<64, true>(q, b0, b1, st)
+                : launch_encode_mfma_d<64, false>(q, b0, b1, st);
         else
-            two ? launch_encode_lane_d<128, true>(q, b0, b1, st)
-                : launch_encode_lane_d<128, false>(q, b0, b1, st);
+            two ? launch_encode_mfma_d<128, true>(q, b0, b1, st)
+                : launch_encode_mfma_d<128, false>(q, b0, b1, st);
         return launch_status(fn);
     }
     if (dtype == TQ_BF16 && d == 256) {

@@ -390,68 +390,6 @@ __device__ __forceinline__ void sign_masks_f32(uint32_t mask, uint32_t (&xm)[kCP
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Packed-bf16 dot products in their three-operand form (the compiler only
-// emits the two-operand form, whose accumulator doubles as destination and
-// needs a copy or a zeroing move first), against sign-pair words in scalar
-// registers.  For the first two Hadamard stages of an encode:
-//   e0 = A.w0, e1 = A.(w0 with its high half negated),
-//   y0 = B.(sigma w2) + e0, y1 = B.(sigma w2, high half negated) + e1,
-// each product exact and each sum rounded once to fp32; the negated forms
-// are the instruction's source-negation modifiers (neg_hi: the high half,
-// neg_lo + neg_hi: both).  A result of this instruction needs three wait
-// states before a different vector instruction reads it; the compiler cannot
-// see into the asm, so the block ends with them (a chained read as the
-// accumulator of the same instruction needs none).  Two such steps in one
-// block (one trailing wait for both): (A, B, w0, w2) -> (y0, y1) and
-// (A', B', w0', w2') -> (z0, z1).
-template <int NEG>  // 0: sigma = +1, 1: sigma = -1
-__device__ __forceinline__ void dot2_pair2_s(uint32_t A, uint32_t B, uint32_t w0, uint32_t w2,
-                                             uint32_t A2, uint32_t B2, uint32_t w0b, uint32_t w2b,
-                                             float &y0, float &y1, float &z0, float &z1)
-{
-    float e0, e1, f0, f1;
-    if constexpr (NEG == 0)
-        asm("v_dot2_f32_bf16 %0, %8, %12, 0\n\t"
-            "v_dot2_f32_bf16 %1, %8, %12, 0 neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %2, %10, %14, 0\n\t"
-            "v_dot2_f32_bf16 %3, %10, %14, 0 neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %4, %9, %13, %0\n\t"
-            "v_dot2_f32_bf16 %5, %9, %13, %1 neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %6, %11, %15, %2\n\t"
-            "v_dot2_f32_bf16 %7, %11, %15, %3 neg_hi:[0,1,0]\n\t"
-            "s_nop 2"
-            : "=&v"(e0), "=&v"(e1), "=&v"(f0), "=&v"(f1), "=&v"(y0), "=&v"(y1), "=&v"(z0), "=v"(z1)
-            : "v"(A), "v"(B), "v"(A2), "v"(B2), "s"(w0), "s"(w2), "s"(w0b), "s"(w2b));
-    else
-        asm("v_dot2_f32_bf16 %0, %8, %12, 0\n\t"
-            "v_dot2_f32_bf16 %1, %8, %12, 0 neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %2, %10, %14, 0\n\t"
-            "v_dot2_f32_bf16 %3, %10, %14, 0 neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %4, %9, %13, %0 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %5, %9, %13, %1 neg_lo:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %6, %11, %15, %2 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"
-            "v_dot2_f32_bf16 %7, %11, %15, %3 neg_lo:[0,1,0]\n\t"
-            "s_nop 2"
-            : "=&v"(e0), "=&v"(e1), "=&v"(f0), "=&v"(f1), "=&v"(y0), "=&v"(y1), "=&v"(z0), "=v"(z1)
-            : "v"(A), "v"(B), "v"(A2), "v"(B2), "s"(w0), "s"(w2), "s"(w0b), "s"(w2b));
-}
-
-// Both signs of sigma for one pair (d = 64: a single pass)
-__device__ __forceinline__ void dot2_quad_s(uint32_t A, uint32_t B, uint32_t w0, uint32_t w2,
-                                            float &y0, float &y1, float &y2, float &y3)
-{
-    float e0, e1;
-    asm("v_dot2_f32_bf16 %0, %6, %8, 0\n\t"
-        "v_dot2_f32_bf16 %1, %6, %8, 0 neg_hi:[0,1,0]\n\t"
-        "v_dot2_f32_bf16 %2, %7, %9, %0\n\t"
-        "v_dot2_f32_bf16 %3, %7, %9, %1 neg_hi:[0,1,0]\n\t"
-        "v_dot2_f32_bf16 %4, %7, %9, %0 neg_lo:[0,1,0] neg_hi:[0,1,0]\n\t"
-        "v_dot2_f32_bf16 %5, %7, %9, %1 neg_lo:[0,1,0]\n\t"
-        "s_nop 2"
-        : "=&v"(e0), "=&v"(e1), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=v"(y3)
-        : "v"(A), "v"(B), "s"(w0), "s"(w2));
-}
-
 // idx_k = base_k + (t_k > b_k) for four outputs.  Each compare writes its own
 // scalar register pair, so no compare waits for the previous add (the
 // compiler puts every compare in VCC, and a compare's result must be two wait

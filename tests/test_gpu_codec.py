@@ -81,6 +81,35 @@ def test_encode_decode_all_bits_ragged(tq, orc, d, dtype):
     tally.check()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_encode_rows_at_high_low_word_addresses(tq, orc, d):
+    """bf16 rows whose device addresses have the low 32-bit word at or above
+    2^31 (a view into a buffer past such a boundary): the encode builds its
+    load addresses from 32-bit halves, which must widen without sign."""
+    n = 300
+    nbytes = n * d * 2
+    buf = torch.empty((1 << 32) + nbytes + 4096, dtype=torch.uint8, device="cuda")
+    base = buf.data_ptr()
+    # first 16-byte aligned offset whose address has the low word >= 2^31
+    lo = base & 0xFFFFFFFF
+    off = 0 if lo >= (1 << 31) else (1 << 31) - lo
+    off = (off + 15) // 16 * 16
+    assert ((base + off) & 0xFFFFFFFF) >= (1 << 31) and off + nbytes <= buf.numel()
+    k = buf[off:off + nbytes].view(torch.bfloat16).view(n, d)
+    k.copy_(kvgen.normal((n, d), 41 + d, "cuda", torch.bfloat16))
+    v = kvgen.normal((n, d), 42 + d, "cuda", torch.bfloat16)
+    tally = BandTally()
+    kp, kn, vp, vn = tq.tq_encode(k, v, 4, 2, SEED)
+    torch.cuda.synchronize()
+    for x, bits, pk, nm in ((k, 4, kp, kn), (v, 2, vp, vn)):
+        op, on, u = orc.encode(_np(x).astype(np.float32), d, bits, SEED, want_u=True)
+        _, bnd = orc.codebook_float(d, bits)
+        check_norms(nm.cpu().numpy(), on)
+        check_indices(pk.cpu().numpy(), op, u, d, bits, bnd, tally=tally)
+    tally.check()
+    del k, buf
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_rotate_forward_inverse(tq, orc, d):
     x = kvgen.normal((333, d), 5, "cuda")
