@@ -654,23 +654,28 @@ template <int B0, int B1, bool S2>
 __global__ __launch_bounds__(kE256Block) __attribute__((amdgpu_waves_per_eu(2)))
 void encode256_kernel(Encode256Params p)
 {
-    __shared__ float2 lut0[kLutBins];
-    __shared__ float2 lut1[kLutBins];
+    __shared__ float2 lut[(B0 > 2 || B1 > 2) ? kLutBins : 1];
     __shared__ __attribute__((aligned(16))) uint8_t stage[64 * kE256Stride];
     __shared__ E256Shared sh;
-    if constexpr (B0 != 2)
-        build_lut(lut0, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
-    if constexpr (B1 > 2)
-        build_lut(lut1, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
-    __syncthreads();
-    const uint32_t key0 = lut_key(lut0), key1 = lut_key(lut1);
+    // one group of 64 rows of one side per workgroup, every group of the
+    // first side before any of the second: the launch walks memory as one
+    // compact window
+    const int64_t n_rows = p.n_rows;
+    const int64_t nb = (n_rows + 63) / 64;  // groups per side
+    const bool second = B1 > 0 && (int64_t)blockIdx.x >= nb;
+    const int64_t g0 = ((int64_t)blockIdx.x - (second ? nb : 0)) * 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-    const int64_t n_rows = p.n_rows;
-    const int64_t stride = (int64_t)gridDim.x * 64;
-    const uint8_t *src0 = static_cast<const uint8_t *>(p.side[0].src);
-    const uint8_t *src1 = static_cast<const uint8_t *>(p.side[1].src);
-    int64_t g0 = (int64_t)blockIdx.x * 64;
+    const uint8_t *src = static_cast<const uint8_t *>(second ? p.side[1].src : p.side[0].src);
+    u32x4 pf[8];
+    load_quarter_group(src, g0, n_rows, wave, lane, pf);
+    if (second) {
+        if constexpr (B1 > 2)
+            build_lut(lut, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
+    } else {
+        if constexpr (B0 > 2)
+            build_lut(lut, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
+    }
     // the sign bits of this lane's staging columns 8 (lane % 32) .. + 7, as
     // xor masks of the bf16 pairs
     u32x4 flip;
@@ -683,32 +688,16 @@ void encode256_kernel(Encode256Params p)
             f[j] = (((sw >> (2 * j)) & 1u) << 15) | (((sw >> (2 * j + 1)) & 1u) << 31);
         flip = u32x4{f[0], f[1], f[2], f[3]};
     }
-    u32x4 pf[8];
-    load_quarter_group(src0, g0, n_rows, wave, lane, pf);
-#pragma unroll 1
-    for (; g0 < n_rows; g0 += stride) {
-        // the rows to prefetch, as values the loop cannot strength-reduce
-        // (per-chunk address induction variables would take registers);
-        // group indices fit 32 bits (2^31 groups of 64 bf16 rows of 512
-        // bytes would be 64 TiB)
-        int gc = __builtin_amdgcn_readfirstlane((int)(g0 >> 6));
-        int gn = __builtin_amdgcn_readfirstlane((int)((g0 + stride) >> 6));
-        asm volatile("" : "+s"(gc), "+s"(gn));
-        const int64_t gcur = (int64_t)gc * 64, gnext = (int64_t)gn * 64;
-        stage_quarter_group(pf, stage, wave, lane, flip);
-        __syncthreads();
-        if constexpr (B1 > 0)
-            load_quarter_group(src1, gcur, n_rows, wave, lane, pf);
-        else
-            load_quarter_group(src0, gnext, n_rows, wave, lane, pf);
-        encode256_group<B0, S2>(p.side[0], g0, n_rows, key0, stage, sh, p.s2);
-        if constexpr (B1 > 0) {
-            stage_quarter_group(pf, stage, wave, lane, flip);
-            __syncthreads();
-            load_quarter_group(src0, gnext, n_rows, wave, lane, pf);
-            encode256_group<B1, S2>(p.side[1], g0, n_rows, key1, stage, sh, p.s2);
+    stage_quarter_group(pf, stage, wave, lane, flip);
+    __syncthreads();
+    const uint32_t key = lut_key(lut);
+    if constexpr (B1 > 0) {
+        if (second) {
+            encode256_group<(B1 > 0 ? B1 : B0), S2>(p.side[1], g0, n_rows, key, stage, sh, p.s2);
+            return;
         }
     }
+    encode256_group<B0, S2>(p.side[0], g0, n_rows, key, stage, sh, p.s2);
 }
 
 // ------------------------------------- encode, bf16 rows on the matrix cores
@@ -1622,12 +1611,10 @@ template <int B0, int B1, bool S2>
 void launch_encode256_k(const Encode256Params &q, hipStream_t st)
 {
     auto kern = encode256_kernel<B0, B1, S2>;
-    const int64_t groups = (q.n_rows + 63) / 64;  // 64 rows per workgroup
-    int64_t cap = (int64_t)device_cus() * resident_blocks(kern, kE256Block);
-    if (cap < 1)
-        cap = 1;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(groups < cap ? groups : cap)), dim3(kE256Block), 0,
-                       st, q);
+    // one group of 64 rows per workgroup and side, the first side's first
+    const int64_t groups = (q.n_rows + 63) / 64;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(groups * (B1 > 0 ? 2 : 1))), dim3(kE256Block), 0, st,
+                       q);
 }
 
 // sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
