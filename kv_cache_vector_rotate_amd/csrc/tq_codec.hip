@@ -282,423 +282,13 @@ __device__ __forceinline__ f32x2 lut_entry(float t, uint32_t key)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Sum of squares of NB bytes of a staged bf16 row (products exact, fp32 sums).
-template <int NB>
-__device__ __forceinline__ float row_sumsq(const uint8_t *row)
-{
-    float ss0 = 0.0f, ss1 = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NB / 16; m++) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(row + 16 * m);
-        const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int c = 0; c < 4; c += 2) {
-            ss0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xw[c]), as_bf16x2(xw[c]), ss0, false);
-            ss1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xw[c + 1]), as_bf16x2(xw[c + 1]), ss1, false);
-        }
-    }
-    return ss0 + ss1;
-}
-
-// ------------------------------------------- encode, bf16 rows of d = 256
-// Four waves per group of 64 rows.  One row per lane, as above, but the 256
-// outputs are split between the four waves of a workgroup: wave w computes
-// outputs 64 w .. 64 w + 63 (one pass) from one LDS stage of the group that
-// all four load and read.  Per wave this keeps the registers holding the next
-// group's loads at a quarter of a group, and every sign in the first stages
-// is wave-uniform.
-//
-// First stages: the rows are staged with the sign diagonal applied (an xor
-// of the bf16 sign bits on the way into LDS: z = s x, exact).  The stages
-// across 128 (a = w >> 1) and across 64 (b = w & 1) and the stage h = 1 then
-// give, for output 64 w + 2c + e,
-//   u = A.(1, (-1)^e) + (-1)^b B.(..) + (-1)^a C.(..) + (-1)^(a+b) E.(..)
-// with A, B, C, E the bf16 pairs (z_j, z_j+1) of columns j = 2c, 2c + 64,
-// 2c + 128, 2c + 192: four bf16 dot products per output (exact products,
-// fp32 sums) against the one word (1, 1), every sign being one of the
-// instruction's negation modifiers.  The stages h = 2 .. 32 follow in fp32
-// on the wave's 64 outputs.
-
+// ------------------------------------------- encode, shared types
 struct SignBits8 {
     uint32_t w[8];  // bit k of w[k / 32] set: coordinate k is negated
 };
 
-struct Encode256Params {
-    EncodeSide side[2];
-    int64_t n_rows;
-    SignBits8 s1;  // the sign diagonal: bit k set where s_k = -1
-    SignBits8 s2;  // second diagonal of the two-sided rotation
-};
-
-constexpr int kE256Block = 256;        // four waves
-constexpr int kE256Stride = 512 + 16;  // LDS bytes per staged row
-
-__device__ __forceinline__ float flip_by8(float t, const SignBits8 &s2, int k)
-{
-    return __uint_as_float(__float_as_uint(t) ^ ((s2.w[k >> 5] << (31 - (k & 31))) & 0x80000000u));
-}
-
-// u for outputs e = 0, 1 of column pair c: the four products accumulate in
-// order A, B, C, E.  NB, NC, NE: negate the B, C, E terms.  Each step's
-// result is read only as the accumulator of the next dot product (no wait
-// states); the block ends with the three the first other reader needs.
-#define TQ_D2M0_0 ""
-#define TQ_D2M0_1 " neg_lo:[0,1,0] neg_hi:[0,1,0]"
-#define TQ_D2M1_0 " neg_hi:[0,1,0]"
-#define TQ_D2M1_1 " neg_lo:[0,1,0]"
-#define TQ_D2M0(n) TQ_D2M0_##n
-#define TQ_D2M1(n) TQ_D2M1_##n
-#define TQ_DOT2_FOUR(NB, NC, NE)                                                        \
-    asm("v_dot2_f32_bf16 %0, %4, %8, 0\n\t"                                               \
-        "v_dot2_f32_bf16 %1, %4, %8, 0 neg_hi:[0,1,0]\n\t"                                \
-        "v_dot2_f32_bf16 %0, %5, %9, %0" TQ_D2M0(NB) "\n\t"                               \
-        "v_dot2_f32_bf16 %1, %5, %9, %1" TQ_D2M1(NB) "\n\t"                               \
-        "v_dot2_f32_bf16 %0, %6, %10, %0" TQ_D2M0(NC) "\n\t"                              \
-        "v_dot2_f32_bf16 %1, %6, %10, %1" TQ_D2M1(NC) "\n\t"                              \
-        "v_dot2_f32_bf16 %2, %7, %11, %0" TQ_D2M0(NE) "\n\t"                              \
-        "v_dot2_f32_bf16 %3, %7, %11, %1" TQ_D2M1(NE) "\n\t"                              \
-        "s_nop 2"                                                                         \
-        : "=&v"(t0), "=&v"(t1), "=&v"(y0), "=v"(y1)                                       \
-        : "v"(A), "v"(B), "v"(C), "v"(E), "s"(wa), "s"(wb), "s"(wc), "s"(we))
-
-template <int W, int P>  // W = a, P = b
-__device__ __forceinline__ void dot2_four_s(uint32_t A, uint32_t B, uint32_t C, uint32_t E,
-                                            uint32_t wa, uint32_t wb, uint32_t wc, uint32_t we,
-                                            float &y0, float &y1)
-{
-    float t0, t1;
-    if constexpr (W == 0 && P == 0)
-        TQ_DOT2_FOUR(0, 0, 0);
-    else if constexpr (W == 0 && P == 1)
-        TQ_DOT2_FOUR(1, 0, 1);
-    else if constexpr (W == 1 && P == 0)
-        TQ_DOT2_FOUR(0, 1, 1);
-    else
-        TQ_DOT2_FOUR(1, 1, 0);
-}
-#undef TQ_DOT2_FOUR
-#undef TQ_D2M1
-#undef TQ_D2M0
-#undef TQ_D2M1_1
-#undef TQ_D2M1_0
-#undef TQ_D2M0_1
-#undef TQ_D2M0_0
-
 typedef const __attribute__((address_space(3))) uint8_t LdsBytes;
 typedef const __attribute__((address_space(3))) u32x4 LdsU32x4;
-
-// v[k] = output 64 (2 W + P) + k before the stages h = 2 .. 32
-template <int W, int P>
-__device__ __forceinline__ void first_stage256(LdsBytes *row, float (&v)[64])
-{
-    const uint32_t one2 = 0x3F803F80u;  // bf16 (1, 1)
-#pragma unroll
-    for (int m = 0; m < 8; m++) {
-        const u32x4 a = *reinterpret_cast<LdsU32x4 *>(row + 16 * m);
-        const u32x4 b = *reinterpret_cast<LdsU32x4 *>(row + 128 + 16 * m);
-        const u32x4 c = *reinterpret_cast<LdsU32x4 *>(row + 256 + 16 * m);
-        const u32x4 e = *reinterpret_cast<LdsU32x4 *>(row + 384 + 16 * m);
-        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-        const uint32_t cw[4] = {c.x, c.y, c.z, c.w}, ew[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int j = 4 * m + q;  // column pair
-            dot2_four_s<W, P>(aw[q], bw[q], cw[q], ew[q], one2, one2, one2, one2, v[2 * j],
-                              v[2 * j + 1]);
-        }
-    }
-}
-
-// This wave's 16 rows of the group starting at row g0 (rows 16 wave ..):
-// chunk c of lane l is bytes [1024 c + 16 l, +16) of those rows (rows past
-// n_rows read as zeros).
-__device__ __forceinline__ void load_quarter_group(const uint8_t *src, int64_t g0,
-                                                   int64_t n_rows, int wave, int lane,
-                                                   u32x4 (&pf)[8])
-{
-    const int64_t r0 = g0 + 16 * wave;
-    const u32x4 *gp = reinterpret_cast<const u32x4 *>(src + r0 * 512) + lane;
-    if (r0 + 16 <= n_rows) {
-#pragma unroll
-        for (int c = 0; c < 8; c++)
-            pf[c] = __builtin_nontemporal_load(gp + 64 * c);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; c++)
-            pf[c] = r0 + 2 * c + (lane >> 5) < n_rows ? __builtin_nontemporal_load(gp + 64 * c)
-                                                     : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// ... into the LDS stage with the sign diagonal applied: every chunk of a
-// lane covers the same eight columns, whose sign bits are `flip`
-__device__ __forceinline__ void stage_quarter_group(const u32x4 (&pf)[8], uint8_t *stg, int wave,
-                                                    int lane, const u32x4 &flip)
-{
-#pragma unroll
-    for (int c = 0; c < 8; c++)
-        *reinterpret_cast<u32x4 *>(stg + (16 * wave + 2 * c + (lane >> 5)) * kE256Stride +
-                                   (lane & 31) * 16) =
-            u32x4{pf[c].x ^ flip.x, pf[c].y ^ flip.y, pf[c].z ^ flip.z, pf[c].w ^ flip.w};
-}
-
-// Scratch of a group shared by the four waves
-struct E256Shared {
-    float ss[4][64];  // each wave's quarter of every row's sum of squares
-    float rss[64];    // rows taking the rescale path: sum of squares (or the
-    int rexp[64];     // non-finite norm), exponent, and whether the row holds
-    int rbad[64];     // an Inf or a NaN
-};
-
-// The pass of wave 2 W + P over the staged group: this wave's quarter of
-// each packed row into wl
-template <int W, int P, int BITS, bool S2>
-__device__ __forceinline__ void e256_pass(const EncodeSide &s, const uint32_t key,
-                                          const uint8_t *mine, const SignBits8 &s2, float t,
-                                          uint32_t (&wl)[2 * BITS])
-{
-    constexpr int HL = 32;         // half-width of the last stage
-    constexpr int K0 = 64 * (2 * W + P);  // the wave's first output
-    // the four passes read the same LDS addresses; an opaque copy of the row
-    // address (an LDS offset: reads through a generic pointer would be flat
-    // loads) keeps the compiler from hoisting those reads above the switch
-    // between them (all 32 at once, which would spill)
-    uint32_t off = (uint32_t)(uintptr_t)(LdsBytes *)mine;
-    asm volatile("" : "+v"(off));
-    float v[64];
-    first_stage256<W, P>((LdsBytes *)(uintptr_t)off, v);
-#pragma unroll
-    for (int h = 2; h < HL; h *= 2)
-#pragma unroll
-        for (int j = 0; j < 64; j += 2 * h)
-#pragma unroll
-            for (int i = j; i < j + h; i++) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-    if constexpr (BITS == 2) {
-        // boundaries -b, 0, b equally spaced: with T' = u / b the index is
-        // 1 - clamp(floor(-T'), -2, 1); the words collect sum c 4^k and
-        // take 0x55..55 - that at the end
-        const float t2 = t * s.code.istep;
-#pragma unroll
-        for (int i = 0; i < HL; i++) {
-            const float bt = v[i + HL] * t2;
-            float ta = fmaf(v[i], t2, bt);
-            float tb = fmaf(v[i], t2, -bt);
-            if constexpr (S2) {
-                ta = flip_by8(ta, s2, K0 + i);
-                tb = flip_by8(tb, s2, K0 + i + HL);
-            }
-            pack_c2(ta, tb, 2 * (i & 15), 2 * ((i + HL) & 15), wl[i >> 4], wl[(i + HL) >> 4]);
-        }
-    } else {
-        constexpr int NB = 16;  // batches of four outputs
-        auto first_of = [](int q) { return 2 * HL * ((2 * q) / HL) + (2 * q) % HL; };
-        float tt[2][4], bb[2][4];
-        uint32_t base[2][4];
-        auto issue = [&](int q, int slot) {
-            const int i = first_of(q);
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const float bt = v[i + h + HL] * t;
-                tt[slot][h] = fmaf(v[i + h], t, bt);
-                tt[slot][h + 2] = fmaf(v[i + h], t, -bt);
-            }
-            if constexpr (S2) {
-                const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    tt[slot][r] = flip_by8(tt[slot][r], s2, K0 + k[r]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const f32x2 e = lut_entry(tt[slot][r], key);
-                bb[slot][r] = e.x;
-                base[slot][r] = __float_as_uint(e.y);
-            }
-        };
-        issue(0, 0);
-#pragma unroll
-        for (int q = 0; q < NB; q++) {
-            if (q + 1 < NB)
-                issue(q + 1, (q + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            uint32_t idx[4];
-            bucket_add4(tt[q & 1], bb[q & 1], base[q & 1], idx);
-            const int i = first_of(q);
-            const int k[4] = {i, i + 1, i + HL, i + 1 + HL};
-#pragma unroll
-            for (int r = 0; r < 4; r++)
-                put_bits(wl, k[r] * BITS, BITS, idx[r]);
-        }
-    }
-}
-
-// Encode the staged group of 64 rows starting at row g0 for one side
-template <int BITS, bool S2>
-__device__ __forceinline__ void encode256_group(const EncodeSide &s, const int64_t g0,
-                                                const int64_t n_rows, const uint32_t key,
-                                                uint8_t *stg, E256Shared &sh, const SignBits8 &s2)
-{
-    constexpr int RB = 32 * BITS;  // packed bytes per row
-    constexpr int NWQ = 2 * BITS;  // packed words per quarter row
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-    uint8_t *mine = stg + lane * kE256Stride;
-    const int nvalid = (int)min<int64_t>(64, n_rows - g0);
-    // sum of squares: each wave takes a quarter of every row
-    sh.ss[wave][lane] = row_sumsq<128>(mine + 128 * wave);
-    __syncthreads();
-    float ss = (sh.ss[0][lane] + sh.ss[1][lane]) + (sh.ss[2][lane] + sh.ss[3][lane]);
-    int nexp = 0;
-    bool bad = false;
-    const bool rare = !(ss >= 0x1p-100f && ss <= 0x1p100f);
-    // the same rows are rare in every wave (the same sums): a branch all
-    // four waves take or all skip
-    if (__builtin_amdgcn_ballot_w64(rare) != 0) {
-        if (wave == 0 && rare) {
-            // rewrite the staged row as x * 2^-nexp (max |x| in [1/2, 1)),
-            // or zeros if it holds Inf or NaN (as mfma_block does); the
-            // loops stay rolled: unrolled, their 32 row reads would all be
-            // in registers at once and push the common path into spills
-            float mx = 0.0f;
-#pragma unroll 2
-            for (int m = 0; m < 32; m++) {
-                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int c = 0; c < 4; c++)
-                    mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(xw[c])), fabsf(bf16_hi(xw[c]))));
-            }
-            const float ss0 = ss;
-            bad = !(mx <= FLT_MAX) || ss0 != ss0;
-            if (!bad && mx > 0.0f)
-                (void)frexpf(mx, &nexp);
-            ss = 0.0f;
-#pragma unroll 2
-            for (int m = 0; m < 32; m++) {
-                const u32x4 x4 = *reinterpret_cast<const u32x4 *>(mine + 16 * m);
-                uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const float x0 = bad ? 0.0f : ldexpf(bf16_lo(xw[c]), -nexp);
-                    const float x1 = bad ? 0.0f : ldexpf(bf16_hi(xw[c]), -nexp);
-                    ss = fmaf(x0, x0, ss);
-                    ss = fmaf(x1, x1, ss);
-                    xw[c] = (__float_as_uint(x1) & 0xFFFF0000u) | (__float_as_uint(x0) >> 16);
-                }
-                *reinterpret_cast<u32x4 *>(mine + 16 * m) = u32x4{xw[0], xw[1], xw[2], xw[3]};
-            }
-            if (bad)
-                ss = ss0 + mx;  // stored as the norm: not finite
-            sh.rss[lane] = ss;
-            sh.rexp[lane] = nexp;
-            sh.rbad[lane] = bad ? 1 : 0;
-        }
-        __syncthreads();
-        if (rare) {
-            ss = sh.rss[lane];
-            nexp = sh.rexp[lane];
-            bad = sh.rbad[lane] != 0;
-        }
-    }
-    const float t = (ss > 0.0f && !bad) ? 128.0f / sqrtf(256.0f * ss) : 0.0f;
-    const float nstore = bad ? ss : ldexpf(sqrtf(ss), nexp);
-    uint32_t wl[NWQ];
-#pragma unroll
-    for (int q = 0; q < NWQ; q++)
-        wl[q] = 0u;
-    switch (wave) {
-    case 0: e256_pass<0, 0, BITS, S2>(s, key, mine, s2, t, wl); break;
-    case 1: e256_pass<0, 1, BITS, S2>(s, key, mine, s2, t, wl); break;
-    case 2: e256_pass<1, 0, BITS, S2>(s, key, mine, s2, t, wl); break;
-    default: e256_pass<1, 1, BITS, S2>(s, key, mine, s2, t, wl); break;
-    }
-    if constexpr (BITS == 2) {
-#pragma unroll
-        for (int q = 0; q < NWQ; q++)
-            wl[q] = 0x55555555u - wl[q];
-    }
-    if (wave == 0 && lane < nvalid)
-        *as_global(s.norms + g0 + lane) = nstore;
-    __syncthreads();  // every wave is done with the staged rows
-    // packed rows, densely (the group's global layout), each wave its quarter
-    // of every row (8 BITS bytes); then whole-line stores by all four waves
-#pragma unroll
-    for (int q = 0; q < NWQ / 2; q++)
-        *reinterpret_cast<u32x2 *>(stg + lane * RB + wave * (RB / 4) + 8 * q) =
-            u32x2{wl[2 * q], wl[2 * q + 1]};
-    __syncthreads();
-    {
-        constexpr int NG = 64 * RB / 16;  // 16-byte granules of the group
-        const int bytes = nvalid * RB;    // a multiple of 16
-        __attribute__((address_space(1))) uint8_t *dst = as_global(s.packed + g0 * RB);
-#pragma unroll
-        for (int q = 0; q < (NG + kE256Block - 1) / kE256Block; q++) {
-            const int e = kE256Block * q + (int)threadIdx.x;
-            if (e < NG && 16 * e < bytes) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(stg + 16 * e);
-                __builtin_nontemporal_store(x, reinterpret_cast<__attribute__((address_space(1))) u32x4 *>(dst) + e);
-            }
-        }
-    }
-    __syncthreads();  // the stage is free for the next group
-}
-
-// Persistent loop over groups; with two sides each workgroup encodes group g
-// of the first side, then of the second.  The next staging's loads are
-// issued before the current one is transformed.
-template <int B0, int B1, bool S2>
-__global__ __launch_bounds__(kE256Block) __attribute__((amdgpu_waves_per_eu(2)))
-void encode256_kernel(Encode256Params p)
-{
-    __shared__ float2 lut[(B0 > 2 || B1 > 2) ? kLutBins : 1];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[64 * kE256Stride];
-    __shared__ E256Shared sh;
-    // one group of 64 rows of one side per workgroup, every group of the
-    // first side before any of the second: the launch walks memory as one
-    // compact window
-    const int64_t n_rows = p.n_rows;
-    const int64_t nb = (n_rows + 63) / 64;  // groups per side
-    const bool second = B1 > 0 && (int64_t)blockIdx.x >= nb;
-    const int64_t g0 = ((int64_t)blockIdx.x - (second ? nb : 0)) * 64;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
-    const uint8_t *src = static_cast<const uint8_t *>(second ? p.side[1].src : p.side[0].src);
-    u32x4 pf[8];
-    load_quarter_group(src, g0, n_rows, wave, lane, pf);
-    if (second) {
-        if constexpr (B1 > 2)
-            build_lut(lut, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
-    } else {
-        if constexpr (B0 > 2)
-            build_lut(lut, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
-    }
-    // the sign bits of this lane's staging columns 8 (lane % 32) .. + 7, as
-    // xor masks of the bf16 pairs
-    u32x4 flip;
-    {
-        const int col = 8 * (lane & 31);
-        const uint32_t sw = p.s1.w[col >> 5] >> (col & 31);
-        uint32_t f[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-            f[j] = (((sw >> (2 * j)) & 1u) << 15) | (((sw >> (2 * j + 1)) & 1u) << 31);
-        flip = u32x4{f[0], f[1], f[2], f[3]};
-    }
-    stage_quarter_group(pf, stage, wave, lane, flip);
-    __syncthreads();
-    const uint32_t key = lut_key(lut);
-    if constexpr (B1 > 0) {
-        if (second) {
-            encode256_group<(B1 > 0 ? B1 : B0), S2>(p.side[1], g0, n_rows, key, stage, sh, p.s2);
-            return;
-        }
-    }
-    encode256_group<B0, S2>(p.side[0], g0, n_rows, key, stage, sh, p.s2);
-}
 
 // ------------------------------------- encode, bf16 rows on the matrix cores
 // For d = 32 Q the Hadamard matrix (Sylvester order) factors over coordinate
@@ -1013,7 +603,10 @@ __device__ __forceinline__ void mfma_block(u32x4 (&x)[D / 32], const u32x4 (&am)
     for (int a = 0; a < Q; a++) {
         if constexpr (S2) {
             // the second diagonal's signs of coordinates 32 a + 8 kq + j
-            const uint32_t sb = s2.w[a] >> (8 * kq);
+            // (taken per block: hoisted, the Q words would stay in registers)
+            int kql = kq;
+            asm volatile("" : "+v"(kql));
+            const uint32_t sb = s2.w[a] >> (8 * kql);
 #pragma unroll
             for (int j = 0; j < 8; j++)
                 T[a][j] = __uint_as_float(__float_as_uint(T[a][j]) ^ ((sb << (31 - j)) & 0x80000000u));
@@ -1165,7 +758,7 @@ __device__ __forceinline__ void mfma_group(const EncodeSide &s, int64_t g0, int6
 // arithmetic reaches 76% of HBM in this order and about 70% when each wave
 // loops over many groups or alternates the sides.
 template <int D, int B0, int B1, bool S2>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(S2 && D == 128 ? 3 : 4)))
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : 4)))
 void encode_mfma_kernel(EncodeMfmaParams p)
 {
     constexpr int Q = D / 32, R = ring_slots<D>();
@@ -1606,34 +1199,6 @@ int resident_blocks(K kern, int block = kBlock)
     return n;
 }
 
-// sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
-template <int B0, int B1, bool S2>
-void launch_encode256_k(const Encode256Params &q, hipStream_t st)
-{
-    auto kern = encode256_kernel<B0, B1, S2>;
-    // one group of 64 rows per workgroup and side, the first side's first
-    const int64_t groups = (q.n_rows + 63) / 64;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(groups * (B1 > 0 ? 2 : 1))), dim3(kE256Block), 0, st,
-                       q);
-}
-
-// sides ordered so that side[0] has the larger width (B0 >= B1; B1 = 0: one side)
-template <bool S2>
-void launch_encode256(const Encode256Params &q, int b0, int b1, hipStream_t st)
-{
-    switch (10 * b0 + b1) {
-    case 40: launch_encode256_k<4, 0, S2>(q, st); break;
-    case 30: launch_encode256_k<3, 0, S2>(q, st); break;
-    case 20: launch_encode256_k<2, 0, S2>(q, st); break;
-    case 44: launch_encode256_k<4, 4, S2>(q, st); break;
-    case 43: launch_encode256_k<4, 3, S2>(q, st); break;
-    case 42: launch_encode256_k<4, 2, S2>(q, st); break;
-    case 33: launch_encode256_k<3, 3, S2>(q, st); break;
-    case 32: launch_encode256_k<3, 2, S2>(q, st); break;
-    default: launch_encode256_k<2, 2, S2>(q, st); break;
-    }
-}
-
 template <int D, int B0, int B1, bool S2>
 void launch_encode_mfma_k(const EncodeMfmaParams &q, hipStream_t st)
 {
@@ -1834,7 +1399,8 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
     p.n_rows = n_rows;
     p.d_in = d;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (dtype == TQ_BF16 && d <= 128 && d == D) {
+    if (dtype == TQ_BF16 && d == D) {
+        // bf16 rows of exactly 64, 128 or 256 values: the matrix-core encode
         EncodeMfmaParams q;
         q.side[0] = p.side[0];
         q.side[1] = p.side[1];
@@ -1851,32 +1417,20 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
         tq::sign_words(d, seed, q.s1.w);
         tq::sign_words2(d, seed, flags, q.s2.w);
         const bool two = (flags & TQ_FLAG_TWO_SIDED) != 0;
-        if (d == 64)
+        switch (d) {
+        case 64:
             two ? launch_encode_mfma_d<64, true>(q, b0, b1, st)
                 : launch_encode_mfma_d<64, false>(q, b0, b1, st);
-        else
+            break;
+        case 128:
             two ? launch_encode_mfma_d<128, true>(q, b0, b1, st)
                 : launch_encode_mfma_d<128, false>(q, b0, b1, st);
-        return launch_status(fn);
-    }
-    if (dtype == TQ_BF16 && d == 256) {
-        Encode256Params q;
-        q.side[0] = p.side[0];
-        q.side[1] = p.side[1];
-        if (sides == 2 && q.side[1].code.bits > q.side[0].code.bits) {
-            q.side[0] = p.side[1];
-            q.side[1] = p.side[0];
+            break;
+        default:
+            two ? launch_encode_mfma_d<256, true>(q, b0, b1, st)
+                : launch_encode_mfma_d<256, false>(q, b0, b1, st);
+            break;
         }
-        const int b0 = q.side[0].code.bits, b1 = sides == 2 ? q.side[1].code.bits : 0;
-        if (sides == 1)
-            q.side[1] = q.side[0];  // unused
-        q.n_rows = n_rows;
-        tq::sign_words(256, seed, q.s1.w);
-        tq::sign_words2(256, seed, flags, q.s2.w);
-        if (flags & TQ_FLAG_TWO_SIDED)
-            launch_encode256<true>(q, b0, b1, st);
-        else
-            launch_encode256<false>(q, b0, b1, st);
         return launch_status(fn);
     }
     tq::sign_words(D, seed, p.signs);
