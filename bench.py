@@ -134,15 +134,15 @@ def _known_kernels():
     n3 = L3 * H3 * T3
     n5 = H5 * T5
     return {
-        "encode_lane_kernel<128, 4, 2, false>":
+        "encode_mfma_kernel<128, 4, 2, false>":
             ("encode_k4v2", enc_bytes(n3, D3, BK3, 2) + enc_bytes(n3, D3, BV3, 2)),
         "decode_kernel<128, 4, false>": ("decode_k4", dec_bytes(n3, D3, BK3)),
         "decode_kernel<128, 2, false>": ("decode_v2", dec_bytes(n3, D3, BV3)),
         "attn_partial_wave_kernel<128, 4, 2, 4>":
             ("attn_decode", attn_bytes(B4, HQ4, HKV4, D4, T4, BK4, BV4)),
-        "encode_lane_kernel<64, 3, 2, false>":
+        "encode_mfma_kernel<64, 3, 2, false>":
             ("long_encode_d64", enc_bytes(n5, 64, BK5, 2) + enc_bytes(n5, 64, BV5, 2)),
-        "encode256_kernel<3, 2, false>":
+        "encode_mfma_kernel<256, 3, 2, false>":
             ("long_encode_d256", enc_bytes(n5, 256, BK5, 2) + enc_bytes(n5, 256, BV5, 2)),
         "decode_kernel<64, 3, false>": ("long_decode_k3_d64", dec_bytes(n5, 64, BK5)),
         "decode_kernel<64, 2, false>": ("long_decode_v2_d64", dec_bytes(n5, 64, BV5)),

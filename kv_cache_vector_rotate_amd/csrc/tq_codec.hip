@@ -23,6 +23,8 @@
 #include <algorithm>
 #include <cfloat>
 #include <cmath>
+#include <cstddef>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -322,30 +324,43 @@ struct EncodeMfmaParams {
     int64_t n_rows;
     SignBits8 s1;  // the sign diagonal: bit k set where s_k = -1
     SignBits8 s2;  // second diagonal of the two-sided rotation
+    // the bucketize table of side lut_side (-1: none), built on the host
+    // (the same entries build_lut computes); a workgroup of that side copies
+    // it from the kernel arguments instead of building it
+    int lut_side;
+    float2 lut[kLutBins];
 };
 
 // The constant operand of segment a, M-block mb for this lane: bf16 pairs
 // (H_32)[b'][k] s_{32 a + k} for its row m = lane % 16 and k = 8 kq + j.
+// (H_32)[b'][k] = (-1)^parity(b' & k) splits over the bits of b' =
+// 8 (m / 4) + 4 mb + m % 4 and k = 8 kq + j: parity((m / 4) & kq) for every
+// j, j >= 4 when mb = 1, and parity((m % 4) & j), whose masks over j are
+// 0x00, 0xAA, 0xCC, 0x66.  With the segment's signs (bits 8 kq .. 8 kq + 7
+// of s1.w[a]) that is one byte of negations per (a, mb), spread into four
+// words of bf16 pairs.
 template <int Q>
 __device__ __forceinline__ void mfma_rotation_operand(const SignBits8 &s1, int lane,
                                                       u32x4 (&am)[Q][2])
 {
     const int m = lane & 15, kq = lane >> 4;
+    const uint32_t h0 = ((__popc((m >> 2) & kq) & 1) ? 0xFFu : 0u) ^
+                        ((0x66CCAA00u >> (8 * (m & 3))) & 0xFFu);
 #pragma unroll
-    for (int a = 0; a < Q; a++)
+    for (int a = 0; a < Q; a++) {
+        const uint32_t sg = (s1.w[a] >> (8 * kq)) & 0xFFu;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++) {
-            const int bp = 8 * (m >> 2) + 4 * mb + (m & 3);
+            const uint32_t neg = h0 ^ sg ^ (mb ? 0xF0u : 0u);
             uint32_t w[4];
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-                const int k0 = 8 * kq + 2 * jj, k1 = k0 + 1;
-                const uint32_t n0 = ((uint32_t)__popc(bp & k0) ^ (s1.w[a] >> k0)) & 1u;
-                const uint32_t n1 = ((uint32_t)__popc(bp & k1) ^ (s1.w[a] >> k1)) & 1u;
-                w[jj] = (0x3F80u | (n0 << 15)) | ((0x3F80u | (n1 << 15)) << 16);
+                const uint32_t t = neg >> (2 * jj);
+                w[jj] = 0x3F803F80u | ((t << 15) & 0x8000u) | ((t << 30) & 0x80000000u);
             }
             am[a][mb] = u32x4{w[0], w[1], w[2], w[3]};
         }
+    }
 }
 
 // Ring of block inputs in LDS: the loads of a block go straight from memory
@@ -725,9 +740,7 @@ __device__ __forceinline__ void mfma_group(const EncodeSide &s, int64_t g0, int6
 {
     constexpr int Q = D / 32, R = ring_slots<D>(), SLOT = Q * kSeg;
     const uint8_t *src = static_cast<const uint8_t *>(s.src);
-#pragma unroll
-    for (int u = 0; u < R; u++)
-        issue_block_lds<D>(src, g0 + 16 * u, n_rows, lane, slots + u * SLOT);
+    // (the first R blocks' loads were issued by the caller)
 #pragma unroll 1
     for (int u = 0; u < 4; u++) {
         const int64_t r0 = g0 + 16 * u;
@@ -770,7 +783,26 @@ void encode_mfma_kernel(EncodeMfmaParams p)
     const int64_t n_rows = p.n_rows;
     const int64_t nb = (n_rows + 255) / 256;  // workgroups per side
     const bool second = B1 > 0 && (int64_t)blockIdx.x >= nb;
-    if (second) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t g0 = (((int64_t)blockIdx.x - (second ? nb : 0)) * (kBlock / 64) + wave) * 64;
+    // the group's first loads go out before the set-up below (rows past the
+    // end load the last row, so a wave past n_rows issues them too)
+    {
+        const uint8_t *src = static_cast<const uint8_t *>(second ? p.side[1].src : p.side[0].src);
+#pragma unroll
+        for (int u = 0; u < R; u++)
+            issue_block_lds<D>(src, g0 + 16 * u, n_rows, lane, ring[wave] + u * SLOT);
+    }
+    if (p.lut_side == (second ? 1 : 0)) {
+        // the table from the kernel arguments (one 8-byte load per entry)
+        typedef const __attribute__((address_space(4))) u32x2 KU32x2;
+        KU32x2 *klut = (KU32x2 *)((const __attribute__((address_space(4))) char *)
+                                      __builtin_amdgcn_kernarg_segment_ptr() +
+                                  offsetof(EncodeMfmaParams, lut));
+        for (int i = threadIdx.x; i < kLutBins; i += kBlock)
+            reinterpret_cast<u32x2 *>(lut)[i] = klut[i];
+    } else if (second) {
         if constexpr (B1 > 2)
             build_lut(lut, p.side[1].code.bnd, (1 << B1) - 1, kLutScale);
     } else {
@@ -778,11 +810,10 @@ void encode_mfma_kernel(EncodeMfmaParams p)
             build_lut(lut, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
     }
     __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t g0 = (((int64_t)blockIdx.x - (second ? nb : 0)) * (kBlock / 64) + wave) * 64;
-    if (g0 >= n_rows)
+    if (g0 >= n_rows) {
+        wait_vmcnt<0>();  // no load into LDS outlives the wave
         return;
+    }
     u32x4 am[Q][2];
     mfma_rotation_operand<Q>(p.s1, lane, am);
     const uint32_t key = lut_key(lut);
@@ -1199,6 +1230,29 @@ int resident_blocks(K kern, int block = kBlock)
     return n;
 }
 
+// The bucketize table as build_lut fills it on the device (the same float
+// operations: the bin edges are exact multiples of 1/128 less or more the
+// slack, each rounded once, so the entries are identical)
+void host_lut(const float *bnd, int nbnd, float bscale, float2 *lut)
+{
+    for (int i = 0; i < kLutBins; i++) {
+        const float lo = ((float)(i - kLutZero) - 0.5f) * (1.0f / kLutScale) - kLutSlack;
+        const float hi = ((float)(i - kLutZero) + 0.5f) * (1.0f / kLutScale) + kLutSlack;
+        int base = 0;
+        float inside = __builtin_huge_valf();
+        for (int j = 0; j < nbnd; j++) {
+            const float b = bnd[j];
+            if (b < lo)
+                base++;
+            else if (b <= hi && inside == __builtin_huge_valf())
+                inside = b;
+        }
+        float base_bits;
+        std::memcpy(&base_bits, &base, sizeof base_bits);
+        lut[i] = make_float2(inside * bscale, base_bits);
+    }
+}
+
 template <int D, int B0, int B1, bool S2>
 void launch_encode_mfma_k(const EncodeMfmaParams &q, hipStream_t st)
 {
@@ -1416,6 +1470,13 @@ extern "C" int tq_encode(const void *k_rows, const void *v_rows, int dtype, int6
             q.s1.w[w] = q.s2.w[w] = 0u;
         tq::sign_words(d, seed, q.s1.w);
         tq::sign_words2(d, seed, flags, q.s2.w);
+        // one side's table travels with the arguments (the first side with
+        // more than two bits); the other side, if it needs one, builds it
+        q.lut_side = b0 > 2 ? 0 : b1 > 2 ? 1 : -1;
+        if (q.lut_side >= 0) {
+            const CodeTable &c = q.side[q.lut_side].code;
+            host_lut(c.bnd, (1 << c.bits) - 1, kLutScale, q.lut);
+        }
         const bool two = (flags & TQ_FLAG_TWO_SIDED) != 0;
         switch (d) {
         case 64:

@@ -160,15 +160,15 @@ def test_edge_rows(tq, orc):
 
 @pytest.mark.parametrize("sides", [1, 2])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_edge_rows_d128_d256(tq, orc, bits, d, dtype, sides):
+def test_edge_rows(tq, orc, bits, d, dtype, sides):
     """Zero, constant, spike, exact-tie, tiny and huge rows against the
     oracle; rows holding an Inf or a NaN encode as the zero row with a
     non-finite norm; power-of-two scale invariance (indices identical, norms
-    scaled exactly, except that the one-lane-per-row bf16 kernels sum a
-    rescaled row's squares in another order: there within 1e-6).  sides = 2
-    encodes the rows as K and as V in one call (the two results must be
+    scaled exactly, except that the bf16 matrix-core kernels sum a rescaled
+    row's squares in another order: there within 1e-6).  sides = 2 encodes
+    the rows as K and as V in one call (the two results must be
     identical)."""
     def tq_encode(rows, bits_k, bits_v, seed):
         if sides == 1:
@@ -178,7 +178,7 @@ def test_edge_rows_d128_d256(tq, orc, bits, d, dtype, sides):
         assert torch.equal(kn_.nan_to_num(), vn_.nan_to_num())
         return kp_, kn_, None, None
 
-    lane_per_row = dtype == torch.bfloat16
+    bf16_rows = dtype == torch.bfloat16
     rng = np.random.default_rng(5)
     e = np.eye(d, dtype=np.float32)
     base = rng.standard_normal((6, d)).astype(np.float32)
@@ -209,7 +209,7 @@ def test_edge_rows_d128_d256(tq, orc, bits, d, dtype, sides):
         sp, sn, _, _ = tq_encode(xs, bits, 2, SEED)
         assert np.array_equal(sp.cpu().numpy(), gp[7:])
         want = gn[7:] * np.float32(2.0 ** k)
-        if abs(k) > 20 and lane_per_row:
+        if abs(k) > 20 and bf16_rows:
             np.testing.assert_allclose(sn.cpu().numpy(), want, rtol=1e-6)
         else:
             assert np.array_equal(sn.cpu().numpy(), want)
@@ -303,8 +303,8 @@ def test_config5_long_context_codec_sampled(tq, orc):
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_encode_decode_flags(tq, orc, d, dtype, flags):
     """N(0, 1/d) codebooks (flag 1) and the two-sided rotation (flag 2): every
-    bit width on both sides of one launch (the one-lane-per-row kernel for
-    bf16 d <= 128, the lane-slice kernel otherwise), then decode."""
+    bit width on both sides of one launch (the matrix-core kernel for bf16
+    rows, the lane-slice kernel for fp32), then decode."""
     density = orc.GAUSS if flags & 1 else orc.BETA
     two = bool(flags & 2)
     n = 4096 + 29
