@@ -337,28 +337,36 @@ struct EncodeMfmaParams {
 // 8 (m / 4) + 4 mb + m % 4 and k = 8 kq + j: parity((m / 4) & kq) for every
 // j, j >= 4 when mb = 1, and parity((m % 4) & j), whose masks over j are
 // 0x00, 0xAA, 0xCC, 0x66.  With the segment's signs (bits 8 kq .. 8 kq + 7
-// of s1.w[a]) that is one byte of negations per (a, mb), spread into four
-// words of bf16 pairs.
+// of s1.w[a]) that is one byte of negations per (a, mb); `spread` maps each
+// nibble of it to two words of bf16 (+-1, +-1) pairs.
+__device__ __forceinline__ uint32_t spread_word(uint32_t t)
+{
+    return 0x3F803F80u | ((t & 1u) << 15) | ((t & 2u) << 30);
+}
+
+__device__ __forceinline__ void fill_spread(u32x2 *spread)
+{
+    if (threadIdx.x < 16)
+        spread[threadIdx.x] = u32x2{spread_word(threadIdx.x & 3u), spread_word(threadIdx.x >> 2)};
+}
+
 template <int Q>
 __device__ __forceinline__ void mfma_rotation_operand(const SignBits8 &s1, int lane,
-                                                      u32x4 (&am)[Q][2])
+                                                      const u32x2 *spread, u32x4 (&am)[Q][2])
 {
     const int m = lane & 15, kq = lane >> 4;
     const uint32_t h0 = ((__popc((m >> 2) & kq) & 1) ? 0xFFu : 0u) ^
                         ((0x66CCAA00u >> (8 * (m & 3))) & 0xFFu);
+    const __attribute__((address_space(3))) u32x2 *sp =
+        (const __attribute__((address_space(3))) u32x2 *)spread;
 #pragma unroll
     for (int a = 0; a < Q; a++) {
         const uint32_t sg = (s1.w[a] >> (8 * kq)) & 0xFFu;
 #pragma unroll
         for (int mb = 0; mb < 2; mb++) {
             const uint32_t neg = h0 ^ sg ^ (mb ? 0xF0u : 0u);
-            uint32_t w[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-                const uint32_t t = neg >> (2 * jj);
-                w[jj] = 0x3F803F80u | ((t << 15) & 0x8000u) | ((t << 30) & 0x80000000u);
-            }
-            am[a][mb] = u32x4{w[0], w[1], w[2], w[3]};
+            const u32x2 lo = sp[neg & 15u], hi = sp[neg >> 4];
+            am[a][mb] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
     }
 }
@@ -778,6 +786,7 @@ void encode_mfma_kernel(EncodeMfmaParams p)
     constexpr int RBM = D * B0 / 8;  // B0 >= B1
     constexpr int SLOT = Q * kSeg;   // Q regions of 1 KiB, padded
     __shared__ float2 lut[(B0 > 2 || B1 > 2) ? kLutBins : 1];
+    __shared__ u32x2 spread[16];
     __shared__ __attribute__((aligned(16))) uint8_t ring[kBlock / 64][R * SLOT];
     __shared__ __attribute__((aligned(16))) uint8_t stage[kBlock / 64][16 * RBM];
     const int64_t n_rows = p.n_rows;
@@ -809,13 +818,14 @@ void encode_mfma_kernel(EncodeMfmaParams p)
         if constexpr (B0 > 2)
             build_lut(lut, p.side[0].code.bnd, (1 << B0) - 1, kLutScale);
     }
+    fill_spread(spread);
     __syncthreads();
     if (g0 >= n_rows) {
         wait_vmcnt<0>();  // no load into LDS outlives the wave
         return;
     }
     u32x4 am[Q][2];
-    mfma_rotation_operand<Q>(p.s1, lane, am);
+    mfma_rotation_operand<Q>(p.s1, lane, spread, am);
     const uint32_t key = lut_key(lut);
     if constexpr (B1 > 0) {
         if (second) {
