@@ -552,6 +552,14 @@ def bench_long_context(tq, kvgen, reps_codec, reps_attn):
         for l in range(L5):
             tq.tq_attn_decode(c5, l, qs[l], T5, out=outs[HD5[l]], workspace=ws)
 
+    # every layer's K and V into buffers of their own through the multi-layer
+    # window decode: one launch per (head_dim, bits), four in all
+    kall = [torch.empty(1, H5, T5, d, dtype=torch.float32, device="cuda") for d in HD5]
+    vall = [torch.empty(1, H5, T5, d, dtype=torch.float32, device="cuda") for d in HD5]
+
+    def dec_one_call():
+        tq.tq_cache_decode(c5, -1, 0, T5, k_out=kall, v_out=vall)
+
     enc()
     quality = {}
     for l in (0, 1):
@@ -566,6 +574,7 @@ def bench_long_context(tq, kvgen, reps_codec, reps_attn):
     settle(enc, 0.2)
     te = timed_reps(enc, reps_codec, 1)
     td = timed_reps(dec, reps_codec, 1)
+    td1 = timed_reps(dec_one_call, reps_codec, 1)
     ta = timed_reps(att, reps_attn, 2)
     enc_b = sum(enc_bytes(H5 * T5, d, BK5, 2) + enc_bytes(H5 * T5, d, BV5, 2) for d in HD5)
     dec_b = sum(dec_bytes(H5 * T5, d, BK5) + dec_bytes(H5 * T5, d, BV5) for d in HD5)
@@ -574,10 +583,12 @@ def bench_long_context(tq, kvgen, reps_codec, reps_attn):
     return {
         "workload": "long context K3/V2: 1 sequence x 8 KV heads (8 query heads) x 131072 tokens, "
                     "32 layers (head_dim 64 and 256 alternating), bf16 Student-t(3) rows; encode "
-                    "all layers (32 launches), decode all layers (64 launches), attention over all "
-                    "layers (32 calls)",
+                    "all layers (32 launches), decode all layers (64 launches of tq_decode; and in "
+                    "one tq_cache_decode call, four launches, into per-layer buffers), attention "
+                    "over all layers (32 calls)",
         "encode_all_layers": summary(te, enc_b, rows),
         "decode_all_layers": summary(td, dec_b, rows),
+        "decode_all_layers_one_call": summary(td1, dec_b, rows),
         "attention_all_layers": summary(ta, att_b),
         "quality": quality,
     }
