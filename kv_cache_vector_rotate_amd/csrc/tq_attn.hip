@@ -68,6 +68,35 @@ struct AttnParams {
     uint32_t signs2[8];       // second diagonal (two-sided rotation), else zero
 };
 
+// The workgroup's (chunk, group y, sequence).  With two workgroups per KV
+// head (gsplit = 2) both read the KV head's rows: the launch's linear
+// workgroup ids are remapped so that the two of a pair are 8 ids apart, which
+// puts them on the same XCD (workgroups go to the 8 XCDs in turn) at about the
+// same time, and the second read of the rows hits that XCD's L2.  A bijection:
+// each run of 16 ids holds 8 pairs; the last, shorter run pairs neighbours.
+struct AttnBlock {
+    int chunk, y, b;
+};
+
+__device__ __forceinline__ AttnBlock attn_block(const AttnParams &p)
+{
+    if (p.gsplit != 2)
+        return AttnBlock{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    const uint32_t nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
+    const uint32_t L = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const uint32_t full = n & ~15u;
+    uint32_t pair, half;
+    if (L < full) {
+        half = (L >> 3) & 1u;
+        pair = (L >> 4) * 8u + (L & 7u);
+    } else {
+        half = (L - full) & 1u;
+        pair = full / 2u + (L - full) / 2u;
+    }
+    const uint32_t nyp = ny / 2u, rest = pair / nx;
+    return AttnBlock{(int)(pair % nx), (int)(2u * (rest % nyp) + half), (int)(rest / nyp)};
+}
+
 template <int M>
 __device__ __forceinline__ float lane_xor_any(float v)
 {
@@ -492,9 +521,10 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, b = blockIdx.z;
-    const int g = blockIdx.y / p.gsplit;  // KV head
-    const int h0 = blockIdx.y * G;        // first of this workgroup's G query heads
+    const AttnBlock blk = attn_block(p);
+    const int chunk = blk.chunk, b = blk.b;
+    const int g = blk.y / p.gsplit;  // KV head
+    const int h0 = blk.y * G;        // first of this workgroup's G query heads
 
     fill_lookup<BK, G>(tabK, p.centK);
     fill_lookup<BV, G>(tabV, p.centV);
@@ -689,9 +719,10 @@ __global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
     __shared__ __attribute__((aligned(16))) float xbuf[XON ? kBlock / 64 * X::FLOATS : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, b = blockIdx.z;
-    const int g = blockIdx.y / p.gsplit;
-    const int h0 = blockIdx.y * G;
+    const AttnBlock blk = attn_block(p);
+    const int chunk = blk.chunk, b = blk.b;
+    const int g = blk.y / p.gsplit;
+    const int h0 = blk.y * G;
     fill_lookup<BK, G>(tabK, p.centK);
     rotate_queries<D, G>(p, qs, b, h0, wave, lane);
     __syncthreads();
@@ -702,7 +733,7 @@ __global__ __launch_bounds__(kBlock) void attn_scores_kernel(AttnParams p)
     const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
     const uint8_t *kbase = p.kp + rowbase * RBK;
     const float *knb = p.kn + rowbase;
-    float *srow = p.scores + ((int64_t)b * gridDim.y + blockIdx.y) * p.T * G;
+    float *srow = p.scores + ((int64_t)b * gridDim.y + blk.y) * p.T * G;
     const int t_begin = chunk * p.chunk_len;
     const int t_end = min(p.T, t_begin + p.chunk_len);
     float mx[G];
@@ -813,9 +844,10 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
     __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * AST];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = blockIdx.x, b = blockIdx.z;
-    const int g = blockIdx.y / p.gsplit;
-    const int h0 = blockIdx.y * G;
+    const AttnBlock blk = attn_block(p);
+    const int chunk = blk.chunk, b = blk.b;
+    const int g = blk.y / p.gsplit;
+    const int h0 = blk.y * G;
     fill_lookup<BV, G>(tabV, p.centV);
     // the context's largest score of each head: the largest chunk maximum
 #pragma unroll
@@ -851,7 +883,7 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
     const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
     const uint8_t *vbase = p.vp + rowbase * RBV;
     const float *vnb = p.vn + rowbase;
-    const float *srow = p.scores + ((int64_t)b * gridDim.y + blockIdx.y) * p.T * G;
+    const float *srow = p.scores + ((int64_t)b * gridDim.y + blk.y) * p.T * G;
     const int t_begin = chunk * p.chunk_len;
     const int t_end = min(p.T, t_begin + p.chunk_len);
 #pragma unroll 1
