@@ -81,6 +81,27 @@ def test_encode_decode_all_bits_ragged(tq, orc, d, dtype):
     tally.check()
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_encode_bf16_row_counts_at_block_edges(tq, orc, d):
+    """bf16 rows in counts around the matrix-core encode's 16-row blocks and
+    64-row groups (a launch of 256 rows per workgroup and side): partial first
+    blocks, partial groups, workgroups whose later waves start past the last
+    row; K and V of different widths in one launch, against the oracle."""
+    tally = BandTally()
+    for n in (1, 5, 15, 16, 17, 33, 63, 64, 65, 127, 255, 256, 257, 300, 513):
+        k = kvgen.normal((n, d), 900 + n, "cuda", torch.bfloat16)
+        v = kvgen.normal((n, d), 901 + n, "cuda", torch.bfloat16)
+        for bk, bv in ((4, 2), (3, 3)):
+            kp, kn, vp, vn = tq.tq_encode(k, v, bk, bv, SEED)
+            torch.cuda.synchronize()
+            for x, bits, pk, nm in ((k, bk, kp, kn), (v, bv, vp, vn)):
+                op, on, u = orc.encode(_np(x).astype(np.float32), d, bits, SEED, want_u=True)
+                _, bnd = orc.codebook_float(d, bits)
+                check_norms(nm.cpu().numpy(), on)
+                check_indices(pk.cpu().numpy(), op, u, d, bits, bnd, tally=tally)
+    tally.check()
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_encode_rows_at_high_low_word_addresses(tq, orc, d):
     """bf16 rows whose device addresses have the low 32-bit word at or above
