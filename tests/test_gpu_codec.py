@@ -431,10 +431,10 @@ def test_padded_head_dim(tq, orc, d, dtype, flags):
 
 
 @pytest.mark.parametrize("flags", [2, 3])
-def test_flags_persistent_loop_sampled(tq, orc, flags):
-    """K4/V2 bf16 d = 128 with the flags at 600k rows (several groups per wave
-    of the persistent encode, and a ragged last group), compared on sampled
-    rows."""
+def test_flags_large_launch_sampled(tq, orc, flags):
+    """K4/V2 bf16 d = 128 with the flags at 600k rows (a launch of thousands of
+    workgroups per side, the second side's after the first's, and a ragged
+    last group), compared on sampled rows."""
     d, n = 128, 600_000 + 37
     density = orc.GAUSS if flags & 1 else orc.BETA
     k = kvgen.ar1_outliers((1, 1, n, d), 70 + flags, "cuda").reshape(n, d)
