@@ -943,7 +943,11 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
 // 4 (t % (D/4)) .. +3 of the chunks c = t / (D/4), + NG, + 2 NG, ... (NG
 // groups of chunks in parallel, every record read whole-line), the groups'
 // sums meet in LDS in a fixed order, and the first wave applies the single
-// inverse rotation (its first D/32 lanes hold the row).
+// inverse rotation (its first D/32 lanes hold the row).  The records are read
+// in one pass: each group keeps a running maximum of the chunk maxima and
+// rescales its sums when it grows (the log-sum-exp merge of [Foundry]
+// "Optimization: Fused dequant-dot" taken over chunks), and the groups are
+// brought to the common maximum where they meet.
 constexpr int kCombineThreads = 256;
 
 template <int D>
@@ -951,32 +955,30 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
 {
     constexpr int P = D / kCPL, RS = D + 4, Q = D / 4, NG = kCombineThreads / Q;
     __shared__ __attribute__((aligned(16))) float part[NG][D];
-    __shared__ float lsum[NG];
-    __shared__ float wmax[kCombineThreads / 64];
+    __shared__ float lsum[NG], gmax[NG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j4 = tid % Q, grp = tid / Q;
     const int64_t bh = blockIdx.x;
     const float *rec = p.part + bh * p.n_chunks * RS;
-    // the largest chunk maximum
-    float M = -__builtin_huge_valf();
-    for (int c = tid; c < p.n_chunks; c += kCombineThreads)
-        M = fmaxf(M, rec[c * RS + D]);
-    M = max_across<32>(M);
-    M = fmaxf(M, __shfl_xor(M, 32));
-    if (lane == 0)
-        wmax[wave] = M;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kCombineThreads / 64; w++)
-        M = fmaxf(M, wmax[w]);
-    // this thread's group of chunks, in chunk order; the records of UN chunks
-    // are loaded together (one latency per batch: with few (sequence, head)
-    // pairs this kernel is latency-bound)
-    constexpr int UN = 8;
+    constexpr float kNegInf = -__builtin_huge_valf();
+    // the records of UN chunks are loaded together (one latency per batch:
+    // with few (sequence, head) pairs this kernel is latency-bound); every
+    // thread of a group reads the same chunks, so the group's maximum is the
+    // same in all of them
+    constexpr int UN = D >= 256 ? 16 : 8;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float L = 0.0f;
+    float L = 0.0f, m = kNegInf;
+    auto raise_to = [&](float mn) {  // mn >= m; from m = -inf the sums are 0
+        const float s = mn == m ? 1.0f : exp2f(m - mn);
+        o.x *= s;
+        o.y *= s;
+        o.z *= s;
+        o.w *= s;
+        L *= s;
+        m = mn;
+    };
     auto add = [&](float mx, const float4 &t, float lv) {
-        const float w = exp2f(mx - M);
+        const float w = mx == kNegInf ? 0.0f : exp2f(mx - m);
         o.x = fmaf(w, t.x, o.x);
         o.y = fmaf(w, t.y, o.y);
         o.z = fmaf(w, t.z, o.z);
@@ -994,33 +996,50 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParam
             lv[u] = j4 == 0 ? r[D + 1] : 0.0f;
             t[u] = reinterpret_cast<const float4 *>(r)[j4];
         }
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < UN; u++)
+            mn = fmaxf(mn, mx[u]);
+        raise_to(mn);
 #pragma unroll
         for (int u = 0; u < UN; u++)
             add(mx[u], t[u], lv[u]);
     }
     for (; c < p.n_chunks; c += NG) {
         const float *r = rec + c * RS;
-        add(r[D], reinterpret_cast<const float4 *>(r)[j4], j4 == 0 ? r[D + 1] : 0.0f);
+        const float mx = r[D];
+        raise_to(fmaxf(m, mx));
+        add(mx, reinterpret_cast<const float4 *>(r)[j4], j4 == 0 ? r[D + 1] : 0.0f);
     }
     reinterpret_cast<float4 *>(part[grp])[j4] = o;
-    if (j4 == 0)
+    if (j4 == 0) {
         lsum[grp] = L;
+        gmax[grp] = m;
+    }
     __syncthreads();
     if (wave == 0) {
         const int sub = lane % P;
+        float M = kNegInf;
+#pragma unroll
+        for (int g2 = 0; g2 < NG; g2++)
+            M = fmaxf(M, gmax[g2]);
+        float gs[NG];  // each group's factor to the common maximum
+#pragma unroll
+        for (int g2 = 0; g2 < NG; g2++)
+            gs[g2] = gmax[g2] == M ? 1.0f : exp2f(gmax[g2] - M);
         float v[kCPL];
 #pragma unroll
         for (int k = 0; k < kCPL; k++) {
             float a = 0.0f;
 #pragma unroll
             for (int g2 = 0; g2 < NG; g2++)
-                a += part[g2][sub * kCPL + k];
+                a = fmaf(gs[g2], part[g2][sub * kCPL + k], a);
             v[k] = a;
         }
         float Lt = 0.0f;
 #pragma unroll
         for (int g2 = 0; g2 < NG; g2++)
-            Lt += lsum[g2];
+            Lt = fmaf(gs[g2], lsum[g2], Lt);
         apply_signs(v, p.signs2[sub]);
         fwht_row<P>(v, sub);
         const float sc = 1.0f / (Lt * sqrtf((float)D));
