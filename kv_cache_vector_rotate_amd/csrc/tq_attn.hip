@@ -106,6 +106,15 @@ __device__ __forceinline__ float lane_xor_any(float v)
         return lane_xor<M>(v);
 }
 
+// x, with its known bits hidden from the compiler: keeps a value built for
+// byte-wise use (fields already shifted into place) from being folded back
+// into its inputs at every use
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x)
+{
+    asm("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
     x = max_across<32>(x);
@@ -690,6 +699,192 @@ __global__ __launch_bounds__(kBlock) void attn_partial_wave_kernel(AttnParams p)
     write_chunk_record<D, G, CPL, AST>(p, acc, m_run, l_part, accs, red_m, red_l, b, h0, chunk);
 }
 
+// ---- One query head per KV head: the row scan.  With a single query the
+// score of a key row is a sum over its coordinate pairs of a value that
+// depends only on the pair's two indices: the workgroup tabulates the
+// query's partial score for every pair position and index pair, (D/2) x
+// 4^BK floats ([Foundry] "Optimization: Fused dequant-dot": the rotated
+// query against centroid values, here taken two coordinates at a time).
+// Each lane then scores one whole row, one LDS read and one add per pair
+// (all lanes of a read address the same table row, so lanes with equal
+// index pairs share a read), and the row's softmax terms are computed once,
+// not on every lane that holds a slice of it.  The V sum
+// keeps the coordinate split of the per-lane scan (P lanes per row, CPL
+// coordinates each); the weights of a wave's 64 rows reach those lanes
+// through a small per-wave LDS buffer.  Wave w takes rows
+// t_begin + 256 i + 64 w + lane of its chunk.
+template <int D, int BK>
+struct RowScan {
+    static constexpr int QN = 1 << (2 * BK);  // table entries per coordinate pair
+    static constexpr bool ON = BK <= 3 || D * QN * 2 <= 32768;  // table <= 32 KB
+};
+
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(kBlock) void attn_partial_row_kernel(AttnParams p)
+{
+    constexpr int QN = RowScan<D, BK>::QN;
+    constexpr int NPAIR = D / 2;
+    constexpr int RBK = D * BK / 8, RBV = D * BV / 8;
+    constexpr int KW = RBK / 4;               // 32-bit words of a key row
+    constexpr int CPL = 16, P = D / CPL;      // V: lanes per row, coordinates per lane
+    constexpr int RPW = 64 / P;               // V: rows per pass of a wave
+    constexpr int NPASS = 64 / RPW;           // V: passes per 64 rows
+    constexpr int WV = Lookup<BV, 1>::W;
+    static_assert(RBK % 8 == 0 && QN <= kBlock, "row scan layout");
+
+    __shared__ float qtab[NPAIR * QN];
+    __shared__ __attribute__((aligned(16))) float tabV[Lookup<BV, 1>::N * WV];
+    __shared__ float qs[1][D];
+    __shared__ float wbuf[kBlock];            // each wave's 64 weights of the current rows
+    __shared__ float red_m[kBlock / 64][1];
+    __shared__ float red_l[kBlock / 64][1];
+    __shared__ __attribute__((aligned(16))) float accs[kBlock / 64 * D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+
+    fill_lookup<BV, 1>(tabV, p.centV);
+    rotate_queries<D, 1>(p, qs, b, g, wave, lane);
+    __syncthreads();
+    {
+        // entry e of pair m: q'[2m] c[e's low BK bits] + q'[2m+1] c[its high
+        // BK bits]; thread t fills the entries e = t % QN of pairs
+        // m = t / QN, + kBlock / QN, ...
+        const int e = tid % QN;
+        const float c0 = p.centK[e & ((1 << BK) - 1)], c1 = p.centK[e >> BK];
+        for (int m = tid / QN; m < NPAIR; m += kBlock / QN)
+            qtab[m * QN + e] = fmaf(qs[0][2 * m + 1], c1, qs[0][2 * m] * c0);
+    }
+    __syncthreads();
+
+    const int sub = lane % P, rig = lane / P;
+    float acc[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; k++)
+        acc[k] = 0.0f;
+    float m_run = -__builtin_huge_valf();  // the wave's running maximum
+    float l_run = 0.0f;                     // this lane's rows' weights
+
+    const int64_t rowbase = ((int64_t)b * p.Hkv + g) * p.window;
+    const uint8_t *kbase = p.kp + rowbase * RBK;
+    const uint8_t *vbase = p.vp + rowbase * RBV;
+    const float *knb = p.kn + rowbase, *vnb = p.vn + rowbase;
+    const int t_begin = chunk * p.chunk_len;
+    const int t_end = min(p.T, t_begin + p.chunk_len);
+    float *wrow = wbuf + wave * 64;
+
+#pragma unroll 1
+    for (int t0 = t_begin + 64 * wave; t0 < t_end; t0 += kBlock) {
+        // this lane's key row and both norms; the V slices of the wave's
+        // NPASS passes; rows past the context read the last row (masked)
+        const int t = t0 + lane;
+        const bool valid = t < t_end;
+        const int tt = valid ? t : t_end - 1;
+        uint32_t kw[KW];
+        {
+            const uint2 *kr = reinterpret_cast<const uint2 *>(kbase + (uint32_t)tt * RBK);
+#pragma unroll
+            for (int i = 0; i < KW / 2; i++) {
+                const uint2 v = kr[i];
+                kw[2 * i] = v.x;
+                kw[2 * i + 1] = v.y;
+            }
+        }
+        const float kn = knb[tt], vn = vnb[tt];
+        uint64_t vb[NPASS];  // CPL * BV bits each
+#pragma unroll
+        for (int j = 0; j < NPASS; j++) {
+            const int tv = min(t0 + j * RPW + rig, t_end - 1);
+            vb[j] = load_slice_bits<BV, CPL>(vbase,
+                                             (uint32_t)tv * RBV + (uint32_t)(sub * (CPL * BV / 8)));
+        }
+        // the row's score (log2 units): pair m's field, shifted to bit 2,
+        // addresses entry e of table row m (row offset in the instruction)
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NPAIR; m++) {
+            constexpr int FW = 2 * BK;
+            const int o = FW * m, wi = o / 32, ob = o % 32;
+            uint32_t f;
+            if (ob + FW > 32)
+                f = __builtin_amdgcn_alignbit(kw[wi + 1], kw[wi], ob - 2);
+            else if (ob >= 2)
+                f = kw[wi] >> (ob - 2);
+            else
+                f = kw[wi] << (2 - ob);
+            const float v = *reinterpret_cast<const float *>(
+                reinterpret_cast<const char *>(qtab + m * QN) + (f & (uint32_t)((QN - 1) << 2)));
+            if (m & 1)
+                s1 += v;
+            else
+                s0 += v;
+        }
+        const float sc = valid ? (s0 + s1) * kn : -__builtin_huge_valf();
+        // running maximum of the wave (lane 0's row is always valid)
+        const float mx = wave_max(sc);
+        if (mx > m_run) {
+            const float fac = exp2f(m_run - mx);  // 0 on the first rows
+            l_run *= fac;
+#pragma unroll
+            for (int k = 0; k < CPL; k++)
+                acc[k] *= fac;
+            m_run = mx;
+        }
+        // weights below 2^-126 flush to 0 (v_exp_f32); invalid rows give 0
+        const float pr = __builtin_amdgcn_exp2f(sc - m_run);
+        l_run += pr;
+        // the weights go to the V lanes through this wave's LDS buffer (one
+        // wave writes and reads it; its LDS accesses complete in order)
+        wrow[lane] = pr * vn;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < NPASS; j++) {
+            const float w = wrow[j * RPW + rig];
+            if constexpr (BV == 2) {
+                // the eight 4-bit pair indices, times the entry size (8
+                // bytes), one to a byte: a table address is one byte extract
+                const uint32_t v32 = (uint32_t)vb[j];  // 32 bits at BV = 2
+                const uint32_t ev = opaque_u32((v32 << 3) & 0x78787878u);  // pairs 0, 2, 4, 6
+                const uint32_t od = opaque_u32((v32 >> 1) & 0x78787878u);  // pairs 1, 3, 5, 7
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    const uint32_t a = __builtin_amdgcn_ubfe(m & 1 ? od : ev, 8 * (m >> 1), 8);
+                    const float2 cv = *reinterpret_cast<const float2 *>(
+                        reinterpret_cast<const char *>(tabV) + a);
+                    acc[2 * m] = fmaf(w, cv.x, acc[2 * m]);
+                    acc[2 * m + 1] = fmaf(w, cv.y, acc[2 * m + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < CPL / WV; m++) {
+                    float cc[WV];
+                    lookup<BV, 1>(tabV, vb[j], m, cc);
+#pragma unroll
+                    for (int q = 0; q < WV; q++)
+                        acc[WV * m + q] = fmaf(w, cc[q], acc[WV * m + q]);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // the chunk record: the epilogue sums each coordinate slice over the
+    // lanes of its rig and expects the weight sum the same way, so the
+    // wave's total goes to the rig-0 lanes
+    float l_tot = l_run;
+    l_tot += lane_xor_any<1>(l_tot);
+    l_tot += lane_xor_any<2>(l_tot);
+    l_tot += lane_xor_any<4>(l_tot);
+    l_tot += lane_xor_any<8>(l_tot);
+    l_tot += lane_xor_any<16>(l_tot);
+    l_tot += lane_xor_any<32>(l_tot);
+    float acc1[1][CPL], m1[1] = {m_run}, l1[1] = {rig == 0 ? l_tot : 0.0f};
+#pragma unroll
+    for (int k = 0; k < CPL; k++)
+        acc1[0][k] = acc[k];
+    write_chunk_record<D, 1, CPL, D>(p, acc1, m1, l1, accs, red_m, red_l, b, g, chunk);
+}
+
 // ---- The sparse-V gate ([Atlas] "Sparse V dequant"): the V row of a slot is
 // loaded and decoded only where the row's weight relative to the largest
 // weight of the context, exp(score - max score), exceeds the threshold;
@@ -1131,7 +1326,12 @@ void launch_attn_wave(int G, dim3 grid, AttnParams p, hipStream_t st)
     dim3 block(kBlock);
     p.gsplit = 1;
     switch (G) {
-    case 1: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1>), grid, block, 0, st, p); break;
+    case 1:
+        if constexpr (RowScan<D, BK>::ON)
+            hipLaunchKernelGGL((attn_partial_row_kernel<D, BK, BV>), grid, block, 0, st, p);
+        else
+            hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 1>), grid, block, 0, st, p);
+        break;
     case 2: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 2>), grid, block, 0, st, p); break;
     case 4: hipLaunchKernelGGL((attn_partial_wave_kernel<D, BK, BV, 4>), grid, block, 0, st, p); break;
     default:

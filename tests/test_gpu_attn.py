@@ -59,7 +59,8 @@ def _oracle(orc, cache, layer, q, b, heads, T, scale, sparse_v=0.0):
 @pytest.mark.parametrize("d,bk,bv,G", [(128, 4, 2, 4), (64, 3, 2, 1), (256, 4, 4, 2),
                                        (128, 2, 3, 8), (256, 3, 2, 8), (64, 4, 4, 2),
                                        (128, 3, 4, 1), (128, 4, 2, 2), (64, 2, 2, 4),
-                                       (256, 2, 3, 1), (256, 4, 2, 4), (64, 4, 2, 8)])
+                                       (256, 2, 3, 1), (256, 4, 2, 4), (64, 4, 2, 8),
+                                       (256, 3, 2, 1), (128, 2, 2, 1)])
 @pytest.mark.parametrize("T", [1, 7, 256, 300, 1100])
 def test_attention_small(tq, orc, d, bk, bv, G, T):
     B, Hkv = 2, 2
