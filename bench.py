@@ -148,6 +148,10 @@ def _known_kernels():
         "decode_kernel<64, 2, false>": ("long_decode_v2_d64", dec_bytes(n5, 64, BV5)),
         "decode_kernel<256, 3, false>": ("long_decode_k3_d256", dec_bytes(n5, 256, BK5)),
         "decode_kernel<256, 2, false>": ("long_decode_v2_d256", dec_bytes(n5, 256, BV5)),
+        "attn_partial_row_kernel<64, 3, 2>":
+            ("long_attn_d64", attn_bytes(1, H5, H5, 64, T5, BK5, BV5)),
+        "attn_partial_row_kernel<256, 3, 2>":
+            ("long_attn_d256", attn_bytes(1, H5, H5, 256, T5, BK5, BV5)),
         "append_kernel<256, float>":
             ("gemma_append", enc_bytes(L2 * B2 * H2, D2, BK2, 4) + enc_bytes(L2 * B2 * H2, D2, BV2, 4)),
     }
