@@ -1143,12 +1143,19 @@ __global__ __launch_bounds__(kBlock) void attn_gated_v_kernel(AttnParams p)
 // rescales its sums when it grows (the log-sum-exp merge of [Foundry]
 // "Optimization: Fused dequant-dot" taken over chunks), and the groups are
 // brought to the common maximum where they meet.
-constexpr int kCombineThreads = 256;
+// Threads per merge workgroup: 512 at head_dim 256 (eight chunk groups), so
+// that a long context's records load in one batch per thread, else 256.
+template <int D>
+constexpr int combine_threads()
+{
+    return D >= 256 ? 512 : 256;
+}
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnParams p)
+__global__ __launch_bounds__(combine_threads<D>()) void attn_combine_kernel(AttnParams p)
 {
-    constexpr int P = D / kCPL, RS = D + 4, Q = D / 4, NG = kCombineThreads / Q;
+    constexpr int CT = combine_threads<D>();
+    constexpr int P = D / kCPL, RS = D + 4, Q = D / 4, NG = CT / Q;
     __shared__ __attribute__((aligned(16))) float part[NG][D];
     __shared__ float lsum[NG], gmax[NG];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1402,7 +1409,7 @@ void launch_attn_d(int BK, int BV, int G, dim3 grid, const AttnParams &p, hipStr
     default: launch_attn_bv<D, 4>(BV, G, grid, p, st); break;
     }
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)(grid.z * p.Hq)),
-                       dim3(kCombineThreads), 0, st, p);
+                       dim3(combine_threads<D>()), 0, st, p);
 }
 
 // Workspace layout: the chunk records [B][Hq][n_chunks][D + 4] floats; with
