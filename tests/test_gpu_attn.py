@@ -76,11 +76,12 @@ def test_attention_small(tq, orc, d, bk, bv, G, T):
             check_attention(o[b, h], ref[h])
 
 
-def test_attention_ring_window_and_scale(tq, orc):
+@pytest.mark.parametrize("d,G,bk,bv", [(128, 4, 4, 2), (256, 1, 3, 2), (64, 1, 3, 2)])
+def test_attention_ring_window_and_scale(tq, orc, d, G, bk, bv):
     """ctx_len beyond the window reads every slot; explicit scale; a peaked
-    softmax (keys x 8)."""
-    d, B, Hkv, G, W = 128, 1, 2, 4, 700
-    cache = tq.TQCache(1, B, Hkv, W, d, 4, 2, SEED)
+    softmax (keys x 8); the exchange scan and the row scan."""
+    B, Hkv, W = 1, 2, 700
+    cache = tq.TQCache(1, B, Hkv, W, d, bk, bv, SEED)
     _fill(tq, cache, 0, 21, kscale=8.0)
     q = (kvgen.normal((B, Hkv * G, d), 22, "cuda") * 2.0).to(torch.bfloat16)
     o = tq.tq_attn_decode(cache, 0, q, 5000, scale=0.3).cpu().numpy()
