@@ -232,6 +232,32 @@ def test_attention_sparse_v_dominant_row_across_chunks(tq, orc, t_dom):
         check_attention(o[0, h], ref[h])
 
 
+@pytest.mark.parametrize("t_dom", [5, 19990])
+def test_attention_dominant_row_one_query_head(tq, orc, t_dom):
+    """One query head per KV head (the row scan) over a 20000-slot context
+    split into 79 chunks per head, with one row whose score leads every other
+    by 10 early or late in the context: the merge's running maximum is set by
+    the first chunk, or raised by the last and every earlier sum rescaled."""
+    d, B, Hkv, G, T, bk, bv = 256, 1, 2, 1, 20000, 3, 2
+    cache = tq.TQCache(1, B, Hkv, T, d, bk, bv, SEED)
+    _fill(tq, cache, 0, 97 + t_dom)
+    kp = cache.k_packed[0][0, 0].cpu().numpy()
+    kn = cache.k_norms[0][0, 0].cpu().numpy()
+    Kh = orc.decode(kp, kn, d, bk, SEED, f64=True)
+    q = kvgen.normal((B, Hkv * G, d), 98, "cuda", torch.bfloat16)
+    q[0, 0] = torch.from_numpy(Kh[t_dom] / np.linalg.norm(Kh[t_dom]) * 3.0).to(torch.bfloat16).cuda()
+    qf = q[0, 0].float().cpu().numpy().astype(np.float64)
+    scale = 1 / math.sqrt(d)
+    s = scale * Kh @ qf
+    f = (np.delete(s, t_dom).max() + 10.0) / s[t_dom]
+    assert f > 1
+    cache.k_norms[0][0, 0, t_dom] *= float(f)
+    o = tq.tq_attn_decode(cache, 0, q, T).cpu().numpy()
+    ref = _oracle(orc, cache, 0, q, 0, range(Hkv * G), T, scale)
+    for h in range(Hkv * G):
+        check_attention(o[0, h], ref[h])
+
+
 def test_config4_attention_sparse_v_sampled(tq, orc):
     """The bench's attention launch with the sparse-V gate at 1e-3, sampled."""
     B, Hq, Hkv, d, T = 32, 32, 8, 128, 16384
